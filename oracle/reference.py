@@ -1,0 +1,49 @@
+"""Plain definitions every tiled / pipelined result must equal (oracle).
+
+* tile copy (global -> LDS -> global): the output equals the input bit for
+  bit; tiling, swizzle, the stage ring and the out-of-bounds fill never reach
+  the output ("copy_async -> tma" and "copy_async -> ldgsts", "Demonstration
+  program": the tile is read back unchanged).
+* elementwise: y[i] = op(inputs[i]) element by element ("elementwise ->
+  smem", "Demonstration program": the tile equals sqrt(A)).
+* streamed elementwise with per-row scalars: for a tensor x whose rows are
+  its innermost runs, y[r, c] = op(a[r], x[r, c], b[r]) with
+  fma = a*x + b, add = x + b, mul = a*x; unary ops ignore a and b.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import ops
+
+
+def tile_copy(x: np.ndarray) -> np.ndarray:
+    return np.array(x, copy=True)
+
+
+def ewise(op: str, inputs, out_dtype) -> np.ndarray:
+    """Elementwise op over equal-shape inputs (fma takes a, b, c -> a*b + c)."""
+    if op == "zero":
+        return ops.zero(np.shape(inputs[0]) if inputs else (), out_dtype)
+    if op in ops.UNARY:
+        return ops.UNARY[op](inputs[0], out_dtype)
+    if op in ops.BINARY:
+        return ops.BINARY[op](inputs[0], inputs[1], out_dtype)
+    if op == "fma":
+        return ops.fma(inputs[0], inputs[1], inputs[2], out_dtype)
+    raise ValueError(f"unknown op {op}")
+
+
+def stream_ewise(op: str, x: np.ndarray, a=None, b=None, out_dtype=np.float32) -> np.ndarray:
+    """y = op(a[row], x, b[row]) with one scalar of a and b per innermost row."""
+    if op in ("zero", "sqrt", "exp"):
+        return ewise(op, [x], out_dtype)
+    a_b = None if a is None else np.asarray(a)[..., None]
+    b_b = None if b is None else np.asarray(b)[..., None]
+    if op == "fma":
+        return ops.fma(a_b, x, b_b, out_dtype)
+    if op == "add":
+        return ops.add(x, b_b, out_dtype)
+    if op == "mul":
+        return ops.mul(a_b, x, out_dtype)
+    raise ValueError(f"unknown op {op}")
