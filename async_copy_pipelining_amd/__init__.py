@@ -1,0 +1,168 @@
+"""Python binding of the acp C ABI (``include/acp.h``): argument marshalling only.
+
+Every function has the name of the C entry point it wraps and forwards to it
+through ctypes; all work happens in ``libacp.so`` (hand-written HIP kernels
+for gfx950).  Pointer arguments accept an ``int`` device address or any
+object with ``data_ptr()`` (a torch tensor); stream arguments accept an
+``int`` handle or an object with ``cuda_stream`` (a torch stream).  A non-OK
+status raises ``AcpError`` carrying the status and ``acp_last_error()``.
+
+Importing this package fails when ``libacp.so`` has not been built: there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libacp.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m async_copy_pipelining_amd.build` "
+        "(the HIP library is the only implementation)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# acp_status
+ACP_OK, ACP_ERR_INVALID, ACP_ERR_DECLINED, ACP_ERR_UNSUPPORTED, ACP_ERR_LDS, ACP_ERR_HIP = range(6)
+STATUS_NAMES = {0: "OK", 1: "INVALID", 2: "DECLINED", 3: "UNSUPPORTED", 4: "LDS", 5: "HIP"}
+# acp_dtype
+ACP_U8, ACP_U16, ACP_U32, ACP_U64, ACP_F16, ACP_F32 = range(6)
+DTYPES = {"u8": ACP_U8, "u16": ACP_U16, "u32": ACP_U32, "u64": ACP_U64, "f16": ACP_F16, "f32": ACP_F32}
+# acp_swizzle / acp_oob
+ACP_SWIZZLE_NONE, ACP_SWIZZLE_128B = 0, 3
+ACP_OOB_ZERO = 0
+# acp_op
+ACP_OP_ZERO, ACP_OP_SQRT, ACP_OP_EXP, ACP_OP_ADD, ACP_OP_MUL, ACP_OP_FMA, ACP_OP_COPY = range(7)
+OPS = {"zero": ACP_OP_ZERO, "sqrt": ACP_OP_SQRT, "exp": ACP_OP_EXP, "add": ACP_OP_ADD,
+       "mul": ACP_OP_MUL, "fma": ACP_OP_FMA, "copy": ACP_OP_COPY}
+ACP_MAX_RANK = 5
+
+
+class AcpError(RuntimeError):
+    def __init__(self, status: int, reason: str):
+        super().__init__(f"acp {STATUS_NAMES.get(status, status)}: {reason}")
+        self.status = status
+        self.reason = reason
+
+
+class acp_tile_desc(ctypes.Structure):
+    _fields_ = [("opaque", ctypes.c_ubyte * 256)]
+
+
+class acp_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("rank", ctypes.c_int32), ("desc_elem_bytes", ctypes.c_int32),
+        ("dims", ctypes.c_int64 * ACP_MAX_RANK), ("strides", ctypes.c_int64 * ACP_MAX_RANK),
+        ("box", ctypes.c_int32 * ACP_MAX_RANK),
+        ("issues", ctypes.c_int32), ("n_issue_axes", ctypes.c_int32), ("n_image_axes", ctypes.c_int32),
+        ("swizzle", ctypes.c_int32), ("promoted", ctypes.c_int32),
+        ("threads", ctypes.c_int32), ("vec", ctypes.c_int32), ("vec_bytes", ctypes.c_int32),
+        ("outer", ctypes.c_int32), ("tile_bytes", ctypes.c_int64), ("n_tiles", ctypes.c_int64),
+    ]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_DESC_P = ctypes.POINTER(acp_tile_desc)
+
+_SIGS = {
+    "acp_abi_version": ([], _I),
+    "acp_last_error": ([], ctypes.c_char_p),
+    "acp_encode_tiled": ([_DESC_P, _I, _I, _P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                          ctypes.POINTER(ctypes.c_int32), _I, _I], _I),
+    "acp_plan_query": ([_DESC_P, _I, _I, ctypes.POINTER(acp_plan_info)], _I),
+    "acp_tile_copy": ([_DESC_P, _DESC_P, _I, _P], _I),
+    "acp_tile_ewise": ([_I, _DESC_P, ctypes.POINTER(_DESC_P), _I, _I, _P], _I),
+    "acp_stream_ewise": ([_I, _DESC_P, _DESC_P, _P, _P, ctypes.POINTER(ctypes.c_int32), _I, _I, _I, _P], _I),
+    "acp_debug_lds_image": ([_DESC_P, ctypes.c_int64, _I, _P, _P], _I),
+    "acp_debug_ring_trace": ([_I, _I, _I, _I, _P, _P], _I),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    return int(x)
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        return None
+    if hasattr(s, "cuda_stream"):
+        return int(s.cuda_stream)
+    return int(s)
+
+
+def _check(status: int) -> None:
+    if status != ACP_OK:
+        raise AcpError(status, _lib.acp_last_error().decode())
+
+
+def acp_abi_version() -> int:
+    return int(_lib.acp_abi_version())
+
+
+def acp_last_error() -> str:
+    return _lib.acp_last_error().decode()
+
+
+def acp_encode_tiled(dtype, gbase, shape, strides, box, swizzle=ACP_SWIZZLE_NONE, oob=ACP_OOB_ZERO) -> acp_tile_desc:
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    r = len(shape)
+    d = acp_tile_desc()
+    _check(_lib.acp_encode_tiled(ctypes.byref(d), dt, r, _ptr(gbase), (ctypes.c_int64 * r)(*shape),
+                                 (ctypes.c_int64 * r)(*strides), (ctypes.c_int32 * r)(*box), int(swizzle), int(oob)))
+    return d
+
+
+def acp_plan_query(desc: acp_tile_desc, threads: int = 0, copy_only: bool = True) -> dict:
+    info = acp_plan_info()
+    _check(_lib.acp_plan_query(ctypes.byref(desc), int(threads), 1 if copy_only else 0, ctypes.byref(info)))
+    r = info.rank
+    return {
+        "rank": r, "desc_elem_bytes": info.desc_elem_bytes,
+        "dims": list(info.dims[:r]), "strides": list(info.strides[:r]), "box": list(info.box[:r]),
+        "issues": info.issues, "n_issue_axes": info.n_issue_axes, "n_image_axes": info.n_image_axes,
+        "swizzle": info.swizzle, "promoted": bool(info.promoted), "threads": info.threads,
+        "vec": info.vec, "vec_bytes": info.vec_bytes, "outer": info.outer,
+        "tile_bytes": info.tile_bytes, "n_tiles": info.n_tiles,
+    }
+
+
+def acp_tile_copy(src: acp_tile_desc, dst: acp_tile_desc, threads: int, stream=None) -> None:
+    _check(_lib.acp_tile_copy(ctypes.byref(src), ctypes.byref(dst), int(threads), _stream(stream)))
+
+
+def acp_tile_ewise(op, out: acp_tile_desc, ins, threads: int, stream=None) -> None:
+    opc = OPS[op] if isinstance(op, str) else int(op)
+    arr = (_DESC_P * max(1, len(ins)))(*[ctypes.pointer(d) for d in ins])
+    _check(_lib.acp_tile_ewise(opc, ctypes.byref(out), arr, len(ins), int(threads), _stream(stream)))
+
+
+def acp_stream_ewise(op, out: acp_tile_desc, x: acp_tile_desc, row_a, row_b, stage_box, stages: int,
+                     threads: int, workgroups: int = 0, stream=None) -> None:
+    opc = OPS[op] if isinstance(op, str) else int(op)
+    sb = (ctypes.c_int32 * len(stage_box))(*stage_box)
+    _check(_lib.acp_stream_ewise(opc, ctypes.byref(out), ctypes.byref(x), _ptr(row_a), _ptr(row_b), sb,
+                                 int(stages), int(threads), int(workgroups), _stream(stream)))
+
+
+def acp_debug_lds_image(src: acp_tile_desc, tile_index: int, threads: int, out_bytes, stream=None) -> None:
+    _check(_lib.acp_debug_lds_image(ctypes.byref(src), int(tile_index), int(threads), _ptr(out_bytes),
+                                    _stream(stream)))
+
+
+def acp_debug_ring_trace(n_iters: int, stages: int, loads: int, stores: int, out_events, stream=None) -> None:
+    _check(_lib.acp_debug_ring_trace(int(n_iters), int(stages), int(loads), int(stores), _ptr(out_events),
+                                     _stream(stream)))

@@ -1,0 +1,510 @@
+// C ABI of acp: argument validation, planning and kernel launch.
+//
+// Every entry point returns an acp_status and records a reason string for
+// acp_last_error() (the pages' dispatch predicates return an (ok, reason)
+// pair: "copy_async -> tma", "What it accepts"; "elementwise -> smem",
+// "What it accepts").  Planning is pure host code; compute calls enqueue one
+// kernel on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "acp.h"
+#include "acp_engine.hpp"
+#include "acp_plan.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+acp_status ret(acp_status s, const std::string& why = std::string()) {
+  g_last_error = (s == ACP_OK) ? std::string() : why;
+  return s;
+}
+
+acp_status from_plan(acp::PlanStatus s, const std::string& why) {
+  if (s == acp::PlanStatus::Invalid) return ret(ACP_ERR_INVALID, why);
+  if (s == acp::PlanStatus::Declined) return ret(ACP_ERR_DECLINED, why);
+  return ACP_OK;
+}
+
+bool load_desc(const acp_tile_desc* d, acp::DescData* out) {
+  if (!d) return false;
+  std::memcpy(out, d->opaque, sizeof(acp::DescData));
+  return out->magic == acp::kDescMagic;
+}
+
+bool same_geometry(const acp::DescData& a, const acp::DescData& b, bool strides) {
+  if (a.rank != b.rank) return false;
+  for (int d = 0; d < a.rank; ++d) {
+    if (a.shape[d] != b.shape[d] || a.box[d] != b.box[d]) return false;
+    if (strides && a.strides[d] != b.strides[d]) return false;
+  }
+  return true;
+}
+
+int log2i(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+int device_lds_limit() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 65536;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) return 65536;
+  return v;
+}
+
+bool xcd_remap_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("ACP_XCD_REMAP");
+    return !(e && e[0] == '0');
+  }();
+  return on;
+}
+
+// Everything one launch of the engine needs.
+struct Launch {
+  acp::EngineArgs args;
+  acp::KernelKey key;
+  unsigned grid = 0, block = 0, lds = 0;
+  int64_t n_tiles = 0;
+};
+
+struct EngineRequest {
+  int op;                      // acp_op
+  int mode;                    // 0 copy, 1 tile ewise, 2 stream
+  const acp::DescData* x;      // layout of every staged operand
+  const acp::DescData* out;
+  const void* in_ptrs[3];
+  int n_in;
+  const int32_t* stage_box;    // per dim of x
+  int stages, threads, workgroups;
+  const float* row_a;
+  const float* row_b;
+  bool row_ops;
+  bool copy_only;
+};
+
+acp_status prepare(const EngineRequest& q, Launch* L) {
+  const acp::DescData& x = *q.x;
+  const acp::DescData& o = *q.out;
+  const int r = x.rank;
+  std::string why;
+  acp::Plan p;
+  acp::PlanStatus ps = acp::plan_box_with(x, q.stage_box, q.copy_only, &p, &why);
+  if (ps != acp::PlanStatus::Ok) return from_plan(ps, why);
+
+  uint64_t align = 0;
+  for (int k = 0; k < q.n_in; ++k) align |= reinterpret_cast<uint64_t>(q.in_ptrs[k]);
+  if (q.mode == 1 && q.n_in == 0) align |= x.gbase;
+  ps = acp::plan_partition(&p, q.threads, align, &why);
+  if (ps != acp::PlanStatus::Ok) return from_plan(ps, why);
+
+  const int ei = x.esize, eo = o.esize;
+  // The output side stores vec * eo bytes per round: its base and strides
+  // must honour that width (capped at 16), else fall back to 4-byte rounds.
+  auto out_ok = [&](int vb) {
+    const int64_t ob = static_cast<int64_t>(vb) / ei * eo;
+    const int64_t need = ob >= 16 ? 16 : ob;
+    if (o.gbase % static_cast<uint64_t>(need)) return false;
+    for (int d = 0; d + 1 < r; ++d)
+      if ((o.strides[d] * eo) % need) return false;
+    if ((o.shape[r - 1] * eo) % need) return false;
+    return true;
+  };
+  if (!out_ok(p.vec_bytes)) {
+    if (p.vec_bytes == 16 && (p.tile_bytes() % (static_cast<int64_t>(q.threads) * 4)) == 0 && out_ok(4)) {
+      p.vec_bytes = 4;
+      p.vec = 4 / ei;
+      p.outer = static_cast<int>(p.tile_bytes() / (static_cast<int64_t>(q.threads) * 4));
+    } else {
+      return ret(ACP_ERR_DECLINED, "output base or strides are not aligned to the chosen vector width");
+    }
+  }
+  if (q.mode != 0 && p.vec_bytes < ei) return ret(ACP_ERR_DECLINED, "vector narrower than one element");
+  if (q.mode != 0 && (p.vec_bytes / ei) * eo < 2) return ret(ACP_ERR_UNSUPPORTED, "output chunk below 2 bytes");
+  if (p.outer > acp::kMaxOuter)
+    return ret(ACP_ERR_UNSUPPORTED, "staged tile needs more than 8 rounds per thread; use more threads or a smaller box");
+  if (p.tile_bytes() >= (int64_t(1) << 31)) return ret(ACP_ERR_UNSUPPORTED, "staged tile too large");
+
+  acp::EngineArgs& A = L->args;
+  std::memset(&A, 0, sizeof(A));
+  for (int k = 0; k < q.n_in; ++k) A.in[k] = static_cast<const char*>(q.in_ptrs[k]);
+  A.out = reinterpret_cast<char*>(o.gbase);
+  A.row_a = q.row_a ? q.row_a : q.row_b;
+  A.row_b = q.row_b ? q.row_b : q.row_a;
+  A.rank = r;
+
+  // packed strides of the row array (shape[:-1]) and of a stage's rows
+  int64_t rowstride[acp::kDims] = {};
+  int64_t srow[acp::kDims] = {};
+  int64_t rs = 1, n_rows = 1;
+  for (int d = r - 2; d >= 0; --d) {
+    rowstride[d] = rs;
+    rs *= x.shape[d];
+    srow[d] = n_rows;
+    n_rows *= q.stage_box[d];
+  }
+
+  int64_t n_tiles = 1, subs = 1, max_x = 0, max_o = 0;
+  int64_t xstride[acp::kDims] = {}, ostride[acp::kDims] = {};
+  int n_partial = 0;
+  for (int d = 0; d < acp::kDims; ++d) A.pslot_of_dim[d] = -1;
+  for (int s = 0; s < acp::kPartial; ++s) A.prem[s] = 0xFFFFFFFFu;
+  for (int d = 0; d < r; ++d) {
+    const int64_t sb = q.stage_box[d];
+    if (x.box[d] % sb != 0) return ret(ACP_ERR_INVALID, "stage box must divide the descriptor box in every dim");
+    const int64_t nst = (x.shape[d] + sb - 1) / sb;
+    const int64_t sub = x.box[d] / sb;
+    const int64_t tg = (nst + sub - 1) / sub;
+    xstride[d] = x.strides[d] * ei;
+    ostride[d] = o.strides[d] * eo;
+    A.sbox[d] = static_cast<uint32_t>(sb);
+    A.nst[d] = static_cast<uint32_t>(nst);
+    const int64_t rem = nst ? x.shape[d] - (nst - 1) * sb : sb;
+    if (rem < sb) {
+      if (n_partial == acp::kPartial)
+        return ret(ACP_ERR_UNSUPPORTED, "more than 4 dims end in a partial stage");
+      A.pslot_of_dim[d] = n_partial;
+      A.prem[n_partial] = static_cast<uint32_t>(rem);
+      ++n_partial;
+    }
+    A.sub[d] = static_cast<uint32_t>(sub);
+    acp::magic_for(A.sub[d], &A.sub_mag[d], &A.sub_sh[d]);
+    A.tgrid[d] = static_cast<uint32_t>(tg ? tg : 1);
+    acp::magic_for(A.tgrid[d], &A.tg_mag[d], &A.tg_sh[d]);
+    A.xstep[d] = sb * xstride[d];
+    A.ostep[d] = sb * ostride[d];
+    A.rstep[d] = d < r - 1 ? sb * rowstride[d] : 0;
+    max_x += (sb - 1) * xstride[d];
+    max_o += (sb - 1) * ostride[d];
+    n_tiles *= tg;
+    subs *= sub;
+  }
+  // bytes from each tensor's base to one past its last element
+  auto span = [&](const acp::DescData& t) -> uint64_t {
+    uint64_t last = 0;
+    for (int d = 0; d < t.rank; ++d) {
+      if (t.shape[d] == 0) return 0;
+      last += static_cast<uint64_t>(t.shape[d] - 1) * static_cast<uint64_t>(t.strides[d]) * t.esize;
+    }
+    return last + t.esize;
+  };
+  A.in_span = span(x);
+  A.out_span = span(o);
+  A.total_rows = static_cast<uint64_t>(rs);
+  if (max_x + 16 >= (int64_t(1) << 31) || max_o + 32 >= (int64_t(1) << 31))
+    return ret(ACP_ERR_UNSUPPORTED, "a stage spans more than 2 GiB");
+  if (n_tiles * subs >= (int64_t(1) << 31)) return ret(ACP_ERR_UNSUPPORTED, "more than 2^31 stages");
+  A.n_tiles = static_cast<uint32_t>(n_tiles);
+  A.subs = static_cast<uint32_t>(subs);
+  acp::magic_for(A.subs, &A.subs_mag, &A.subs_sh);
+  L->n_tiles = n_tiles;
+
+  const std::vector<acp::Axis> axes = p.image_axes();
+  A.n_axes = static_cast<int>(axes.size());
+  for (size_t k = 0; k < axes.size(); ++k) {
+    const int d = axes[k].dim;
+    A.ax_count[k] = static_cast<uint32_t>(axes[k].count);
+    acp::magic_for(A.ax_count[k], &A.ax_mag[k], &A.ax_sh[k]);
+    A.ax_step[k] = static_cast<uint32_t>(axes[k].step);
+    A.ax_xs[k] = static_cast<uint32_t>(axes[k].step * xstride[d]);
+    A.ax_os[k] = static_cast<uint32_t>(axes[k].step * ostride[d]);
+    A.ax_rs[k] = d < r - 1 ? static_cast<uint32_t>(axes[k].step * srow[d]) : 0u;
+    A.ax_pslot[k] = A.pslot_of_dim[d];
+  }
+  A.esize_log2 = log2i(ei);
+  A.outer = p.outer;
+  A.waves = q.threads / 64;
+  A.swizzle = x.swizzle == 3 ? 1 : 0;
+  A.n_in = q.n_in;
+
+  const int64_t in_img = align_up(p.tile_bytes(), 1024);
+  const int64_t out_img = q.mode == 1 ? align_up(p.tile_elems() * eo, 1024) : 0;
+  A.in_image_bytes = static_cast<uint32_t>(in_img);
+  A.out_image_off = static_cast<uint32_t>(q.n_in * in_img);
+  A.ab_off = static_cast<uint32_t>(q.n_in * in_img + out_img);
+  A.row_ops = q.row_ops ? 1 : 0;
+  if (q.row_ops) {
+    if (n_rows > 64) return ret(ACP_ERR_UNSUPPORTED, "per-row scalars need at most 64 rows per stage");
+    A.n_rows = static_cast<int32_t>(n_rows);
+    A.ab_instr = static_cast<int32_t>((n_rows + 31) / 32);
+    A.ab_wave_bytes = static_cast<uint32_t>(A.ab_instr * 256);
+  }
+  const int64_t slot = align_up(A.ab_off + (q.row_ops ? A.waves * A.ab_wave_bytes : 0), 1024);
+  A.slot_bytes = static_cast<uint32_t>(slot);
+
+  const int64_t trips_max = subs * ((q.workgroups > 0 && q.workgroups < n_tiles)
+                                        ? (n_tiles + q.workgroups - 1) / q.workgroups : 1);
+  const int slots = static_cast<int>(q.stages < trips_max ? q.stages : trips_max);
+  A.stages = slots < 1 ? 1 : slots;
+  const int64_t lds = slot * A.stages;
+  const int limit = device_lds_limit();
+  if (lds > limit)
+    return ret(ACP_ERR_LDS, "ring needs " + std::to_string(lds) + " bytes of LDS, device allows " +
+                                std::to_string(limit));
+
+  unsigned grid = static_cast<unsigned>(n_tiles);
+  if (q.workgroups > 0) grid = static_cast<unsigned>(q.workgroups);
+  A.xcd_remap = (q.workgroups > 0 && grid % 8 == 0 && xcd_remap_enabled()) ? 1 : 0;
+  L->grid = grid;
+  L->block = static_cast<unsigned>(q.threads);
+  L->lds = static_cast<unsigned>(lds);
+  L->key = acp::KernelKey{q.op, q.mode == 0 ? ACP_U32 : static_cast<int>(x.dtype),
+                          q.mode == 0 ? ACP_U32 : static_cast<int>(o.dtype), p.vec_bytes, q.mode};
+  return ACP_OK;
+}
+
+acp_status launch(const Launch& L, void* stream) {
+  if (L.n_tiles == 0) return ret(ACP_OK);
+  const void* k = acp::engine_kernel(L.key);
+  if (!k) return ret(ACP_ERR_UNSUPPORTED, "op / dtype combination is not in the registry");
+  const hipError_t e = acp::engine_launch(k, L.args, L.grid, L.block, L.lds, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ret(ACP_OK);
+}
+
+bool is_float(int dt) { return dt == ACP_F16 || dt == ACP_F32; }
+
+}  // namespace
+
+extern "C" {
+
+int acp_abi_version(void) { return ACP_ABI_VERSION; }
+
+const char* acp_last_error(void) { return g_last_error.c_str(); }
+
+acp_status acp_encode_tiled(acp_tile_desc* out, acp_dtype dtype, int rank, const void* gbase,
+                            const int64_t* shape, const int64_t* strides, const int32_t* box,
+                            acp_swizzle swizzle, acp_oob oob) {
+  if (!out || !shape || !strides || !box) return ret(ACP_ERR_INVALID, "null argument");
+  if (!gbase) return ret(ACP_ERR_INVALID, "null tensor address");
+  const int es = acp::dtype_size(dtype);
+  if (es < 0) return ret(ACP_ERR_INVALID, "unknown dtype");
+  if (rank < 1 || rank > ACP_MAX_INPUT_RANK) return ret(ACP_ERR_INVALID, "rank must be 1..8");
+  if (swizzle != ACP_SWIZZLE_NONE && swizzle != ACP_SWIZZLE_128B) return ret(ACP_ERR_INVALID, "unknown swizzle");
+  if (oob != ACP_OOB_ZERO) return ret(ACP_ERR_INVALID, "unknown out-of-bounds fill");
+  acp::DescData d;
+  std::memset(&d, 0, sizeof(d));
+  d.magic = acp::kDescMagic;
+  d.dtype = static_cast<uint8_t>(dtype);
+  d.esize = static_cast<uint8_t>(es);
+  d.rank = static_cast<uint8_t>(rank);
+  d.swizzle = static_cast<uint8_t>(swizzle);
+  d.oob = static_cast<uint8_t>(oob);
+  d.gbase = reinterpret_cast<uint64_t>(gbase);
+  for (int k = 0; k < rank; ++k) {
+    if (shape[k] < 0 || strides[k] < 1 || box[k] < 1)
+      return ret(ACP_ERR_INVALID, "extents must be >= 0, strides and box >= 1");
+    d.shape[k] = shape[k];
+    d.strides[k] = strides[k];
+    d.box[k] = box[k];
+  }
+  acp::Plan p;
+  std::string why;
+  const acp::PlanStatus ps = acp::plan_box(d, true, &p, &why);
+  if (ps != acp::PlanStatus::Ok) return from_plan(ps, why);
+  std::memset(out->opaque, 0, sizeof(out->opaque));
+  std::memcpy(out->opaque, &d, sizeof(d));
+  return ret(ACP_OK);
+}
+
+acp_status acp_plan_query(const acp_tile_desc* desc, int threads, int copy_only, acp_plan_info* out) {
+  acp::DescData d;
+  if (!out || !load_desc(desc, &d)) return ret(ACP_ERR_INVALID, "not an encoded descriptor");
+  acp::Plan p;
+  std::string why;
+  acp::PlanStatus ps = acp::plan_box(d, copy_only != 0, &p, &why);
+  if (ps != acp::PlanStatus::Ok) return from_plan(ps, why);
+  if (threads) {
+    ps = acp::plan_partition(&p, threads, d.gbase, &why);
+    if (ps != acp::PlanStatus::Ok) return from_plan(ps, why);
+  }
+  std::memset(out, 0, sizeof(*out));
+  out->rank = static_cast<int32_t>(p.dims.size());
+  out->desc_elem_bytes = p.desc_esize;
+  for (int k = 0; k < out->rank; ++k) {
+    const acp::DescDim& dd = p.dims[p.dims.size() - 1 - k];
+    out->dims[k] = dd.extent;
+    out->strides[k] = dd.stride;
+    out->box[k] = static_cast<int32_t>(dd.box);
+  }
+  out->issues = static_cast<int32_t>(p.issues());
+  out->n_issue_axes = static_cast<int32_t>(p.issue_axes.size());
+  out->n_image_axes = static_cast<int32_t>(p.image_axes().size());
+  out->swizzle = p.swizzle;
+  out->promoted = p.promoted ? 1 : 0;
+  out->threads = p.threads;
+  out->vec = p.vec;
+  out->vec_bytes = p.vec_bytes;
+  out->outer = p.outer;
+  out->tile_bytes = p.tile_bytes();
+  out->n_tiles = p.n_tiles();
+  return ret(ACP_OK);
+}
+
+acp_status acp_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, int threads, void* hip_stream) {
+  acp::DescData s, d;
+  if (!load_desc(src, &s) || !load_desc(dst, &d)) return ret(ACP_ERR_INVALID, "not an encoded descriptor");
+  // validate_copy_op: both sides laid out, equal dtype, equal extents
+  if (s.dtype != d.dtype) return ret(ACP_ERR_INVALID, "not a valid copy op: dtypes differ");
+  if (!same_geometry(s, d, false)) return ret(ACP_ERR_INVALID, "not a valid copy op: shapes or boxes differ");
+  if (s.gbase == d.gbase) return ret(ACP_ERR_INVALID, "source and destination are the same tensor");
+  EngineRequest q{};
+  q.op = ACP_OP_COPY;
+  q.mode = 0;
+  q.x = &s;
+  q.out = &d;
+  q.in_ptrs[0] = reinterpret_cast<const void*>(s.gbase);
+  q.n_in = 1;
+  q.stage_box = s.box;
+  q.stages = 1;
+  q.threads = threads;
+  q.copy_only = true;
+  Launch L;
+  const acp_status st = prepare(q, &L);
+  if (st != ACP_OK) return st;
+  return launch(L, hip_stream);
+}
+
+acp_status acp_tile_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_desc* const* in, int n_in,
+                          int threads, void* hip_stream) {
+  acp::DescData o;
+  if (!load_desc(out, &o)) return ret(ACP_ERR_INVALID, "not an encoded output descriptor");
+  int need = -1;
+  switch (op) {
+    case ACP_OP_ZERO: need = n_in <= 1 ? n_in : -1; break;
+    case ACP_OP_SQRT: case ACP_OP_EXP: need = 1; break;
+    case ACP_OP_ADD: case ACP_OP_MUL: need = 2; break;
+    case ACP_OP_FMA: need = 3; break;
+    default: return ret(ACP_ERR_INVALID, "unknown op for tile_ewise");
+  }
+  if (need != n_in) return ret(ACP_ERR_INVALID, "wrong number of operands for the op");
+  if (n_in > 0 && !in) return ret(ACP_ERR_INVALID, "null operand list");
+  acp::DescData ins[3];
+  for (int k = 0; k < n_in; ++k) {
+    if (!load_desc(in[k], &ins[k])) return ret(ACP_ERR_INVALID, "not an encoded operand descriptor");
+    if (!same_geometry(ins[k], ins[0], true) || ins[k].dtype != ins[0].dtype || ins[k].swizzle != ins[0].swizzle)
+      return ret(ACP_ERR_INVALID, "operands must share one layout (dtype, shape, strides, box, swizzle)");
+  }
+  const acp::DescData& anchor = n_in ? ins[0] : o;
+  if (!same_geometry(anchor, o, false)) return ret(ACP_ERR_INVALID, "output shape or box differs from the operands");
+  const int ti = anchor.dtype, to = o.dtype;
+  if (!is_float(ti) || !is_float(to)) return ret(ACP_ERR_UNSUPPORTED, "elementwise ops take float16 or float32");
+  if ((op == ACP_OP_ADD || op == ACP_OP_MUL || op == ACP_OP_FMA || op == ACP_OP_ZERO) && ti != to)
+    return ret(ACP_ERR_UNSUPPORTED, "this op keeps the operand type");
+  EngineRequest q{};
+  q.op = op;
+  q.mode = 1;
+  q.x = &anchor;
+  q.out = &o;
+  for (int k = 0; k < n_in; ++k) q.in_ptrs[k] = reinterpret_cast<const void*>(ins[k].gbase);
+  q.n_in = n_in;
+  q.stage_box = anchor.box;
+  q.stages = 1;
+  q.threads = threads;
+  q.copy_only = false;
+  Launch L;
+  const acp_status st = prepare(q, &L);
+  if (st != ACP_OK) return st;
+  return launch(L, hip_stream);
+}
+
+acp_status acp_stream_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_desc* x, const float* row_a,
+                            const float* row_b, const int32_t* stage_box, int stages, int threads, int workgroups,
+                            void* hip_stream) {
+  acp::DescData xd, od;
+  if (!load_desc(x, &xd) || !load_desc(out, &od)) return ret(ACP_ERR_INVALID, "not an encoded descriptor");
+  if (!stage_box) return ret(ACP_ERR_INVALID, "null stage box");
+  if (stages < 2 || stages > 4) return ret(ACP_ERR_INVALID, "stages must be 2, 3 or 4");
+  if (workgroups < 0) return ret(ACP_ERR_INVALID, "workgroups must be >= 0");
+  if (!same_geometry(xd, od, false)) return ret(ACP_ERR_INVALID, "output shape or box differs from x");
+  if (xd.gbase == od.gbase) return ret(ACP_ERR_INVALID, "in-place streaming is not supported");
+  for (int d = 0; d < xd.rank; ++d)
+    if (stage_box[d] < 1) return ret(ACP_ERR_INVALID, "stage box must be >= 1");
+  bool row_ops = false;
+  switch (op) {
+    case ACP_OP_ZERO: case ACP_OP_SQRT: case ACP_OP_EXP:
+      if (!is_float(xd.dtype) || !is_float(od.dtype))
+        return ret(ACP_ERR_UNSUPPORTED, "elementwise ops take float16 or float32");
+      if (op == ACP_OP_ZERO && xd.dtype != od.dtype) return ret(ACP_ERR_UNSUPPORTED, "zero keeps the type");
+      break;
+    case ACP_OP_ADD: case ACP_OP_MUL: case ACP_OP_FMA:
+      if (xd.dtype != ACP_F32 || od.dtype != ACP_F32)
+        return ret(ACP_ERR_UNSUPPORTED, "per-row ops take float32 x and output");
+      if ((op != ACP_OP_ADD && !row_a) || (op != ACP_OP_MUL && !row_b))
+        return ret(ACP_ERR_INVALID, "missing per-row scalar array");
+      row_ops = true;
+      break;
+    default: return ret(ACP_ERR_INVALID, "unknown op for stream_ewise");
+  }
+  if (xd.rank < 2 && row_ops) return ret(ACP_ERR_INVALID, "per-row scalars need rank >= 2");
+  EngineRequest q{};
+  q.op = op;
+  q.mode = 2;
+  q.x = &xd;
+  q.out = &od;
+  q.in_ptrs[0] = reinterpret_cast<const void*>(xd.gbase);
+  q.n_in = 1;
+  q.stage_box = stage_box;
+  q.stages = stages;
+  q.threads = threads;
+  q.workgroups = workgroups;
+  q.row_a = row_a;
+  q.row_b = row_b;
+  q.row_ops = row_ops;
+  q.copy_only = false;
+  Launch L;
+  const acp_status st = prepare(q, &L);
+  if (st != ACP_OK) return st;
+  return launch(L, hip_stream);
+}
+
+acp_status acp_debug_lds_image(const acp_tile_desc* src, int64_t tile_index, int threads, void* out_bytes,
+                               void* hip_stream) {
+  acp::DescData s;
+  if (!load_desc(src, &s) || !out_bytes) return ret(ACP_ERR_INVALID, "bad descriptor or output");
+  EngineRequest q{};
+  q.op = ACP_OP_COPY;
+  q.mode = 0;
+  q.x = &s;
+  q.out = &s;
+  q.in_ptrs[0] = reinterpret_cast<const void*>(s.gbase);
+  q.n_in = 1;
+  q.stage_box = s.box;
+  q.stages = 1;
+  q.threads = threads;
+  q.copy_only = true;
+  Launch L;
+  const acp_status st = prepare(q, &L);
+  if (st != ACP_OK) return st;
+  if (tile_index < 0 || tile_index >= L.n_tiles) return ret(ACP_ERR_INVALID, "tile index out of range");
+  L.args.tile0 = static_cast<uint32_t>(tile_index);
+  acp::Plan p;
+  std::string why;
+  acp::plan_box(s, true, &p, &why);
+  const hipError_t e = acp::lds_image_launch(acp::lds_image_kernel(L.key.vec_bytes), L.args, L.block, L.lds,
+                                             out_bytes, static_cast<uint32_t>(p.tile_bytes()),
+                                             static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ret(ACP_OK);
+}
+
+acp_status acp_debug_ring_trace(int n_iters, int stages, int loads, int stores, int32_t* out_events,
+                                void* hip_stream) {
+  if (!out_events || n_iters < 0 || stages < 1 || stages > 4 || loads < 0 || stores < 0)
+    return ret(ACP_ERR_INVALID, "bad ring trace arguments");
+  if (n_iters == 0) return ret(ACP_OK);
+  const hipError_t e = acp::ring_trace_launch(n_iters, stages, loads, stores, out_events,
+                                              static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ret(ACP_OK);
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Launch contract between the host API and the stage-ring engine kernels.
+//
+// One engine runs all three operations: a workgroup walks "trips" (one staged
+// sub-box each) through a ring of LDS slots.  tile_copy and tile_ewise run
+// one trip per workgroup in a single slot; stream_ewise runs a 2..4-slot ring
+// over many trips ("Add TMA support for circular buffering pass", "Loop
+// Structure").  Every field is computed on the host by the planner.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace acp {
+
+constexpr int kDims = 8;       // tensor dims the engine indexes
+constexpr int kAxes = 12;      // LDS-image axes
+constexpr int kMaxOuter = 8;   // rounds per thread per trip
+constexpr int kPartial = 4;    // dims that may end in a partial stage
+constexpr uint32_t kOobOffset = 0x80000000u;  // buffer offset past num_records: loads 0, stores dropped
+
+struct EngineArgs {
+  const char* in[3];   // staged operands (same layout)
+  char* out;
+  const float* row_a;  // per-row scalars (row ops), never null when staged
+  const float* row_b;
+  // per tensor dim d < rank
+  int64_t xstep[kDims];      // input bytes per stage step along d
+  int64_t ostep[kDims];      // output bytes per stage step along d
+  int64_t rstep[kDims];      // packed rows per stage step along d (d < rank-1)
+  uint32_t sbox[kDims];      // stage box
+  uint32_t nst[kDims];       // stages covering the tensor along d
+  uint32_t sub[kDims], sub_mag[kDims], sub_sh[kDims];   // stages per tile along d
+  uint32_t tgrid[kDims], tg_mag[kDims], tg_sh[kDims];   // tiles along d
+  int32_t pslot_of_dim[kDims];  // partial-stage slot of dim d, -1 if its stages are all full
+  // partial slots: dims whose last stage is cut by the tensor edge
+  uint32_t prem[kPartial];   // valid extent of that last stage (0xFFFFFFFF for unused slots)
+  // LDS image axes, outermost-first; strides are per index of the axis
+  uint32_t ax_count[kAxes], ax_mag[kAxes], ax_sh[kAxes], ax_step[kAxes];
+  uint32_t ax_xs[kAxes];     // input bytes
+  uint32_t ax_os[kAxes];     // output bytes
+  uint32_t ax_rs[kAxes];     // packed stage rows
+  int32_t ax_pslot[kAxes];   // partial slot of the axis' dim, -1 if none
+  int32_t rank, n_axes;
+  uint32_t subs, subs_mag, subs_sh;  // stages per tile
+  uint32_t n_tiles;
+  uint32_t tile0;                    // first tile (debug image)
+  int32_t esize_log2;                // staged element size
+  int32_t outer, waves, swizzle, stages, n_in;
+  // LDS slot layout (bytes)
+  uint32_t in_image_bytes;   // stride between operand images in a slot
+  uint32_t out_image_off;    // output image (staged output only)
+  uint32_t ab_off;           // per-row scalar area
+  uint32_t ab_wave_bytes;    // per wave
+  uint32_t slot_bytes;
+  int32_t n_rows, ab_instr;  // rows per stage; 4-byte loads per wave per stage for a/b
+  int32_t row_ops;
+  int32_t xcd_remap;
+  // extents (bytes from the tensor base to one past its last element): the
+  // buffer resources end there, so no access can leave its tensor
+  uint64_t in_span, out_span;
+  uint64_t total_rows;       // rows of the per-row scalar arrays
+};
+
+// Which kernel variant a launch needs.
+struct KernelKey {
+  int op;        // acp_op
+  int tin;       // acp_dtype of staged operands
+  int tout;      // acp_dtype of the output
+  int vec_bytes; // 16 or 4
+  int mode;      // 0 copy, 1 tile ewise (output staged in LDS), 2 stream
+};
+
+// Kernel for `key`, or nullptr when that combination is not built.
+const void* engine_kernel(const KernelKey& key);
+hipError_t engine_launch(const void* kernel, const EngineArgs& args, unsigned grid, unsigned block,
+                         unsigned lds_bytes, hipStream_t stream);
+const void* lds_image_kernel(int vec_bytes);
+hipError_t lds_image_launch(const void* kernel, const EngineArgs& args, unsigned block, unsigned lds_bytes,
+                            void* out_bytes, uint32_t image_bytes, hipStream_t stream);
+hipError_t ring_trace_launch(int n_iters, int stages, int loads, int stores, int32_t* out,
+                             hipStream_t stream);
+
+// Magic numbers for n / d with n < 2^31: q = (n * mag) >> (31 + sh).
+inline void magic_for(uint32_t d, uint32_t* mag, uint32_t* sh) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  const unsigned __int128 num = (static_cast<unsigned __int128>(1) << (31 + s)) + d - 1;
+  *mag = static_cast<uint32_t>(num / d);
+  *sh = s;
+}
+
+}  // namespace acp

@@ -1,0 +1,564 @@
+// Stage-ring engine for gfx950 (CDNA4): direct-to-LDS tile loads, a per-wave
+// completion count in place of per-stage barriers, elementwise ops on the
+// staged tile, and coalesced buffer stores.  Included by the kernel
+// translation units only.
+//
+// Design (what the pages describe, re-built for gfx950):
+// * "copy_async -> tma" moves a whole tile with one descriptor-driven
+//   instruction that completes on a barrier; "copy_async -> ldgsts" has every
+//   thread issue 16-byte asynchronous copies to its own shared address.
+//   gfx950 has neither a tensor engine nor per-thread LDS destinations for
+//   asynchronous loads: its direct-to-LDS buffer loads write lane l's 16 (or
+//   4) bytes at M0 + 16 * l (4 * l), so one wave instruction fills one
+//   contiguous 1 KiB (256 B) of LDS.  A tile's LDS image is therefore filled
+//   in contiguous blocks and the swizzle is applied on the GLOBAL side: lane
+//   l fetches the logical chunk the swizzle maps onto its physical slot (the
+//   swizzle is an involution).
+// * The [outer, threads, vec] partition of "elementwise -> smem" is also the
+//   load partition: round f of thread t loads, and later consumes, the same
+//   physical chunk (f * threads + t).  Every wave thus consumes only bytes it
+//   loaded itself, completion is the wave's own in-order count of
+//   outstanding memory operations (s_waitcnt vmcnt) and the ring needs no
+//   workgroup barrier.  Reusing a slot (the hazard the circular-buffer
+//   pseudo-code leaves implicit) is safe because the wave's LDS reads of the
+//   previous occupant completed before that data was stored.
+// * Out-of-bounds chunks get a buffer offset past the resource's range: the
+//   hardware writes zeros into LDS (the descriptor's zero fill) and drops
+//   such stores, so every wave issues the same number of memory operations
+//   and the wait counts stay exact.
+// * Direct-to-LDS loads and the waits are inline asm: the compiler treats any
+//   pending direct-to-LDS load as aliasing every LDS read and would put a
+//   full vmcnt(0) wait before each one, collapsing the ring.
+// * Launch arguments are read through the kernarg segment pointer (address
+//   space 4): scalar loads, no per-lane copy of the argument block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "acp_engine.hpp"
+
+namespace acp {
+namespace dev {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef const EngineArgs __attribute__((address_space(4))) CArgs;
+
+constexpr int kOpZero = 0, kOpSqrt = 1, kOpExp = 2, kOpAdd = 3, kOpMul = 4, kOpFma = 5, kOpCopy = 6;
+constexpr int kU32 = 2, kF16 = 4, kF32 = 5;
+
+__device__ __forceinline__ CArgs* kargs() {
+  return (CArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
+}
+
+__device__ __forceinline__ uint32_t swz128(uint32_t o) { return o ^ (((o >> 7) & 7u) << 4); }
+
+__device__ __forceinline__ uint32_t mdiv(uint32_t n, uint32_t mag, uint32_t sh) {
+  return static_cast<uint32_t>((static_cast<uint64_t>(n) * mag) >> (31 + sh));
+}
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t uni(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+
+// Range of a buffer resource starting `off` bytes into a tensor of `span`
+// bytes: it ends at the tensor's end (and below the out-of-bounds offset).
+__device__ __forceinline__ uint32_t range_from(uint64_t span, uint64_t off) {
+  const uint64_t left = span > off ? span - off : 0;
+  return static_cast<uint32_t>(left < kOobOffset ? left : kOobOffset - 16u);
+}
+
+// Buffer resource for the asm loads: raw (stride 0), 32-bit data format.
+__device__ __forceinline__ v4i rsrc_v4(const void* base, uint32_t range) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r.x = uni(static_cast<int>(static_cast<uint32_t>(a)));
+  r.y = uni(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu));
+  r.z = uni(static_cast<int>(range));
+  r.w = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_store(void* base, uint32_t range) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(range), 0x00020000);
+}
+
+// s_nop 4 covers the wait states between an SGPR / M0 write and a
+// direct-to-LDS instruction reading it.
+__device__ __forceinline__ void dma_b128(v4i rsrc, uint32_t voff, uint32_t m0) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0)
+               : "memory");
+}
+__device__ __forceinline__ void dma_b32(v4i rsrc, uint32_t voff, uint32_t m0) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0)
+               : "memory");
+}
+__device__ __forceinline__ void dma_global_b32(const void* addr, uint32_t m0) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, off" ::"v"(addr), "{m0}"(m0) : "memory");
+}
+
+// Wait until at most k of this wave's memory operations are outstanding.
+// Completion is in issue order, so this retires everything issued before the
+// k most recent operations.  k above the 6-bit field clamps to 63 (a
+// stronger wait).
+__device__ __forceinline__ void wait_vmcnt(int k) {
+  switch (k < 63 ? k : 63) {
+#define ACP_W(n) \
+  case n: asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory"); break;
+    ACP_W(0) ACP_W(1) ACP_W(2) ACP_W(3) ACP_W(4) ACP_W(5) ACP_W(6) ACP_W(7)
+    ACP_W(8) ACP_W(9) ACP_W(10) ACP_W(11) ACP_W(12) ACP_W(13) ACP_W(14) ACP_W(15)
+    ACP_W(16) ACP_W(17) ACP_W(18) ACP_W(19) ACP_W(20) ACP_W(21) ACP_W(22) ACP_W(23)
+    ACP_W(24) ACP_W(25) ACP_W(26) ACP_W(27) ACP_W(28) ACP_W(29) ACP_W(30) ACP_W(31)
+    ACP_W(32) ACP_W(33) ACP_W(34) ACP_W(35) ACP_W(36) ACP_W(37) ACP_W(38) ACP_W(39)
+    ACP_W(40) ACP_W(41) ACP_W(42) ACP_W(43) ACP_W(44) ACP_W(45) ACP_W(46) ACP_W(47)
+    ACP_W(48) ACP_W(49) ACP_W(50) ACP_W(51) ACP_W(52) ACP_W(53) ACP_W(54) ACP_W(55)
+    ACP_W(56) ACP_W(57) ACP_W(58) ACP_W(59) ACP_W(60) ACP_W(61) ACP_W(62) ACP_W(63)
+#undef ACP_W
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Ring control ("Add TMA support for circular buffering pass", "Loop
+// Structure" and "Detailed Pseudo-Code"): the prologue loads min(S-1, N)
+// trips; the main loop loads trip i+S-1 into slot (i+S-1) % S, waits for
+// trip i in slot i % S and consumes it; the epilogue only waits and
+// consumes.  `allowed` is the number of this wave's memory operations issued
+// after the last load of trip i when its wait executes: the loads of trips
+// i+1..min(i+S-1, N-1) (d each) and the stores of every consume since trip
+// i's load (st each).  With S == 1 the ring is load, wait, consume.
+
+__device__ __forceinline__ int allowed(int i, int n, int s, int d, int st) {
+  int ahead = n - 1 - i;
+  if (ahead > s - 1) ahead = s - 1;
+  const int behind = i < s - 1 ? i : s - 1;
+  return ahead * d + behind * st;
+}
+
+template <class P>
+__device__ __forceinline__ void run_ring(P& p, int n, int s, int d, int st) {
+  const int pro = n < s - 1 ? n : s - 1;
+  for (int j = 0; j < pro; ++j) p.load(j, j);
+  const int nmain = n - (s - 1) > 0 ? n - (s - 1) : 0;
+  int cur = 0, ld = s - 1;
+  int i = 0;
+  for (; i < nmain; ++i) {
+    p.load(i + s - 1, ld);
+    p.wait(i, cur, allowed(i, n, s, d, st));
+    p.consume(i, cur);
+    cur = (cur + 1 == s) ? 0 : cur + 1;
+    ld = (ld + 1 == s) ? 0 : ld + 1;
+  }
+  for (; i < n; ++i) {
+    p.wait(i, cur, allowed(i, n, s, d, st));
+    p.consume(i, cur);
+    cur = (cur + 1 == s) ? 0 : cur + 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Op registry ("elementwise -> smem", "What it accepts" and "How inputs
+// change the algorithm").  IEEE binary32 / binary16 arithmetic with
+// round-to-nearest-even and no flush of denormals; fma is fused.
+
+template <int DT> struct DType;
+template <> struct DType<kF32> { typedef float T; };
+template <> struct DType<kF16> { typedef _Float16 T; };
+template <> struct DType<kU32> { typedef uint32_t T; };
+
+template <typename T> __device__ __forceinline__ float to_f(T v) { return static_cast<float>(v); }
+template <typename T> __device__ __forceinline__ T from_f(float v) { return static_cast<T>(v); }
+
+template <int OP, int TIN, int TOUT> struct Op;
+
+template <int TIN, int TOUT> struct Op<kOpSqrt, TIN, TOUT> {
+  typedef typename DType<TIN>::T TI;
+  typedef typename DType<TOUT>::T TO;
+  static constexpr int NIN = 1;
+  static constexpr bool ROW = false;
+  static __device__ __forceinline__ TO f(TI x, TI, TI, float, float) { return from_f<TO>(__builtin_sqrtf(to_f(x))); }
+};
+template <int TIN, int TOUT> struct Op<kOpExp, TIN, TOUT> {
+  typedef typename DType<TIN>::T TI;
+  typedef typename DType<TOUT>::T TO;
+  static constexpr int NIN = 1;
+  static constexpr bool ROW = false;
+  static __device__ __forceinline__ TO f(TI x, TI, TI, float, float) { return from_f<TO>(expf(to_f(x))); }
+};
+template <int TIN, int TOUT> struct Op<kOpZero, TIN, TOUT> {
+  typedef typename DType<TIN>::T TI;
+  typedef typename DType<TOUT>::T TO;
+  static constexpr int NIN = 0;
+  static constexpr bool ROW = false;
+  static __device__ __forceinline__ TO f(TI, TI, TI, float, float) { return TO(0); }
+};
+// Byte copy: 32-bit words move unchanged.
+template <> struct Op<kOpCopy, kU32, kU32> {
+  typedef uint32_t TI;
+  typedef uint32_t TO;
+  static constexpr int NIN = 1;
+  static constexpr bool ROW = false;
+  static __device__ __forceinline__ TO f(TI x, TI, TI, float, float) { return x; }
+};
+// Staged operands: add / mul of binary16 via binary32 are exact then
+// rounded once (24 >= 2 * 11 + 2); fma is fused in the operand type.
+template <int T> struct Op<kOpAdd, T, T> {
+  typedef typename DType<T>::T TI;
+  typedef TI TO;
+  static constexpr int NIN = 2;
+  static constexpr bool ROW = false;
+  static __device__ __forceinline__ TO f(TI a, TI b, TI, float, float) { return from_f<TO>(to_f(a) + to_f(b)); }
+};
+template <int T> struct Op<kOpMul, T, T> {
+  typedef typename DType<T>::T TI;
+  typedef TI TO;
+  static constexpr int NIN = 2;
+  static constexpr bool ROW = false;
+  static __device__ __forceinline__ TO f(TI a, TI b, TI, float, float) { return from_f<TO>(to_f(a) * to_f(b)); }
+};
+template <> struct Op<kOpFma, kF32, kF32> {
+  typedef float TI;
+  typedef float TO;
+  static constexpr int NIN = 3;
+  static constexpr bool ROW = false;
+  static __device__ __forceinline__ TO f(TI a, TI b, TI c, float, float) { return __builtin_fmaf(a, b, c); }
+};
+template <> struct Op<kOpFma, kF16, kF16> {
+  typedef _Float16 TI;
+  typedef _Float16 TO;
+  static constexpr int NIN = 3;
+  static constexpr bool ROW = false;
+  static __device__ __forceinline__ TO f(TI a, TI b, TI c, float, float) { return __builtin_fmaf16(a, b, c); }
+};
+// Streamed x with per-row scalars (binary32): add x + b, mul a * x, fma a * x + b.
+template <int OPC> struct RowOp {
+  typedef float TI;
+  typedef float TO;
+  static constexpr int NIN = 1;
+  static constexpr bool ROW = true;
+  static __device__ __forceinline__ TO f(TI x, TI, TI, float a, float b) {
+    if constexpr (OPC == kOpAdd) return x + b;
+    if constexpr (OPC == kOpMul) return a * x;
+    return __builtin_fmaf(a, x, b);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Per-lane map of the rounds f < outer: physical chunk (f * waves + wave) *
+// 64 + lane of a slot, its logical position through the swizzle, and from the
+// image axes its offsets inside the stage.  Computed once per workgroup.
+
+struct LaneMap {
+  uint32_t xoff[kMaxOuter];   // input byte offset from the stage origin
+  uint32_t ooff[kMaxOuter];   // output byte offset from the stage origin
+  uint32_t oobm[kMaxOuter];   // partial slots along which the chunk lies past the edge
+  uint32_t lpos[kMaxOuter];   // logical byte offset of the chunk in the image
+  uint32_t abo[kMaxOuter];    // LDS offset of the chunk's row scalar (row ops)
+};
+
+template <int VB>
+__device__ __forceinline__ void build_map(CArgs* A, int wave, int lane, LaneMap& m) {
+  const int outer = A->outer, waves = A->waves, n_axes = A->n_axes;
+#pragma unroll
+  for (int g = 0; g < kMaxOuter; ++g) m.xoff[g] = m.ooff[g] = m.oobm[g] = m.lpos[g] = m.abo[g] = 0;
+#pragma nounroll
+  for (int f = 0; f < outer; ++f) {
+    const uint32_t pb = ((f * waves + wave) * 64u + lane) * VB;
+    const uint32_t lb = A->swizzle ? swz128(pb) : pb;
+    const uint32_t sub_byte = lb & ((1u << A->esize_log2) - 1u);  // copies of elements wider than VB
+    uint32_t e = lb >> A->esize_log2;
+    uint32_t xo = sub_byte, oo = sub_byte, row = 0;
+    uint32_t rel[kPartial] = {0, 0, 0, 0};
+#pragma nounroll
+    for (int k = n_axes - 1; k >= 0; --k) {
+      const uint32_t q = mdiv(e, A->ax_mag[k], A->ax_sh[k]);
+      const uint32_t idx = e - q * A->ax_count[k];
+      e = q;
+      xo += idx * A->ax_xs[k];
+      oo += idx * A->ax_os[k];
+      row += idx * A->ax_rs[k];
+      const int ps = A->ax_pslot[k];
+#pragma unroll
+      for (int s = 0; s < kPartial; ++s)
+        if (ps == s) rel[s] += idx * A->ax_step[k];
+    }
+    uint32_t ob = 0;
+#pragma unroll
+    for (int s = 0; s < kPartial; ++s)
+      if (rel[s] >= A->prem[s]) ob |= 1u << s;
+    const uint32_t abo = (row >> 5) * 256u + (row & 31u) * 4u;
+#pragma unroll
+    for (int g = 0; g < kMaxOuter; ++g)
+      if (g == f) {
+        m.xoff[g] = xo;
+        m.ooff[g] = oo;
+        m.oobm[g] = ob;
+        m.lpos[g] = lb;
+        m.abo[g] = abo;
+      }
+  }
+}
+
+struct Trip {
+  uint64_t xbase, obase, rbase;
+  uint32_t last;   // partial slots along which this stage is the cut last one
+  bool beyond;     // stage lies entirely past the tensor
+};
+
+__device__ __forceinline__ Trip trip_geometry(CArgs* A, uint32_t wg, uint32_t grid, int j) {
+  const uint32_t tl = mdiv(static_cast<uint32_t>(j), A->subs_mag, A->subs_sh);
+  uint32_t sub = static_cast<uint32_t>(j) - tl * A->subs;
+  uint32_t tile = A->tile0 + wg + tl * grid;
+  Trip t{0, 0, 0, 0u, false};
+#pragma nounroll
+  for (int d = A->rank - 1; d >= 0; --d) {
+    const uint32_t qt = mdiv(tile, A->tg_mag[d], A->tg_sh[d]);
+    const uint32_t tc = tile - qt * A->tgrid[d];
+    tile = qt;
+    const uint32_t qs = mdiv(sub, A->sub_mag[d], A->sub_sh[d]);
+    const uint32_t scs = sub - qs * A->sub[d];
+    sub = qs;
+    const uint32_t sc = tc * A->sub[d] + scs;
+    if (sc >= A->nst[d]) t.beyond = true;
+    const int ps = A->pslot_of_dim[d];
+    if (ps >= 0 && sc + 1 == A->nst[d]) t.last |= 1u << ps;
+    t.xbase += static_cast<uint64_t>(sc) * static_cast<uint64_t>(A->xstep[d]);
+    t.obase += static_cast<uint64_t>(sc) * static_cast<uint64_t>(A->ostep[d]);
+    t.rbase += static_cast<uint64_t>(sc) * static_cast<uint64_t>(A->rstep[d]);
+  }
+  if (t.beyond) t.xbase = t.obase = t.rbase = 0;
+  return t;
+}
+
+// Per-lane row-scalar sources: lane l < 32 loads a[row], l >= 32 loads b[row]
+// for stage rows q * 32 + (l & 31).  row_ptr[0] is the lane's array,
+// row_ptr[1 + q] the row's byte offset from the stage's first row, row_bad[q]
+// the partial slots along which the row lies past the edge (all bits when
+// the stage has no such row).
+__device__ __forceinline__ void build_rows(CArgs* A, int lane, uint64_t* row_ptr, uint32_t* row_bad) {
+  // both pointers are read as scalars first: a lane-dependent address into
+  // the argument block would become a vector load whose wait lands in the ring
+  const uint64_t pa = reinterpret_cast<uint64_t>(A->row_a), pb = reinterpret_cast<uint64_t>(A->row_b);
+  const uint64_t ua = (static_cast<uint64_t>(uni(static_cast<uint32_t>(pa >> 32))) << 32) | uni(static_cast<uint32_t>(pa));
+  const uint64_t ub = (static_cast<uint64_t>(uni(static_cast<uint32_t>(pb >> 32))) << 32) | uni(static_cast<uint32_t>(pb));
+  row_ptr[0] = lane < 32 ? ua : ub;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    row_ptr[1 + q] = 0;
+    row_bad[q] = ~0u;
+    if (!A->row_ops || q >= A->ab_instr) continue;
+    uint32_t r = q * 32u + (lane & 31);
+    if (r >= static_cast<uint32_t>(A->n_rows)) continue;
+    uint64_t off = 0;
+    uint32_t bad = 0;
+    for (int d = A->rank - 2; d >= 0; --d) {
+      const uint32_t sb = A->sbox[d];
+      const uint32_t rel = r % sb;
+      r /= sb;
+      off += static_cast<uint64_t>(rel) * static_cast<uint64_t>(A->rstep[d] / sb);
+      const int ps = A->pslot_of_dim[d];
+      if (ps >= 0 && rel >= A->prem[ps]) bad |= 1u << ps;
+    }
+    row_ptr[1 + q] = off * 4u;
+    row_bad[q] = bad;
+  }
+}
+
+// Loads of one trip into one slot: every staged operand (outer rounds of
+// VB-byte direct-to-LDS loads) and, for row ops, the stage's per-row scalars.
+template <int VB>
+__device__ __forceinline__ void issue_loads(CArgs* A, const LaneMap& m, const Trip& t, uint32_t slot_lds, int wave,
+                                            const uint64_t* row_ptr, const uint32_t* row_bad) {
+  const int outer = A->outer, waves = A->waves, n_in = A->n_in;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    if (k >= n_in) continue;
+    const v4i rs = rsrc_v4(A->in[k] + t.xbase, range_from(A->in_span, t.xbase));
+    const uint32_t img = slot_lds + k * A->in_image_bytes;
+#pragma unroll
+    for (int f = 0; f < kMaxOuter; ++f) {
+      if (f >= outer) continue;
+      const bool ok = !t.beyond && (m.oobm[f] & t.last) == 0;
+      const uint32_t voff = ok ? m.xoff[f] : kOobOffset;
+      const uint32_t m0 = img + (f * waves + wave) * 64u * VB;
+      if constexpr (VB == 16)
+        dma_b128(rs, voff, m0);
+      else
+        dma_b32(rs, voff, m0);
+    }
+  }
+  if (A->row_ops) {
+    // rows that do not exist (or lie past the edge) read row 0 of the array
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (q >= A->ab_instr) continue;
+      const bool ok = !t.beyond && (row_bad[q] & t.last) == 0;
+      uint64_t row = ok ? t.rbase + row_ptr[1 + q] / 4u : 0u;
+      if (row >= A->total_rows) row = 0;
+      const uint64_t addr = row_ptr[0] + row * 4u;
+      dma_global_b32(reinterpret_cast<const void*>(addr), slot_lds + A->ab_off + wave * A->ab_wave_bytes + q * 256u);
+    }
+  }
+}
+
+template <int OB>
+__device__ __forceinline__ void store_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t voff, const uint32_t* w) {
+  if constexpr (OB == 32) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rs, voff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[4], w[5], w[6], w[7]}, rs, voff + 16u, 0, 0);
+  } else if constexpr (OB == 16) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rs, voff, 0, 0);
+  } else if constexpr (OB == 8) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, rs, voff, 0, 0);
+  } else if constexpr (OB == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32(w[0], rs, voff, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w[0]), rs, voff, 0, 0);
+  }
+}
+
+template <class OP, int VB>
+struct ChunkShape {
+  static constexpr int EI = sizeof(typename OP::TI);
+  static constexpr int EO = sizeof(typename OP::TO);
+  static constexpr int NE = VB / EI;            // elements per chunk
+  static constexpr int OB = NE * EO;            // output bytes per chunk
+  static constexpr int ST = OB == 32 ? 2 : 1;   // stores per chunk
+};
+
+// Consume one trip: read the staged chunks, apply the op, (tile ewise) write
+// the result into the slot's output image and read it back, store.
+template <class OP, int VB, bool STAGE_OUT>
+__device__ __forceinline__ void consume_trip(CArgs* A, const LaneMap& m, const Trip& t, unsigned char* lds,
+                                             uint32_t slot, int wave, int lane) {
+  typedef ChunkShape<OP, VB> CS;
+  typedef typename OP::TI TI;
+  typedef typename OP::TO TO;
+  const int outer = A->outer, waves = A->waves;
+  const uint32_t in_img = A->in_image_bytes;
+  const __amdgpu_buffer_rsrc_t rs = rsrc_store(A->out + t.obase, range_from(A->out_span, t.obase));
+#pragma unroll
+  for (int f = 0; f < kMaxOuter; ++f) {
+    if (f >= outer) continue;
+    const uint32_t chunk = slot + ((f * waves + wave) * 64u + lane) * VB;
+    TI in[3][CS::NE];
+#pragma unroll
+    for (int k = 0; k < (OP::NIN ? OP::NIN : 1); ++k) {
+      if (k >= OP::NIN) {
+        __builtin_memset(in[k], 0, sizeof(in[k]));
+      } else if constexpr (VB == 16) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(__builtin_assume_aligned(lds + chunk + k * in_img, 16));
+        __builtin_memcpy(in[k], &v, 16);
+      } else {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(__builtin_assume_aligned(lds + chunk + k * in_img, 4));
+        __builtin_memcpy(in[k], &v, 4);
+      }
+    }
+    float ra = 0.f, rb = 0.f;
+    if constexpr (OP::ROW) {
+      const uint32_t ab = slot + A->ab_off + wave * A->ab_wave_bytes + m.abo[f];
+      ra = *reinterpret_cast<const float*>(lds + ab);
+      rb = *reinterpret_cast<const float*>(lds + ab + 128u);
+    }
+    TO res[CS::NE];
+#pragma unroll
+    for (int e = 0; e < CS::NE; ++e)
+      res[e] = OP::f(in[0][e], in[OP::NIN > 1 ? 1 : 0][e], in[OP::NIN > 2 ? 2 : 0][e], ra, rb);
+    uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    __builtin_memcpy(words, res, CS::OB);
+    if constexpr (STAGE_OUT) {
+      // the output tile lives in LDS ("elementwise -> smem": every operand,
+      // the output included, is in shared memory) and is copied out from there
+      const uint32_t lo = (m.lpos[f] >> A->esize_log2) * CS::EO;
+      constexpr int P = (CS::OB + 15) / 16;
+      constexpr int PB = CS::OB < 16 ? CS::OB : 16;
+#pragma unroll
+      for (int piece = 0; piece < P; ++piece) {
+        const uint32_t lp = lo + piece * 16;
+        __builtin_memcpy(lds + slot + A->out_image_off + (A->swizzle ? swz128(lp) : lp), words + piece * 4, PB);
+      }
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int piece = 0; piece < P; ++piece) {
+        const uint32_t lp = lo + piece * 16;
+        __builtin_memcpy(words + piece * 4, lds + slot + A->out_image_off + (A->swizzle ? swz128(lp) : lp), PB);
+      }
+    }
+    const bool ok = !t.beyond && (m.oobm[f] & t.last) == 0;
+    store_chunk<CS::OB>(rs, ok ? m.ooff[f] : kOobOffset, words);
+  }
+}
+
+template <class OP, int VB, bool STAGE_OUT>
+struct EnginePolicy {
+  CArgs* A;
+  const LaneMap& m;
+  unsigned char* lds;
+  uint32_t lds0, wg, grid;
+  int wave, lane;
+  const uint64_t* row_ptr;
+  const uint32_t* row_bad;
+
+  __device__ __forceinline__ void load(int j, int slot) {
+    const Trip t = trip_geometry(A, wg, grid, j);
+    issue_loads<VB>(A, m, t, lds0 + slot * A->slot_bytes, wave, row_ptr, row_bad);
+  }
+  __device__ __forceinline__ void wait(int, int, int k) { wait_vmcnt(k); }
+  __device__ __forceinline__ void consume(int i, int slot) {
+    const Trip t = trip_geometry(A, wg, grid, i);
+    consume_trip<OP, VB, STAGE_OUT>(A, m, t, lds, slot * A->slot_bytes, wave, lane);
+  }
+};
+
+// The engine kernel.  The EngineArgs parameter fixes the launch ABI; the
+// body reads it through the kernarg segment pointer.
+template <class OP, int VB, bool STAGE_OUT>
+__global__ __launch_bounds__(1024) void engine_kernel_t(const EngineArgs) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+  CArgs* A = kargs();
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const int lane = threadIdx.x & 63;
+  const int wave = uni(static_cast<int>(threadIdx.x >> 6));
+  const uint32_t grid = gridDim.x;
+  uint32_t wg = blockIdx.x;
+  if (A->xcd_remap) wg = (wg & 7u) * (grid >> 3) + (wg >> 3);
+  const uint32_t n_tiles = A->n_tiles;
+  const uint32_t tiles = wg < n_tiles ? (n_tiles - wg + grid - 1) / grid : 0;
+  const int n = static_cast<int>(tiles * A->subs);
+  if (n == 0) return;
+  LaneMap m;
+  build_map<VB>(A, wave, lane, m);
+  uint64_t row_ptr[3];
+  uint32_t row_bad[2];
+  build_rows(A, lane, row_ptr, row_bad);
+  EnginePolicy<OP, VB, STAGE_OUT> pol{A, m, lds, lds0, wg, grid, wave, lane, row_ptr, row_bad};
+  typedef ChunkShape<OP, VB> CS;
+  const int d = A->n_in * A->outer + (A->row_ops ? A->ab_instr : 0);
+  const int st = A->outer * CS::ST;
+  run_ring(pol, n, A->stages, d, st);
+}
+
+}  // namespace dev
+
+struct KernelEntry {
+  KernelKey key;
+  const void* fn;
+};
+
+#define ACP_K(OPC, TIN, TOUT, VB, MODE, ...) \
+  KernelEntry{KernelKey{OPC, TIN, TOUT, VB, MODE}, \
+              reinterpret_cast<const void*>(&dev::engine_kernel_t<__VA_ARGS__, VB, (MODE == 1)>)}
+#define ACP_BOTH(OPC, TIN, TOUT, MODE, ...) ACP_K(OPC, TIN, TOUT, 16, MODE, __VA_ARGS__), ACP_K(OPC, TIN, TOUT, 4, MODE, __VA_ARGS__)
+
+template <size_t N>
+const void* find_entry(const KernelEntry (&table)[N], const KernelKey& k) {
+  for (const KernelEntry& e : table)
+    if (e.key.op == k.op && e.key.tin == k.tin && e.key.tout == k.tout && e.key.vec_bytes == k.vec_bytes &&
+        e.key.mode == k.mode)
+      return e.fn;
+  return nullptr;
+}
+
+}  // namespace acp

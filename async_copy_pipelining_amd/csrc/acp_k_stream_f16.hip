@@ -1,0 +1,16 @@
+// Engine instantiations: streamed ops with float16 staged input.
+#include "acp_engine_impl.hpp"
+
+namespace acp {
+using namespace dev;
+namespace {
+const KernelEntry kTable[] = {
+    ACP_BOTH(kOpZero, kF16, kF16, 2, Op<kOpZero, kF16, kF16>),
+    ACP_BOTH(kOpSqrt, kF16, kF32, 2, Op<kOpSqrt, kF16, kF32>),
+    ACP_BOTH(kOpSqrt, kF16, kF16, 2, Op<kOpSqrt, kF16, kF16>),
+    ACP_BOTH(kOpExp, kF16, kF32, 2, Op<kOpExp, kF16, kF32>),
+    ACP_BOTH(kOpExp, kF16, kF16, 2, Op<kOpExp, kF16, kF16>),
+};
+}  // namespace
+const void* lookup_stream_f16(const KernelKey& k) { return find_entry(kTable, k); }
+}  // namespace acp

@@ -1,0 +1,19 @@
+// Engine instantiations: streamed ops with float32 staged input.
+#include "acp_engine_impl.hpp"
+
+namespace acp {
+using namespace dev;
+namespace {
+const KernelEntry kTable[] = {
+    ACP_BOTH(kOpZero, kF32, kF32, 2, Op<kOpZero, kF32, kF32>),
+    ACP_BOTH(kOpSqrt, kF32, kF32, 2, Op<kOpSqrt, kF32, kF32>),
+    ACP_BOTH(kOpSqrt, kF32, kF16, 2, Op<kOpSqrt, kF32, kF16>),
+    ACP_BOTH(kOpExp, kF32, kF32, 2, Op<kOpExp, kF32, kF32>),
+    ACP_BOTH(kOpExp, kF32, kF16, 2, Op<kOpExp, kF32, kF16>),
+    ACP_BOTH(kOpAdd, kF32, kF32, 2, RowOp<kOpAdd>),
+    ACP_BOTH(kOpMul, kF32, kF32, 2, RowOp<kOpMul>),
+    ACP_BOTH(kOpFma, kF32, kF32, 2, RowOp<kOpFma>),
+};
+}  // namespace
+const void* lookup_stream_f32(const KernelKey& k) { return find_entry(kTable, k); }
+}  // namespace acp

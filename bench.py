@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Throughput of the pipelined tile copy + elementwise path on one MI355X.
+
+Default workload: y = a[row] * x + b[row] over a [128, 500, 1024] float32
+tensor streamed through a 4-stage LDS ring (stage = 4 rows x 1024), the
+configuration the HBM-roofline target is quoted on.  One step = one launch
+of acp_stream_ewise over the whole tensor.  Inputs are seeded synthetic
+tensors resident in HBM; three buffer sets are rotated so that consecutive
+steps never hit data left in the 256 MB last-level cache by the previous one.
+
+Prints ONE JSON line (rank 0) with the metric, the roofline of the streaming
+kernel (HIP events around every timed launch, on the stream it runs on) and
+the CPU oracle timed on a bounded sample of the same workload.
+
+Other workloads (for measurement only): --workload c2 | c3 | c5.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "achieved HBM GB/s (and % of peak) for pipelined tile copy+ewise, 1 MI355X"
+PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["acp_engine_impl.hpp", "acp_k_stream_f32.hip", "acp_k_stream_f16.hip",
+                  "acp_k_tile.hip", "acp_k_copy.hip", "acp_api.cpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "async_copy_pipelining_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{workload_key}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", txt)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--stages", type=int, default=4)
+    ap.add_argument("--rows", type=int, default=4, help="rows per ring stage (c4)")
+    ap.add_argument("--threads", type=int, default=256)
+    ap.add_argument("--workgroups", type=int, default=0, help="persistent workgroups (0: 256 x --wg-per-cu)")
+    ap.add_argument("--wg-per-cu", type=int, default=2)
+    ap.add_argument("--sets", type=int, default=3, help="rotated buffer sets")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only: every box has one MI355X; "
+                                   "run with --gpus 1", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import async_copy_pipelining_amd as acp
+    import workloads as W
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.uint8).reshape(-1).copy()).to(dev)
+
+    def packed(shape):
+        st, out = 1, []
+        for e in reversed(shape):
+            out.append(st)
+            st *= e
+        return tuple(reversed(out))
+
+    wl = args.workload
+    launches = []          # one callable per buffer set
+    if wl == "c4":
+        shape = (128, 500, 1024)
+        stage = (1, args.rows, 1024)
+        x, a, b = W.fma_rows_f32(shape, seed=4)
+        G = args.workgroups or 256 * args.wg_per_cu
+        for s in range(args.sets):
+            xd, ad, bd = to_dev(x), to_dev(a), to_dev(b)
+            yd = torch.empty(x.nbytes, dtype=torch.uint8, device=dev)
+            xdesc = acp.acp_encode_tiled("f32", xd, shape, packed(shape), stage)
+            ydesc = acp.acp_encode_tiled("f32", yd, shape, packed(shape), stage)
+            launches.append((lambda xdesc=xdesc, ydesc=ydesc, ad=ad, bd=bd, keep=(xd, yd):
+                             acp.acp_stream_ewise("fma", ydesc, xdesc, ad, bd, stage, args.stages,
+                                                  args.threads, G, stream)))
+        bytes_per = x.nbytes * 2 + a.nbytes + b.nbytes
+        dtype = "f32"
+        config = {"workload": f"stream fma y=a[row]*x+b[row], [128,500,1024] f32, {args.stages}-stage LDS ring, "
+                              f"stage (1,{args.rows},1024)", "shape": list(shape), "stages": args.stages,
+                  "stage_box": list(stage), "threads": args.threads, "workgroups": G}
+        key = f"stream_fma_f32_128x500x1024_s{args.stages}_r{args.rows}"
+    elif wl == "c2":
+        x = W.sqrt_tiles_f32(65536, seed=2)
+        shape = x.shape
+        for s in range(args.sets):
+            xd = to_dev(x)
+            yd = torch.empty(x.nbytes, dtype=torch.uint8, device=dev)
+            xdesc = acp.acp_encode_tiled("f32", xd, shape, packed(shape), (1, 32, 32))
+            ydesc = acp.acp_encode_tiled("f32", yd, shape, packed(shape), (1, 32, 32))
+            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
+                            acp.acp_tile_ewise("sqrt", ydesc, [xdesc], 256, stream))
+        bytes_per, dtype = x.nbytes * 2, "f32"
+        config = {"workload": "tile sqrt, 65536 tiles of 32x32 f32, 256 threads, one tile per workgroup"}
+        key = "tile_sqrt_f32_65536x32x32"
+    elif wl == "c3":
+        shape = (128, 500, 1024)
+        x = W.normal_f16(shape, seed=3)
+        for s in range(args.sets):
+            xd = to_dev(x)
+            yd = torch.empty(x.nbytes, dtype=torch.uint8, device=dev)
+            xdesc = acp.acp_encode_tiled("f16", xd, shape, packed(shape), (1, 128, 32))
+            ydesc = acp.acp_encode_tiled("f16", yd, shape, packed(shape), (1, 128, 32))
+            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
+                            acp.acp_tile_copy(xdesc, ydesc, 128, stream))
+        bytes_per, dtype = x.nbytes * 2, "f16"
+        config = {"workload": "tile copy, [128,500,1024] f16, 128x32 tiles, 128 threads"}
+        key = "tile_copy_f16_128x500x1024"
+    else:
+        shape, pitch = (4, 8, 64, 128, 256), 264
+        storage, strides = W.padded_uniform_f16(shape, pitch=pitch, seed=5)
+        n = int(np.prod(shape))
+        for s in range(args.sets):
+            xd = to_dev(storage)
+            yd = torch.empty(n * 4, dtype=torch.uint8, device=dev)
+            xdesc = acp.acp_encode_tiled("f16", xd, shape, strides, (1, 2, 16, 64, 64), acp.ACP_SWIZZLE_128B)
+            ydesc = acp.acp_encode_tiled("f32", yd, shape, packed(shape), (1, 2, 16, 64, 64))
+            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
+                            acp.acp_stream_ewise("exp", ydesc, xdesc, None, None, (1, 1, 1, 64, 64),
+                                                 args.stages, 256, 0, stream))
+        bytes_per, dtype = n * 2 + n * 4, "f16->f32"
+        config = {"workload": "rank-5 exp (4,8,64,128,256) f16 pitch 264 -> f32, box (1,2,16,64,64), "
+                              f"{args.stages}-stage swizzled ring, stage (1,1,1,64,64)"}
+        key = f"stream_exp_rank5_s{args.stages}"
+
+    for i in range(args.warmup):
+        launches[i % len(launches)]()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        launches[i % len(launches)]()
+        ends[i].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per_launch = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    avg_launch_ms = sum(per_launch) / len(per_launch)
+    ms_per_step = total_ms / args.steps
+    value = bytes_per / (ms_per_step * 1e-3) / 1e9
+    achieved = bytes_per / (avg_launch_ms * 1e-3) / 1e9
+
+    traffic = traffic_from_profiles(key)
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic (seeded numpy draws resident in HBM, 3 rotated buffer sets)",
+        "config": config,
+        "percent_of_peak": round(100.0 * value / PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": bytes_per,
+                     "avg_launch_ms": round(avg_launch_ms, 5), "median_launch_ms": round(per_launch[len(per_launch) // 2], 5),
+                     "kernel_source_hash": kernel_hash()},
+    }
+    if not args.no_cpu_baseline and wl == "c4":
+        result["cpu_baseline"] = cpu_baseline_c4(args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_c4(budget_s: float):
+    """The oracle's streamed fma on whole [500, 1024] slabs of the same
+    workload, slab after slab until the time budget is spent."""
+    import numpy as np
+
+    import workloads as W
+    from oracle import reference as REF
+
+    x, a, b = W.fma_rows_f32((128, 500, 1024), seed=4)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        REF.stream_ewise("fma", x[done], a[done], b[done], np.float32)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done == 128:
+            break
+    nbytes = done * (500 * 1024 * 4 * 2 + 500 * 8)
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of 128 [500,1024] slabs of the c4 workload, {el:.1f} s, numpy single thread"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * acp.h -- pipelined asynchronous tile copy + elementwise for AMD MI355X (gfx950).
+ *
+ * A small C ABI over three operations on multi-dimensional tiles staged in LDS:
+ *
+ *   acp_tile_copy     global -> LDS -> global, one tile per workgroup
+ *   acp_tile_ewise    elementwise op on LDS-resident operand tiles
+ *   acp_stream_ewise  tiles streamed through a 2..4-stage LDS ring
+ *
+ * plus the host-side descriptor encoder / planner they share.  The method
+ * follows four pages:
+ *   [tma]    "copy_async -> tma"            (TVM TIRx docs)
+ *   [smem]   "elementwise -> smem"          (TVM TIRx docs)
+ *   [ldgsts] "copy_async -> ldgsts"         (TVM TIRx docs)
+ *   [cb]     "Add TMA support for circular buffering pass" (nvFuser PR #2833)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Status.  Every call returns an acp_status; nothing throws across the ABI.
+ *   ACP_ERR_INVALID      malformed request (null pointer, bad enum, shape or
+ *                        operand mismatch) -- the "anything else is an error"
+ *                        class of [tma] "Algorithm" step 1;
+ *   ACP_ERR_DECLINED     well formed, but no legal plan exists ([tma] final
+ *                        paragraph of "How inputs change the algorithm";
+ *                        [ldgsts] "the variant declines");
+ *   ACP_ERR_UNSUPPORTED  op / dtype combination outside the registry
+ *                        ([smem] "What it accepts": check_extras), or a plan
+ *                        beyond this library's kernel limits;
+ *   ACP_ERR_LDS          the staged tiles do not fit the device's LDS;
+ *   ACP_ERR_HIP          a HIP runtime call or kernel launch failed.
+ *   acp_last_error() returns the reason for the calling thread's last
+ *   non-OK status (the pages' predicates return an (ok, reason) pair).
+ * Ownership.  Descriptors are caller-owned plain data; the library keeps no
+ *   reference to them after a call returns.  A descriptor embeds the tensor's
+ *   device address, so the tensor must outlive every enqueued use and moving
+ *   the tensor means encoding again ([tma] "Algorithm" step 3: encoded once
+ *   on the host, reused by the caller).  Device pointers and streams are
+ *   borrowed.
+ * Asynchrony.  Compute calls validate and plan on the host (errors return
+ *   synchronously), then enqueue one kernel on `hip_stream` (a hipStream_t;
+ *   NULL = the null stream) and return.  Completion is stream order; the
+ *   caller synchronizes.  Inside a kernel the library owns every wait: unlike
+ *   the pages' copy_async (whose caller commits and waits), completion of
+ *   the staged loads is tracked by the kernel itself.
+ * Threads.  `threads` is the workgroup size: a multiple of 64 (one gfx950
+ *   wavefront) from 64 to 1024.
+ * Layout.  Shapes, strides and boxes are outermost-first; strides are in
+ *   elements; the innermost stride must be 1.  Out-of-bounds elements of a
+ *   partial tile read as zero and are never written.
+ */
+#ifndef ACP_H
+#define ACP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ACP_ABI_VERSION 1
+#define ACP_MAX_INPUT_RANK 8   /* rank of a tensor handed to the encoder */
+#define ACP_MAX_RANK 5         /* descriptor rank after planning ([tma] "What it accepts") */
+#define ACP_MAX_BOX 256        /* per-dimension box limit ([cb] "Lowering Details") */
+#define ACP_MAX_ISSUES 256     /* loads per tile the planner may create when shrinking */
+#define ACP_MAX_IMAGE_AXES 12  /* axes of a tile's LDS image */
+#define ACP_MAX_EWISE_INPUTS 3
+
+typedef enum {
+  ACP_OK = 0,
+  ACP_ERR_INVALID = 1,
+  ACP_ERR_DECLINED = 2,
+  ACP_ERR_UNSUPPORTED = 3,
+  ACP_ERR_LDS = 4,
+  ACP_ERR_HIP = 5
+} acp_status;
+
+typedef enum { ACP_U8 = 0, ACP_U16 = 1, ACP_U32 = 2, ACP_U64 = 3, ACP_F16 = 4, ACP_F32 = 5 } acp_dtype;
+
+/* LDS layout of a staged tile.  ACP_SWIZZLE_128B carries the mode number of
+ * [tma]'s worked example (3): 16-byte chunk index XOR (128-byte row index
+ * mod 8) on stage-relative LDS byte offsets. */
+typedef enum { ACP_SWIZZLE_NONE = 0, ACP_SWIZZLE_128B = 3 } acp_swizzle;
+
+/* Out-of-bounds fill: zero, the last encode argument of [tma]'s example. */
+typedef enum { ACP_OOB_ZERO = 0 } acp_oob;
+
+/* Op registry ([smem] "What it accepts", "How inputs change the algorithm"):
+ *   ZERO  y = +0                     SQRT  y = sqrt(x)      EXP  y = exp(x)
+ *   ADD   y = x0 + x1                MUL   y = x0 * x1
+ *   FMA   y = x0 * x1 + x2 (fused, one rounding)
+ * For acp_stream_ewise the second and third operands are per-row scalars:
+ *   ADD y = x + b[row], MUL y = a[row] * x, FMA y = a[row] * x + b[row].
+ * COPY (acp_tile_copy only) moves raw bytes. */
+typedef enum {
+  ACP_OP_ZERO = 0,
+  ACP_OP_SQRT = 1,
+  ACP_OP_EXP = 2,
+  ACP_OP_ADD = 3,
+  ACP_OP_MUL = 4,
+  ACP_OP_FMA = 5,
+  ACP_OP_COPY = 6
+} acp_op;
+
+/* Host-encoded tile descriptor (the cuTensorMap of [tma], re-designed):
+ * plain data, caller-owned, 256 bytes, 64-byte aligned; contents private. */
+typedef struct {
+  __attribute__((aligned(64))) unsigned char opaque[256];
+} acp_tile_desc;
+
+/* What the planner chose for one tile of a descriptor ([tma] "Algorithm"
+ * step 2, [smem] "Algorithm" step 2, [ldgsts] "Algorithm" step 1). */
+typedef struct {
+  int32_t rank;              /* descriptor rank, <= 5 */
+  int32_t desc_elem_bytes;   /* element size after promotion (copies only) */
+  int64_t dims[ACP_MAX_RANK];    /* innermost-first, in desc elements */
+  int64_t strides[ACP_MAX_RANK]; /* bytes, innermost-first; strides[0] == desc_elem_bytes */
+  int32_t box[ACP_MAX_RANK];     /* innermost-first, in desc elements */
+  int32_t issues;            /* loads per tile (product of the issue axes) */
+  int32_t n_issue_axes;
+  int32_t n_image_axes;      /* axes of the tile's LDS image */
+  int32_t swizzle;           /* acp_swizzle */
+  int32_t promoted;          /* 1 when the element type was widened */
+  int32_t threads;           /* partition; all four are 0 when threads == 0 */
+  int32_t vec;               /* elements per thread per round */
+  int32_t vec_bytes;         /* bytes per thread per round (16 or 4 on gfx950) */
+  int32_t outer;             /* rounds: tile elements / (threads * vec) */
+  int64_t tile_bytes;        /* bytes of one tile's LDS image */
+  int64_t n_tiles;           /* tiles covering the tensor */
+} acp_plan_info;
+
+/* ABI version of the loaded library (ACP_ABI_VERSION). */
+int acp_abi_version(void);
+
+/* Reason for the calling thread's last non-OK status; "" if none.  The
+ * pointer stays valid until the thread's next acp_* call. */
+const char* acp_last_error(void);
+
+/* Encode a descriptor for tiles of `box` over a tensor at `gbase`
+ * ([tma] "Algorithm" step 3; "Generated TIRx IR" shows the worked call).
+ *   out      caller-owned descriptor to fill
+ *   dtype    element type
+ *   rank     1..ACP_MAX_INPUT_RANK
+ *   gbase    device address of element (0, ..., 0); never dereferenced here
+ *   shape    rank extents >= 1
+ *   strides  rank element strides >= 1, innermost == 1
+ *   box      rank tile extents >= 1 (may exceed 256: the planner splits it)
+ *   swizzle  LDS layout of the staged tile
+ *   oob      ACP_OOB_ZERO
+ * Runs the box-level plan search and returns ACP_ERR_DECLINED when no legal
+ * descriptor exists (rank > 5 after shrinking, no swizzle-atom-aligned
+ * innermost box, innermost stride != 1).  Pure host code. */
+acp_status acp_encode_tiled(acp_tile_desc* out, acp_dtype dtype, int rank, const void* gbase,
+                            const int64_t* shape, const int64_t* strides, const int32_t* box,
+                            acp_swizzle swizzle, acp_oob oob);
+
+/* Report the plan of `desc` for a workgroup of `threads` (0: descriptor
+ * only).  `copy_only` != 0 allows element-type promotion (byte copies);
+ * elementwise plans never promote.  Pure host code. */
+acp_status acp_plan_query(const acp_tile_desc* desc, int threads, int copy_only, acp_plan_info* out);
+
+/* Copy every tile of `src` to the same coordinates of `dst` through LDS:
+ * direct-to-LDS loads (16 or 4 bytes per lane, swizzled per `src`), a
+ * per-wave completion wait, then LDS reads and coalesced stores
+ * ([tma] and [ldgsts] "Demonstration program").  One workgroup per tile.
+ * `src` and `dst` must have equal dtype, shape and box ([tma]
+ * validate_copy_op); `dst` may have other strides.  Overlapping src/dst
+ * memory is not supported. */
+acp_status acp_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, int threads,
+                         void* hip_stream);
+
+/* out = op(in[0], ..., in[n_in-1]) tile by tile with every operand staged
+ * in LDS and the result written to an LDS tile before it is copied out
+ * ([smem]).  n_in: ZERO 0 or 1, SQRT/EXP 1, ADD/MUL 2, FMA 3.  All inputs
+ * share dtype, shape, strides, box and swizzle (one anchor layout); `out`
+ * has the same shape and box.  Types: SQRT/EXP f16|f32 -> f16|f32;
+ * ADD/MUL/FMA inputs and output one of f16|f32; ZERO -> f16|f32. */
+acp_status acp_tile_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_desc* const* in,
+                          int n_in, int threads, void* hip_stream);
+
+/* Stream the tiles of `x` through an LDS ring of `stages` (2..4) buffers
+ * ([cb] "Loop Structure"): a prologue issues stages-1 loads, the main loop
+ * issues the load of trip i+stages-1 into stage (i+stages-1) % stages and
+ * then waits for stage i % stages, the epilogue drains.  Each trip stages a
+ * `stage_box` sub-box of x's box (x's box is the workgroup tile; stage_box
+ * must divide it per dim; its planned load count may exceed one).
+ *   op          ZERO, SQRT, EXP (x f16|f32 -> out f16|f32) or
+ *               ADD, MUL, FMA (x and out f32, per-row scalars)
+ *   out         same shape and box as x; any strides
+ *   row_a/row_b device float32 arrays over x's outer dims (shape[:-1],
+ *               packed row-major); FMA needs both, MUL row_a, ADD row_b;
+ *               NULL otherwise
+ *   workgroups  0: one workgroup per tile of x; G > 0: G persistent
+ *               workgroups, workgroup w walks tiles w, w+G, ... with one
+ *               continuous ring
+ * Completion per stage is the wave's in-order count of outstanding memory
+ * operations (s_waitcnt vmcnt) in place of the pages' per-stage barriers. */
+acp_status acp_stream_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_desc* x,
+                            const float* row_a, const float* row_b, const int32_t* stage_box,
+                            int stages, int threads, int workgroups, void* hip_stream);
+
+/* Test export: the raw LDS bytes of tile `tile_index` of `src` after its
+ * direct-to-LDS load, written to `out_bytes` (device, tile_bytes long). */
+acp_status acp_debug_lds_image(const acp_tile_desc* src, int64_t tile_index, int threads,
+                               void* out_bytes, void* hip_stream);
+
+/* Test export: run the ring control of acp_stream_ewise for one wave with
+ * `n_iters` trips, `stages` buffers, `loads` and `stores` memory operations
+ * per trip, recording 3 * n_iters events of 4 int32 each
+ * (kind 0 load / 1 wait / 2 consume, trip, stage, outstanding-op count
+ * allowed at the wait) into device memory `out_events`. */
+acp_status acp_debug_ring_trace(int n_iters, int stages, int loads, int stores, int32_t* out_events,
+                                void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ACP_H */

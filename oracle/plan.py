@@ -189,8 +189,8 @@ def plan_box(esize: int, shape, strides, box, swizzle: int = SWIZZLE_NONE,
     r = len(shape)
     if not (1 <= r <= MAX_INPUT_RANK) or len(strides) != r or len(box) != r:
         raise Invalid("rank must be 1..8 with matching shape/strides/box")
-    if any(s < 1 for s in shape) or any(b < 1 for b in box) or any(s < 1 for s in strides):
-        raise Invalid("extents, strides and box must be >= 1")
+    if any(s < 0 for s in shape) or any(b < 1 for b in box) or any(s < 1 for s in strides):
+        raise Invalid("extents must be >= 0 (0: an empty tensor), strides and box >= 1")
     if esize not in (1, 2, 4, 8):
         raise Invalid("element size must be 1, 2, 4 or 8 bytes")
     if swizzle not in (SWIZZLE_NONE, SWIZZLE_128B):

@@ -14,7 +14,9 @@ sections "Description", "Loop Structure" and "Detailed Pseudo-Code":
 * post-epilogue: release the per-stage barriers.
 
 Readings: when ``N < stages - 1`` the prologue issues only ``N`` loads and
-the epilogue starts at 0 (the page's bounds assume ``N >= stages - 1``).  The
+the epilogue starts at 0 (the page's bounds assume ``N >= stages - 1``).
+The same formulas with one stage give load, wait, compute per iteration
+(no overlap); the one-tile-per-workgroup copy and elementwise calls use it.  The
 load of iteration ``j`` always goes to stage ``j % stages`` (for
 ``j = i + stages - 1`` this is the page's ``load_stage`` formula).
 
@@ -41,8 +43,8 @@ class Event:
 
 
 def schedule(n_iters: int, stages: int, loads: int = 1, stores: int = 0):
-    if stages < 2:
-        raise ValueError("a circular buffer needs at least 2 stages")
+    if stages < 1:
+        raise ValueError("a ring needs at least 1 stage")
     events = []
     issued = []          # the memory-op stream: iteration tag per op ("L", j) or ("S", i)
 

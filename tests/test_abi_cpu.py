@@ -1,0 +1,135 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every entry point
+the header declares, and its host planner agrees field by field with the
+oracle planner (no GPU work is launched here)."""
+import os
+import random
+import re
+
+import pytest
+
+import async_copy_pipelining_amd as acp
+from oracle import plan as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE_BASE = 1 << 20   # encode never dereferences the address
+
+
+def test_library_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "acp.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"^\s*(?:acp_status|int|const char\*)\s+(acp_\w+)\s*\(", header, re.M))
+    assert declared == set(acp.EXPORTED)
+    for name in declared:
+        assert hasattr(acp._lib, name)
+    assert acp.acp_abi_version() == 1
+
+
+def _cmp(dt, shape, strides, box, swz, threads, copy_only, base=FAKE_BASE):
+    """Run both planners; return (oracle outcome, library outcome)."""
+    try:
+        p = P.plan(dt, shape, strides, box, swz, threads=threads, copy_only=copy_only, base_addr=base)
+        o = ("ok", p.rank, [d.extent for d in reversed(p.dims)], [d.stride for d in reversed(p.dims)],
+             [d.box for d in reversed(p.dims)], p.issues, len(p.image_axes), p.promoted,
+             p.vec, p.vec_bytes, p.outer, p.tile_bytes)
+    except P.Declined:
+        o = ("declined",)
+    except P.Invalid:
+        o = ("invalid",)
+    try:
+        # encode checks the box with promotion allowed; the query then plans
+        # with the requested mode and thread count
+        d = acp.acp_encode_tiled(dt, base, shape, strides, box, swz)
+        q = acp.acp_plan_query(d, threads, copy_only)
+        c = ("ok", q["rank"], q["dims"], q["strides"], q["box"], q["issues"], q["n_image_axes"], q["promoted"],
+             q["vec"], q["vec_bytes"], q["outer"], q["tile_bytes"])
+    except acp.AcpError as e:
+        c = {acp.ACP_ERR_DECLINED: ("declined",), acp.ACP_ERR_INVALID: ("invalid",)}[e.status]
+    return o, c
+
+
+WORKED = [
+    ("f16", (8, 256), (256, 1), (8, 256), 3, 64, True),
+    ("f32", (65536, 32, 32), (1024, 32, 1), (1, 32, 32), 0, 256, False),
+    ("f16", (128, 500, 1024), (512000, 1024, 1), (1, 128, 32), 0, 128, True),
+    ("f32", (128, 500, 1024), (512000, 1024, 1), (1, 4, 1024), 0, 256, False),
+    ("f16", (4, 8, 64, 128, 256), (17301504, 2162688, 33792, 264, 1), (1, 1, 1, 64, 64), 3, 256, False),
+    ("f16", (4, 8, 64, 128, 256), (17301504, 2162688, 33792, 264, 1), (1, 2, 16, 64, 64), 3, 256, False),
+    ("u8", (8, 128), (128, 1), (8, 128), 0, 64, True),
+    ("f16", (600, 64), (64, 1), (600, 64), 0, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", WORKED, ids=[str(i) for i in range(len(WORKED))])
+def test_planner_matches_oracle_on_worked_cases(case):
+    o, c = _cmp(*case)
+    assert o[0] == "ok" and o == c
+
+
+def test_planner_matches_oracle_on_alignment_table():
+    for base, vb, outer in ((FAKE_BASE, 16, 4), (FAKE_BASE + 8, 4, 16), (FAKE_BASE + 4, 4, 16)):
+        o, c = _cmp("f16", (128, 32), (32, 1), (128, 32), 0, 128, True, base=base)
+        assert o == c and c[9] == vb and c[10] == outer
+    o, c = _cmp("f16", (128, 32), (32, 1), (128, 32), 0, 128, True, base=FAKE_BASE + 2)
+    assert o == c == ("declined",)
+
+
+def test_planner_matches_oracle_randomized():
+    rng = random.Random(2024)
+    n_ok = n_decl = 0
+    for _ in range(1500):
+        r = rng.randint(1, 7)
+        dt = rng.choice(["u8", "u16", "f16", "f32", "u64"])
+        shape = [rng.choice([1, 2, 3, 4, 5, 8, 16, 33]) for _ in range(r)]
+        shape[-1] = rng.choice([4, 8, 16, 24, 32, 64, 96, 128, 256, 300, 512, 1024, 2048])
+        box = [rng.randint(1, s) for s in shape]
+        if rng.random() < 0.7:
+            box[-1] = rng.choice([b for b in range(1, shape[-1] + 1) if shape[-1] % b == 0])
+        strides, st = [], 1
+        pad = rng.choice([0, 0, 0, 2, 8, 16])
+        for k, ext in enumerate(reversed(shape)):
+            strides.append(st)
+            st *= ext + (pad if k == 0 else 0)
+        strides = list(reversed(strides))
+        if rng.random() < 0.03:
+            strides[-1] = 2
+        swz = rng.choice([0, 3])
+        threads = rng.choice([0, 64, 128, 256, 1024])
+        copy_only = rng.random() < 0.5
+        base = FAKE_BASE + rng.choice([0, 0, 0, 4, 8])
+        o, c = _cmp(dt, shape, strides, box, swz, threads, copy_only, base)
+        assert o == c, (dt, shape, strides, box, swz, threads, copy_only, base)
+        n_ok += o[0] == "ok"
+        n_decl += o[0] == "declined"
+    assert n_ok > 300 and n_decl > 50
+
+
+def test_status_codes_and_reasons():
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_encode_tiled("f16", FAKE_BASE, (8, 256), (1, 8), (8, 256))
+    assert e.value.status == acp.ACP_ERR_DECLINED and "innermost stride" in e.value.reason
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_encode_tiled("f16", 0, (8, 256), (256, 1), (8, 256))
+    assert e.value.status == acp.ACP_ERR_INVALID
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_encode_tiled("f16", FAKE_BASE, (8, 96), (96, 1), (8, 96), acp.ACP_SWIZZLE_128B)
+    assert e.value.status == acp.ACP_ERR_DECLINED and "swizzle-atom" in e.value.reason
+    d = acp.acp_encode_tiled("f16", FAKE_BASE, (8, 256), (256, 1), (8, 256))
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_plan_query(d, 96)
+    assert e.value.status == acp.ACP_ERR_INVALID
+    # stream_ewise argument errors are caught on the host before any launch
+    x = acp.acp_encode_tiled("f32", FAKE_BASE, (4, 8, 256), (2048, 256, 1), (1, 4, 256))
+    y = acp.acp_encode_tiled("f32", FAKE_BASE * 2, (4, 8, 256), (2048, 256, 1), (1, 4, 256))
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_stream_ewise("fma", y, x, FAKE_BASE * 3, FAKE_BASE * 4, (1, 4, 256), 5, 256)
+    assert e.value.status == acp.ACP_ERR_INVALID and "stages" in e.value.reason
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_stream_ewise("fma", y, x, None, FAKE_BASE * 4, (1, 4, 256), 3, 256)
+    assert e.value.status == acp.ACP_ERR_INVALID
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_stream_ewise("fma", y, x, FAKE_BASE * 3, FAKE_BASE * 4, (1, 3, 256), 3, 256)
+    assert e.value.status == acp.ACP_ERR_INVALID and "divide" in e.value.reason
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_tile_copy(x, acp.acp_encode_tiled("f16", FAKE_BASE, (4, 8, 256), (2048, 256, 1), (1, 4, 256)), 256)
+    assert e.value.status == acp.ACP_ERR_INVALID and "valid copy" in e.value.reason
+    assert acp.acp_last_error() != ""

@@ -1,0 +1,143 @@
+"""GPU parity of acp_tile_copy and the direct-to-LDS image against the oracle.
+
+Copy must be bit-identical to its input (the plain definition); the raw LDS
+bytes of a staged tile must equal the oracle's swizzled, zero-filled image.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import async_copy_pipelining_amd as acp  # noqa: E402
+import workloads as W  # noqa: E402
+from oracle import plan as P  # noqa: E402
+from oracle import tiles as T  # noqa: E402
+from tests.gpu_util import dev, empty_bytes, encode, host, packed_strides, stream  # noqa: E402
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _lds_image(desc, tile, threads, nbytes):
+    out = empty_bytes(nbytes, 0x5A)
+    acp.acp_debug_lds_image(desc, tile, threads, out, stream())
+    return host(out, np.uint8)[:nbytes].tobytes()
+
+
+def test_c1_swizzled_copy_is_bit_identical_and_image_matches():
+    say("C1 8x256 f16 swizzled copy, 64 threads")
+    x = W.tile_bits_f16((8, 256), seed=1)
+    xd, yd = dev(x), empty_bytes(x.nbytes)
+    src = encode("f16", xd, (8, 256), (256, 1), (8, 256), acp.ACP_SWIZZLE_128B)
+    dst = encode("f16", yd, (8, 256), (256, 1), (8, 256), acp.ACP_SWIZZLE_128B)
+    info = acp.acp_plan_query(src, 64)
+    assert (info["rank"], info["vec"], info["outer"]) == (3, 8, 4)
+    acp.acp_tile_copy(src, dst, 64, stream())
+    assert np.array_equal(host(yd, np.uint16), x.view(np.uint16).reshape(-1))
+    p = P.plan("f16", (8, 256), (256, 1), (8, 256), P.SWIZZLE_128B, threads=64)
+    assert _lds_image(src, 0, 64, 4096) == T.lds_image(x.reshape(-1), p, 0)
+
+
+@pytest.mark.parametrize("threads", [64, 128, 256])
+def test_ragged_copy_small_and_partial_tile_image(threads):
+    shape, box = (3, 300, 96), (1, 128, 32)   # rows 300 = 2 * 128 + 44, several tiles
+    say(f"ragged copy {shape} box {box} threads {threads}")
+    x = W.normal_f16(shape, seed=3)
+    xd, yd = dev(x), empty_bytes(x.nbytes)
+    st = packed_strides(shape)
+    src = encode("f16", xd, shape, st, box)
+    dst = encode("f16", yd, shape, st, box)
+    acp.acp_tile_copy(src, dst, threads, stream())
+    assert np.array_equal(host(yd, np.uint16, shape), x.view(np.uint16))
+    p = P.plan("f16", shape, st, box, threads=threads)
+    grid = P.tile_grid(shape, box)
+    for tc in [(0, 0, 0), (1, 2, 1), (2, 2, 2)]:              # full, partial rows, partial rows
+        t = int(np.ravel_multi_index(tc, grid))
+        assert _lds_image(src, t, threads, p.tile_bytes) == T.lds_image(x.reshape(-1), p, t)
+
+
+def test_c3_full_size_copy():
+    shape, box = (128, 500, 1024), (1, 128, 32)
+    say(f"C3 full copy {shape} box {box} 128 threads")
+    x = W.normal_f16(shape, seed=3)
+    xd, yd = dev(x), empty_bytes(x.nbytes)
+    st = packed_strides(shape)
+    src = encode("f16", xd, shape, st, box)
+    dst = encode("f16", yd, shape, st, box)
+    info = acp.acp_plan_query(src, 128)
+    assert (info["vec"], info["vec_bytes"], info["outer"]) == (8, 16, 4)
+    assert info["n_tiles"] == 128 * 4 * 32
+    acp.acp_tile_copy(src, dst, 128, stream())
+    torch.cuda.synchronize()
+    assert torch.equal(xd, yd)
+
+
+def test_swizzled_multi_atom_tiles_and_strided_output():
+    shape, box = (5, 40, 512), (1, 16, 256)     # swizzle splits 512-byte rows into 4 atoms; rows ragged
+    say(f"swizzled copy {shape} box {box} into a padded output")
+    x = W.normal_f16(shape, seed=7)
+    xd = dev(x)
+    opitch = 520
+    ost = (40 * opitch, opitch, 1)
+    yd = empty_bytes(5 * 40 * opitch * 2, 0x00)
+    src = encode("f16", xd, shape, packed_strides(shape), box, acp.ACP_SWIZZLE_128B)
+    dst = encode("f16", yd, shape, ost, box)
+    acp.acp_tile_copy(src, dst, 256, stream())
+    y = host(yd, np.uint16).reshape(5, 40, opitch)
+    assert np.array_equal(y[:, :, :512], x.view(np.uint16))
+    assert not np.any(y[:, :, 512:])                        # the pitch padding was never written
+    p = P.plan("f16", shape, packed_strides(shape), box, P.SWIZZLE_128B, threads=256)
+    t = int(np.ravel_multi_index((4, 2, 1), P.tile_grid(shape, box)))
+    assert _lds_image(src, t, 256, p.tile_bytes) == T.lds_image(x.reshape(-1), p, t)
+
+
+@pytest.mark.parametrize("misalign", [4, 8])
+def test_four_byte_path_when_only_4_or_8_aligned(misalign):
+    shape, box = (64, 256), (64, 32)
+    say(f"4-byte direct-to-LDS path, base misaligned by {misalign}")
+    x = W.normal_f16(shape, seed=8)
+    xd = empty_bytes(x.nbytes + 64)
+    xd[misalign:misalign + x.nbytes] = dev(x)
+    yd = empty_bytes(x.nbytes + 64)
+    st = packed_strides(shape)
+    src = encode("f16", xd, shape, st, box, offset_bytes=misalign)
+    dst = encode("f16", yd, shape, st, box, offset_bytes=misalign)
+    info = acp.acp_plan_query(src, 128)
+    assert info["vec_bytes"] == 4
+    acp.acp_tile_copy(src, dst, 128, stream())
+    y = host(yd, np.uint8)
+    assert np.array_equal(y[misalign:misalign + x.nbytes].view(np.uint16), x.view(np.uint16).reshape(-1))
+    assert np.all(y[:misalign] == 0xA5) and np.all(y[misalign + x.nbytes:] == 0xA5)
+
+
+@pytest.mark.parametrize("dt,np_dt", [("u8", np.uint8), ("u64", np.uint64), ("u32", np.uint32)])
+def test_other_element_types(dt, np_dt):
+    shape, box = (7, 33, 128), (2, 8, 128)
+    say(f"copy {dt} {shape} box {box}")
+    rng = np.random.default_rng(9)
+    x = rng.integers(0, 255, size=int(np.prod(shape)) * np.dtype(np_dt).itemsize, dtype=np.uint8)
+    xd, yd = dev(x), empty_bytes(x.nbytes)
+    st = packed_strides(shape)
+    src = encode(dt, xd, shape, st, box)
+    dst = encode(dt, yd, shape, st, box)
+    acp.acp_tile_copy(src, dst, 64, stream())
+    assert np.array_equal(host(yd, np.uint8), x)
+
+
+def test_box_larger_than_tensor_and_empty_tensor():
+    say("box larger than the tensor; empty tensor")
+    x = W.normal_f16((3, 40), seed=10)
+    xd, yd = dev(x), empty_bytes(x.nbytes)
+    src = encode("f16", xd, (3, 40), (40, 1), (8, 64))
+    dst = encode("f16", yd, (3, 40), (40, 1), (8, 64))
+    acp.acp_tile_copy(src, dst, 64, stream())
+    assert np.array_equal(host(yd, np.uint16, (3, 40)), x.view(np.uint16))
+    p = P.plan("f16", (3, 40), (40, 1), (8, 64), threads=64)
+    assert _lds_image(src, 0, 64, p.tile_bytes) == T.lds_image(x.reshape(-1), p, 0)
+    e = encode("f16", xd, (0, 40), (40, 1), (8, 64))
+    f = encode("f16", yd, (0, 40), (40, 1), (8, 64))
+    acp.acp_tile_copy(e, f, 64, stream())                     # no tiles: returns without a launch
+    torch.cuda.synchronize()

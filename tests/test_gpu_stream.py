@@ -1,0 +1,160 @@
+"""GPU parity of acp_stream_ewise (the 2..4-stage LDS ring) and of the ring
+control itself against the oracle."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import async_copy_pipelining_amd as acp  # noqa: E402
+import workloads as W  # noqa: E402
+from oracle import reference as REF  # noqa: E402
+from oracle import ring as RING  # noqa: E402
+from tests.gpu_util import dev, empty_bytes, encode, host, packed_strides, stream, ulp_diff  # noqa: E402
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+@pytest.mark.parametrize("stages", [1, 2, 3, 4])
+def test_ring_trace_matches_oracle_schedule(stages):
+    say(f"ring trace stages {stages}")
+    for n in range(0, 17):
+        for loads, stores in ((1, 0), (5, 4), (9, 8), (2, 1)):
+            ev = RING.schedule(n, stages, loads, stores)
+            out = torch.full((max(1, 3 * n) * 4,), -1, dtype=torch.int32, device="cuda:0")
+            acp.acp_debug_ring_trace(n, stages, loads, stores, out, stream())
+            got = host(out, np.int32).reshape(-1, 4)[:3 * n]
+            want = np.array([[e.kind, e.iteration, e.stage, e.count] for e in ev], dtype=np.int32).reshape(-1, 4)
+            assert np.array_equal(got, want), (n, stages, loads, stores)
+
+
+def _fma_case(shape, stage_box, box, stages, threads, workgroups, seed=4):
+    x, a, b = W.fma_rows_f32(shape, seed=seed)
+    xd, ad, bd = dev(x), dev(a), dev(b)
+    yd = empty_bytes(x.nbytes)
+    st = packed_strides(shape)
+    xdesc = encode("f32", xd, shape, st, box)
+    ydesc = encode("f32", yd, shape, st, box)
+    acp.acp_stream_ewise("fma", ydesc, xdesc, ad, bd, stage_box, stages, threads, workgroups, stream())
+    return x, a, b, host(yd, np.float32, shape)
+
+
+@pytest.mark.parametrize("stages", [2, 3, 4])
+@pytest.mark.parametrize("workgroups", [0, 8, 5])
+def test_c4_small_ragged_fma(stages, workgroups):
+    # 37 rows = 9 stages of 4 rows + 1: the last stage is cut; with
+    # workgroup tiles of 12 rows two stages of the last tile lie beyond the tensor
+    shape, stage_box = (3, 37, 1024), (1, 4, 1024)
+    box = (1, 12, 1024) if workgroups == 0 else stage_box
+    say(f"C4 small fma {shape} stage {stage_box} box {box} S={stages} wg={workgroups}")
+    x, a, b, y = _fma_case(shape, stage_box, box, stages, 256, workgroups)
+    ref = REF.stream_ewise("fma", x, a, b, np.float32)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("op", ["add", "mul"])
+def test_row_add_mul(op):
+    shape, stage_box = (2, 9, 512), (1, 2, 512)
+    say(f"row {op} {shape} stage {stage_box}")
+    x, a, b = W.fma_rows_f32(shape, seed=5)
+    xd, ad, bd = dev(x), dev(a), dev(b)
+    yd = empty_bytes(x.nbytes)
+    st = packed_strides(shape)
+    xdesc = encode("f32", xd, shape, st, stage_box)
+    ydesc = encode("f32", yd, shape, st, stage_box)
+    acp.acp_stream_ewise(op, ydesc, xdesc, ad if op == "mul" else None, bd if op == "add" else None,
+                         stage_box, 3, 128, 4, stream())
+    ref = REF.stream_ewise(op, x, a, b, np.float32)
+    assert np.array_equal(host(yd, np.float32, shape).view(np.uint32), ref.view(np.uint32))
+
+
+def test_many_rows_per_stage_and_two_scalar_loads():
+    # 48 rows per stage -> two 4-byte row-scalar loads per wave
+    shape, stage_box = (2, 100, 64), (1, 48, 64)
+    say(f"fma with 48 rows per stage {shape}")
+    x, a, b, y = _fma_case(shape, stage_box, stage_box, 3, 64, 0, seed=6)
+    ref = REF.stream_ewise("fma", x, a, b, np.float32)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+
+
+def test_c4_full_size_bench_config_sampled():
+    shape, stage_box = (128, 500, 1024), (1, 4, 1024)
+    say("C4 full fma [128,500,1024] stage (1,4,1024) S=4 persistent 512 workgroups")
+    x, a, b, y = _fma_case(shape, stage_box, stage_box, 4, 256, 512)
+    rng = np.random.default_rng(44)
+    i0 = rng.integers(0, 128, 3000)
+    i1 = rng.integers(0, 500, 3000)
+    ref = REF.stream_ewise("fma", x[i0, i1][:, None, :], a[i0, i1][:, None], b[i0, i1][:, None], np.float32)[:, 0]
+    assert np.array_equal(y[i0, i1].view(np.uint32), ref.view(np.uint32))
+    # every row was written (the buffer started as 0xA5A5A5A5 = -2.9e-16)
+    assert not np.any(y.view(np.uint32) == 0xA5A5A5A5)
+
+
+def _exp_table_on_gpu():
+    """GPU exp of every float16 in [-4, 4) (34817 values) through the C5 path."""
+    bits = np.concatenate([np.arange(0x0000, 0x4400), np.arange(0x8000, 0xC401)]).astype(np.uint16)
+    assert len(bits) == 34817
+    rows = -(-len(bits) // 64)
+    padded = np.zeros(rows * 64, np.uint16)
+    padded[:len(bits)] = bits
+    x = padded.view(np.float16).reshape(rows, 64)
+    xd = dev(x)
+    yd = empty_bytes(x.size * 4)
+    xdesc = encode("f16", xd, x.shape, (64, 1), (64, 64), acp.ACP_SWIZZLE_128B)
+    ydesc = encode("f32", yd, x.shape, (64, 1), (64, 64))
+    acp.acp_stream_ewise("exp", ydesc, xdesc, None, None, (8, 64), 4, 64, 0, stream())
+    y = host(yd, np.float32).reshape(-1)[:len(bits)]
+    return bits, y
+
+
+def test_exp_exhaustive_f16_inputs_within_one_ulp():
+    say("exp over all 34817 float16 inputs in [-4, 4)")
+    bits, y = _exp_table_on_gpu()
+    ref = REF.ewise("exp", [bits.view(np.float16)], np.float32)
+    d = ulp_diff(y, ref)
+    assert d.max() <= 1
+    print(f"exp table: {np.count_nonzero(d == 0)} / {len(d)} bit-exact", flush=True)
+
+
+def test_c5_small_rank5_exp():
+    shape, pitch = (1, 2, 4, 64, 128), 136
+    say(f"C5 small rank-5 exp {shape} pitch {pitch}")
+    storage, strides = W.padded_uniform_f16(shape, pitch=pitch, seed=5)
+    xd = dev(storage)
+    n = int(np.prod(shape))
+    yd = empty_bytes(n * 4)
+    xdesc = encode("f16", xd, shape, strides, (1, 2, 4, 64, 64), acp.ACP_SWIZZLE_128B)
+    ydesc = encode("f32", yd, shape, packed_strides(shape), (1, 2, 4, 64, 64))
+    acp.acp_stream_ewise("exp", ydesc, xdesc, None, None, (1, 1, 1, 64, 64), 4, 256, 0, stream())
+    y = host(yd, np.float32, shape)
+    x = W.strided_view(storage, shape, strides)
+    ref = REF.ewise("exp", [x], np.float32)
+    assert not np.any(np.isnan(y))
+    assert ulp_diff(y.reshape(-1), ref.reshape(-1)).max() <= 1
+
+
+def test_c5_full_size_matches_exp_table():
+    shape, pitch = (4, 8, 64, 128, 256), 264
+    say(f"C5 full rank-5 exp {shape} pitch {pitch}, box (1,2,16,64,64), stage (1,1,1,64,64), S=4")
+    bits, table = _exp_table_on_gpu()
+    lut = torch.zeros(65536, dtype=torch.int32, device="cuda:0")
+    lut[torch.from_numpy(bits.astype(np.int64)).cuda()] = torch.from_numpy(table.view(np.int32).copy()).cuda()
+    storage, strides = W.padded_uniform_f16(shape, pitch=pitch, seed=5)
+    xd = dev(storage)
+    n = int(np.prod(shape))
+    yd = empty_bytes(n * 4)
+    box = (1, 2, 16, 64, 64)
+    xdesc = encode("f16", xd, shape, strides, box, acp.ACP_SWIZZLE_128B)
+    ydesc = encode("f32", yd, shape, packed_strides(shape), box)
+    info = acp.acp_plan_query(xdesc, 256, copy_only=False)
+    assert info["rank"] == 5
+    acp.acp_stream_ewise("exp", ydesc, xdesc, None, None, (1, 1, 1, 64, 64), 4, 256, 0, stream())
+    torch.cuda.synchronize()
+    xbits = xd.view(torch.int16).view(-1, pitch)[:, :256].reshape(-1).to(torch.int64) & 0xFFFF
+    want = lut[xbits]
+    got = yd.view(torch.int32)
+    assert torch.equal(got, want)
+    assert not torch.isnan(yd.view(torch.float32)).any()

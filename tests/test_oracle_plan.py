@@ -102,7 +102,10 @@ def test_invalid_requests():
     with pytest.raises(P.Invalid):
         P.plan("f16", (8, 256), (256, 1), (8, 256), threads=96)
     with pytest.raises(P.Invalid):
-        P.plan("f16", (8, 0), (256, 1), (8, 256))
+        P.plan("f16", (8, -1), (256, 1), (8, 256))
+    # extent 0 is an empty tensor: a valid plan that covers no tiles
+    p = P.plan("f16", (0, 256), (256, 1), (8, 256))
+    assert P.tile_grid(p.shape, p.box) == (0, 1)
     with pytest.raises(P.Invalid):
         P.plan("f16", (8,) * 9, (1,) * 9, (1,) * 9)
 
