@@ -23,6 +23,14 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python -m async_copy_pipelining_amd.build` "
         "(the HIP library is the only implementation)")
 
+try:
+    # torch bundles its own HIP runtime under the same soname; loading torch
+    # first makes libacp.so bind to that copy, so torch-allocated memory and
+    # streams and acp's launches live in one runtime.
+    import torch  # noqa: F401
+except ImportError:  # pragma: no cover - acp itself does not need torch
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 # acp_status

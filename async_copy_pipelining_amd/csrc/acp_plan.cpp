@@ -114,8 +114,8 @@ PlanStatus plan_box_with(const DescData& dd, const int32_t* boxp, bool copy_only
   if (dd.swizzle != 0 && dd.swizzle != 3)
     return fail(reason, PlanStatus::Invalid, "swizzle must be none or 128-byte");
   for (int d = 0; d < r; ++d)
-    if (dd.shape[d] < 1 || dd.strides[d] < 1 || boxp[d] < 1)
-      return fail(reason, PlanStatus::Invalid, "extents, strides and box must be >= 1");
+    if (dd.shape[d] < 0 || dd.strides[d] < 1 || boxp[d] < 1)
+      return fail(reason, PlanStatus::Invalid, "extents must be >= 0 (0: an empty tensor), strides and box >= 1");
 
   Plan p;
   p.esize = es;

@@ -123,7 +123,7 @@ def test_other_element_types(dt, np_dt):
     st = packed_strides(shape)
     src = encode(dt, xd, shape, st, box)
     dst = encode(dt, yd, shape, st, box)
-    acp.acp_tile_copy(src, dst, 64, stream())
+    acp.acp_tile_copy(src, dst, 256, stream())
     assert np.array_equal(host(yd, np.uint8), x)
 
 

@@ -75,7 +75,7 @@ def test_many_rows_per_stage_and_two_scalar_loads():
     # 48 rows per stage -> two 4-byte row-scalar loads per wave
     shape, stage_box = (2, 100, 64), (1, 48, 64)
     say(f"fma with 48 rows per stage {shape}")
-    x, a, b, y = _fma_case(shape, stage_box, stage_box, 3, 64, 0, seed=6)
+    x, a, b, y = _fma_case(shape, stage_box, stage_box, 3, 256, 0, seed=6)
     ref = REF.stream_ewise("fma", x, a, b, np.float32)
     assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
 
@@ -94,9 +94,10 @@ def test_c4_full_size_bench_config_sampled():
 
 
 def _exp_table_on_gpu():
-    """GPU exp of every float16 in [-4, 4) (34817 values) through the C5 path."""
-    bits = np.concatenate([np.arange(0x0000, 0x4400), np.arange(0x8000, 0xC401)]).astype(np.uint16)
-    assert len(bits) == 34817
+    """GPU exp of every float16 in [-4, 4] (34818 values: U(-4, 4) rounded to
+    float16 reaches +4.0 as well) through the C5 path."""
+    bits = np.concatenate([np.arange(0x0000, 0x4401), np.arange(0x8000, 0xC401)]).astype(np.uint16)
+    assert len(bits) == 34818
     rows = -(-len(bits) // 64)
     padded = np.zeros(rows * 64, np.uint16)
     padded[:len(bits)] = bits
@@ -111,7 +112,7 @@ def _exp_table_on_gpu():
 
 
 def test_exp_exhaustive_f16_inputs_within_one_ulp():
-    say("exp over all 34817 float16 inputs in [-4, 4)")
+    say("exp over all 34818 float16 inputs in [-4, 4]")
     bits, y = _exp_table_on_gpu()
     ref = REF.ewise("exp", [bits.view(np.float16)], np.float32)
     d = ulp_diff(y, ref)
