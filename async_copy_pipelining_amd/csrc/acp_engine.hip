@@ -20,12 +20,13 @@ __global__ __launch_bounds__(1024) void lds_image_kernel_t(const EngineArgs, uns
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   const int lane = threadIdx.x & 63;
   const int wave = uni(static_cast<int>(threadIdx.x >> 6));
+  const Loc L = load_loc(A);
   LaneMap m;
   build_map<VB>(A, wave, lane, m);
   uint64_t row_ptr[3] = {0, 0, 0};
   uint32_t row_bad[2] = {~0u, ~0u};
-  const Trip t = trip_geometry(A, 0, 1, 0);
-  issue_loads<VB>(A, m, t, lds0, wave, row_ptr, row_bad);
+  const Trip t = trip_geometry(A, L, 0, 1, 0);
+  issue_loads<VB>(L, m, t, lds0, wave, row_ptr, row_bad);
   wait_vmcnt(0);
   __syncthreads();
   for (uint32_t o = threadIdx.x * 4u; o < bytes; o += blockDim.x * 4u)

@@ -60,6 +60,14 @@ struct EngineArgs {
   // buffer resources end there, so no access can leave its tensor
   uint64_t in_span, out_span;
   uint64_t total_rows;       // rows of the per-row scalar arrays
+  // Linear stage grid: one stage per tile, no partial stage and a row-major
+  // contiguous grid, so stage t starts at t * lin_x input bytes, t * lin_o
+  // output bytes and row t * lin_r.  lin == 0 selects the general path.
+  int32_t lin;
+  int64_t lin_x, lin_o, lin_r;
+  // cache policy of the direct-to-LDS loads and of the stores: 0 default,
+  // 1 non-temporal (streamed data, no reuse expected)
+  int32_t load_nt, store_nt;
 };
 
 // Which kernel variant a launch needs.
@@ -68,7 +76,8 @@ struct KernelKey {
   int tin;       // acp_dtype of staged operands
   int tout;      // acp_dtype of the output
   int vec_bytes; // 16 or 4
-  int mode;      // 0 copy, 1 tile ewise (output staged in LDS), 2 stream
+  int mode;      // 0 copy, 1 tile ewise (output staged in LDS), 2 stream, 3 stream on a linear grid
+  int outer;     // mode 3: rounds per thread (1, 2, 4 or 8); 0 otherwise
 };
 
 // Kernel for `key`, or nullptr when that combination is not built.

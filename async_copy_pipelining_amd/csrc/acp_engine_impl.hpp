@@ -87,13 +87,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_store(void* base, uint32_
 
 // s_nop 4 covers the wait states between an SGPR / M0 write and a
 // direct-to-LDS instruction reading it.
-__device__ __forceinline__ void dma_b128(v4i rsrc, uint32_t voff, uint32_t m0) {
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0)
-               : "memory");
+__device__ __forceinline__ void dma_b128(v4i rsrc, uint32_t voff, uint32_t m0, bool nt) {
+  if (nt)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0)
+                 : "memory");
+  else
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0)
+                 : "memory");
 }
-__device__ __forceinline__ void dma_b32(v4i rsrc, uint32_t voff, uint32_t m0) {
-  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0)
-               : "memory");
+__device__ __forceinline__ void dma_b32(v4i rsrc, uint32_t voff, uint32_t m0, bool nt) {
+  if (nt)
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0)
+                 : "memory");
+  else
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0)
+                 : "memory");
 }
 __device__ __forceinline__ void dma_global_b32(const void* addr, uint32_t m0) {
   asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, off" ::"v"(addr), "{m0}"(m0) : "memory");
@@ -301,17 +309,76 @@ __device__ __forceinline__ void build_map(CArgs* A, int wave, int lane, LaneMap&
   }
 }
 
+// Launch values the ring touches every trip, read from the argument block
+// once: they then live in registers across the asm statements (whose memory
+// clobbers would otherwise force a reload of every argument per trip).
+struct Loc {
+  const char* in[3];
+  char* out;
+  uint64_t in_span, out_span, total_rows;
+  int64_t lin_x, lin_o, lin_r;
+  int lin, load_nt, store_nt;
+  int outer, waves, n_in, row_ops, ab_instr;
+  uint32_t in_image_bytes, slot_bytes, ab_off, ab_wave_bytes, out_image_off, subs, tile0;
+};
+
+__device__ __forceinline__ uint64_t uni64(uint64_t v) {
+  return (static_cast<uint64_t>(uni(static_cast<uint32_t>(v >> 32))) << 32) | uni(static_cast<uint32_t>(v));
+}
+template <typename P> __device__ __forceinline__ P* unip(P* p) {
+  return reinterpret_cast<P*>(uni64(reinterpret_cast<uint64_t>(p)));
+}
+
+// Every value passes through readfirstlane: the result is a register value
+// the compiler cannot re-derive by reloading the argument block inside the
+// ring (a reload would also cost an lgkmcnt wait that drains the LDS reads).
+__device__ __forceinline__ Loc load_loc(CArgs* A) {
+  Loc L;
+  for (int k = 0; k < 3; ++k) L.in[k] = unip(A->in[k]);
+  L.out = unip(A->out);
+  L.in_span = uni64(A->in_span);
+  L.out_span = uni64(A->out_span);
+  L.total_rows = uni64(A->total_rows);
+  L.lin_x = static_cast<int64_t>(uni64(static_cast<uint64_t>(A->lin_x)));
+  L.lin_o = static_cast<int64_t>(uni64(static_cast<uint64_t>(A->lin_o)));
+  L.lin_r = static_cast<int64_t>(uni64(static_cast<uint64_t>(A->lin_r)));
+  L.lin = uni(A->lin);
+  L.load_nt = uni(A->load_nt);
+  L.store_nt = uni(A->store_nt);
+  L.outer = uni(A->outer);
+  L.waves = uni(A->waves);
+  L.n_in = uni(A->n_in);
+  L.row_ops = uni(A->row_ops);
+  L.ab_instr = uni(A->ab_instr);
+  L.in_image_bytes = uni(A->in_image_bytes);
+  L.slot_bytes = uni(A->slot_bytes);
+  L.ab_off = uni(A->ab_off);
+  L.ab_wave_bytes = uni(A->ab_wave_bytes);
+  L.out_image_off = uni(A->out_image_off);
+  L.subs = uni(A->subs);
+  L.tile0 = uni(A->tile0);
+  return L;
+}
+
 struct Trip {
   uint64_t xbase, obase, rbase;
   uint32_t last;   // partial slots along which this stage is the cut last one
   bool beyond;     // stage lies entirely past the tensor
 };
 
-__device__ __forceinline__ Trip trip_geometry(CArgs* A, uint32_t wg, uint32_t grid, int j) {
-  const uint32_t tl = mdiv(static_cast<uint32_t>(j), A->subs_mag, A->subs_sh);
-  uint32_t sub = static_cast<uint32_t>(j) - tl * A->subs;
-  uint32_t tile = A->tile0 + wg + tl * grid;
+__device__ __forceinline__ Trip trip_geometry(CArgs* A, const Loc& L, uint32_t wg, uint32_t grid, int j) {
   Trip t{0, 0, 0, 0u, false};
+  if (L.lin) {
+    // one stage per tile, exact tiling, row-major contiguous grid
+    const uint64_t s = static_cast<uint64_t>(L.tile0) + wg + static_cast<uint64_t>(j) * grid;
+    t.xbase = s * static_cast<uint64_t>(L.lin_x);
+    t.obase = s * static_cast<uint64_t>(L.lin_o);
+    t.rbase = s * static_cast<uint64_t>(L.lin_r);
+    return t;
+  }
+  const uint32_t tl = mdiv(static_cast<uint32_t>(j), A->subs_mag, A->subs_sh);
+  uint32_t sub = static_cast<uint32_t>(j) - tl * L.subs;
+  uint32_t tile = L.tile0 + wg + tl * grid;
 #pragma nounroll
   for (int d = A->rank - 1; d >= 0; --d) {
     const uint32_t qt = mdiv(tile, A->tg_mag[d], A->tg_sh[d]);
@@ -369,54 +436,64 @@ __device__ __forceinline__ void build_rows(CArgs* A, int lane, uint64_t* row_ptr
 // Loads of one trip into one slot: every staged operand (outer rounds of
 // VB-byte direct-to-LDS loads) and, for row ops, the stage's per-row scalars.
 template <int VB>
-__device__ __forceinline__ void issue_loads(CArgs* A, const LaneMap& m, const Trip& t, uint32_t slot_lds, int wave,
+__device__ __forceinline__ void issue_loads(const Loc& L, const LaneMap& m, const Trip& t, uint32_t slot_lds, int wave,
                                             const uint64_t* row_ptr, const uint32_t* row_bad) {
-  const int outer = A->outer, waves = A->waves, n_in = A->n_in;
+  const bool nt = L.load_nt != 0;
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
-    if (k >= n_in) continue;
-    const v4i rs = rsrc_v4(A->in[k] + t.xbase, range_from(A->in_span, t.xbase));
-    const uint32_t img = slot_lds + k * A->in_image_bytes;
+    if (k >= L.n_in) continue;
+    const v4i rs = rsrc_v4(L.in[k] + t.xbase, range_from(L.in_span, t.xbase));
+    const uint32_t img = slot_lds + k * L.in_image_bytes;
 #pragma unroll
     for (int f = 0; f < kMaxOuter; ++f) {
-      if (f >= outer) continue;
+      if (f >= L.outer) continue;
       const bool ok = !t.beyond && (m.oobm[f] & t.last) == 0;
       const uint32_t voff = ok ? m.xoff[f] : kOobOffset;
-      const uint32_t m0 = img + (f * waves + wave) * 64u * VB;
+      const uint32_t m0 = img + (f * L.waves + wave) * 64u * VB;
       if constexpr (VB == 16)
-        dma_b128(rs, voff, m0);
+        dma_b128(rs, voff, m0, nt);
       else
-        dma_b32(rs, voff, m0);
+        dma_b32(rs, voff, m0, nt);
     }
   }
-  if (A->row_ops) {
+  if (L.row_ops) {
     // rows that do not exist (or lie past the edge) read row 0 of the array
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      if (q >= A->ab_instr) continue;
+      if (q >= L.ab_instr) continue;
       const bool ok = !t.beyond && (row_bad[q] & t.last) == 0;
       uint64_t row = ok ? t.rbase + row_ptr[1 + q] / 4u : 0u;
-      if (row >= A->total_rows) row = 0;
+      if (row >= L.total_rows) row = 0;
       const uint64_t addr = row_ptr[0] + row * 4u;
-      dma_global_b32(reinterpret_cast<const void*>(addr), slot_lds + A->ab_off + wave * A->ab_wave_bytes + q * 256u);
+      dma_global_b32(reinterpret_cast<const void*>(addr), slot_lds + L.ab_off + wave * L.ab_wave_bytes + q * 256u);
     }
   }
 }
 
-template <int OB>
-__device__ __forceinline__ void store_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t voff, const uint32_t* w) {
+template <int OB, int CP>
+__device__ __forceinline__ void store_chunk_cp(__amdgpu_buffer_rsrc_t rs, uint32_t voff, const uint32_t* w) {
   if constexpr (OB == 32) {
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rs, voff, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[4], w[5], w[6], w[7]}, rs, voff + 16u, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rs, voff, 0, CP);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[4], w[5], w[6], w[7]}, rs, voff + 16u, 0, CP);
   } else if constexpr (OB == 16) {
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rs, voff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rs, voff, 0, CP);
   } else if constexpr (OB == 8) {
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, rs, voff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, rs, voff, 0, CP);
   } else if constexpr (OB == 4) {
-    __builtin_amdgcn_raw_buffer_store_b32(w[0], rs, voff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(w[0], rs, voff, 0, CP);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w[0]), rs, voff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w[0]), rs, voff, 0, CP);
   }
+}
+
+// Stores go out non-temporal (cache policy bit NT) unless disabled: the
+// output is written once and never read back by the kernel.
+template <int OB>
+__device__ __forceinline__ void store_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t voff, const uint32_t* w, bool nt) {
+  if (nt)
+    store_chunk_cp<OB, 2>(rs, voff, w);
+  else
+    store_chunk_cp<OB, 0>(rs, voff, w);
 }
 
 template <class OP, int VB>
@@ -431,14 +508,14 @@ struct ChunkShape {
 // Consume one trip: read the staged chunks, apply the op, (tile ewise) write
 // the result into the slot's output image and read it back, store.
 template <class OP, int VB, bool STAGE_OUT>
-__device__ __forceinline__ void consume_trip(CArgs* A, const LaneMap& m, const Trip& t, unsigned char* lds,
-                                             uint32_t slot, int wave, int lane) {
+__device__ __forceinline__ void consume_trip(const Loc& L, int esize_log2, int swizzle, const LaneMap& m,
+                                             const Trip& t, unsigned char* lds, uint32_t slot, int wave, int lane) {
   typedef ChunkShape<OP, VB> CS;
   typedef typename OP::TI TI;
   typedef typename OP::TO TO;
-  const int outer = A->outer, waves = A->waves;
-  const uint32_t in_img = A->in_image_bytes;
-  const __amdgpu_buffer_rsrc_t rs = rsrc_store(A->out + t.obase, range_from(A->out_span, t.obase));
+  const int outer = L.outer, waves = L.waves;
+  const uint32_t in_img = L.in_image_bytes;
+  const __amdgpu_buffer_rsrc_t rs = rsrc_store(L.out + t.obase, range_from(L.out_span, t.obase));
 #pragma unroll
   for (int f = 0; f < kMaxOuter; ++f) {
     if (f >= outer) continue;
@@ -458,7 +535,7 @@ __device__ __forceinline__ void consume_trip(CArgs* A, const LaneMap& m, const T
     }
     float ra = 0.f, rb = 0.f;
     if constexpr (OP::ROW) {
-      const uint32_t ab = slot + A->ab_off + wave * A->ab_wave_bytes + m.abo[f];
+      const uint32_t ab = slot + L.ab_off + wave * L.ab_wave_bytes + m.abo[f];
       ra = *reinterpret_cast<const float*>(lds + ab);
       rb = *reinterpret_cast<const float*>(lds + ab + 128u);
     }
@@ -471,44 +548,45 @@ __device__ __forceinline__ void consume_trip(CArgs* A, const LaneMap& m, const T
     if constexpr (STAGE_OUT) {
       // the output tile lives in LDS ("elementwise -> smem": every operand,
       // the output included, is in shared memory) and is copied out from there
-      const uint32_t lo = (m.lpos[f] >> A->esize_log2) * CS::EO;
+      const uint32_t lo = (m.lpos[f] >> esize_log2) * CS::EO;
       constexpr int P = (CS::OB + 15) / 16;
       constexpr int PB = CS::OB < 16 ? CS::OB : 16;
 #pragma unroll
       for (int piece = 0; piece < P; ++piece) {
         const uint32_t lp = lo + piece * 16;
-        __builtin_memcpy(lds + slot + A->out_image_off + (A->swizzle ? swz128(lp) : lp), words + piece * 4, PB);
+        __builtin_memcpy(lds + slot + L.out_image_off + (swizzle ? swz128(lp) : lp), words + piece * 4, PB);
       }
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int piece = 0; piece < P; ++piece) {
         const uint32_t lp = lo + piece * 16;
-        __builtin_memcpy(words + piece * 4, lds + slot + A->out_image_off + (A->swizzle ? swz128(lp) : lp), PB);
+        __builtin_memcpy(words + piece * 4, lds + slot + L.out_image_off + (swizzle ? swz128(lp) : lp), PB);
       }
     }
     const bool ok = !t.beyond && (m.oobm[f] & t.last) == 0;
-    store_chunk<CS::OB>(rs, ok ? m.ooff[f] : kOobOffset, words);
+    store_chunk<CS::OB>(rs, ok ? m.ooff[f] : kOobOffset, words, L.store_nt != 0);
   }
 }
 
 template <class OP, int VB, bool STAGE_OUT>
 struct EnginePolicy {
   CArgs* A;
+  const Loc& L;
   const LaneMap& m;
   unsigned char* lds;
   uint32_t lds0, wg, grid;
-  int wave, lane;
+  int wave, lane, esize_log2, swizzle;
   const uint64_t* row_ptr;
   const uint32_t* row_bad;
 
   __device__ __forceinline__ void load(int j, int slot) {
-    const Trip t = trip_geometry(A, wg, grid, j);
-    issue_loads<VB>(A, m, t, lds0 + slot * A->slot_bytes, wave, row_ptr, row_bad);
+    const Trip t = trip_geometry(A, L, wg, grid, j);
+    issue_loads<VB>(L, m, t, lds0 + slot * L.slot_bytes, wave, row_ptr, row_bad);
   }
   __device__ __forceinline__ void wait(int, int, int k) { wait_vmcnt(k); }
   __device__ __forceinline__ void consume(int i, int slot) {
-    const Trip t = trip_geometry(A, wg, grid, i);
-    consume_trip<OP, VB, STAGE_OUT>(A, m, t, lds, slot * A->slot_bytes, wave, lane);
+    const Trip t = trip_geometry(A, L, wg, grid, i);
+    consume_trip<OP, VB, STAGE_OUT>(L, esize_log2, swizzle, m, t, lds, slot * L.slot_bytes, wave, lane);
   }
 };
 
@@ -528,16 +606,149 @@ __global__ __launch_bounds__(1024) void engine_kernel_t(const EngineArgs) {
   const uint32_t tiles = wg < n_tiles ? (n_tiles - wg + grid - 1) / grid : 0;
   const int n = static_cast<int>(tiles * A->subs);
   if (n == 0) return;
+  const Loc L = load_loc(A);
+  const int esize_log2 = A->esize_log2, swizzle = A->swizzle, stages = A->stages;
   LaneMap m;
   build_map<VB>(A, wave, lane, m);
   uint64_t row_ptr[3];
   uint32_t row_bad[2];
   build_rows(A, lane, row_ptr, row_bad);
-  EnginePolicy<OP, VB, STAGE_OUT> pol{A, m, lds, lds0, wg, grid, wave, lane, row_ptr, row_bad};
+  EnginePolicy<OP, VB, STAGE_OUT> pol{A, L, m, lds, lds0, wg, grid, wave, lane, esize_log2, swizzle, row_ptr, row_bad};
   typedef ChunkShape<OP, VB> CS;
-  const int d = A->n_in * A->outer + (A->row_ops ? A->ab_instr : 0);
-  const int st = A->outer * CS::ST;
-  run_ring(pol, n, A->stages, d, st);
+  const int d = L.n_in * L.outer + (L.row_ops ? L.ab_instr : 0);
+  const int st = L.outer * CS::ST;
+  run_ring(pol, n, stages, d, st);
+}
+
+// ---------------------------------------------------------------------------
+// Streaming fast path: a linear stage grid (one full stage per tile, row-major
+// contiguous), 16-byte rounds, one staged operand, OUTER rounds per thread
+// known at compile time.  Same ring control and wait counts as the general
+// engine; per trip only the stage base (one multiply) changes, and no chunk
+// can be out of bounds.
+
+template <class OP, int OUTER>
+struct LinPolicy {
+  unsigned char* lds;
+  const char* in0;
+  char* out;
+  uint64_t in_span, out_span;
+  uint64_t lin_x, lin_o, lin_r, total_rows;
+  uint32_t lds0, slot_bytes, ab_base, wg, grid, waves_kb;  // waves_kb: LDS bytes of one round
+  int wave, lane, ab_instr;
+  bool load_nt, store_nt;
+  uint32_t xoff[OUTER], ooff[OUTER], abo[OUTER];
+  const uint64_t* row_ptr;   // [0] lane's array, [1 + q] row byte offset in the stage
+  const uint32_t* row_ok;    // lane has a row in load q
+
+  __device__ __forceinline__ uint64_t stage(int j) const { return wg + static_cast<uint64_t>(j) * grid; }
+
+  __device__ __forceinline__ void load(int j, int slot) {
+    const uint64_t s = stage(j);
+    const uint64_t xb = s * lin_x;
+    const v4i rs = rsrc_v4(in0 + xb, range_from(in_span, xb));
+    const uint32_t base = lds0 + slot * slot_bytes + wave * 1024u;
+#pragma unroll
+    for (int f = 0; f < OUTER; ++f) dma_b128(rs, xoff[f], base + f * waves_kb, load_nt);
+    if constexpr (OP::ROW) {
+      const uint64_t rb = s * lin_r;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (q >= ab_instr) continue;
+        uint64_t row = row_ok[q] ? rb + row_ptr[1 + q] / 4u : 0u;
+        if (row >= total_rows) row = 0;
+        const uint64_t addr = row_ptr[0] + row * 4u;
+        dma_global_b32(reinterpret_cast<const void*>(addr), lds0 + slot * slot_bytes + ab_base + q * 256u);
+      }
+    }
+  }
+  __device__ __forceinline__ void wait(int, int, int k) { wait_vmcnt(k); }
+
+  __device__ __forceinline__ void consume(int i, int slot) {
+    typedef ChunkShape<OP, 16> CS;
+    typedef typename OP::TI TI;
+    typedef typename OP::TO TO;
+    const uint64_t s = stage(i);
+    const uint64_t ob = s * lin_o;
+    const __amdgpu_buffer_rsrc_t rs = rsrc_store(out + ob, range_from(out_span, ob));
+    const uint32_t sl = slot * slot_bytes;
+    u32x4 v[OUTER];
+    float ra[OUTER], rb[OUTER];
+#pragma unroll
+    for (int f = 0; f < OUTER; ++f) {
+      v[f] = *reinterpret_cast<const u32x4*>(__builtin_assume_aligned(lds + sl + f * waves_kb + wave * 1024u + lane * 16u, 16));
+      if constexpr (OP::ROW) {
+        ra[f] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f]);
+        rb[f] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f] + 128u);
+      } else {
+        ra[f] = rb[f] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < OUTER; ++f) {
+      TI in[CS::NE];
+      __builtin_memcpy(in, &v[f], 16);
+      TO res[CS::NE];
+#pragma unroll
+      for (int e = 0; e < CS::NE; ++e) res[e] = OP::f(in[e], in[e], in[e], ra[f], rb[f]);
+      uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      __builtin_memcpy(words, res, CS::OB);
+      store_chunk<CS::OB>(rs, ooff[f], words, store_nt);
+    }
+  }
+};
+
+template <class OP, int OUTER>
+__global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+  CArgs* A = kargs();
+  const int lane = threadIdx.x & 63;
+  const int wave = uni(static_cast<int>(threadIdx.x >> 6));
+  const uint32_t grid = gridDim.x;
+  uint32_t wg = blockIdx.x;
+  if (A->xcd_remap) wg = (wg & 7u) * (grid >> 3) + (wg >> 3);
+  const uint32_t n_tiles = A->n_tiles;
+  const int n = static_cast<int>(wg < n_tiles ? (n_tiles - wg + grid - 1) / grid : 0);
+  if (n == 0) return;
+  LaneMap m;
+  build_map<16>(A, wave, lane, m);
+  uint64_t row_ptr[3];
+  uint32_t row_bad[2];
+  build_rows(A, lane, row_ptr, row_bad);
+  uint32_t row_ok[2] = {row_bad[0] == 0u, row_bad[1] == 0u};
+  const Loc L = load_loc(A);
+  LinPolicy<OP, OUTER> p;
+  p.lds = lds;
+  p.in0 = L.in[0];
+  p.out = L.out;
+  p.in_span = L.in_span;
+  p.out_span = L.out_span;
+  p.lin_x = static_cast<uint64_t>(L.lin_x);
+  p.lin_o = static_cast<uint64_t>(L.lin_o);
+  p.lin_r = static_cast<uint64_t>(L.lin_r);
+  p.total_rows = L.total_rows;
+  p.lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  p.slot_bytes = L.slot_bytes;
+  p.ab_base = L.ab_off + wave * L.ab_wave_bytes;
+  p.wg = wg;
+  p.grid = grid;
+  p.wave = wave;
+  p.lane = lane;
+  p.ab_instr = L.ab_instr;
+  p.load_nt = L.load_nt != 0;
+  p.store_nt = L.store_nt != 0;
+  p.waves_kb = static_cast<uint32_t>(L.waves) * 1024u;
+#pragma unroll
+  for (int f = 0; f < OUTER; ++f) {
+    p.xoff[f] = m.xoff[f];
+    p.ooff[f] = m.ooff[f];
+    p.abo[f] = m.abo[f];
+  }
+  p.row_ptr = row_ptr;
+  p.row_ok = row_ok;
+  typedef ChunkShape<OP, 16> CS;
+  const int d = OUTER + (OP::ROW ? L.ab_instr : 0);
+  run_ring(p, n, uni(A->stages), d, OUTER * CS::ST);
 }
 
 }  // namespace dev
@@ -548,15 +759,20 @@ struct KernelEntry {
 };
 
 #define ACP_K(OPC, TIN, TOUT, VB, MODE, ...) \
-  KernelEntry{KernelKey{OPC, TIN, TOUT, VB, MODE}, \
+  KernelEntry{KernelKey{OPC, TIN, TOUT, VB, MODE, 0}, \
               reinterpret_cast<const void*>(&dev::engine_kernel_t<__VA_ARGS__, VB, (MODE == 1)>)}
+#define ACP_L(OPC, TIN, TOUT, OUTER, ...) \
+  KernelEntry{KernelKey{OPC, TIN, TOUT, 16, 3, OUTER}, reinterpret_cast<const void*>(&dev::stream_lin_kernel_t<__VA_ARGS__, OUTER>)}
+#define ACP_LIN(OPC, TIN, TOUT, ...) \
+  ACP_L(OPC, TIN, TOUT, 1, __VA_ARGS__), ACP_L(OPC, TIN, TOUT, 2, __VA_ARGS__), ACP_L(OPC, TIN, TOUT, 4, __VA_ARGS__), \
+      ACP_L(OPC, TIN, TOUT, 8, __VA_ARGS__)
 #define ACP_BOTH(OPC, TIN, TOUT, MODE, ...) ACP_K(OPC, TIN, TOUT, 16, MODE, __VA_ARGS__), ACP_K(OPC, TIN, TOUT, 4, MODE, __VA_ARGS__)
 
 template <size_t N>
 const void* find_entry(const KernelEntry (&table)[N], const KernelKey& k) {
   for (const KernelEntry& e : table)
     if (e.key.op == k.op && e.key.tin == k.tin && e.key.tout == k.tout && e.key.vec_bytes == k.vec_bytes &&
-        e.key.mode == k.mode)
+        e.key.mode == k.mode && e.key.outer == k.outer)
       return e.fn;
   return nullptr;
 }

@@ -10,6 +10,12 @@ const KernelEntry kTable[] = {
     ACP_BOTH(kOpSqrt, kF16, kF16, 2, Op<kOpSqrt, kF16, kF16>),
     ACP_BOTH(kOpExp, kF16, kF32, 2, Op<kOpExp, kF16, kF32>),
     ACP_BOTH(kOpExp, kF16, kF16, 2, Op<kOpExp, kF16, kF16>),
+    // linear-grid fast path
+    ACP_LIN(kOpZero, kF16, kF16, Op<kOpZero, kF16, kF16>),
+    ACP_LIN(kOpSqrt, kF16, kF32, Op<kOpSqrt, kF16, kF32>),
+    ACP_LIN(kOpSqrt, kF16, kF16, Op<kOpSqrt, kF16, kF16>),
+    ACP_LIN(kOpExp, kF16, kF32, Op<kOpExp, kF16, kF32>),
+    ACP_LIN(kOpExp, kF16, kF16, Op<kOpExp, kF16, kF16>),
 };
 }  // namespace
 const void* lookup_stream_f16(const KernelKey& k) { return find_entry(kTable, k); }

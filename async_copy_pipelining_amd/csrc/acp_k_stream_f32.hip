@@ -13,6 +13,15 @@ const KernelEntry kTable[] = {
     ACP_BOTH(kOpAdd, kF32, kF32, 2, RowOp<kOpAdd>),
     ACP_BOTH(kOpMul, kF32, kF32, 2, RowOp<kOpMul>),
     ACP_BOTH(kOpFma, kF32, kF32, 2, RowOp<kOpFma>),
+    // linear-grid fast path
+    ACP_LIN(kOpZero, kF32, kF32, Op<kOpZero, kF32, kF32>),
+    ACP_LIN(kOpSqrt, kF32, kF32, Op<kOpSqrt, kF32, kF32>),
+    ACP_LIN(kOpSqrt, kF32, kF16, Op<kOpSqrt, kF32, kF16>),
+    ACP_LIN(kOpExp, kF32, kF32, Op<kOpExp, kF32, kF32>),
+    ACP_LIN(kOpExp, kF32, kF16, Op<kOpExp, kF32, kF16>),
+    ACP_LIN(kOpAdd, kF32, kF32, RowOp<kOpAdd>),
+    ACP_LIN(kOpMul, kF32, kF32, RowOp<kOpMul>),
+    ACP_LIN(kOpFma, kF32, kF32, RowOp<kOpFma>),
 };
 }  // namespace
 const void* lookup_stream_f32(const KernelKey& k) { return find_entry(kTable, k); }
