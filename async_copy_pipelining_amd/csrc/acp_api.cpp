@@ -65,10 +65,15 @@ int device_lds_limit() {
 //   ACP_XCD_REMAP=0  keep blockIdx order for persistent grids (default: tiles
 //                    of consecutive workgroups stay on one XCD)
 //   ACP_STORE_NT=0   cached stores (default: non-temporal)
-//   ACP_LOAD_NT=0    cached direct-to-LDS loads (default: non-temporal)
+//   ACP_LOAD_NT=0|1  cached / non-temporal direct-to-LDS loads (default:
+//                    non-temporal for contiguous stages on a linear grid)
 // Non-temporal on both sides measured 6.2 TB/s against 5.8 TB/s cached for
-// the 262 MB fp32 stream (the staged data is touched once).
-//   ACP_FAST_PATH=0  always use the general engine for streaming
+// the 262 MB fp32 stream (the staged data is touched once); cached loads
+// measured 3.6 against 3.1 TB/s for 128x32 float16 tiles, whose 64-byte rows
+// share each cache line with the neighbouring tile.
+//   ACP_FAST_PATH=0  no linear-grid streaming kernel
+//   ACP_GEN_PATH=0   no general lean kernel (the rolled engine runs instead)
+//   ACP_SCALAR_ROWS=0  stage per-row scalars in LDS even when rows are uniform per wave block
 bool env_flag(const char* name, bool dflt) {
   const char* e = std::getenv(name);
   if (!e || !e[0]) return dflt;
@@ -244,10 +249,18 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
     A.lin_o = lin ? lo : 0;
     A.lin_r = lin ? lr : 0;
   }
+  // Loads go out non-temporal only where no two stages share a cache line:
+  // a linear grid of contiguous stages (each input byte is read once).
+  // Elsewhere (2-D tiles whose rows are shorter than a line, padded rows)
+  // the neighbouring stage reads the rest of the line from L2.
   static const bool store_nt = env_flag("ACP_STORE_NT", true);
-  static const bool load_nt = env_flag("ACP_LOAD_NT", true);
+  static const int load_nt_env = [] {
+    const char* e = std::getenv("ACP_LOAD_NT");
+    return (!e || !e[0]) ? -1 : (e[0] != '0' ? 1 : 0);
+  }();
+  const bool contiguous_stages = A.lin && A.lin_x == p.tile_bytes() && A.lin_x % 128 == 0;
   A.store_nt = store_nt ? 1 : 0;
-  A.load_nt = load_nt ? 1 : 0;
+  A.load_nt = load_nt_env >= 0 ? load_nt_env : (contiguous_stages ? 1 : 0);
   if (n_tiles * subs >= (int64_t(1) << 31)) return ret(ACP_ERR_UNSUPPORTED, "more than 2^31 stages");
   A.n_tiles = static_cast<uint32_t>(n_tiles);
   A.subs = static_cast<uint32_t>(subs);
@@ -275,8 +288,7 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   const int64_t in_img = align_up(p.tile_bytes(), 1024);
   const int64_t out_img = q.mode == 1 ? align_up(p.tile_elems() * eo, 1024) : 0;
   A.in_image_bytes = static_cast<uint32_t>(in_img);
-  A.out_image_off = static_cast<uint32_t>(q.n_in * in_img);
-  A.ab_off = static_cast<uint32_t>(q.n_in * in_img + out_img);
+  A.ab_off = static_cast<uint32_t>(q.n_in * in_img);
   A.row_ops = q.row_ops ? 1 : 0;
   if (q.row_ops) {
     if (n_rows > 64) return ret(ACP_ERR_UNSUPPORTED, "per-row scalars need at most 64 rows per stage");
@@ -291,7 +303,11 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
                                         ? (n_tiles + q.workgroups - 1) / q.workgroups : 1);
   const int slots = static_cast<int>(q.stages < trips_max ? q.stages : trips_max);
   A.stages = slots < 1 ? 1 : slots;
-  const int64_t lds = slot * A.stages;
+  // The staged output image lies after the ring, one per workgroup: each
+  // lane writes its chunks there and reads the same bytes back before its
+  // store, so trips can share it and it costs no ring slot.
+  A.out_image_off = static_cast<uint32_t>(slot * A.stages);
+  const int64_t lds = slot * A.stages + out_img;
   const int limit = device_lds_limit();
   if (lds > limit)
     return ret(ACP_ERR_LDS, "ring needs " + std::to_string(lds) + " bytes of LDS, device allows " +
@@ -299,12 +315,17 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
 
   unsigned grid = static_cast<unsigned>(n_tiles);
   if (q.workgroups > 0) grid = static_cast<unsigned>(q.workgroups);
-  A.xcd_remap = (q.workgroups > 0 && grid % 8 == 0 && xcd_remap_enabled()) ? 1 : 0;
+  // consecutive tiles (which often share cache lines at their edges) run on
+  // one XCD and hence one L2: blockIdx b -> (b % 8) * (G / 8) + b / 8
+  A.xcd_remap = (grid % 8 == 0 && grid >= 16 && xcd_remap_enabled()) ? 1 : 0;
   L->grid = grid;
   L->block = static_cast<unsigned>(q.threads);
   L->lds = static_cast<unsigned>(lds);
+  // every 1 KiB wave block inside one row: the innermost image run holds a
+  // whole number of such blocks and nothing permutes it
+  A.row_uniform = (q.row_ops && A.swizzle == 0 && (axes.back().count * ei) % (64 * p.vec_bytes) == 0) ? 1 : 0;
   L->key = acp::KernelKey{q.op, q.mode == 0 ? ACP_U32 : static_cast<int>(x.dtype),
-                          q.mode == 0 ? ACP_U32 : static_cast<int>(o.dtype), p.vec_bytes, q.mode, 0};
+                          q.mode == 0 ? ACP_U32 : static_cast<int>(o.dtype), p.vec_bytes, q.mode, 0, 0};
   // streaming on a linear grid with 16-byte rounds: the lean kernel
   static const bool fast_ok = env_flag("ACP_FAST_PATH", true);
   if (fast_ok && q.mode == 2 && A.lin && p.vec_bytes == 16 && q.n_in == 1 &&
@@ -312,7 +333,20 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
     acp::KernelKey fk = L->key;
     fk.mode = 3;
     fk.outer = p.outer;
+    static const bool srow_ok = env_flag("ACP_SCALAR_ROWS", true);
+    fk.srow = (A.row_uniform && srow_ok) ? 1 : 0;
     if (acp::engine_kernel(fk)) L->key = fk;
+  }
+  // any other grid with 16-byte rounds: the general lean kernel
+  static const bool gen_ok = env_flag("ACP_GEN_PATH", true);
+  if (gen_ok && L->key.mode <= 2 && p.vec_bytes == 16 &&
+      (p.outer == 1 || p.outer == 2 || p.outer == 4 || p.outer == 8)) {
+    acp::KernelKey gk = L->key;
+    gk.mode = q.mode + 4;
+    gk.outer = p.outer;
+    static const bool srow_ok = env_flag("ACP_SCALAR_ROWS", true);
+    gk.srow = (q.mode == 2 && A.row_uniform && srow_ok) ? 1 : 0;
+    if (acp::engine_kernel(gk)) L->key = gk;
   }
   return ACP_OK;
 }
@@ -327,6 +361,49 @@ acp_status launch(const Launch& L, void* stream) {
 }
 
 bool is_float(int dt) { return dt == ACP_F16 || dt == ACP_F32; }
+
+int device_cu_count() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 256;
+  return v;
+}
+
+// Tile copy and tile elementwise: the result of a tile does not depend on
+// which workgroup moves it, so large tile counts run on a persistent grid
+// that walks tiles w, w+G, ... through a ring of ACP_TILE_STAGES slots
+// (default 2).  Workgroups per CU (ACP_TILE_WG_PER_CU overrides): enough
+// that about 32 KiB of loads per CU are in flight while the previous trip is
+// consumed (measured best for both 4 KiB and 8 KiB tiles), at most 32 waves
+// per CU and what the LDS holds.
+void tile_schedule(const acp::Plan& p, int n_in, int threads, int64_t out_image, int* workgroups, int* stages) {
+  static const int env_per_cu = [] {
+    const char* e = std::getenv("ACP_TILE_WG_PER_CU");
+    return (e && std::atoi(e) > 0) ? std::atoi(e) : 0;
+  }();
+  static const int slots = [] {
+    const char* e = std::getenv("ACP_TILE_STAGES");
+    return (e && std::atoi(e) > 0 && std::atoi(e) <= 4) ? std::atoi(e) : 2;
+  }();
+  const int64_t n_tiles = p.n_tiles();
+  const int64_t img = align_up(p.tile_bytes(), 1024);
+  const int64_t ops = std::max(1, n_in);
+  int64_t per_cu = env_per_cu;
+  if (per_cu == 0) {
+    const int64_t lds_wg = slots * ops * img + align_up(out_image, 1024);
+    per_cu = std::max<int64_t>(1, 32768 / (ops * p.tile_bytes()));
+    per_cu = std::min<int64_t>(per_cu, std::max(1, 32 / std::max(1, threads / 64)));
+    per_cu = std::min<int64_t>(per_cu, std::max<int64_t>(1, device_lds_limit() / lds_wg));
+  }
+  const int64_t g = static_cast<int64_t>(device_cu_count()) * per_cu;
+  if (n_tiles > g) {
+    *workgroups = static_cast<int>(g);
+    *stages = slots;
+  } else {
+    *workgroups = 0;  // one workgroup per tile, one trip each
+    *stages = 1;
+  }
+}
 
 }  // namespace
 
@@ -420,9 +497,14 @@ acp_status acp_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, int
   q.in_ptrs[0] = reinterpret_cast<const void*>(s.gbase);
   q.n_in = 1;
   q.stage_box = s.box;
-  q.stages = 1;
   q.threads = threads;
   q.copy_only = true;
+  {
+    acp::Plan p;
+    std::string why;
+    if (acp::plan_box(s, true, &p, &why) == acp::PlanStatus::Ok) tile_schedule(p, 1, threads, 0, &q.workgroups, &q.stages);
+    else q.stages = 1;
+  }
   Launch L;
   const acp_status st = prepare(q, &L);
   if (st != ACP_OK) return st;
@@ -463,9 +545,15 @@ acp_status acp_tile_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_de
   for (int k = 0; k < n_in; ++k) q.in_ptrs[k] = reinterpret_cast<const void*>(ins[k].gbase);
   q.n_in = n_in;
   q.stage_box = anchor.box;
-  q.stages = 1;
   q.threads = threads;
   q.copy_only = false;
+  {
+    acp::Plan p;
+    std::string why;
+    if (acp::plan_box(anchor, false, &p, &why) == acp::PlanStatus::Ok)
+      tile_schedule(p, n_in, threads, p.tile_elems() * o.esize, &q.workgroups, &q.stages);
+    else q.stages = 1;
+  }
   Launch L;
   const acp_status st = prepare(q, &L);
   if (st != ACP_OK) return st;

@@ -5,6 +5,7 @@ namespace acp {
 
 const void* lookup_copy(const KernelKey& k);
 const void* lookup_tile(const KernelKey& k);
+const void* lookup_tile_gen(const KernelKey& k);
 const void* lookup_stream_f32(const KernelKey& k);
 const void* lookup_stream_f16(const KernelKey& k);
 
@@ -60,6 +61,7 @@ __global__ void ring_trace_kernel(int n, int s, int loads, int stores, int32_t* 
 const void* engine_kernel(const KernelKey& k) {
   if (const void* f = lookup_copy(k)) return f;
   if (const void* f = lookup_tile(k)) return f;
+  if (const void* f = lookup_tile_gen(k)) return f;
   if (const void* f = lookup_stream_f32(k)) return f;
   return lookup_stream_f16(k);
 }

@@ -49,7 +49,7 @@ struct EngineArgs {
   int32_t outer, waves, swizzle, stages, n_in;
   // LDS slot layout (bytes)
   uint32_t in_image_bytes;   // stride between operand images in a slot
-  uint32_t out_image_off;    // output image (staged output only)
+  uint32_t out_image_off;    // output image (staged output only), after the ring slots
   uint32_t ab_off;           // per-row scalar area
   uint32_t ab_wave_bytes;    // per wave
   uint32_t slot_bytes;
@@ -68,6 +68,9 @@ struct EngineArgs {
   // cache policy of the direct-to-LDS loads and of the stores: 0 default,
   // 1 non-temporal (streamed data, no reuse expected)
   int32_t load_nt, store_nt;
+  // Row ops whose every 1 KiB wave block lies inside one row: the per-row
+  // scalars are read through the scalar cache instead of being staged.
+  int32_t row_uniform;
 };
 
 // Which kernel variant a launch needs.
@@ -76,8 +79,10 @@ struct KernelKey {
   int tin;       // acp_dtype of staged operands
   int tout;      // acp_dtype of the output
   int vec_bytes; // 16 or 4
-  int mode;      // 0 copy, 1 tile ewise (output staged in LDS), 2 stream, 3 stream on a linear grid
-  int outer;     // mode 3: rounds per thread (1, 2, 4 or 8); 0 otherwise
+  int mode;      // 0 copy, 1 tile ewise (output staged in LDS), 2 stream, 3 stream on a linear grid,
+                 // 4 / 5 / 6: copy / tile ewise / stream in the general lean kernel
+  int outer;     // modes 3..6: rounds per thread (1, 2, 4 or 8); 0 otherwise
+  int srow;      // modes 3 and 6, row ops: per-row scalars through the scalar cache
 };
 
 // Kernel for `key`, or nullptr when that combination is not built.

@@ -269,14 +269,15 @@ struct LaneMap {
 template <int VB>
 __device__ __forceinline__ void build_map(CArgs* A, int wave, int lane, LaneMap& m) {
   const int outer = A->outer, waves = A->waves, n_axes = A->n_axes;
+  const int swz = A->swizzle, es_log2 = A->esize_log2;
 #pragma unroll
   for (int g = 0; g < kMaxOuter; ++g) m.xoff[g] = m.ooff[g] = m.oobm[g] = m.lpos[g] = m.abo[g] = 0;
 #pragma nounroll
   for (int f = 0; f < outer; ++f) {
     const uint32_t pb = ((f * waves + wave) * 64u + lane) * VB;
-    const uint32_t lb = A->swizzle ? swz128(pb) : pb;
-    const uint32_t sub_byte = lb & ((1u << A->esize_log2) - 1u);  // copies of elements wider than VB
-    uint32_t e = lb >> A->esize_log2;
+    const uint32_t lb = swz ? swz128(pb) : pb;
+    const uint32_t sub_byte = lb & ((1u << es_log2) - 1u);  // copies of elements wider than VB
+    uint32_t e = lb >> es_log2;
     uint32_t xo = sub_byte, oo = sub_byte, row = 0;
     uint32_t rel[kPartial] = {0, 0, 0, 0};
 #pragma nounroll
@@ -289,13 +290,13 @@ __device__ __forceinline__ void build_map(CArgs* A, int wave, int lane, LaneMap&
       row += idx * A->ax_rs[k];
       const int ps = A->ax_pslot[k];
 #pragma unroll
-      for (int s = 0; s < kPartial; ++s)
-        if (ps == s) rel[s] += idx * A->ax_step[k];
+      for (int s2 = 0; s2 < kPartial; ++s2)
+        if (ps == s2) rel[s2] += idx * A->ax_step[k];
     }
     uint32_t ob = 0;
 #pragma unroll
-    for (int s = 0; s < kPartial; ++s)
-      if (rel[s] >= A->prem[s]) ob |= 1u << s;
+    for (int s2 = 0; s2 < kPartial; ++s2)
+      if (rel[s2] >= A->prem[s2]) ob |= 1u << s2;
     const uint32_t abo = (row >> 5) * 256u + (row & 31u) * 4u;
 #pragma unroll
     for (int g = 0; g < kMaxOuter; ++g)
@@ -554,13 +555,13 @@ __device__ __forceinline__ void consume_trip(const Loc& L, int esize_log2, int s
 #pragma unroll
       for (int piece = 0; piece < P; ++piece) {
         const uint32_t lp = lo + piece * 16;
-        __builtin_memcpy(lds + slot + L.out_image_off + (swizzle ? swz128(lp) : lp), words + piece * 4, PB);
+        __builtin_memcpy(lds + L.out_image_off + (swizzle ? swz128(lp) : lp), words + piece * 4, PB);
       }
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int piece = 0; piece < P; ++piece) {
         const uint32_t lp = lo + piece * 16;
-        __builtin_memcpy(words + piece * 4, lds + slot + L.out_image_off + (swizzle ? swz128(lp) : lp), PB);
+        __builtin_memcpy(words + piece * 4, lds + L.out_image_off + (swizzle ? swz128(lp) : lp), PB);
       }
     }
     const bool ok = !t.beyond && (m.oobm[f] & t.last) == 0;
@@ -627,7 +628,7 @@ __global__ __launch_bounds__(1024) void engine_kernel_t(const EngineArgs) {
 // engine; per trip only the stage base (one multiply) changes, and no chunk
 // can be out of bounds.
 
-template <class OP, int OUTER>
+template <class OP, int OUTER, bool SROW>
 struct LinPolicy {
   unsigned char* lds;
   const char* in0;
@@ -640,6 +641,12 @@ struct LinPolicy {
   uint32_t xoff[OUTER], ooff[OUTER], abo[OUTER];
   const uint64_t* row_ptr;   // [0] lane's array, [1 + q] row byte offset in the stage
   const uint32_t* row_ok;    // lane has a row in load q
+  // SROW: this wave's row (relative to the stage) of each round, and the
+  // scalars of the trip being consumed, read through the scalar cache
+  const float __attribute__((address_space(4)))* ca;
+  const float __attribute__((address_space(4)))* cb;
+  uint32_t row_of[OUTER];
+  float sa[OUTER], sb[OUTER];
 
   __device__ __forceinline__ uint64_t stage(int j) const { return wg + static_cast<uint64_t>(j) * grid; }
 
@@ -650,7 +657,7 @@ struct LinPolicy {
     const uint32_t base = lds0 + slot * slot_bytes + wave * 1024u;
 #pragma unroll
     for (int f = 0; f < OUTER; ++f) dma_b128(rs, xoff[f], base + f * waves_kb, load_nt);
-    if constexpr (OP::ROW) {
+    if constexpr (OP::ROW && !SROW) {
       const uint64_t rb = s * lin_r;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -662,7 +669,19 @@ struct LinPolicy {
       }
     }
   }
-  __device__ __forceinline__ void wait(int, int, int k) { wait_vmcnt(k); }
+  __device__ __forceinline__ void wait(int i, int, int k) {
+    if constexpr (OP::ROW && SROW) {
+      // scalar loads of trip i's rows go out before the stage wait, so their
+      // latency hides behind it
+      const uint64_t rb = stage(i) * lin_r;
+#pragma unroll
+      for (int f = 0; f < OUTER; ++f) {
+        sa[f] = ca[rb + row_of[f]];
+        sb[f] = cb[rb + row_of[f]];
+      }
+    }
+    wait_vmcnt(k);
+  }
 
   __device__ __forceinline__ void consume(int i, int slot) {
     typedef ChunkShape<OP, 16> CS;
@@ -677,7 +696,10 @@ struct LinPolicy {
 #pragma unroll
     for (int f = 0; f < OUTER; ++f) {
       v[f] = *reinterpret_cast<const u32x4*>(__builtin_assume_aligned(lds + sl + f * waves_kb + wave * 1024u + lane * 16u, 16));
-      if constexpr (OP::ROW) {
+      if constexpr (OP::ROW && SROW) {
+        ra[f] = sa[f];
+        rb[f] = sb[f];
+      } else if constexpr (OP::ROW) {
         ra[f] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f]);
         rb[f] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f] + 128u);
       } else {
@@ -698,7 +720,7 @@ struct LinPolicy {
   }
 };
 
-template <class OP, int OUTER>
+template <class OP, int OUTER, bool SROW>
 __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
   CArgs* A = kargs();
@@ -712,12 +734,12 @@ __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
   if (n == 0) return;
   LaneMap m;
   build_map<16>(A, wave, lane, m);
-  uint64_t row_ptr[3];
-  uint32_t row_bad[2];
-  build_rows(A, lane, row_ptr, row_bad);
+  uint64_t row_ptr[3] = {0, 0, 0};
+  uint32_t row_bad[2] = {~0u, ~0u};
+  if constexpr (OP::ROW && !SROW) build_rows(A, lane, row_ptr, row_bad);
   uint32_t row_ok[2] = {row_bad[0] == 0u, row_bad[1] == 0u};
   const Loc L = load_loc(A);
-  LinPolicy<OP, OUTER> p;
+  LinPolicy<OP, OUTER, SROW> p;
   p.lds = lds;
   p.in0 = L.in[0];
   p.out = L.out;
@@ -746,8 +768,283 @@ __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
   }
   p.row_ptr = row_ptr;
   p.row_ok = row_ok;
+  p.ca = (const float __attribute__((address_space(4)))*)(unip(A->row_a));
+  p.cb = (const float __attribute__((address_space(4)))*)(unip(A->row_b));
+#pragma unroll
+  for (int f = 0; f < OUTER; ++f) {
+    // the whole 1 KiB block of this wave and round lies in one row
+    const uint32_t abo = uni(m.abo[f]);
+    p.row_of[f] = (abo >> 8) * 32u + (abo & 255u) / 4u;
+    p.sa[f] = p.sb[f] = 0.f;
+  }
   typedef ChunkShape<OP, 16> CS;
-  const int d = OUTER + (OP::ROW ? L.ab_instr : 0);
+  const int d = OUTER + ((OP::ROW && !SROW) ? L.ab_instr : 0);
+  run_ring(p, n, uni(A->stages), d, OUTER * CS::ST);
+}
+
+// ---------------------------------------------------------------------------
+// General lean kernel: any stage grid (partial and out-of-range stages,
+// sub-stages inside a workgroup tile, persistent grids), 16-byte rounds,
+// OUTER rounds per thread known at compile time.  Trip geometry lives in a
+// table in VGPR lanes: lane l of every wave computes trip (batch * 64 + l)
+// with vector arithmetic, and each trip reads its row with v_readlane.  Two
+// table sets alternate so that the load cursor (up to S-1 trips ahead) can
+// enter the next batch while the consume cursor finishes the current one.
+
+struct TripRow {
+  uint32_t xlo, xhi, olo, ohi, rlo, flags;  // flags: bits 0..3 last-stage slots, bit 8 out of range
+};
+
+__device__ __forceinline__ TripRow trip_lane(CArgs* A, uint32_t wg, uint32_t grid, uint32_t tile0, uint32_t subs,
+                                             uint32_t subs_mag, uint32_t subs_sh, int rank, uint32_t j) {
+  const uint32_t tl = mdiv(j, subs_mag, subs_sh);
+  uint32_t sub = j - tl * subs;
+  uint32_t tile = tile0 + wg + tl * grid;
+  uint64_t xb = 0, ob = 0, rb = 0;
+  uint32_t flags = 0;
+  // rolled: the per-dim parameters are read on each refill (once per 64
+  // trips) rather than held in scalar registers across the ring
+#pragma nounroll
+  for (int d = rank - 1; d >= 0; --d) {
+    const uint32_t qt = mdiv(tile, A->tg_mag[d], A->tg_sh[d]);
+    const uint32_t tc = tile - qt * A->tgrid[d];
+    tile = qt;
+    const uint32_t qs = mdiv(sub, A->sub_mag[d], A->sub_sh[d]);
+    const uint32_t scs = sub - qs * A->sub[d];
+    sub = qs;
+    const uint32_t sc = tc * A->sub[d] + scs;
+    const uint32_t nst = A->nst[d];
+    if (sc >= nst) flags |= 0x100u;
+    const int ps = A->pslot_of_dim[d];
+    if (ps >= 0 && sc + 1 == nst) flags |= 1u << ps;
+    xb += static_cast<uint64_t>(sc) * static_cast<uint64_t>(A->xstep[d]);
+    ob += static_cast<uint64_t>(sc) * static_cast<uint64_t>(A->ostep[d]);
+    rb += static_cast<uint64_t>(sc) * static_cast<uint64_t>(A->rstep[d]);
+  }
+  if (tile != 0) flags |= 0x100u;  // past the last tile
+  if (flags & 0x100u) xb = ob = rb = 0;
+  return TripRow{static_cast<uint32_t>(xb), static_cast<uint32_t>(xb >> 32), static_cast<uint32_t>(ob),
+                 static_cast<uint32_t>(ob >> 32), static_cast<uint32_t>(rb), flags};
+}
+
+__device__ __forceinline__ uint32_t rdl(uint32_t v, uint32_t lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), static_cast<int>(lane)));
+}
+
+template <class OP, int MODE, int OUTER, bool SROW>
+struct GenPolicy {
+  static constexpr bool STAGE_OUT = (MODE == 1);
+  static constexpr int NS = (MODE == 1) ? OP::NIN : 1;   // staged operands
+  CArgs* A;
+  unsigned char* lds;
+  const char* in[3];
+  char* out;
+  uint64_t in_span, out_span, total_rows;
+  uint32_t lds0, slot_bytes, in_image_bytes, out_image_off, ab_base, waves_kb, wg, grid, tile0, subs, subs_mag, subs_sh;
+  int wave, lane, rank, ab_instr, swizzle, esize_log2;
+  bool load_nt, store_nt;
+  uint32_t xoff[OUTER], ooff[OUTER], oobm[OUTER], lpos[OUTER], abo[OUTER];
+  TripRow tab[2];
+  const uint64_t* row_ptr;   // [0] lane's array, [1 + q] row byte offset in the stage
+  const uint32_t* row_bad;   // partial slots along which the lane's row q lies past the edge
+  // SROW: this wave's row (relative to the stage) of each round, and the
+  // scalars of the trip being consumed, read through the scalar cache
+  const float __attribute__((address_space(4)))* ca;
+  const float __attribute__((address_space(4)))* cb;
+  uint32_t row_of[OUTER];
+  float sa[OUTER], sb[OUTER];
+
+  __device__ __forceinline__ void fill(int set, uint32_t j0) {
+    const TripRow r = trip_lane(A, wg, grid, tile0, subs, subs_mag, subs_sh, rank, j0 + static_cast<uint32_t>(lane));
+    if (set == 0) tab[0] = r; else tab[1] = r;
+  }
+  struct T {
+    uint64_t xb, ob, rb;
+    uint32_t flags;
+  };
+  __device__ __forceinline__ T row(int j) const {
+    const uint32_t l = static_cast<uint32_t>(j) & 63u;
+    const TripRow& r = ((j >> 6) & 1) ? tab[1] : tab[0];
+    T t;
+    t.xb = (static_cast<uint64_t>(rdl(r.xhi, l)) << 32) | rdl(r.xlo, l);
+    t.ob = (static_cast<uint64_t>(rdl(r.ohi, l)) << 32) | rdl(r.olo, l);
+    t.rb = rdl(r.rlo, l);
+    t.flags = rdl(r.flags, l);
+    return t;
+  }
+
+  __device__ __forceinline__ void load(int j, int slot) {
+    if (j > 0 && (j & 63) == 0) fill((j >> 6) & 1, static_cast<uint32_t>(j));
+    const T t = row(j);
+    const bool beyond = (t.flags & 0x100u) != 0;
+    const uint32_t last = t.flags & 0xFFu;
+    const uint32_t sbase = lds0 + slot * slot_bytes + wave * 1024u;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const v4i rs = rsrc_v4(in[k] + t.xb, range_from(in_span, t.xb));
+#pragma unroll
+      for (int f = 0; f < OUTER; ++f) {
+        const bool ok = !beyond && (oobm[f] & last) == 0;
+        dma_b128(rs, ok ? xoff[f] : kOobOffset, sbase + k * in_image_bytes + f * waves_kb, load_nt);
+      }
+    }
+    if constexpr (OP::ROW && !SROW) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (q >= ab_instr) continue;
+        const bool ok = !beyond && (row_bad[q] & last) == 0;
+        uint64_t r = ok ? t.rb + row_ptr[1 + q] / 4u : 0u;
+        if (r >= total_rows) r = 0;
+        dma_global_b32(reinterpret_cast<const void*>(row_ptr[0] + r * 4u), lds0 + slot * slot_bytes + ab_base + q * 256u);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void wait(int i, int, int k) {
+    if constexpr (OP::ROW && SROW) {
+      // rows of a cut stage may lie past the tensor: their results are
+      // never stored, and they read row 0 instead of memory past the arrays
+      const T t = row(i);
+#pragma unroll
+      for (int f = 0; f < OUTER; ++f) {
+        uint64_t r = t.rb + row_of[f];
+        if (r >= total_rows) r = 0;
+        sa[f] = ca[r];
+        sb[f] = cb[r];
+      }
+    }
+    wait_vmcnt(k);
+  }
+
+  __device__ __forceinline__ void consume(int i, int slot) {
+    typedef ChunkShape<OP, 16> CS;
+    typedef typename OP::TI TI;
+    typedef typename OP::TO TO;
+    const T t = row(i);
+    const bool beyond = (t.flags & 0x100u) != 0;
+    const uint32_t last = t.flags & 0xFFu;
+    const __amdgpu_buffer_rsrc_t rs = rsrc_store(out + t.ob, range_from(out_span, t.ob));
+    const uint32_t sl = slot * slot_bytes;
+    u32x4 v[NS > 0 ? NS : 1][OUTER];
+    float ra[OUTER], rb[OUTER];
+#pragma unroll
+    for (int f = 0; f < OUTER; ++f) {
+#pragma unroll
+      for (int k = 0; k < NS; ++k)
+        v[k][f] = *reinterpret_cast<const u32x4*>(
+            __builtin_assume_aligned(lds + sl + k * in_image_bytes + f * waves_kb + wave * 1024u + lane * 16u, 16));
+      if constexpr (NS == 0) v[0][f] = u32x4{0, 0, 0, 0};
+      if constexpr (OP::ROW && SROW) {
+        ra[f] = sa[f];
+        rb[f] = sb[f];
+      } else if constexpr (OP::ROW) {
+        ra[f] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f]);
+        rb[f] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f] + 128u);
+      } else {
+        ra[f] = rb[f] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < OUTER; ++f) {
+      TI in0[CS::NE], in1[CS::NE], in2[CS::NE];
+      __builtin_memcpy(in0, &v[0][f], 16);
+      __builtin_memcpy(in1, &v[NS > 1 ? 1 : 0][f], 16);
+      __builtin_memcpy(in2, &v[NS > 2 ? 2 : 0][f], 16);
+      TO res[CS::NE];
+#pragma unroll
+      for (int e = 0; e < CS::NE; ++e) res[e] = OP::f(in0[e], in1[e], in2[e], ra[f], rb[f]);
+      uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      __builtin_memcpy(words, res, CS::OB);
+      if constexpr (STAGE_OUT) {
+        // the output tile is LDS-resident ("elementwise -> smem") and is copied out from there
+        const uint32_t lo = (lpos[f] >> esize_log2) * CS::EO;
+        constexpr int P = (CS::OB + 15) / 16;
+        constexpr int PB = CS::OB < 16 ? CS::OB : 16;
+#pragma unroll
+        for (int piece = 0; piece < P; ++piece) {
+          const uint32_t lp = lo + piece * 16;
+          __builtin_memcpy(lds + out_image_off + (swizzle ? swz128(lp) : lp), words + piece * 4, PB);
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int piece = 0; piece < P; ++piece) {
+          const uint32_t lp = lo + piece * 16;
+          __builtin_memcpy(words + piece * 4, lds + out_image_off + (swizzle ? swz128(lp) : lp), PB);
+        }
+      }
+      const bool ok = !beyond && (oobm[f] & last) == 0;
+      store_chunk<CS::OB>(rs, ok ? ooff[f] : kOobOffset, words, store_nt);
+    }
+  }
+};
+
+template <class OP, int MODE, int OUTER, bool SROW>
+__global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+  CArgs* A = kargs();
+  const int lane = threadIdx.x & 63;
+  const int wave = uni(static_cast<int>(threadIdx.x >> 6));
+  const uint32_t grid = gridDim.x;
+  uint32_t wg = blockIdx.x;
+  if (A->xcd_remap) wg = (wg & 7u) * (grid >> 3) + (wg >> 3);
+  const uint32_t n_tiles = A->n_tiles;
+  const uint32_t tiles = wg < n_tiles ? (n_tiles - wg + grid - 1) / grid : 0;
+  const int n = static_cast<int>(tiles * A->subs);
+  if (n == 0) return;
+  LaneMap m;
+  build_map<16>(A, wave, lane, m);
+  uint64_t row_ptr[3] = {0, 0, 0};
+  uint32_t row_bad[2] = {~0u, ~0u};
+  if constexpr (OP::ROW && !SROW) build_rows(A, lane, row_ptr, row_bad);
+  const Loc L = load_loc(A);
+  GenPolicy<OP, MODE, OUTER, SROW> p;
+  p.A = A;
+  p.lds = lds;
+  for (int k = 0; k < 3; ++k) p.in[k] = L.in[k];
+  p.out = L.out;
+  p.in_span = L.in_span;
+  p.out_span = L.out_span;
+  p.total_rows = L.total_rows;
+  p.lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  p.slot_bytes = L.slot_bytes;
+  p.in_image_bytes = L.in_image_bytes;
+  p.out_image_off = L.out_image_off;
+  p.ab_base = L.ab_off + wave * L.ab_wave_bytes;
+  p.waves_kb = static_cast<uint32_t>(L.waves) * 1024u;
+  p.wg = wg;
+  p.grid = grid;
+  p.tile0 = L.tile0;
+  p.subs = L.subs;
+  p.subs_mag = uni(A->subs_mag);
+  p.subs_sh = uni(A->subs_sh);
+  p.wave = wave;
+  p.lane = lane;
+  p.rank = uni(A->rank);
+  p.ab_instr = L.ab_instr;
+  p.swizzle = uni(A->swizzle);
+  p.esize_log2 = uni(A->esize_log2);
+  p.load_nt = L.load_nt != 0;
+  p.store_nt = L.store_nt != 0;
+  p.row_ptr = row_ptr;
+  p.row_bad = row_bad;
+  p.ca = (const float __attribute__((address_space(4)))*)(unip(A->row_a));
+  p.cb = (const float __attribute__((address_space(4)))*)(unip(A->row_b));
+#pragma unroll
+  for (int f = 0; f < OUTER; ++f) {
+    p.xoff[f] = m.xoff[f];
+    p.ooff[f] = m.ooff[f];
+    p.oobm[f] = m.oobm[f];
+    p.lpos[f] = m.lpos[f];
+    p.abo[f] = m.abo[f];
+    const uint32_t abo = uni(m.abo[f]);
+    p.row_of[f] = (abo >> 8) * 32u + (abo & 255u) / 4u;
+    p.sa[f] = p.sb[f] = 0.f;
+  }
+  p.tab[1] = TripRow{0, 0, 0, 0, 0, 0};
+  p.fill(0, 0u);
+  typedef ChunkShape<OP, 16> CS;
+  constexpr int NS = GenPolicy<OP, MODE, OUTER, SROW>::NS;
+  const int d = NS * OUTER + ((OP::ROW && !SROW) ? L.ab_instr : 0);
   run_ring(p, n, uni(A->stages), d, OUTER * CS::ST);
 }
 
@@ -759,20 +1056,36 @@ struct KernelEntry {
 };
 
 #define ACP_K(OPC, TIN, TOUT, VB, MODE, ...) \
-  KernelEntry{KernelKey{OPC, TIN, TOUT, VB, MODE, 0}, \
+  KernelEntry{KernelKey{OPC, TIN, TOUT, VB, MODE, 0, 0}, \
               reinterpret_cast<const void*>(&dev::engine_kernel_t<__VA_ARGS__, VB, (MODE == 1)>)}
-#define ACP_L(OPC, TIN, TOUT, OUTER, ...) \
-  KernelEntry{KernelKey{OPC, TIN, TOUT, 16, 3, OUTER}, reinterpret_cast<const void*>(&dev::stream_lin_kernel_t<__VA_ARGS__, OUTER>)}
+#define ACP_L(OPC, TIN, TOUT, OUTER, SR, ...)                         \
+  KernelEntry{KernelKey{OPC, TIN, TOUT, 16, 3, OUTER, SR}, \
+              reinterpret_cast<const void*>(&dev::stream_lin_kernel_t<__VA_ARGS__, OUTER, (SR != 0)>)}
 #define ACP_LIN(OPC, TIN, TOUT, ...) \
-  ACP_L(OPC, TIN, TOUT, 1, __VA_ARGS__), ACP_L(OPC, TIN, TOUT, 2, __VA_ARGS__), ACP_L(OPC, TIN, TOUT, 4, __VA_ARGS__), \
-      ACP_L(OPC, TIN, TOUT, 8, __VA_ARGS__)
+  ACP_L(OPC, TIN, TOUT, 1, 0, __VA_ARGS__), ACP_L(OPC, TIN, TOUT, 2, 0, __VA_ARGS__), ACP_L(OPC, TIN, TOUT, 4, 0, __VA_ARGS__), \
+      ACP_L(OPC, TIN, TOUT, 8, 0, __VA_ARGS__)
+#define ACP_G1(OPC, TIN, TOUT, MODE, OUTER, SR, ...) \
+  KernelEntry{KernelKey{OPC, TIN, TOUT, 16, (MODE) + 4, OUTER, SR}, \
+              reinterpret_cast<const void*>(&dev::gen_kernel_t<__VA_ARGS__, MODE, OUTER, (SR != 0)>)}
+// general lean kernels: mode key 4 (copy), 5 (tile ewise), 6 (stream)
+#define ACP_GEN(OPC, TIN, TOUT, MODE, ...) \
+  ACP_G1(OPC, TIN, TOUT, MODE, 1, 0, __VA_ARGS__), ACP_G1(OPC, TIN, TOUT, MODE, 2, 0, __VA_ARGS__), \
+      ACP_G1(OPC, TIN, TOUT, MODE, 4, 0, __VA_ARGS__), ACP_G1(OPC, TIN, TOUT, MODE, 8, 0, __VA_ARGS__)
+#define ACP_GEN_ROW(OPC, ...) \
+  ACP_GEN(OPC, kF32, kF32, 2, __VA_ARGS__), ACP_G1(OPC, kF32, kF32, 2, 1, 1, __VA_ARGS__), \
+      ACP_G1(OPC, kF32, kF32, 2, 2, 1, __VA_ARGS__), ACP_G1(OPC, kF32, kF32, 2, 4, 1, __VA_ARGS__), \
+      ACP_G1(OPC, kF32, kF32, 2, 8, 1, __VA_ARGS__)
+#define ACP_LIN_ROW(OPC, ...)                                                                              \
+  ACP_LIN(OPC, kF32, kF32, __VA_ARGS__), ACP_L(OPC, kF32, kF32, 1, 1, __VA_ARGS__),                          \
+      ACP_L(OPC, kF32, kF32, 2, 1, __VA_ARGS__), ACP_L(OPC, kF32, kF32, 4, 1, __VA_ARGS__), \
+      ACP_L(OPC, kF32, kF32, 8, 1, __VA_ARGS__)
 #define ACP_BOTH(OPC, TIN, TOUT, MODE, ...) ACP_K(OPC, TIN, TOUT, 16, MODE, __VA_ARGS__), ACP_K(OPC, TIN, TOUT, 4, MODE, __VA_ARGS__)
 
 template <size_t N>
 const void* find_entry(const KernelEntry (&table)[N], const KernelKey& k) {
   for (const KernelEntry& e : table)
     if (e.key.op == k.op && e.key.tin == k.tin && e.key.tout == k.tout && e.key.vec_bytes == k.vec_bytes &&
-        e.key.mode == k.mode && e.key.outer == k.outer)
+        e.key.mode == k.mode && e.key.outer == k.outer && e.key.srow == k.srow)
       return e.fn;
   return nullptr;
 }

@@ -16,6 +16,12 @@ const KernelEntry kTable[] = {
     ACP_LIN(kOpSqrt, kF16, kF16, Op<kOpSqrt, kF16, kF16>),
     ACP_LIN(kOpExp, kF16, kF32, Op<kOpExp, kF16, kF32>),
     ACP_LIN(kOpExp, kF16, kF16, Op<kOpExp, kF16, kF16>),
+    // general lean kernel
+    ACP_GEN(kOpZero, kF16, kF16, 2, Op<kOpZero, kF16, kF16>),
+    ACP_GEN(kOpSqrt, kF16, kF32, 2, Op<kOpSqrt, kF16, kF32>),
+    ACP_GEN(kOpSqrt, kF16, kF16, 2, Op<kOpSqrt, kF16, kF16>),
+    ACP_GEN(kOpExp, kF16, kF32, 2, Op<kOpExp, kF16, kF32>),
+    ACP_GEN(kOpExp, kF16, kF16, 2, Op<kOpExp, kF16, kF16>),
 };
 }  // namespace
 const void* lookup_stream_f16(const KernelKey& k) { return find_entry(kTable, k); }

@@ -19,9 +19,18 @@ const KernelEntry kTable[] = {
     ACP_LIN(kOpSqrt, kF32, kF16, Op<kOpSqrt, kF32, kF16>),
     ACP_LIN(kOpExp, kF32, kF32, Op<kOpExp, kF32, kF32>),
     ACP_LIN(kOpExp, kF32, kF16, Op<kOpExp, kF32, kF16>),
-    ACP_LIN(kOpAdd, kF32, kF32, RowOp<kOpAdd>),
-    ACP_LIN(kOpMul, kF32, kF32, RowOp<kOpMul>),
-    ACP_LIN(kOpFma, kF32, kF32, RowOp<kOpFma>),
+    ACP_LIN_ROW(kOpAdd, RowOp<kOpAdd>),
+    ACP_LIN_ROW(kOpMul, RowOp<kOpMul>),
+    ACP_LIN_ROW(kOpFma, RowOp<kOpFma>),
+    // general lean kernel
+    ACP_GEN(kOpZero, kF32, kF32, 2, Op<kOpZero, kF32, kF32>),
+    ACP_GEN(kOpSqrt, kF32, kF32, 2, Op<kOpSqrt, kF32, kF32>),
+    ACP_GEN(kOpSqrt, kF32, kF16, 2, Op<kOpSqrt, kF32, kF16>),
+    ACP_GEN(kOpExp, kF32, kF32, 2, Op<kOpExp, kF32, kF32>),
+    ACP_GEN(kOpExp, kF32, kF16, 2, Op<kOpExp, kF32, kF16>),
+    ACP_GEN_ROW(kOpAdd, RowOp<kOpAdd>),
+    ACP_GEN_ROW(kOpMul, RowOp<kOpMul>),
+    ACP_GEN_ROW(kOpFma, RowOp<kOpFma>),
 };
 }  // namespace
 const void* lookup_stream_f32(const KernelKey& k) { return find_entry(kTable, k); }

@@ -58,7 +58,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c4", choices=["c2", "c3", "c4", "c5", "calib"],
+                    help="c4: the streamed fma (default); c2/c3/c5: the other workloads; "
+                         "calib: torch's copy of 256 MiB, the known-size kernel that scales HBM counters")
     ap.add_argument("--stages", type=int, default=4)
     ap.add_argument("--rows", type=int, default=4, help="rows per ring stage (c4)")
     ap.add_argument("--threads", type=int, default=256)
@@ -144,6 +146,15 @@ def main():
         bytes_per, dtype = x.nbytes * 2, "f16"
         config = {"workload": "tile copy, [128,500,1024] f16, 128x32 tiles, 128 threads"}
         key = "tile_copy_f16_128x500x1024"
+    elif wl == "calib":
+        n = 256 << 20
+        for s in range(args.sets):
+            xd = torch.ones(n, dtype=torch.uint8, device=dev)
+            yd = torch.empty(n, dtype=torch.uint8, device=dev)
+            launches.append(lambda xd=xd, yd=yd: yd.copy_(xd))
+        bytes_per, dtype = 2 * n, "u8"
+        config = {"workload": "torch copy_ of 256 MiB (counter calibration: 268435456 B read, 268435456 B written)"}
+        key = "calib_copy_256MiB"
     else:
         shape, pitch = (4, 8, 64, 128, 256), 264
         storage, strides = W.padded_uniform_f16(shape, pitch=pitch, seed=5)

@@ -141,3 +141,24 @@ def test_box_larger_than_tensor_and_empty_tensor():
     f = encode("f16", yd, (0, 40), (40, 1), (8, 64))
     acp.acp_tile_copy(e, f, 64, stream())                     # no tiles: returns without a launch
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("shape,box,threads", [
+    ((3001, 16, 64), (1, 16, 64), 128),        # 3001 whole tiles: more than one per workgroup, uneven
+    ((7, 1333, 256), (1, 4, 256), 64),         # 334 tiles per batch, the last one a single row
+    ((4100, 2, 512), (1, 2, 512), 64),         # swizzled copy below
+])
+def test_persistent_grid_ragged_tile_counts(shape, box, threads):
+    swz = acp.ACP_SWIZZLE_128B if shape[0] == 4100 else acp.ACP_SWIZZLE_NONE
+    say(f"persistent copy {shape} box {box} threads {threads} swizzle {swz}")
+    x = W.normal_f16(shape, seed=11)
+    xd, yd = dev(x), empty_bytes(x.nbytes)
+    st = packed_strides(shape)
+    src = encode("f16", xd, shape, st, box, swz)
+    dst = encode("f16", yd, shape, st, box, swz)
+    info = acp.acp_plan_query(src, threads)
+    assert info["n_tiles"] > 2048       # beyond one tile per workgroup of the persistent grid
+    assert info["vec_bytes"] == 16
+    acp.acp_tile_copy(src, dst, threads, stream())
+    torch.cuda.synchronize()
+    assert torch.equal(xd, yd)

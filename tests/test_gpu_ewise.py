@@ -96,3 +96,19 @@ def test_denormals_survive_fma_and_mul():
     y = run_tile_ewise("fma", [a, b, c], "f32", "f32", shape, (1, 64, 64), 256)
     assert np.array_equal(y, REF.ewise("fma", [a, b, c], np.float32))
     assert np.count_nonzero(y) == y.size
+
+
+@pytest.mark.parametrize("op,dt,shape,box,threads", [
+    ("fma", "f16", (2500, 16, 64), (1, 16, 64), 64),      # 2500 tiles, uneven over the grid
+    ("sqrt", "f32", (12, 1501, 64), (1, 8, 64), 64),      # 188 tiles per batch, the last one 5 rows
+])
+def test_persistent_grid_ragged_tile_ewise(op, dt, shape, box, threads):
+    say(f"persistent tile_ewise {op} {dt} {shape} box {box} threads {threads}")
+    if op == "fma":
+        ins = [W.normal_f16(shape, seed=s) for s in (21, 22, 23)]
+    else:
+        ins = [np.abs(W.fma_rows_f32(shape, seed=24)[0])]
+    y = run_tile_ewise(op, ins, dt, dt, shape, box, threads)
+    ref = REF.ewise(op, ins, NP[dt])
+    assert np.array_equal(y.view(np.uint16 if dt == "f16" else np.uint32),
+                          ref.view(np.uint16 if dt == "f16" else np.uint32))
