@@ -266,6 +266,43 @@ struct LaneMap {
   uint32_t abo[kMaxOuter];    // LDS offset of the chunk's row scalar (row ops)
 };
 
+// Offsets of the staged byte at physical LDS position pb of the image: the
+// logical byte lb (through the swizzle), its input and output byte offsets
+// from the stage origin, its stage row (row ops) and the partial slots along
+// which it lies past the edge.
+struct ByteMap {
+  uint32_t lb, xo, oo, row, ob;
+};
+
+__device__ __forceinline__ ByteMap map_byte(CArgs* A, uint32_t pb, int n_axes, int swz, int es_log2) {
+  ByteMap r;
+  r.lb = swz ? swz128(pb) : pb;
+  const uint32_t sub_byte = r.lb & ((1u << es_log2) - 1u);  // copies of elements wider than the chunk
+  uint32_t e = r.lb >> es_log2;
+  r.xo = sub_byte;
+  r.oo = sub_byte;
+  r.row = 0;
+  uint32_t rel[kPartial] = {0, 0, 0, 0};
+#pragma nounroll
+  for (int k = n_axes - 1; k >= 0; --k) {
+    const uint32_t q = mdiv(e, A->ax_mag[k], A->ax_sh[k]);
+    const uint32_t idx = e - q * A->ax_count[k];
+    e = q;
+    r.xo += idx * A->ax_xs[k];
+    r.oo += idx * A->ax_os[k];
+    r.row += idx * A->ax_rs[k];
+    const int ps = A->ax_pslot[k];
+#pragma unroll
+    for (int s2 = 0; s2 < kPartial; ++s2)
+      if (ps == s2) rel[s2] += idx * A->ax_step[k];
+  }
+  r.ob = 0;
+#pragma unroll
+  for (int s2 = 0; s2 < kPartial; ++s2)
+    if (rel[s2] >= A->prem[s2]) r.ob |= 1u << s2;
+  return r;
+}
+
 template <int VB>
 __device__ __forceinline__ void build_map(CArgs* A, int wave, int lane, LaneMap& m) {
   const int outer = A->outer, waves = A->waves, n_axes = A->n_axes;
@@ -274,38 +311,43 @@ __device__ __forceinline__ void build_map(CArgs* A, int wave, int lane, LaneMap&
   for (int g = 0; g < kMaxOuter; ++g) m.xoff[g] = m.ooff[g] = m.oobm[g] = m.lpos[g] = m.abo[g] = 0;
 #pragma nounroll
   for (int f = 0; f < outer; ++f) {
-    const uint32_t pb = ((f * waves + wave) * 64u + lane) * VB;
-    const uint32_t lb = swz ? swz128(pb) : pb;
-    const uint32_t sub_byte = lb & ((1u << es_log2) - 1u);  // copies of elements wider than VB
-    uint32_t e = lb >> es_log2;
-    uint32_t xo = sub_byte, oo = sub_byte, row = 0;
-    uint32_t rel[kPartial] = {0, 0, 0, 0};
-#pragma nounroll
-    for (int k = n_axes - 1; k >= 0; --k) {
-      const uint32_t q = mdiv(e, A->ax_mag[k], A->ax_sh[k]);
-      const uint32_t idx = e - q * A->ax_count[k];
-      e = q;
-      xo += idx * A->ax_xs[k];
-      oo += idx * A->ax_os[k];
-      row += idx * A->ax_rs[k];
-      const int ps = A->ax_pslot[k];
-#pragma unroll
-      for (int s2 = 0; s2 < kPartial; ++s2)
-        if (ps == s2) rel[s2] += idx * A->ax_step[k];
-    }
-    uint32_t ob = 0;
-#pragma unroll
-    for (int s2 = 0; s2 < kPartial; ++s2)
-      if (rel[s2] >= A->prem[s2]) ob |= 1u << s2;
-    const uint32_t abo = (row >> 5) * 256u + (row & 31u) * 4u;
+    const ByteMap b = map_byte(A, ((f * waves + wave) * 64u + lane) * VB, n_axes, swz, es_log2);
+    const uint32_t abo = (b.row >> 5) * 256u + (b.row & 31u) * 4u;
 #pragma unroll
     for (int g = 0; g < kMaxOuter; ++g)
       if (g == f) {
-        m.xoff[g] = xo;
-        m.ooff[g] = oo;
-        m.oobm[g] = ob;
-        m.lpos[g] = lb;
+        m.xoff[g] = b.xo;
+        m.ooff[g] = b.oo;
+        m.oobm[g] = b.ob;
+        m.lpos[g] = b.lb;
         m.abo[g] = abo;
+      }
+  }
+}
+
+// Consumer pieces of a widening op: every 16-byte round of a wave (1 KiB of
+// LDS) is consumed as two halves of 512 B, lane l taking the 8 bytes at
+// 8 * l of each half.  Eight input bytes widen to 16 output bytes, so every
+// store instruction writes 1 KiB of whole output rows instead of 16-byte
+// pieces 32 bytes apart.  Piece 2 * f + h: output offset, partial slots and
+// logical image byte.
+template <int N>
+__device__ __forceinline__ void build_pieces(CArgs* A, int wave, int lane, int outer, uint32_t (&oo)[N],
+                                             uint32_t (&ob)[N], uint32_t (&lp)[N]) {
+  const int waves = A->waves, n_axes = A->n_axes;
+  const int swz = A->swizzle, es_log2 = A->esize_log2;
+#pragma unroll
+  for (int g = 0; g < N; ++g) oo[g] = ob[g] = lp[g] = 0;
+#pragma nounroll
+  for (int q = 0; q < 2 * outer; ++q) {
+    const uint32_t f = q >> 1, h = q & 1;
+    const ByteMap b = map_byte(A, (f * waves + wave) * 1024u + h * 512u + lane * 8u, n_axes, swz, es_log2);
+#pragma unroll
+    for (int g = 0; g < N; ++g)
+      if (g == q) {
+        oo[g] = b.oo;
+        ob[g] = b.ob;
+        lp[g] = b.lb;
       }
   }
 }
@@ -577,8 +619,8 @@ struct EnginePolicy {
   unsigned char* lds;
   uint32_t lds0, wg, grid;
   int wave, lane, esize_log2, swizzle;
-  const uint64_t* row_ptr;
-  const uint32_t* row_bad;
+  uint64_t row_ptr[3];   // by value: a pointer to the caller's arrays would keep them in scratch memory
+  uint32_t row_bad[2];
 
   __device__ __forceinline__ void load(int j, int slot) {
     const Trip t = trip_geometry(A, L, wg, grid, j);
@@ -614,7 +656,8 @@ __global__ __launch_bounds__(1024) void engine_kernel_t(const EngineArgs) {
   uint64_t row_ptr[3];
   uint32_t row_bad[2];
   build_rows(A, lane, row_ptr, row_bad);
-  EnginePolicy<OP, VB, STAGE_OUT> pol{A, L, m, lds, lds0, wg, grid, wave, lane, esize_log2, swizzle, row_ptr, row_bad};
+  EnginePolicy<OP, VB, STAGE_OUT> pol{A, L, m, lds, lds0, wg, grid, wave, lane, esize_log2, swizzle,
+                                      {row_ptr[0], row_ptr[1], row_ptr[2]}, {row_bad[0], row_bad[1]}};
   typedef ChunkShape<OP, VB> CS;
   const int d = L.n_in * L.outer + (L.row_ops ? L.ab_instr : 0);
   const int st = L.outer * CS::ST;
@@ -791,6 +834,15 @@ __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
 // table sets alternate so that the load cursor (up to S-1 trips ahead) can
 // enter the next batch while the consume cursor finishes the current one.
 
+// Rounds consumed together: the largest power of two dividing `total` (a
+// power of two) whose staged operands (ns each) stay within `cap` registers'
+// worth of chunks.
+constexpr int round_group(int total, int ns, int cap) {
+  int g = total;
+  while (g > 1 && g * (ns > 0 ? ns : 1) > cap) g /= 2;
+  return g;
+}
+
 struct TripRow {
   uint32_t xlo, xhi, olo, ohi, rlo, flags;  // flags: bits 0..3 last-stage slots, bit 8 out of range
 };
@@ -835,6 +887,11 @@ template <class OP, int MODE, int OUTER, bool SROW>
 struct GenPolicy {
   static constexpr bool STAGE_OUT = (MODE == 1);
   static constexpr int NS = (MODE == 1) ? OP::NIN : 1;   // staged operands
+  // widening ops (16 input bytes -> 32 output bytes) consume 8-byte pieces
+  // (tile ops up to 4 rounds: beyond, the piece maps no longer fit in registers)
+  static constexpr bool SPLIT = (MODE == 2 || (MODE == 1 && OUTER <= 4)) && ChunkShape<OP, 16>::OB == 32;
+  static constexpr int NP = SPLIT ? 2 * OUTER : 1;
+  uint32_t pooff[NP], poobm[NP], plpos[NP];
   CArgs* A;
   unsigned char* lds;
   const char* in[3];
@@ -844,9 +901,11 @@ struct GenPolicy {
   int wave, lane, rank, ab_instr, swizzle, esize_log2;
   bool load_nt, store_nt;
   uint32_t xoff[OUTER], ooff[OUTER], oobm[OUTER], lpos[OUTER], abo[OUTER];
-  TripRow tab[2];
-  const uint64_t* row_ptr;   // [0] lane's array, [1 + q] row byte offset in the stage
-  const uint32_t* row_bad;   // partial slots along which the lane's row q lies past the edge
+  // two table sets as separate members: a dynamically indexed array would
+  // live in scratch memory, whose loads share the wave's vmcnt with the ring
+  TripRow tab0, tab1;
+  uint64_t row_ptr[3];   // [0] lane's array, [1 + q] row byte offset in the stage
+  uint32_t row_bad[2];   // partial slots along which the lane's row q lies past the edge
   // SROW: this wave's row (relative to the stage) of each round, and the
   // scalars of the trip being consumed, read through the scalar cache
   const float __attribute__((address_space(4)))* ca;
@@ -856,7 +915,13 @@ struct GenPolicy {
 
   __device__ __forceinline__ void fill(int set, uint32_t j0) {
     const TripRow r = trip_lane(A, wg, grid, tile0, subs, subs_mag, subs_sh, rank, j0 + static_cast<uint32_t>(lane));
-    if (set == 0) tab[0] = r; else tab[1] = r;
+    // field-wise selects: a conditional store of the whole row would be
+    // merged into one store through a selected address, i.e. into memory
+    const bool lo = set == 0;
+    tab0 = TripRow{lo ? r.xlo : tab0.xlo, lo ? r.xhi : tab0.xhi, lo ? r.olo : tab0.olo,
+                   lo ? r.ohi : tab0.ohi, lo ? r.rlo : tab0.rlo, lo ? r.flags : tab0.flags};
+    tab1 = TripRow{lo ? tab1.xlo : r.xlo, lo ? tab1.xhi : r.xhi, lo ? tab1.olo : r.olo,
+                   lo ? tab1.ohi : r.ohi, lo ? tab1.rlo : r.rlo, lo ? tab1.flags : r.flags};
   }
   struct T {
     uint64_t xb, ob, rb;
@@ -864,12 +929,12 @@ struct GenPolicy {
   };
   __device__ __forceinline__ T row(int j) const {
     const uint32_t l = static_cast<uint32_t>(j) & 63u;
-    const TripRow& r = ((j >> 6) & 1) ? tab[1] : tab[0];
+    const bool hi = ((j >> 6) & 1) != 0;
     T t;
-    t.xb = (static_cast<uint64_t>(rdl(r.xhi, l)) << 32) | rdl(r.xlo, l);
-    t.ob = (static_cast<uint64_t>(rdl(r.ohi, l)) << 32) | rdl(r.olo, l);
-    t.rb = rdl(r.rlo, l);
-    t.flags = rdl(r.flags, l);
+    t.xb = (static_cast<uint64_t>(rdl(hi ? tab1.xhi : tab0.xhi, l)) << 32) | rdl(hi ? tab1.xlo : tab0.xlo, l);
+    t.ob = (static_cast<uint64_t>(rdl(hi ? tab1.ohi : tab0.ohi, l)) << 32) | rdl(hi ? tab1.olo : tab0.olo, l);
+    t.rb = rdl(hi ? tab1.rlo : tab0.rlo, l);
+    t.flags = rdl(hi ? tab1.flags : tab0.flags, l);
     return t;
   }
 
@@ -916,6 +981,49 @@ struct GenPolicy {
     wait_vmcnt(k);
   }
 
+  // Widening ops: 8 input bytes per lane and piece, 16 output bytes.
+  __device__ __forceinline__ void consume_pieces(__amdgpu_buffer_rsrc_t rs, uint32_t sl, bool beyond, uint32_t last) {
+    typedef typename OP::TI TI;
+    typedef typename OP::TO TO;
+    constexpr int NE = 8 / sizeof(TI);
+    constexpr int GRP = round_group(NP, NS, 32);
+    static_assert(NP % GRP == 0, "piece groups must tile the pieces");
+#pragma unroll
+    for (int g0 = 0; g0 < NP; g0 += GRP) {
+      u32x2 v[NS > 0 ? NS : 1][GRP];
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const int q = g0 + u, f = q >> 1, h = q & 1;
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+          v[k][u] = *reinterpret_cast<const u32x2*>(__builtin_assume_aligned(
+              lds + sl + k * in_image_bytes + f * waves_kb + wave * 1024u + h * 512u + lane * 8u, 8));
+        if constexpr (NS == 0) v[0][u] = u32x2{0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const int q = g0 + u;
+        TI in0[NE], in1[NE], in2[NE];
+        __builtin_memcpy(in0, &v[0][u], 8);
+        __builtin_memcpy(in1, &v[NS > 1 ? 1 : 0][u], 8);
+        __builtin_memcpy(in2, &v[NS > 2 ? 2 : 0][u], 8);
+        TO res[NE];
+#pragma unroll
+        for (int e = 0; e < NE; ++e) res[e] = OP::f(in0[e], in1[e], in2[e], 0.f, 0.f);
+        uint32_t words[4];
+        __builtin_memcpy(words, res, 16);
+        if constexpr (STAGE_OUT) {
+          const uint32_t lo = (plpos[q] >> esize_log2) * sizeof(TO);
+          __builtin_memcpy(lds + out_image_off + (swizzle ? swz128(lo) : lo), words, 16);
+          asm volatile("" ::: "memory");
+          __builtin_memcpy(words, lds + out_image_off + (swizzle ? swz128(lo) : lo), 16);
+        }
+        const bool ok = !beyond && (poobm[q] & last) == 0;
+        store_chunk<16>(rs, ok ? pooff[q] : kOobOffset, words, store_nt);
+      }
+    }
+  }
+
   __device__ __forceinline__ void consume(int i, int slot) {
     typedef ChunkShape<OP, 16> CS;
     typedef typename OP::TI TI;
@@ -925,55 +1033,67 @@ struct GenPolicy {
     const uint32_t last = t.flags & 0xFFu;
     const __amdgpu_buffer_rsrc_t rs = rsrc_store(out + t.ob, range_from(out_span, t.ob));
     const uint32_t sl = slot * slot_bytes;
-    u32x4 v[NS > 0 ? NS : 1][OUTER];
-    float ra[OUTER], rb[OUTER];
-#pragma unroll
-    for (int f = 0; f < OUTER; ++f) {
-#pragma unroll
-      for (int k = 0; k < NS; ++k)
-        v[k][f] = *reinterpret_cast<const u32x4*>(
-            __builtin_assume_aligned(lds + sl + k * in_image_bytes + f * waves_kb + wave * 1024u + lane * 16u, 16));
-      if constexpr (NS == 0) v[0][f] = u32x4{0, 0, 0, 0};
-      if constexpr (OP::ROW && SROW) {
-        ra[f] = sa[f];
-        rb[f] = sb[f];
-      } else if constexpr (OP::ROW) {
-        ra[f] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f]);
-        rb[f] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f] + 128u);
-      } else {
-        ra[f] = rb[f] = 0.f;
-      }
+    if constexpr (SPLIT) {
+      consume_pieces(rs, sl, beyond, last);
+      return;
     }
+    // rounds in groups whose staged operands fit in registers together
+    constexpr int GRP = round_group(OUTER, NS, 16);
+    static_assert(OUTER % GRP == 0, "round groups must tile the rounds");
 #pragma unroll
-    for (int f = 0; f < OUTER; ++f) {
-      TI in0[CS::NE], in1[CS::NE], in2[CS::NE];
-      __builtin_memcpy(in0, &v[0][f], 16);
-      __builtin_memcpy(in1, &v[NS > 1 ? 1 : 0][f], 16);
-      __builtin_memcpy(in2, &v[NS > 2 ? 2 : 0][f], 16);
-      TO res[CS::NE];
+    for (int g0 = 0; g0 < OUTER; g0 += GRP) {
+      u32x4 v[NS > 0 ? NS : 1][GRP];
+      float ra[GRP], rb[GRP];
 #pragma unroll
-      for (int e = 0; e < CS::NE; ++e) res[e] = OP::f(in0[e], in1[e], in2[e], ra[f], rb[f]);
-      uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      __builtin_memcpy(words, res, CS::OB);
-      if constexpr (STAGE_OUT) {
-        // the output tile is LDS-resident ("elementwise -> smem") and is copied out from there
-        const uint32_t lo = (lpos[f] >> esize_log2) * CS::EO;
-        constexpr int P = (CS::OB + 15) / 16;
-        constexpr int PB = CS::OB < 16 ? CS::OB : 16;
+      for (int u = 0; u < GRP; ++u) {
+        const int f = g0 + u;
 #pragma unroll
-        for (int piece = 0; piece < P; ++piece) {
-          const uint32_t lp = lo + piece * 16;
-          __builtin_memcpy(lds + out_image_off + (swizzle ? swz128(lp) : lp), words + piece * 4, PB);
-        }
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int piece = 0; piece < P; ++piece) {
-          const uint32_t lp = lo + piece * 16;
-          __builtin_memcpy(words + piece * 4, lds + out_image_off + (swizzle ? swz128(lp) : lp), PB);
+        for (int k = 0; k < NS; ++k)
+          v[k][u] = *reinterpret_cast<const u32x4*>(
+              __builtin_assume_aligned(lds + sl + k * in_image_bytes + f * waves_kb + wave * 1024u + lane * 16u, 16));
+        if constexpr (NS == 0) v[0][u] = u32x4{0, 0, 0, 0};
+        if constexpr (OP::ROW && SROW) {
+          ra[u] = sa[f];
+          rb[u] = sb[f];
+        } else if constexpr (OP::ROW) {
+          ra[u] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f]);
+          rb[u] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f] + 128u);
+        } else {
+          ra[u] = rb[u] = 0.f;
         }
       }
-      const bool ok = !beyond && (oobm[f] & last) == 0;
-      store_chunk<CS::OB>(rs, ok ? ooff[f] : kOobOffset, words, store_nt);
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const int f = g0 + u;
+        TI in0[CS::NE], in1[CS::NE], in2[CS::NE];
+        __builtin_memcpy(in0, &v[0][u], 16);
+        __builtin_memcpy(in1, &v[NS > 1 ? 1 : 0][u], 16);
+        __builtin_memcpy(in2, &v[NS > 2 ? 2 : 0][u], 16);
+        TO res[CS::NE];
+#pragma unroll
+        for (int e = 0; e < CS::NE; ++e) res[e] = OP::f(in0[e], in1[e], in2[e], ra[u], rb[u]);
+        uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        __builtin_memcpy(words, res, CS::OB);
+        if constexpr (STAGE_OUT) {
+          // the output tile is LDS-resident ("elementwise -> smem") and is copied out from there
+          const uint32_t lo = (lpos[f] >> esize_log2) * CS::EO;
+          constexpr int P = (CS::OB + 15) / 16;
+          constexpr int PB = CS::OB < 16 ? CS::OB : 16;
+#pragma unroll
+          for (int piece = 0; piece < P; ++piece) {
+            const uint32_t lp = lo + piece * 16;
+            __builtin_memcpy(lds + out_image_off + (swizzle ? swz128(lp) : lp), words + piece * 4, PB);
+          }
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int piece = 0; piece < P; ++piece) {
+            const uint32_t lp = lo + piece * 16;
+            __builtin_memcpy(words + piece * 4, lds + out_image_off + (swizzle ? swz128(lp) : lp), PB);
+          }
+        }
+        const bool ok = !beyond && (oobm[f] & last) == 0;
+        store_chunk<CS::OB>(rs, ok ? ooff[f] : kOobOffset, words, store_nt);
+      }
     }
   }
 };
@@ -1025,8 +1145,10 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   p.esize_log2 = uni(A->esize_log2);
   p.load_nt = L.load_nt != 0;
   p.store_nt = L.store_nt != 0;
-  p.row_ptr = row_ptr;
-  p.row_bad = row_bad;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) p.row_ptr[q] = row_ptr[q];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) p.row_bad[q] = row_bad[q];
   p.ca = (const float __attribute__((address_space(4)))*)(unip(A->row_a));
   p.cb = (const float __attribute__((address_space(4)))*)(unip(A->row_b));
 #pragma unroll
@@ -1040,7 +1162,8 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
     p.row_of[f] = (abo >> 8) * 32u + (abo & 255u) / 4u;
     p.sa[f] = p.sb[f] = 0.f;
   }
-  p.tab[1] = TripRow{0, 0, 0, 0, 0, 0};
+  if constexpr (GenPolicy<OP, MODE, OUTER, SROW>::SPLIT) build_pieces(A, wave, lane, OUTER, p.pooff, p.poobm, p.plpos);
+  p.tab1 = TripRow{0, 0, 0, 0, 0, 0};
   p.fill(0, 0u);
   typedef ChunkShape<OP, 16> CS;
   constexpr int NS = GenPolicy<OP, MODE, OUTER, SROW>::NS;

@@ -2,9 +2,10 @@
 """Throughput of the pipelined tile copy + elementwise path on one MI355X.
 
 Default workload: y = a[row] * x + b[row] over a [128, 500, 1024] float32
-tensor streamed through a 4-stage LDS ring (stage = 4 rows x 1024), the
-configuration the HBM-roofline target is quoted on.  One step = one launch
-of acp_stream_ewise over the whole tensor.  Inputs are seeded synthetic
+tensor streamed through a 4-stage LDS ring (stage = 2 rows x 1024, one
+persistent workgroup per CU), the configuration the HBM-roofline target is
+quoted on.  One step = one launch of acp_stream_ewise over the whole tensor.
+The same line also reports the 2- and 3-stage rings ("ring_stages").  Inputs are seeded synthetic
 tensors resident in HBM; three buffer sets are rotated so that consecutive
 steps never hit data left in the 256 MB last-level cache by the previous one.
 
@@ -27,8 +28,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "achieved HBM GB/s (and % of peak) for pipelined tile copy+ewise, 1 MI355X"
 PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["acp_engine_impl.hpp", "acp_k_stream_f32.hip", "acp_k_stream_f16.hip",
-                  "acp_k_tile.hip", "acp_k_copy.hip", "acp_api.cpp"]
+KERNEL_SOURCES = ["acp_engine_impl.hpp", "acp_engine.hpp", "acp_k_stream_f32.hip", "acp_k_stream_f16.hip",
+                  "acp_k_tile.hip", "acp_k_tile_gen.hip", "acp_k_copy.hip", "acp_api.cpp"]
 
 
 def kernel_hash() -> str:
@@ -62,13 +63,14 @@ def parse():
                     help="c4: the streamed fma (default); c2/c3/c5: the other workloads; "
                          "calib: torch's copy of 256 MiB, the known-size kernel that scales HBM counters")
     ap.add_argument("--stages", type=int, default=4)
-    ap.add_argument("--rows", type=int, default=4, help="rows per ring stage (c4)")
+    ap.add_argument("--rows", type=int, default=2, help="rows per ring stage (c4)")
     ap.add_argument("--threads", type=int, default=256)
     ap.add_argument("--workgroups", type=int, default=0, help="persistent workgroups (0: 256 x --wg-per-cu)")
-    ap.add_argument("--wg-per-cu", type=int, default=2)
+    ap.add_argument("--wg-per-cu", type=int, default=1)
     ap.add_argument("--sets", type=int, default=3, help="rotated buffer sets")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ring-sweep", action="store_true", help="c4: skip the 2/3-stage report (profiling runs)")
     return ap.parse_args()
 
 
@@ -106,14 +108,20 @@ def main():
         stage = (1, args.rows, 1024)
         x, a, b = W.fma_rows_f32(shape, seed=4)
         G = args.workgroups or 256 * args.wg_per_cu
+        descs, keep = [], []
         for s in range(args.sets):
             xd, ad, bd = to_dev(x), to_dev(a), to_dev(b)
             yd = torch.empty(x.nbytes, dtype=torch.uint8, device=dev)
             xdesc = acp.acp_encode_tiled("f32", xd, shape, packed(shape), stage)
             ydesc = acp.acp_encode_tiled("f32", yd, shape, packed(shape), stage)
+            descs.append((xdesc, ydesc, ad, bd))
+            keep.append((xd, yd))
             launches.append((lambda xdesc=xdesc, ydesc=ydesc, ad=ad, bd=bd, keep=(xd, yd):
                              acp.acp_stream_ewise("fma", ydesc, xdesc, ad, bd, stage, args.stages,
                                                   args.threads, G, stream)))
+        ring_launches = {st: [(lambda xdesc=xdesc, ydesc=ydesc, ad=ad, bd=bd, st=st:
+                               acp.acp_stream_ewise("fma", ydesc, xdesc, ad, bd, stage, st, args.threads, G, stream))
+                              for (xdesc, ydesc, ad, bd) in descs] for st in (2, 3, 4)}
         bytes_per = x.nbytes * 2 + a.nbytes + b.nbytes
         dtype = "f32"
         config = {"workload": f"stream fma y=a[row]*x+b[row], [128,500,1024] f32, {args.stages}-stage LDS ring, "
@@ -131,7 +139,7 @@ def main():
             launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
                             acp.acp_tile_ewise("sqrt", ydesc, [xdesc], 256, stream))
         bytes_per, dtype = x.nbytes * 2, "f32"
-        config = {"workload": "tile sqrt, 65536 tiles of 32x32 f32, 256 threads, one tile per workgroup"}
+        config = {"workload": "tile sqrt, 65536 tiles of 32x32 f32, 256 threads, persistent grid"}
         key = "tile_sqrt_f32_65536x32x32"
     elif wl == "c3":
         shape = (128, 500, 1024)
@@ -204,6 +212,24 @@ def main():
     value = bytes_per / (ms_per_step * 1e-3) / 1e9
     achieved = bytes_per / (avg_launch_ms * 1e-3) / 1e9
 
+    ring = None
+    if wl == "c4" and not args.no_ring_sweep:
+        # the 2-, 3- and 4-stage rings, back to back like `value`
+        ring = {}
+        for st in (2, 3, 4):
+            fns = ring_launches[st] if st != args.stages else launches
+            for i in range(args.warmup):
+                fns[i % len(fns)]()
+            torch.cuda.synchronize()
+            r0 = torch.cuda.Event(enable_timing=True)
+            r1 = torch.cuda.Event(enable_timing=True)
+            r0.record(stream)
+            for i in range(args.steps):
+                fns[i % len(fns)]()
+            r1.record(stream)
+            torch.cuda.synchronize()
+            ring[str(st)] = round(bytes_per / (r0.elapsed_time(r1) / args.steps * 1e-3) / 1e9, 1)
+
     traffic = traffic_from_profiles(key)
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -218,6 +244,8 @@ def main():
                      "avg_launch_ms": round(avg_launch_ms, 5), "median_launch_ms": round(per_launch[len(per_launch) // 2], 5),
                      "kernel_source_hash": kernel_hash()},
     }
+    if ring is not None:
+        result["ring_stages"] = {"unit": "GB/s", **ring}
     if not args.no_cpu_baseline and wl == "c4":
         result["cpu_baseline"] = cpu_baseline_c4(args.cpu_seconds)
     print(json.dumps(result), flush=True)

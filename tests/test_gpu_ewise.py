@@ -63,6 +63,11 @@ CASES = [
     ("exp", 1, "f32", "f32", (3, 70, 128), (1, 16, 128), 256, 0),
     ("exp", 1, "f16", "f32", (2, 50, 256), (1, 8, 256), 128, 3),
     ("exp", 1, "f32", "f16", (3, 70, 128), (1, 16, 128), 256, 0),
+    # eight rounds per thread: three operands consumed in groups of rounds;
+    # a widening op past the 8-byte piece consumer's limit
+    ("fma", 3, "f32", "f32", (3, 70, 128), (1, 16, 128), 64, 0),
+    ("exp", 1, "f16", "f32", (2, 50, 256), (1, 16, 256), 64, 3),
+    ("sqrt", 1, "f16", "f32", (2, 50, 256), (1, 8, 256), 64, 3),
 ]
 
 
