@@ -87,6 +87,7 @@ _SIGS = {
     "acp_stream_ewise": ([_I, _DESC_P, _DESC_P, _P, _P, ctypes.POINTER(ctypes.c_int32), _I, _I, _I, _P], _I),
     "acp_debug_lds_image": ([_DESC_P, ctypes.c_int64, _I, _P, _P], _I),
     "acp_debug_ring_trace": ([_I, _I, _I, _I, _P, _P], _I),
+    "acp_debug_stream_copy": ([_P, _P, ctypes.c_int64, _I, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -174,3 +175,7 @@ def acp_debug_lds_image(src: acp_tile_desc, tile_index: int, threads: int, out_b
 def acp_debug_ring_trace(n_iters: int, stages: int, loads: int, stores: int, out_events, stream=None) -> None:
     _check(_lib.acp_debug_ring_trace(int(n_iters), int(stages), int(loads), int(stores), _ptr(out_events),
                                      _stream(stream)))
+
+
+def acp_debug_stream_copy(dst, src, nbytes: int, workgroups: int = 0, stream=None) -> None:
+    _check(_lib.acp_debug_stream_copy(_ptr(dst), _ptr(src), int(nbytes), int(workgroups), _stream(stream)))

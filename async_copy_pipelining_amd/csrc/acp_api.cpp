@@ -651,4 +651,21 @@ acp_status acp_debug_ring_trace(int n_iters, int stages, int loads, int stores, 
   return ret(ACP_OK);
 }
 
+acp_status acp_debug_stream_copy(void* dst, const void* src, int64_t bytes, int workgroups, void* hip_stream) {
+  if (!dst || !src || bytes < 0 || workgroups < 0) return ret(ACP_ERR_INVALID, "bad stream copy arguments");
+  if (bytes % 16 != 0) return ret(ACP_ERR_INVALID, "stream copy moves whole 16-byte units");
+  if (bytes >= (int64_t(1) << 40)) return ret(ACP_ERR_INVALID, "stream copy size out of range");
+  const char* s = static_cast<const char*>(src);
+  const char* d = static_cast<const char*>(dst);
+  if (s < d + bytes && d < s + bytes) return ret(ACP_ERR_INVALID, "source and destination overlap");
+  if (bytes == 0) return ret(ACP_OK);
+  const int64_t blocks = (bytes + 16383) / 16384;
+  int64_t grid = workgroups > 0 ? workgroups : device_cu_count();
+  if (grid > blocks) grid = blocks;
+  const hipError_t e = acp::stream_copy_launch(src, dst, static_cast<uint64_t>(bytes), static_cast<unsigned>(grid),
+                                               static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ret(ACP_OK);
+}
+
 }  // extern "C"

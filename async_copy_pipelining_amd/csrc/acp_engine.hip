@@ -1,4 +1,5 @@
-// Kernel registry, launch helpers and the two debug kernels of the engine.
+// Kernel registry, launch helpers, the two debug kernels of the engine and the
+// register-path reference copy.
 #include "acp_engine_impl.hpp"
 
 namespace acp {
@@ -56,7 +57,34 @@ __global__ void ring_trace_kernel(int n, int s, int loads, int stores, int32_t* 
   run_ring(p, n, s, loads, stores);
 }
 
+// Measurement reference: a plain register-path copy (no LDS, no ring).
+// Workgroup w copies 16 KiB blocks w, w+G, ...: four 16-byte non-temporal
+// loads per lane, then the four stores.  The block's buffer resources end at
+// the copy's end, so a short last block reads zeros past it and its stores
+// there are dropped.
+__global__ __launch_bounds__(256) void stream_copy_kernel(const char* src, char* dst, uint64_t bytes) {
+  const uint64_t blocks = (bytes + 16383u) / 16384u;
+  for (uint64_t b = blockIdx.x; b < blocks; b += gridDim.x) {
+    const uint64_t off = b * 16384u;
+    const uint64_t left = bytes - off;
+    const int range = static_cast<int>(left < 16384u ? left : 16384u);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src) + off, 0, range, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(dst + off, 0, range, 0x00020000);
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (u * 256 + threadIdx.x) * 16, 0, 2);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], ry, (u * 256 + threadIdx.x) * 16, 0, 2);
+  }
+}
+
 }  // namespace dev
+
+hipError_t stream_copy_launch(const void* src, void* dst, uint64_t bytes, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL(dev::stream_copy_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const char*>(src),
+                     static_cast<char*>(dst), bytes);
+  return hipGetLastError();
+}
 
 const void* engine_kernel(const KernelKey& k) {
   if (const void* f = lookup_copy(k)) return f;

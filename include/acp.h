@@ -211,6 +211,19 @@ acp_status acp_debug_lds_image(const acp_tile_desc* src, int64_t tile_index, int
 acp_status acp_debug_ring_trace(int n_iters, int stages, int loads, int stores, int32_t* out_events,
                                 void* hip_stream);
 
+/* Measurement reference (not part of the pipelined path): copy `bytes`
+ * (a multiple of 16) from device memory `src` to the non-overlapping device
+ * memory `dst` with a plain register-path kernel: no LDS and no ring, each
+ * workgroup of 256 threads moving 16 KiB blocks (four 16-byte non-temporal
+ * loads per lane, then four stores) in a grid-stride loop.  `workgroups` 0
+ * takes one per compute unit.  The caller owns both buffers; the copy is
+ * asynchronous on `hip_stream`.  It gives the bandwidth a plain 1:1
+ * read/write stream reaches on the device, the practical ceiling against
+ * which the ring's streams are compared.  ACP_ERR_INVALID on null pointers,
+ * a size that is negative, not a multiple of 16 or at least 2^40, or
+ * overlapping buffers. */
+acp_status acp_debug_stream_copy(void* dst, const void* src, int64_t bytes, int workgroups, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

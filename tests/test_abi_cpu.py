@@ -133,3 +133,9 @@ def test_status_codes_and_reasons():
         acp.acp_tile_copy(x, acp.acp_encode_tiled("f16", FAKE_BASE, (4, 8, 256), (2048, 256, 1), (1, 4, 256)), 256)
     assert e.value.status == acp.ACP_ERR_INVALID and "valid copy" in e.value.reason
     assert acp.acp_last_error() != ""
+    # the reference stream copy checks its arguments before any launch
+    for dst, src, n, why in ((FAKE_BASE, FAKE_BASE + 64, 128, "overlap"), (FAKE_BASE, FAKE_BASE * 8, 100, "16-byte"),
+                             (FAKE_BASE, FAKE_BASE * 8, -16, "bad"), (None, FAKE_BASE, 16, "bad")):
+        with pytest.raises(acp.AcpError) as e:
+            acp.acp_debug_stream_copy(dst, src, n)
+        assert e.value.status == acp.ACP_ERR_INVALID and why in e.value.reason

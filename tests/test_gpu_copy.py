@@ -162,3 +162,16 @@ def test_persistent_grid_ragged_tile_counts(shape, box, threads):
     acp.acp_tile_copy(src, dst, threads, stream())
     torch.cuda.synchronize()
     assert torch.equal(xd, yd)
+
+
+@pytest.mark.parametrize("nbytes,workgroups", [(16, 0), (16384 * 3 + 48, 2), (5_000_000 - 16 * 7, 0)])
+def test_reference_stream_copy_is_bit_identical(nbytes, workgroups):
+    say(f"reference stream copy of {nbytes} bytes, workgroups {workgroups}")
+    rng = np.random.default_rng(31)
+    x = rng.integers(0, 256, nbytes + 64, dtype=np.uint8)
+    xd = dev(x)
+    yd = empty_bytes(nbytes + 64, 0x5A)
+    acp.acp_debug_stream_copy(yd, xd, nbytes, workgroups, stream())
+    y = host(yd, np.uint8)
+    assert np.array_equal(y[:nbytes], x[:nbytes])
+    assert np.all(y[nbytes:] == 0x5A)      # nothing written past the end
