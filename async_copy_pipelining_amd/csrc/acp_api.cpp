@@ -106,6 +106,7 @@ struct EngineRequest {
   const float* row_b;
   bool row_ops;
   bool copy_only;
+  int tiles_per_trip = 1;      // tile ops on a persistent grid: 1, 2 or 4
 };
 
 acp_status prepare(const EngineRequest& q, Launch* L) {
@@ -285,42 +286,6 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   A.swizzle = x.swizzle == 3 ? 1 : 0;
   A.n_in = q.n_in;
 
-  const int64_t in_img = align_up(p.tile_bytes(), 1024);
-  const int64_t out_img = q.mode == 1 ? align_up(p.tile_elems() * eo, 1024) : 0;
-  A.in_image_bytes = static_cast<uint32_t>(in_img);
-  A.ab_off = static_cast<uint32_t>(q.n_in * in_img);
-  A.row_ops = q.row_ops ? 1 : 0;
-  if (q.row_ops) {
-    if (n_rows > 64) return ret(ACP_ERR_UNSUPPORTED, "per-row scalars need at most 64 rows per stage");
-    A.n_rows = static_cast<int32_t>(n_rows);
-    A.ab_instr = static_cast<int32_t>((n_rows + 31) / 32);
-    A.ab_wave_bytes = static_cast<uint32_t>(A.ab_instr * 256);
-  }
-  const int64_t slot = align_up(A.ab_off + (q.row_ops ? A.waves * A.ab_wave_bytes : 0), 1024);
-  A.slot_bytes = static_cast<uint32_t>(slot);
-
-  const int64_t trips_max = subs * ((q.workgroups > 0 && q.workgroups < n_tiles)
-                                        ? (n_tiles + q.workgroups - 1) / q.workgroups : 1);
-  const int slots = static_cast<int>(q.stages < trips_max ? q.stages : trips_max);
-  A.stages = slots < 1 ? 1 : slots;
-  // The staged output image lies after the ring, one per workgroup: each
-  // lane writes its chunks there and reads the same bytes back before its
-  // store, so trips can share it and it costs no ring slot.
-  A.out_image_off = static_cast<uint32_t>(slot * A.stages);
-  const int64_t lds = slot * A.stages + out_img;
-  const int limit = device_lds_limit();
-  if (lds > limit)
-    return ret(ACP_ERR_LDS, "ring needs " + std::to_string(lds) + " bytes of LDS, device allows " +
-                                std::to_string(limit));
-
-  unsigned grid = static_cast<unsigned>(n_tiles);
-  if (q.workgroups > 0) grid = static_cast<unsigned>(q.workgroups);
-  // consecutive tiles (which often share cache lines at their edges) run on
-  // one XCD and hence one L2: blockIdx b -> (b % 8) * (G / 8) + b / 8
-  A.xcd_remap = (grid % 8 == 0 && grid >= 16 && xcd_remap_enabled()) ? 1 : 0;
-  L->grid = grid;
-  L->block = static_cast<unsigned>(q.threads);
-  L->lds = static_cast<unsigned>(lds);
   // every 1 KiB wave block inside one row: the innermost image run holds a
   // whole number of such blocks and nothing permutes it
   A.row_uniform = (q.row_ops && A.swizzle == 0 && (axes.back().count * ei) % (64 * p.vec_bytes) == 0) ? 1 : 0;
@@ -348,6 +313,49 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
     gk.srow = (q.mode == 2 && A.row_uniform && srow_ok) ? 1 : 0;
     if (acp::engine_kernel(gk)) L->key = gk;
   }
+  // tile ops in the general kernel on a persistent grid: tiles per ring trip
+  int tpt_log2 = 0;
+  if ((L->key.mode == 4 || L->key.mode == 5) && q.workgroups > 0 && subs == 1)
+    while ((2 << tpt_log2) <= q.tiles_per_trip && tpt_log2 < 2) ++tpt_log2;
+  A.tpt_log2 = static_cast<uint32_t>(tpt_log2);
+
+  const int64_t in_img = align_up(p.tile_bytes(), 1024);
+  const int64_t out_img = q.mode == 1 ? align_up(p.tile_elems() * eo, 1024) : 0;
+  A.in_image_bytes = static_cast<uint32_t>(in_img);
+  A.ab_off = static_cast<uint32_t>(q.n_in * in_img);
+  A.row_ops = q.row_ops ? 1 : 0;
+  if (q.row_ops) {
+    if (n_rows > 64) return ret(ACP_ERR_UNSUPPORTED, "per-row scalars need at most 64 rows per stage");
+    A.n_rows = static_cast<int32_t>(n_rows);
+    A.ab_instr = static_cast<int32_t>((n_rows + 31) / 32);
+    A.ab_wave_bytes = static_cast<uint32_t>(A.ab_instr * 256);
+  }
+  const int64_t slot = align_up(A.ab_off + (q.row_ops ? A.waves * A.ab_wave_bytes : 0), 1024) << tpt_log2;
+  A.slot_bytes = static_cast<uint32_t>(slot);
+
+  const int64_t groups = (n_tiles + (int64_t(1) << tpt_log2) - 1) >> tpt_log2;
+  const int64_t trips_max = subs * ((q.workgroups > 0 && q.workgroups < groups)
+                                        ? (groups + q.workgroups - 1) / q.workgroups : 1);
+  const int slots = static_cast<int>(q.stages < trips_max ? q.stages : trips_max);
+  A.stages = slots < 1 ? 1 : slots;
+  // The staged output image lies after the ring, one per workgroup: each
+  // lane writes its chunks there and reads the same bytes back before its
+  // store, so trips can share it and it costs no ring slot.
+  A.out_image_off = static_cast<uint32_t>(slot * A.stages);
+  const int64_t lds = slot * A.stages + out_img;
+  const int limit = device_lds_limit();
+  if (lds > limit)
+    return ret(ACP_ERR_LDS, "ring needs " + std::to_string(lds) + " bytes of LDS, device allows " +
+                                std::to_string(limit));
+
+  unsigned grid = static_cast<unsigned>(n_tiles);
+  if (q.workgroups > 0) grid = static_cast<unsigned>(q.workgroups);
+  // consecutive tiles (which often share cache lines at their edges) run on
+  // one XCD and hence one L2: blockIdx b -> (b % 8) * (G / 8) + b / 8
+  A.xcd_remap = (grid % 8 == 0 && grid >= 16 && xcd_remap_enabled()) ? 1 : 0;
+  L->grid = grid;
+  L->block = static_cast<unsigned>(q.threads);
+  L->lds = static_cast<unsigned>(lds);
   return ACP_OK;
 }
 
@@ -371,12 +379,18 @@ int device_cu_count() {
 
 // Tile copy and tile elementwise: the result of a tile does not depend on
 // which workgroup moves it, so large tile counts run on a persistent grid
-// that walks tiles w, w+G, ... through a ring of ACP_TILE_STAGES slots
-// (default 2).  Workgroups per CU (ACP_TILE_WG_PER_CU overrides): enough
-// that about 32 KiB of loads per CU are in flight while the previous trip is
-// consumed (measured best for both 4 KiB and 8 KiB tiles), at most 32 waves
-// per CU and what the LDS holds.
-void tile_schedule(const acp::Plan& p, int n_in, int threads, int64_t out_image, int* workgroups, int* stages) {
+// that walks tile groups w, w+G, ... through a ring of ACP_TILE_STAGES slots
+// (default 2); a group (one ring trip) is 1, 2 or 4 consecutive tiles.
+// Defaults, the best measured on MI355X (the environment overrides them):
+// * copy: one tile per trip and one workgroup per CU (fewer concurrent
+//   streams keep DRAM pages open; 128x32 float16 tiles ran 4.1 TB/s at one
+//   workgroup per CU against 3.2-3.3 TB/s at 2-4);
+// * elementwise: trips of about 16 KiB (ACP_TILES_PER_TRIP: 1, 2, 4) and
+//   about 32 KiB of loads in flight per CU (ACP_TILE_WG_PER_CU), within 32
+//   waves per CU and the LDS (32x32 float32 sqrt: 5.0-5.4 TB/s with 4 tiles
+//   per trip against 4.5-4.9 with one).
+void tile_schedule(const acp::Plan& p, int n_in, int threads, int64_t out_image, int* workgroups, int* stages,
+                   int* tiles_per_trip) {
   static const int env_per_cu = [] {
     const char* e = std::getenv("ACP_TILE_WG_PER_CU");
     return (e && std::atoi(e) > 0) ? std::atoi(e) : 0;
@@ -385,13 +399,24 @@ void tile_schedule(const acp::Plan& p, int n_in, int threads, int64_t out_image,
     const char* e = std::getenv("ACP_TILE_STAGES");
     return (e && std::atoi(e) > 0 && std::atoi(e) <= 4) ? std::atoi(e) : 2;
   }();
+  static const int env_tpt = [] {
+    const char* e = std::getenv("ACP_TILES_PER_TRIP");
+    const int v = e ? std::atoi(e) : 0;
+    return (v == 1 || v == 2 || v == 4) ? v : 0;
+  }();
   const int64_t n_tiles = p.n_tiles();
   const int64_t img = align_up(p.tile_bytes(), 1024);
   const int64_t ops = std::max(1, n_in);
+  const bool copy = out_image == 0;
+  int tpt = env_tpt;
+  if (tpt == 0) {
+    tpt = 1;
+    while (!copy && tpt < 4 && 2 * tpt * ops * p.tile_bytes() <= 16384) tpt *= 2;
+  }
   int64_t per_cu = env_per_cu;
   if (per_cu == 0) {
-    const int64_t lds_wg = slots * ops * img + align_up(out_image, 1024);
-    per_cu = std::max<int64_t>(1, 32768 / (ops * p.tile_bytes()));
+    const int64_t lds_wg = slots * tpt * ops * img + align_up(out_image, 1024);
+    per_cu = copy ? 1 : std::max<int64_t>(1, 32768 / (tpt * ops * p.tile_bytes()));
     per_cu = std::min<int64_t>(per_cu, std::max(1, 32 / std::max(1, threads / 64)));
     per_cu = std::min<int64_t>(per_cu, std::max<int64_t>(1, device_lds_limit() / lds_wg));
   }
@@ -399,9 +424,11 @@ void tile_schedule(const acp::Plan& p, int n_in, int threads, int64_t out_image,
   if (n_tiles > g) {
     *workgroups = static_cast<int>(g);
     *stages = slots;
+    *tiles_per_trip = tpt;
   } else {
     *workgroups = 0;  // one workgroup per tile, one trip each
     *stages = 1;
+    *tiles_per_trip = 1;
   }
 }
 
@@ -502,7 +529,7 @@ acp_status acp_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, int
   {
     acp::Plan p;
     std::string why;
-    if (acp::plan_box(s, true, &p, &why) == acp::PlanStatus::Ok) tile_schedule(p, 1, threads, 0, &q.workgroups, &q.stages);
+    if (acp::plan_box(s, true, &p, &why) == acp::PlanStatus::Ok) tile_schedule(p, 1, threads, 0, &q.workgroups, &q.stages, &q.tiles_per_trip);
     else q.stages = 1;
   }
   Launch L;
@@ -551,7 +578,7 @@ acp_status acp_tile_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_de
     acp::Plan p;
     std::string why;
     if (acp::plan_box(anchor, false, &p, &why) == acp::PlanStatus::Ok)
-      tile_schedule(p, n_in, threads, p.tile_elems() * o.esize, &q.workgroups, &q.stages);
+      tile_schedule(p, n_in, threads, p.tile_elems() * o.esize, &q.workgroups, &q.stages, &q.tiles_per_trip);
     else q.stages = 1;
   }
   Launch L;

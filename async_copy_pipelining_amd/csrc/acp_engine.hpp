@@ -71,6 +71,11 @@ struct EngineArgs {
   // Row ops whose every 1 KiB wave block lies inside one row: the per-row
   // scalars are read through the scalar cache instead of being staged.
   int32_t row_uniform;
+  // General kernel, tile copy / tile ewise on a persistent grid: every ring
+  // trip stages 2^tpt_log2 consecutive tiles (each with its own images in
+  // the slot), so tiles that share cache lines at their edges are loaded
+  // back to back.  Workgroup w takes tile groups w, w+G, ...
+  uint32_t tpt_log2;
 };
 
 // Which kernel variant a launch needs.

@@ -848,10 +848,11 @@ struct TripRow {
 };
 
 __device__ __forceinline__ TripRow trip_lane(CArgs* A, uint32_t wg, uint32_t grid, uint32_t tile0, uint32_t subs,
-                                             uint32_t subs_mag, uint32_t subs_sh, int rank, uint32_t j) {
+                                             uint32_t subs_mag, uint32_t subs_sh, int rank, uint32_t tpt_log2,
+                                             uint32_t j) {
   const uint32_t tl = mdiv(j, subs_mag, subs_sh);
   uint32_t sub = j - tl * subs;
-  uint32_t tile = tile0 + wg + tl * grid;
+  uint32_t tile = tile0 + (((wg + (tl >> tpt_log2) * grid) << tpt_log2) | (tl & ((1u << tpt_log2) - 1u)));
   uint64_t xb = 0, ob = 0, rb = 0;
   uint32_t flags = 0;
   // rolled: the per-dim parameters are read on each refill (once per 64
@@ -898,6 +899,7 @@ struct GenPolicy {
   char* out;
   uint64_t in_span, out_span, total_rows;
   uint32_t lds0, slot_bytes, in_image_bytes, out_image_off, ab_base, waves_kb, wg, grid, tile0, subs, subs_mag, subs_sh;
+  uint32_t tpt_log2, tile_lds;  // tiles per trip (log2) and LDS bytes of one tile's images in a slot
   int wave, lane, rank, ab_instr, swizzle, esize_log2;
   bool load_nt, store_nt;
   uint32_t xoff[OUTER], ooff[OUTER], oobm[OUTER], lpos[OUTER], abo[OUTER];
@@ -914,7 +916,8 @@ struct GenPolicy {
   float sa[OUTER], sb[OUTER];
 
   __device__ __forceinline__ void fill(int set, uint32_t j0) {
-    const TripRow r = trip_lane(A, wg, grid, tile0, subs, subs_mag, subs_sh, rank, j0 + static_cast<uint32_t>(lane));
+    const TripRow r =
+        trip_lane(A, wg, grid, tile0, subs, subs_mag, subs_sh, rank, tpt_log2, j0 + static_cast<uint32_t>(lane));
     // field-wise selects: a conditional store of the whole row would be
     // merged into one store through a selected address, i.e. into memory
     const bool lo = set == 0;
@@ -938,12 +941,21 @@ struct GenPolicy {
     return t;
   }
 
+  // Table entry e is the workgroup's e-th tile (tile ops) or stage; ring
+  // trip j holds entries j * 2^tpt_log2 ... (a batch boundary of the table
+  // always falls on the first entry of a trip).
   __device__ __forceinline__ void load(int j, int slot) {
-    if (j > 0 && (j & 63) == 0) fill((j >> 6) & 1, static_cast<uint32_t>(j));
+    const int e0 = j << tpt_log2;
+    if (e0 > 0 && (e0 & 63) == 0) fill((e0 >> 6) & 1, static_cast<uint32_t>(e0));
+#pragma nounroll
+    for (int u = 0; u < (1 << tpt_log2); ++u) load_entry(e0 + u, slot * slot_bytes + u * tile_lds);
+  }
+
+  __device__ __forceinline__ void load_entry(int j, uint32_t sl) {
     const T t = row(j);
     const bool beyond = (t.flags & 0x100u) != 0;
     const uint32_t last = t.flags & 0xFFu;
-    const uint32_t sbase = lds0 + slot * slot_bytes + wave * 1024u;
+    const uint32_t sbase = lds0 + sl + wave * 1024u;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const v4i rs = rsrc_v4(in[k] + t.xb, range_from(in_span, t.xb));
@@ -960,7 +972,7 @@ struct GenPolicy {
         const bool ok = !beyond && (row_bad[q] & last) == 0;
         uint64_t r = ok ? t.rb + row_ptr[1 + q] / 4u : 0u;
         if (r >= total_rows) r = 0;
-        dma_global_b32(reinterpret_cast<const void*>(row_ptr[0] + r * 4u), lds0 + slot * slot_bytes + ab_base + q * 256u);
+        dma_global_b32(reinterpret_cast<const void*>(row_ptr[0] + r * 4u), lds0 + sl + ab_base + q * 256u);
       }
     }
   }
@@ -1025,6 +1037,12 @@ struct GenPolicy {
   }
 
   __device__ __forceinline__ void consume(int i, int slot) {
+    const int e0 = i << tpt_log2;
+#pragma nounroll
+    for (int u = 0; u < (1 << tpt_log2); ++u) consume_entry(e0 + u, slot * slot_bytes + u * tile_lds);
+  }
+
+  __device__ __forceinline__ void consume_entry(int i, uint32_t sl) {
     typedef ChunkShape<OP, 16> CS;
     typedef typename OP::TI TI;
     typedef typename OP::TO TO;
@@ -1032,7 +1050,6 @@ struct GenPolicy {
     const bool beyond = (t.flags & 0x100u) != 0;
     const uint32_t last = t.flags & 0xFFu;
     const __amdgpu_buffer_rsrc_t rs = rsrc_store(out + t.ob, range_from(out_span, t.ob));
-    const uint32_t sl = slot * slot_bytes;
     if constexpr (SPLIT) {
       consume_pieces(rs, sl, beyond, last);
       return;
@@ -1107,9 +1124,10 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   const uint32_t grid = gridDim.x;
   uint32_t wg = blockIdx.x;
   if (A->xcd_remap) wg = (wg & 7u) * (grid >> 3) + (wg >> 3);
-  const uint32_t n_tiles = A->n_tiles;
-  const uint32_t tiles = wg < n_tiles ? (n_tiles - wg + grid - 1) / grid : 0;
-  const int n = static_cast<int>(tiles * A->subs);
+  const uint32_t tpt_log2 = uni(A->tpt_log2);
+  const uint32_t groups = (A->n_tiles + (1u << tpt_log2) - 1u) >> tpt_log2;
+  const uint32_t mine = wg < groups ? (groups - wg + grid - 1) / grid : 0;
+  const int n = static_cast<int>(mine * A->subs);  // ring trips
   if (n == 0) return;
   LaneMap m;
   build_map<16>(A, wave, lane, m);
@@ -1118,6 +1136,8 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   if constexpr (OP::ROW && !SROW) build_rows(A, lane, row_ptr, row_bad);
   const Loc L = load_loc(A);
   GenPolicy<OP, MODE, OUTER, SROW> p;
+  p.tpt_log2 = tpt_log2;
+  p.tile_lds = L.slot_bytes >> tpt_log2;
   p.A = A;
   p.lds = lds;
   for (int k = 0; k < 3; ++k) p.in[k] = L.in[k];
@@ -1167,8 +1187,8 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   p.fill(0, 0u);
   typedef ChunkShape<OP, 16> CS;
   constexpr int NS = GenPolicy<OP, MODE, OUTER, SROW>::NS;
-  const int d = NS * OUTER + ((OP::ROW && !SROW) ? L.ab_instr : 0);
-  run_ring(p, n, uni(A->stages), d, OUTER * CS::ST);
+  const int d = (NS * OUTER + ((OP::ROW && !SROW) ? L.ab_instr : 0)) << tpt_log2;
+  run_ring(p, n, uni(A->stages), d, (OUTER * CS::ST) << tpt_log2);
 }
 
 }  // namespace dev

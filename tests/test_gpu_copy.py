@@ -147,6 +147,8 @@ def test_box_larger_than_tensor_and_empty_tensor():
     ((3001, 16, 64), (1, 16, 64), 128),        # 3001 whole tiles: more than one per workgroup, uneven
     ((7, 1333, 256), (1, 4, 256), 64),         # 334 tiles per batch, the last one a single row
     ((4100, 2, 512), (1, 2, 512), 64),         # swizzled copy below
+    ((41, 333, 1000), (1, 32, 16), 64),        # 32-byte rows: two tiles per ring trip; 28 413 tiles (odd),
+                                               # cut rows (333) and a cut last column tile (1000 = 62 * 16 + 8)
 ])
 def test_persistent_grid_ragged_tile_counts(shape, box, threads):
     swz = acp.ACP_SWIZZLE_128B if shape[0] == 4100 else acp.ACP_SWIZZLE_NONE

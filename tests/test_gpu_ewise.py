@@ -106,14 +106,22 @@ def test_denormals_survive_fma_and_mul():
 @pytest.mark.parametrize("op,dt,shape,box,threads", [
     ("fma", "f16", (2500, 16, 64), (1, 16, 64), 64),      # 2500 tiles, uneven over the grid
     ("sqrt", "f32", (12, 1501, 64), (1, 8, 64), 64),      # 188 tiles per batch, the last one 5 rows
+    ("sqrt", "f32", (31, 333, 500), (1, 16, 16), 64),     # 64-byte rows: two tiles per ring trip
+    ("exp", "f16", (20, 333, 1000), (1, 32, 16), 64),     # widening (f16 -> f32), two tiles per trip
 ])
 def test_persistent_grid_ragged_tile_ewise(op, dt, shape, box, threads):
     say(f"persistent tile_ewise {op} {dt} {shape} box {box} threads {threads}")
     if op == "fma":
         ins = [W.normal_f16(shape, seed=s) for s in (21, 22, 23)]
+    elif op == "exp":
+        ins = [W.normal_f16(shape, seed=25)]
     else:
         ins = [np.abs(W.fma_rows_f32(shape, seed=24)[0])]
-    y = run_tile_ewise(op, ins, dt, dt, shape, box, threads)
-    ref = REF.ewise(op, ins, NP[dt])
-    assert np.array_equal(y.view(np.uint16 if dt == "f16" else np.uint32),
-                          ref.view(np.uint16 if dt == "f16" else np.uint32))
+    odt = "f32" if op == "exp" else dt
+    y = run_tile_ewise(op, ins, dt, odt, shape, box, threads)
+    ref = REF.ewise(op, ins, NP[odt])
+    if op == "exp":
+        assert ulp_diff(y.reshape(-1), ref.reshape(-1)).max() <= 1
+    else:
+        assert np.array_equal(y.view(np.uint16 if dt == "f16" else np.uint32),
+                              ref.view(np.uint16 if dt == "f16" else np.uint32))
