@@ -58,8 +58,10 @@ MAX_INPUT_RANK = 8      # rank of the tensor handed to the encoder
 MAX_ISSUES = 256        # loads per tile the shrink step may create
 MAX_IMAGE_AXES = 12     # axes of the LDS image (issue axes + box parts)
 SWIZZLE_NONE = 0
+SWIZZLE_32B = 1
+SWIZZLE_64B = 2
 SWIZZLE_128B = 3        # mode number of the worked example
-ATOM_BYTES = 128
+ATOM_BYTES = 128        # the 128-byte mode's atom (16 << mode bytes in general)
 
 ESIZE = {"u8": 1, "u16": 2, "u32": 4, "u64": 8, "f16": 2, "f32": 4}
 GFX950_VEC_BYTES = (16, 4)
@@ -193,8 +195,9 @@ def plan_box(esize: int, shape, strides, box, swizzle: int = SWIZZLE_NONE,
         raise Invalid("extents must be >= 0 (0: an empty tensor), strides and box >= 1")
     if esize not in (1, 2, 4, 8):
         raise Invalid("element size must be 1, 2, 4 or 8 bytes")
-    if swizzle not in (SWIZZLE_NONE, SWIZZLE_128B):
-        raise Invalid("swizzle must be none or 128-byte")
+    if swizzle not in (SWIZZLE_NONE, SWIZZLE_32B, SWIZZLE_64B, SWIZZLE_128B):
+        raise Invalid("swizzle must be none, 32-, 64- or 128-byte")
+    atom_bytes = _swz.span_bytes(swizzle)
 
     # L1: canonicalize.  The innermost dim must have stride 1; dims of
     # extent 1 with box 1 carry no information and are dropped.
@@ -207,17 +210,17 @@ def plan_box(esize: int, shape, strides, box, swizzle: int = SWIZZLE_NONE,
         dims.append(DescDim(extent=shape[d], stride=strides[d] * esize, box=box[d],
                             parts=[Axis(box[d], d, 1)]))
 
-    # L2: a 128-byte swizzle splits an inner box wider than one atom into
-    # atoms; the atom axis becomes the outermost descriptor dim.
-    if swizzle == SWIZZLE_128B:
+    # L2: a swizzle splits an inner box wider than one atom (16 << mode
+    # bytes) into atoms; the atom axis becomes the outermost descriptor dim.
+    if swizzle != SWIZZLE_NONE:
         inner = dims[-1]
         inner_bytes = inner.box * esize
-        if inner_bytes > ATOM_BYTES:
-            if inner_bytes % ATOM_BYTES or (inner.extent * esize) % ATOM_BYTES:
+        if inner_bytes > atom_bytes:
+            if inner_bytes % atom_bytes or (inner.extent * esize) % atom_bytes:
                 raise Declined("no swizzle-atom-aligned innermost box")
-            w = ATOM_BYTES // esize
+            w = atom_bytes // esize
             d_in = inner.parts[0].dim
-            atom = DescDim(extent=inner.extent // w, stride=ATOM_BYTES, box=inner.box // w,
+            atom = DescDim(extent=inner.extent // w, stride=atom_bytes, box=inner.box // w,
                            parts=[Axis(inner.box // w, d_in, w)], atom=True)
             dims[-1] = DescDim(extent=w, stride=esize, box=w, parts=[Axis(w, d_in, 1)])
             dims.insert(0, atom)
@@ -240,7 +243,7 @@ def plan_box(esize: int, shape, strides, box, swizzle: int = SWIZZLE_NONE,
             merged = DescDim(extent=o.extent * i.extent, stride=i.stride, box=mb,
                              parts=o.parts + i.parts)
             innermost = (k == len(dims) - 1)
-            if innermost and swizzle == SWIZZLE_128B and mb * desc_esize > ATOM_BYTES:
+            if innermost and swizzle != SWIZZLE_NONE and mb * desc_esize > atom_bytes:
                 continue
             if mb > MAX_BOX:
                 if not (innermost and copy_only and
@@ -378,4 +381,4 @@ def image_coords(p: Plan):
 
 def lds_offset(p: Plan, logical_byte: int) -> int:
     """Physical LDS byte offset of a logical image byte."""
-    return _swz.apply(logical_byte, p.swizzle == SWIZZLE_128B)
+    return _swz.swizzle(logical_byte, p.swizzle)

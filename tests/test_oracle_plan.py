@@ -74,6 +74,23 @@ def test_swizzled_2d_tile_gives_rank3():
         assert p.dims[-1].box * P.ESIZE[dt] == 128
 
 
+def test_narrow_swizzle_modes_split_into_their_atoms():
+    # 32- and 64-byte modes: the inner axis splits into 32- / 64-byte atoms,
+    # the atom axis outermost (same construction as the 128-byte example)
+    p = P.plan("f16", (8, 256), (256, 1), (8, 256), P.SWIZZLE_32B)
+    assert p.rank == 3
+    assert [d.extent for d in reversed(p.dims)] == [16, 8, 16]     # 16 f16 = 32 B, 8 rows, 16 atoms of 512 B
+    assert [d.stride for d in reversed(p.dims)] == [2, 512, 32]
+    p = P.plan("f32", (4, 64), (64, 1), (4, 64), P.SWIZZLE_64B)
+    assert [d.box for d in reversed(p.dims)] == [16, 4, 4]
+    # a 48-byte inner box fits the 64-byte atom but is no whole number of 32-byte atoms
+    P.plan("f16", (8, 24), (24, 1), (8, 24), P.SWIZZLE_64B)
+    with pytest.raises(P.Declined, match="swizzle-atom"):
+        P.plan("f16", (8, 24), (24, 1), (8, 24), P.SWIZZLE_32B)
+    with pytest.raises(P.Invalid):
+        P.plan("f16", (8, 24), (24, 1), (8, 24), 4)
+
+
 def test_declines():
     with pytest.raises(P.Declined, match="innermost stride"):
         P.plan("f16", (8, 256), (1, 8), (8, 256))
@@ -172,7 +189,7 @@ def test_bruteforce_small_plans_cover_box_exactly_once():
             strides.append(st)
             st *= ext + (pad if st == 1 else 0)
         strides = list(reversed(strides))
-        swz = rng.choice([P.SWIZZLE_NONE, P.SWIZZLE_128B])
+        swz = rng.choice([P.SWIZZLE_NONE, P.SWIZZLE_32B, P.SWIZZLE_64B, P.SWIZZLE_128B])
         copy_only = rng.random() < 0.5
         try:
             p = P.plan(dt, shape, strides, box, swz, copy_only=copy_only)
@@ -185,7 +202,7 @@ def test_bruteforce_small_plans_cover_box_exactly_once():
         assert p.dims[-1].stride == p.desc_esize
         if swz:
             ib = p.dims[-1].box * p.desc_esize
-            assert ib <= 128 and ib % 16 == 0
+            assert ib <= 16 << swz and ib % 16 == 0
         # the image axes enumerate every box element exactly once
         coords = P.image_coords(p)
         assert len(coords) == len(set(coords))

@@ -3,7 +3,7 @@ plus the page's stage formulas and hand-derived wait counts)."""
 import pytest
 
 from oracle import ring as R
-from oracle.swizzle import swizzle128
+from oracle.swizzle import span_bytes, swizzle, swizzle128
 
 
 def test_swizzle_involution_and_bijection():
@@ -39,6 +39,40 @@ def test_swizzle_hand_values():
     assert swizzle128(3 * 128 + 5 * 16) == 3 * 128 + 6 * 16
     assert swizzle128(7 * 128 + 7 * 16) == 7 * 128 + 0 * 16
     assert swizzle128(9 * 128 + 2 * 16 + 3) == 9 * 128 + 3 * 16 + 3
+
+
+@pytest.mark.parametrize("mode", [1, 2, 3])
+def test_swizzle_modes_invariants(mode):
+    span = span_bytes(mode)
+    assert span == {1: 32, 2: 64, 3: 128}[mode]
+    block = 128 * (span // 16)                      # one full period of the pattern
+    for base in range(0, 4 * block, block):
+        img = [swizzle(base + o, mode) for o in range(block)]
+        assert sorted(img) == list(range(base, base + block))          # bijective per period
+    for o in range(0, 4096):
+        p = swizzle(o, mode)
+        assert swizzle(p, mode) == o                                   # involution
+        assert p // span == o // span                                  # stays in its span
+        assert p % 16 == o % 16                                        # whole 16-byte chunks
+    # over 2**m consecutive 128-byte rows, each logical chunk of a span takes
+    # every physical chunk position of that span once (Latin square)
+    n = span // 16
+    for c in range(n):
+        assert {(swizzle(r * 128 + c * 16, mode) % span) // 16 for r in range(n)} == set(range(n))
+
+
+def test_swizzle_modes_hand_values():
+    # mode 1 (32 B): bit 7 flips bit 4 -- row 1 swaps the two chunks of each span
+    assert swizzle(128 + 0, 1) == 128 + 16
+    assert swizzle(128 + 48 + 5, 1) == 128 + 32 + 5
+    assert swizzle(256 + 16, 1) == 256 + 16            # row 2: bit 7 is 0
+    # mode 2 (64 B): bits 7..8 flip bits 4..5 -- row 3, chunk 1 of a span -> chunk 2
+    assert swizzle(3 * 128 + 16, 2) == 3 * 128 + 32
+    assert swizzle(3 * 128 + 64 + 48, 2) == 3 * 128 + 64 + 0
+    assert swizzle(5 * 128 + 16, 2) == 5 * 128 + 0     # row 5 mod 4 = 1
+    # mode 0 is the identity; mode 3 is the 128-byte pattern
+    assert all(swizzle(o, 0) == o for o in range(2048))
+    assert all(swizzle(o, 3) == swizzle128(o) for o in range(4096))
 
 
 @pytest.mark.parametrize("stages", [2, 3, 4])
