@@ -40,7 +40,7 @@ STATUS_NAMES = {0: "OK", 1: "INVALID", 2: "DECLINED", 3: "UNSUPPORTED", 4: "LDS"
 ACP_U8, ACP_U16, ACP_U32, ACP_U64, ACP_F16, ACP_F32 = range(6)
 DTYPES = {"u8": ACP_U8, "u16": ACP_U16, "u32": ACP_U32, "u64": ACP_U64, "f16": ACP_F16, "f32": ACP_F32}
 # acp_swizzle / acp_oob
-ACP_SWIZZLE_NONE, ACP_SWIZZLE_128B = 0, 3
+ACP_SWIZZLE_NONE, ACP_SWIZZLE_32B, ACP_SWIZZLE_64B, ACP_SWIZZLE_128B = 0, 1, 2, 3
 ACP_OOB_ZERO = 0
 # acp_op
 ACP_OP_ZERO, ACP_OP_SQRT, ACP_OP_EXP, ACP_OP_ADD, ACP_OP_MUL, ACP_OP_FMA, ACP_OP_COPY = range(7)

@@ -283,7 +283,7 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   A.esize_log2 = log2i(ei);
   A.outer = p.outer;
   A.waves = q.threads / 64;
-  A.swizzle = x.swizzle == 3 ? 1 : 0;
+  A.swizzle = (1 << x.swizzle) - 1;  // the mask of row bits XORed into the chunk index
   A.n_in = q.n_in;
 
   // every 1 KiB wave block inside one row: the innermost image run holds a
@@ -448,7 +448,9 @@ acp_status acp_encode_tiled(acp_tile_desc* out, acp_dtype dtype, int rank, const
   const int es = acp::dtype_size(dtype);
   if (es < 0) return ret(ACP_ERR_INVALID, "unknown dtype");
   if (rank < 1 || rank > ACP_MAX_INPUT_RANK) return ret(ACP_ERR_INVALID, "rank must be 1..8");
-  if (swizzle != ACP_SWIZZLE_NONE && swizzle != ACP_SWIZZLE_128B) return ret(ACP_ERR_INVALID, "unknown swizzle");
+  if (swizzle != ACP_SWIZZLE_NONE && swizzle != ACP_SWIZZLE_32B && swizzle != ACP_SWIZZLE_64B &&
+      swizzle != ACP_SWIZZLE_128B)
+    return ret(ACP_ERR_INVALID, "unknown swizzle");
   if (oob != ACP_OOB_ZERO) return ret(ACP_ERR_INVALID, "unknown out-of-bounds fill");
   acp::DescData d;
   std::memset(&d, 0, sizeof(d));

@@ -46,7 +46,8 @@ struct EngineArgs {
   uint32_t n_tiles;
   uint32_t tile0;                    // first tile (debug image)
   int32_t esize_log2;                // staged element size
-  int32_t outer, waves, swizzle, stages, n_in;
+  int32_t outer, waves, stages, n_in;
+  int32_t swizzle;           // 0 (none), 1, 3 or 7: row bits XORed into the 16-byte chunk index
   // LDS slot layout (bytes)
   uint32_t in_image_bytes;   // stride between operand images in a slot
   uint32_t out_image_off;    // output image (staged output only), after the ring slots

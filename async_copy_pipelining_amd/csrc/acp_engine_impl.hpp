@@ -52,7 +52,10 @@ __device__ __forceinline__ CArgs* kargs() {
   return (CArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
 }
 
-__device__ __forceinline__ uint32_t swz128(uint32_t o) { return o ^ (((o >> 7) & 7u) << 4); }
+// XOR swizzle of a stage-relative LDS byte offset: the 16-byte chunk index
+// within its span takes the 128-byte row index modulo the span's chunk
+// count (mask 1, 3, 7 for the 32-, 64-, 128-byte modes; 0 is no swizzle).
+__device__ __forceinline__ uint32_t swz(uint32_t o, uint32_t mask) { return o ^ (((o >> 7) & mask) << 4); }
 
 __device__ __forceinline__ uint32_t mdiv(uint32_t n, uint32_t mag, uint32_t sh) {
   return static_cast<uint32_t>((static_cast<uint64_t>(n) * mag) >> (31 + sh));
@@ -274,9 +277,9 @@ struct ByteMap {
   uint32_t lb, xo, oo, row, ob;
 };
 
-__device__ __forceinline__ ByteMap map_byte(CArgs* A, uint32_t pb, int n_axes, int swz, int es_log2) {
+__device__ __forceinline__ ByteMap map_byte(CArgs* A, uint32_t pb, int n_axes, int swz_mask, int es_log2) {
   ByteMap r;
-  r.lb = swz ? swz128(pb) : pb;
+  r.lb = swz(pb, static_cast<uint32_t>(swz_mask));
   const uint32_t sub_byte = r.lb & ((1u << es_log2) - 1u);  // copies of elements wider than the chunk
   uint32_t e = r.lb >> es_log2;
   r.xo = sub_byte;
@@ -306,12 +309,12 @@ __device__ __forceinline__ ByteMap map_byte(CArgs* A, uint32_t pb, int n_axes, i
 template <int VB>
 __device__ __forceinline__ void build_map(CArgs* A, int wave, int lane, LaneMap& m) {
   const int outer = A->outer, waves = A->waves, n_axes = A->n_axes;
-  const int swz = A->swizzle, es_log2 = A->esize_log2;
+  const int swz_mask = A->swizzle, es_log2 = A->esize_log2;
 #pragma unroll
   for (int g = 0; g < kMaxOuter; ++g) m.xoff[g] = m.ooff[g] = m.oobm[g] = m.lpos[g] = m.abo[g] = 0;
 #pragma nounroll
   for (int f = 0; f < outer; ++f) {
-    const ByteMap b = map_byte(A, ((f * waves + wave) * 64u + lane) * VB, n_axes, swz, es_log2);
+    const ByteMap b = map_byte(A, ((f * waves + wave) * 64u + lane) * VB, n_axes, swz_mask, es_log2);
     const uint32_t abo = (b.row >> 5) * 256u + (b.row & 31u) * 4u;
 #pragma unroll
     for (int g = 0; g < kMaxOuter; ++g)
@@ -335,13 +338,13 @@ template <int N>
 __device__ __forceinline__ void build_pieces(CArgs* A, int wave, int lane, int outer, uint32_t (&oo)[N],
                                              uint32_t (&ob)[N], uint32_t (&lp)[N]) {
   const int waves = A->waves, n_axes = A->n_axes;
-  const int swz = A->swizzle, es_log2 = A->esize_log2;
+  const int swz_mask = A->swizzle, es_log2 = A->esize_log2;
 #pragma unroll
   for (int g = 0; g < N; ++g) oo[g] = ob[g] = lp[g] = 0;
 #pragma nounroll
   for (int q = 0; q < 2 * outer; ++q) {
     const uint32_t f = q >> 1, h = q & 1;
-    const ByteMap b = map_byte(A, (f * waves + wave) * 1024u + h * 512u + lane * 8u, n_axes, swz, es_log2);
+    const ByteMap b = map_byte(A, (f * waves + wave) * 1024u + h * 512u + lane * 8u, n_axes, swz_mask, es_log2);
 #pragma unroll
     for (int g = 0; g < N; ++g)
       if (g == q) {
@@ -597,13 +600,13 @@ __device__ __forceinline__ void consume_trip(const Loc& L, int esize_log2, int s
 #pragma unroll
       for (int piece = 0; piece < P; ++piece) {
         const uint32_t lp = lo + piece * 16;
-        __builtin_memcpy(lds + L.out_image_off + (swizzle ? swz128(lp) : lp), words + piece * 4, PB);
+        __builtin_memcpy(lds + L.out_image_off + swz(lp, swizzle), words + piece * 4, PB);
       }
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int piece = 0; piece < P; ++piece) {
         const uint32_t lp = lo + piece * 16;
-        __builtin_memcpy(words + piece * 4, lds + L.out_image_off + (swizzle ? swz128(lp) : lp), PB);
+        __builtin_memcpy(words + piece * 4, lds + L.out_image_off + swz(lp, swizzle), PB);
       }
     }
     const bool ok = !t.beyond && (m.oobm[f] & t.last) == 0;
@@ -1026,9 +1029,9 @@ struct GenPolicy {
         __builtin_memcpy(words, res, 16);
         if constexpr (STAGE_OUT) {
           const uint32_t lo = (plpos[q] >> esize_log2) * sizeof(TO);
-          __builtin_memcpy(lds + out_image_off + (swizzle ? swz128(lo) : lo), words, 16);
+          __builtin_memcpy(lds + out_image_off + swz(lo, swizzle), words, 16);
           asm volatile("" ::: "memory");
-          __builtin_memcpy(words, lds + out_image_off + (swizzle ? swz128(lo) : lo), 16);
+          __builtin_memcpy(words, lds + out_image_off + swz(lo, swizzle), 16);
         }
         const bool ok = !beyond && (poobm[q] & last) == 0;
         store_chunk<16>(rs, ok ? pooff[q] : kOobOffset, words, store_nt);
@@ -1099,13 +1102,13 @@ struct GenPolicy {
 #pragma unroll
           for (int piece = 0; piece < P; ++piece) {
             const uint32_t lp = lo + piece * 16;
-            __builtin_memcpy(lds + out_image_off + (swizzle ? swz128(lp) : lp), words + piece * 4, PB);
+            __builtin_memcpy(lds + out_image_off + swz(lp, swizzle), words + piece * 4, PB);
           }
           asm volatile("" ::: "memory");
 #pragma unroll
           for (int piece = 0; piece < P; ++piece) {
             const uint32_t lp = lo + piece * 16;
-            __builtin_memcpy(words + piece * 4, lds + out_image_off + (swizzle ? swz128(lp) : lp), PB);
+            __builtin_memcpy(words + piece * 4, lds + out_image_off + swz(lp, swizzle), PB);
           }
         }
         const bool ok = !beyond && (oobm[f] & last) == 0;

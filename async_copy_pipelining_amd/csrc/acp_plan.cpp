@@ -7,15 +7,15 @@
 //
 //  L1  The innermost stride must be 1.  Dims of extent 1 and box 1 carry no
 //      information and are dropped.
-//  L2  Under the 128-byte swizzle an innermost box wider than 128 bytes is
-//      split into 128-byte atoms; the atom axis becomes the outermost
-//      descriptor dim (the only order that gives the worked 8x256 float16
-//      example's byte strides 512, 128).  Otherwise the inner box must be a
-//      whole number of 16-byte chunks.
+//  L2  Under a swizzle an innermost box wider than the mode's atom (16 << mode
+//      bytes: 32, 64 or 128) is split into atoms; the atom axis becomes the
+//      outermost descriptor dim (the only order that gives the worked 8x256
+//      float16 example's byte strides 512, 128).  Otherwise the inner box must
+//      be a whole number of 16-byte chunks.
 //  L3  Adjacent dims merge when the inner one is fully boxed and contiguous
 //      with the outer one and the merged box stays <= 256 (copies may merge
 //      the innermost pair beyond 256 when promotion then fixes it; under the
-//      swizzle the innermost box stays <= 128 bytes; atom axes never merge).
+//      swizzle the innermost box stays within one atom; atom axes never merge).
 //      A copy's innermost box over 256 promotes the element 1 -> 2 -> 4 -> 8
 //      bytes.  Any box still over 256 is cut into equal segments (largest
 //      divisor <= 256; for the innermost dim preferably a 16-byte multiple,
@@ -111,8 +111,8 @@ PlanStatus plan_box_with(const DescData& dd, const int32_t* boxp, bool copy_only
   if (r < 1 || r > kMaxInputRank) return fail(reason, PlanStatus::Invalid, "rank must be 1..8");
   if (es != 1 && es != 2 && es != 4 && es != 8)
     return fail(reason, PlanStatus::Invalid, "element size must be 1, 2, 4 or 8 bytes");
-  if (dd.swizzle != 0 && dd.swizzle != 3)
-    return fail(reason, PlanStatus::Invalid, "swizzle must be none or 128-byte");
+  if (dd.swizzle > 3) return fail(reason, PlanStatus::Invalid, "swizzle must be none, 32-, 64- or 128-byte");
+  const int64_t atom_bytes = dd.swizzle ? (int64_t(16) << dd.swizzle) : 0;
   for (int d = 0; d < r; ++d)
     if (dd.shape[d] < 0 || dd.strides[d] < 1 || boxp[d] < 1)
       return fail(reason, PlanStatus::Invalid, "extents must be >= 0 (0: an empty tensor), strides and box >= 1");
@@ -141,18 +141,18 @@ PlanStatus plan_box_with(const DescData& dd, const int32_t* boxp, bool copy_only
     dims.push_back(dim);
   }
 
-  // L2: swizzle atoms
-  if (dd.swizzle == 3) {
+  // L2: swizzle atoms (16 << mode bytes)
+  if (dd.swizzle != 0) {
     DescDim inner = dims.back();
     const int64_t ib = inner.box * es;
-    if (ib > kAtomBytes) {
-      if (ib % kAtomBytes != 0 || (inner.extent * es) % kAtomBytes != 0)
+    if (ib > atom_bytes) {
+      if (ib % atom_bytes != 0 || (inner.extent * es) % atom_bytes != 0)
         return fail(reason, PlanStatus::Declined, "no swizzle-atom-aligned innermost box");
-      const int64_t w = kAtomBytes / es;
+      const int64_t w = atom_bytes / es;
       const int dim = inner.parts[0].dim;
       DescDim atom;
       atom.extent = inner.extent / w;
-      atom.stride = kAtomBytes;
+      atom.stride = atom_bytes;
       atom.box = inner.box / w;
       atom.parts.push_back(Axis{inner.box / w, dim, w});
       atom.atom = true;
@@ -184,7 +184,7 @@ PlanStatus plan_box_with(const DescData& dd, const int32_t* boxp, bool copy_only
       m.parts = o.parts;
       m.parts.insert(m.parts.end(), i.parts.begin(), i.parts.end());
       const bool innermost = (k == dims.size() - 1);
-      if (innermost && dd.swizzle == 3 && m.box * p.desc_esize > kAtomBytes) continue;
+      if (innermost && dd.swizzle != 0 && m.box * p.desc_esize > atom_bytes) continue;
       if (m.box > kMaxBox) {
         std::vector<DescDim> rest(dims.begin(), dims.begin() + (k - 1));
         if (!(innermost && copy_only && promotion_width(m, rest, p.desc_esize, dd.gbase))) continue;

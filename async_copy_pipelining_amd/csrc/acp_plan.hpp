@@ -20,7 +20,6 @@ constexpr int kMaxRank = 5;
 constexpr int64_t kMaxBox = 256;
 constexpr int64_t kMaxIssues = 256;
 constexpr int kMaxImageAxes = 12;
-constexpr int kAtomBytes = 128;
 constexpr uint32_t kDescMagic = 0x44504341u;  // "ACPD"
 
 enum class PlanStatus { Ok, Invalid, Declined };

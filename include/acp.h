@@ -78,8 +78,12 @@ typedef enum { ACP_U8 = 0, ACP_U16 = 1, ACP_U32 = 2, ACP_U64 = 3, ACP_F16 = 4, A
 
 /* LDS layout of a staged tile.  ACP_SWIZZLE_128B carries the mode number of
  * [tma]'s worked example (3): 16-byte chunk index XOR (128-byte row index
- * mod 8) on stage-relative LDS byte offsets. */
-typedef enum { ACP_SWIZZLE_NONE = 0, ACP_SWIZZLE_128B = 3 } acp_swizzle;
+ * mod 8) on stage-relative LDS byte offsets.  Modes 1 and 2 follow the mode
+ * numbering ([tma] "How inputs change the algorithm": the mode sets the
+ * innermost-box constraint): mode m permutes the 2^m 16-byte chunks of each
+ * 16 * 2^m-byte span by XOR with the 128-byte row index mod 2^m, and an
+ * innermost box wider than 16 * 2^m bytes is split into atoms of that width. */
+typedef enum { ACP_SWIZZLE_NONE = 0, ACP_SWIZZLE_32B = 1, ACP_SWIZZLE_64B = 2, ACP_SWIZZLE_128B = 3 } acp_swizzle;
 
 /* Out-of-bounds fill: zero, the last encode argument of [tma]'s example. */
 typedef enum { ACP_OOB_ZERO = 0 } acp_oob;

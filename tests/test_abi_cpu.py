@@ -92,7 +92,7 @@ def test_planner_matches_oracle_randomized():
         strides = list(reversed(strides))
         if rng.random() < 0.03:
             strides[-1] = 2
-        swz = rng.choice([0, 3])
+        swz = rng.choice([0, 1, 2, 3])
         threads = rng.choice([0, 64, 128, 256, 1024])
         copy_only = rng.random() < 0.5
         base = FAKE_BASE + rng.choice([0, 0, 0, 4, 8])

@@ -75,23 +75,47 @@ def test_c3_full_size_copy():
     assert torch.equal(xd, yd)
 
 
-def test_swizzled_multi_atom_tiles_and_strided_output():
-    shape, box = (5, 40, 512), (1, 16, 256)     # swizzle splits 512-byte rows into 4 atoms; rows ragged
-    say(f"swizzled copy {shape} box {box} into a padded output")
+@pytest.mark.parametrize("mode", [1, 2, 3])
+def test_swizzled_multi_atom_tiles_and_strided_output(mode):
+    shape, box = (5, 40, 512), (1, 16, 256)     # swizzle splits 512-byte rows into atoms; rows ragged
+    say(f"swizzle mode {mode} copy {shape} box {box} into a padded output")
     x = W.normal_f16(shape, seed=7)
     xd = dev(x)
     opitch = 520
     ost = (40 * opitch, opitch, 1)
     yd = empty_bytes(5 * 40 * opitch * 2, 0x00)
-    src = encode("f16", xd, shape, packed_strides(shape), box, acp.ACP_SWIZZLE_128B)
+    src = encode("f16", xd, shape, packed_strides(shape), box, mode)
     dst = encode("f16", yd, shape, ost, box)
     acp.acp_tile_copy(src, dst, 256, stream())
     y = host(yd, np.uint16).reshape(5, 40, opitch)
     assert np.array_equal(y[:, :, :512], x.view(np.uint16))
     assert not np.any(y[:, :, 512:])                        # the pitch padding was never written
-    p = P.plan("f16", shape, packed_strides(shape), box, P.SWIZZLE_128B, threads=256)
+    p = P.plan("f16", shape, packed_strides(shape), box, mode, threads=256)
     t = int(np.ravel_multi_index((4, 2, 1), P.tile_grid(shape, box)))
     assert _lds_image(src, t, 256, p.tile_bytes) == T.lds_image(x.reshape(-1), p, t)
+
+
+@pytest.mark.parametrize("mode,dt,shape,box,threads", [
+    (1, "f16", (8, 256), (8, 256), 64),      # 32-byte atoms, 16 of them
+    (2, "f16", (8, 256), (8, 256), 64),      # 64-byte atoms
+    (1, "f32", (24, 40), (8, 8), 64),        # inner box of one 32-byte atom, no split
+    (2, "u8", (16, 192), (16, 64), 64),      # a 64-byte u8 row
+])
+def test_narrow_swizzle_images_and_copies(mode, dt, shape, box, threads):
+    say(f"swizzle mode {mode} {dt} {shape} box {box} threads {threads}")
+    rng = np.random.default_rng(12)
+    es = P.ESIZE[dt]
+    x = rng.integers(0, 256, size=int(np.prod(shape)) * es, dtype=np.uint8)
+    xd, yd = dev(x), empty_bytes(x.nbytes)
+    st = packed_strides(shape)
+    src = encode(dt, xd, shape, st, box, mode)
+    dst = encode(dt, yd, shape, st, box, mode)
+    acp.acp_tile_copy(src, dst, threads, stream())
+    assert np.array_equal(host(yd, np.uint8), x)
+    p = P.plan(dt, shape, st, box, mode, threads=threads)
+    elems = x.view({1: np.uint8, 2: np.uint16, 4: np.uint32}[es])
+    for t in range(min(3, int(np.prod(P.tile_grid(shape, box))))):
+        assert _lds_image(src, t, threads, p.tile_bytes) == T.lds_image(elems, p, t)
 
 
 @pytest.mark.parametrize("misalign", [4, 8])

@@ -68,6 +68,10 @@ CASES = [
     ("fma", 3, "f32", "f32", (3, 70, 128), (1, 16, 128), 64, 0),
     ("exp", 1, "f16", "f32", (2, 50, 256), (1, 16, 256), 64, 3),
     ("sqrt", 1, "f16", "f32", (2, 50, 256), (1, 8, 256), 64, 3),
+    # 32- and 64-byte swizzles
+    ("exp", 1, "f16", "f32", (2, 50, 256), (1, 8, 256), 128, 1),
+    ("fma", 3, "f32", "f32", (3, 70, 128), (1, 16, 128), 256, 2),
+    ("mul", 2, "f16", "f16", (2, 50, 256), (1, 8, 256), 128, 2),
 ]
 
 

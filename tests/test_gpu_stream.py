@@ -161,19 +161,21 @@ def test_c5_full_size_matches_exp_table():
     assert not torch.isnan(yd.view(torch.float32)).any()
 
 
-@pytest.mark.parametrize("threads,stage_box", [(256, (1, 2, 64, 128)), (256, (1, 1, 64, 128)), (64, (1, 1, 8, 128))])
-def test_widening_stream_pieces_ragged(threads, stage_box):
+@pytest.mark.parametrize("threads,stage_box,mode", [(256, (1, 2, 64, 128), 3), (256, (1, 1, 64, 128), 3),
+                                                    (64, (1, 1, 8, 128), 3), (256, (1, 1, 64, 128), 1),
+                                                    (64, (1, 1, 8, 128), 2)])
+def test_widening_stream_pieces_ragged(threads, stage_box, mode):
     # float16 -> float32 sqrt: 8-byte input pieces, 16-byte stores; 70 rows
     # = 64 + 6 cut the last stage; padded input pitch 136
     shape, pitch = (3, 2, 70, 128), 136
-    say(f"widening stream sqrt {shape} stage {stage_box} threads {threads}")
+    say(f"widening stream sqrt {shape} stage {stage_box} threads {threads} swizzle mode {mode}")
     storage, strides = W.padded_uniform_f16(shape, pitch=pitch, seed=8)
     storage = np.abs(storage)
     xd = dev(storage)
     n = int(np.prod(shape))
     yd = empty_bytes(n * 4)
     box = (1, 2, 64, 128)
-    xdesc = encode("f16", xd, shape, strides, box, acp.ACP_SWIZZLE_128B)
+    xdesc = encode("f16", xd, shape, strides, box, mode)
     ydesc = encode("f32", yd, shape, packed_strides(shape), box)
     acp.acp_stream_ewise("sqrt", ydesc, xdesc, None, None, stage_box, 3, threads, 0, stream())
     y = host(yd, np.float32, shape)
