@@ -85,6 +85,7 @@ _SIGS = {
     "acp_tile_copy": ([_DESC_P, _DESC_P, _I, _P], _I),
     "acp_tile_ewise": ([_I, _DESC_P, ctypes.POINTER(_DESC_P), _I, _I, _P], _I),
     "acp_stream_ewise": ([_I, _DESC_P, _DESC_P, _P, _P, ctypes.POINTER(ctypes.c_int32), _I, _I, _I, _P], _I),
+    "acp_stream_binary": ([_I, _DESC_P, _DESC_P, _DESC_P, ctypes.POINTER(ctypes.c_int32), _I, _I, _I, _I, _P], _I),
     "acp_debug_lds_image": ([_DESC_P, ctypes.c_int64, _I, _P, _P], _I),
     "acp_debug_ring_trace": ([_I, _I, _I, _I, _P, _P], _I),
     "acp_debug_stream_copy": ([_P, _P, ctypes.c_int64, _I, _P], _I),
@@ -165,6 +166,18 @@ def acp_stream_ewise(op, out: acp_tile_desc, x: acp_tile_desc, row_a, row_b, sta
     sb = (ctypes.c_int32 * len(stage_box))(*stage_box)
     _check(_lib.acp_stream_ewise(opc, ctypes.byref(out), ctypes.byref(x), _ptr(row_a), _ptr(row_b), sb,
                                  int(stages), int(threads), int(workgroups), _stream(stream)))
+
+
+STAGING = {"ring": 0, "set": 1}
+
+
+def acp_stream_binary(op, out: acp_tile_desc, x: acp_tile_desc, z: acp_tile_desc, stage_box, stages: int,
+                      threads: int, workgroups: int = 0, z_staging="ring", stream=None) -> None:
+    opc = OPS[op] if isinstance(op, str) else int(op)
+    stg = STAGING[z_staging] if isinstance(z_staging, str) else int(z_staging)
+    sb = (ctypes.c_int32 * len(stage_box))(*stage_box)
+    _check(_lib.acp_stream_binary(opc, ctypes.byref(out), ctypes.byref(x), ctypes.byref(z), sb, int(stages),
+                                  int(threads), int(workgroups), stg, _stream(stream)))
 
 
 def acp_debug_lds_image(src: acp_tile_desc, tile_index: int, threads: int, out_bytes, stream=None) -> None:

@@ -107,6 +107,7 @@ struct EngineRequest {
   bool row_ops;
   bool copy_only;
   int tiles_per_trip = 1;      // tile ops on a persistent grid: 1, 2 or 4
+  int binary = 0;              // stream of two tensors: 1 both on the ring, 2 the second one "Set"
 };
 
 acp_status prepare(const EngineRequest& q, Launch* L) {
@@ -311,7 +312,12 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
     gk.outer = p.outer;
     static const bool srow_ok = env_flag("ACP_SCALAR_ROWS", true);
     gk.srow = (q.mode == 2 && A.row_uniform && srow_ok) ? 1 : 0;
+    gk.variant = q.binary;
     if (acp::engine_kernel(gk)) L->key = gk;
+  }
+  if (q.binary && L->key.variant != q.binary) {
+    return ret(ACP_ERR_UNSUPPORTED,
+               "two-tensor streams need 16-byte rounds and 1, 2, 4 or 8 rounds per thread");
   }
   // tile ops in the general kernel on a persistent grid: tiles per ring trip
   int tpt_log2 = 0;
@@ -633,6 +639,45 @@ acp_status acp_stream_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_
   q.row_b = row_b;
   q.row_ops = row_ops;
   q.copy_only = false;
+  Launch L;
+  const acp_status st = prepare(q, &L);
+  if (st != ACP_OK) return st;
+  return launch(L, hip_stream);
+}
+
+acp_status acp_stream_binary(acp_op op, const acp_tile_desc* out, const acp_tile_desc* x, const acp_tile_desc* z,
+                             const int32_t* stage_box, int stages, int threads, int workgroups, acp_staging z_staging,
+                             void* hip_stream) {
+  acp::DescData xd, zd, od;
+  if (!load_desc(x, &xd) || !load_desc(z, &zd) || !load_desc(out, &od))
+    return ret(ACP_ERR_INVALID, "not an encoded descriptor");
+  if (op != ACP_OP_ADD && op != ACP_OP_MUL) return ret(ACP_ERR_INVALID, "two-tensor streams are add or mul");
+  if (z_staging != ACP_STAGE_RING && z_staging != ACP_STAGE_SET) return ret(ACP_ERR_INVALID, "unknown staging");
+  if (!stage_box) return ret(ACP_ERR_INVALID, "null stage box");
+  if (stages < 2 || stages > 4) return ret(ACP_ERR_INVALID, "stages must be 2, 3 or 4");
+  if (workgroups < 0) return ret(ACP_ERR_INVALID, "workgroups must be >= 0");
+  if (!same_geometry(zd, xd, true) || zd.dtype != xd.dtype || zd.swizzle != xd.swizzle)
+    return ret(ACP_ERR_INVALID, "x and z must share one layout (dtype, shape, strides, box, swizzle)");
+  if (!same_geometry(xd, od, false) || od.dtype != xd.dtype)
+    return ret(ACP_ERR_INVALID, "output dtype, shape or box differs from x");
+  if (!is_float(xd.dtype)) return ret(ACP_ERR_UNSUPPORTED, "two-tensor streams take float16 or float32");
+  if (xd.gbase == od.gbase || zd.gbase == od.gbase) return ret(ACP_ERR_INVALID, "in-place streaming is not supported");
+  for (int d = 0; d < xd.rank; ++d)
+    if (stage_box[d] < 1) return ret(ACP_ERR_INVALID, "stage box must be >= 1");
+  EngineRequest q{};
+  q.op = op;
+  q.mode = 2;
+  q.x = &xd;
+  q.out = &od;
+  q.in_ptrs[0] = reinterpret_cast<const void*>(xd.gbase);
+  q.in_ptrs[1] = reinterpret_cast<const void*>(zd.gbase);
+  q.n_in = 2;
+  q.stage_box = stage_box;
+  q.stages = stages;
+  q.threads = threads;
+  q.workgroups = workgroups;
+  q.copy_only = false;
+  q.binary = z_staging == ACP_STAGE_SET ? 2 : 1;
   Launch L;
   const acp_status st = prepare(q, &L);
   if (st != ACP_OK) return st;

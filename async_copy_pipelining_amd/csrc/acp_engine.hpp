@@ -89,6 +89,8 @@ struct KernelKey {
                  // 4 / 5 / 6: copy / tile ewise / stream in the general lean kernel
   int outer;     // modes 3..6: rounds per thread (1, 2, 4 or 8); 0 otherwise
   int srow;      // modes 3 and 6, row ops: per-row scalars through the scalar cache
+  int variant = 0;  // mode 6, add / mul of two streamed tensors: 1 both on the direct-to-LDS
+                    // ring, 2 the second one loaded synchronously ("Set") into its slot
 };
 
 // Kernel for `key`, or nullptr when that combination is not built.

@@ -887,10 +887,15 @@ __device__ __forceinline__ uint32_t rdl(uint32_t v, uint32_t lane) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), static_cast<int>(lane)));
 }
 
-template <class OP, int MODE, int OUTER, bool SROW>
+template <class OP, int MODE, int OUTER, bool SROW, int ZSET = 0>
 struct GenPolicy {
   static constexpr bool STAGE_OUT = (MODE == 1);
-  static constexpr int NS = (MODE == 1) ? OP::NIN : 1;   // staged operands
+  // staged operands: every input of a tile op or of a two-tensor stream op;
+  // streams with per-row scalars stage x only
+  static constexpr int NS = (MODE == 0 || OP::ROW) ? 1 : OP::NIN;
+  // ZSET: the last staged operand is loaded synchronously (registers, wait,
+  // LDS store) into its image instead of by a direct-to-LDS load
+  static constexpr int NDMA = ZSET ? NS - 1 : NS;
   // widening ops (16 input bytes -> 32 output bytes) consume 8-byte pieces
   // (tile ops up to 4 rounds: beyond, the piece maps no longer fit in registers)
   static constexpr bool SPLIT = (MODE == 2 || (MODE == 1 && OUTER <= 4)) && ChunkShape<OP, 16>::OB == 32;
@@ -960,13 +965,29 @@ struct GenPolicy {
     const uint32_t last = t.flags & 0xFFu;
     const uint32_t sbase = lds0 + sl + wave * 1024u;
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
+    for (int k = 0; k < NDMA; ++k) {
       const v4i rs = rsrc_v4(in[k] + t.xb, range_from(in_span, t.xb));
 #pragma unroll
       for (int f = 0; f < OUTER; ++f) {
         const bool ok = !beyond && (oobm[f] & last) == 0;
         dma_b128(rs, ok ? xoff[f] : kOobOffset, sbase + k * in_image_bytes + f * waves_kb, load_nt);
       }
+    }
+    if constexpr (ZSET) {
+      // synchronous staging: the data must reach registers before it can be
+      // stored to LDS, so the wave waits for all its outstanding loads here
+      const __amdgpu_buffer_rsrc_t rz = rsrc_store(const_cast<char*>(in[NDMA]) + t.xb, range_from(in_span, t.xb));
+      u32x4 zv[OUTER];
+#pragma unroll
+      for (int f = 0; f < OUTER; ++f) {
+        const bool ok = !beyond && (oobm[f] & last) == 0;
+        zv[f] = __builtin_amdgcn_raw_buffer_load_b128(rz, ok ? xoff[f] : kOobOffset, 0, 0);
+      }
+      wait_vmcnt(0);
+#pragma unroll
+      for (int f = 0; f < OUTER; ++f)
+        *reinterpret_cast<u32x4*>(__builtin_assume_aligned(
+            lds + sl + NDMA * in_image_bytes + f * waves_kb + wave * 1024u + lane * 16u, 16)) = zv[f];
     }
     if constexpr (OP::ROW && !SROW) {
 #pragma unroll
@@ -1118,7 +1139,7 @@ struct GenPolicy {
   }
 };
 
-template <class OP, int MODE, int OUTER, bool SROW>
+template <class OP, int MODE, int OUTER, bool SROW, int ZSET = 0>
 __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
   CArgs* A = kargs();
@@ -1138,7 +1159,7 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   uint32_t row_bad[2] = {~0u, ~0u};
   if constexpr (OP::ROW && !SROW) build_rows(A, lane, row_ptr, row_bad);
   const Loc L = load_loc(A);
-  GenPolicy<OP, MODE, OUTER, SROW> p;
+  GenPolicy<OP, MODE, OUTER, SROW, ZSET> p;
   p.tpt_log2 = tpt_log2;
   p.tile_lds = L.slot_bytes >> tpt_log2;
   p.A = A;
@@ -1185,11 +1206,12 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
     p.row_of[f] = (abo >> 8) * 32u + (abo & 255u) / 4u;
     p.sa[f] = p.sb[f] = 0.f;
   }
-  if constexpr (GenPolicy<OP, MODE, OUTER, SROW>::SPLIT) build_pieces(A, wave, lane, OUTER, p.pooff, p.poobm, p.plpos);
+  if constexpr (GenPolicy<OP, MODE, OUTER, SROW, ZSET>::SPLIT)
+    build_pieces(A, wave, lane, OUTER, p.pooff, p.poobm, p.plpos);
   p.tab1 = TripRow{0, 0, 0, 0, 0, 0};
   p.fill(0, 0u);
   typedef ChunkShape<OP, 16> CS;
-  constexpr int NS = GenPolicy<OP, MODE, OUTER, SROW>::NS;
+  constexpr int NS = GenPolicy<OP, MODE, OUTER, SROW, ZSET>::NS;
   const int d = (NS * OUTER + ((OP::ROW && !SROW) ? L.ab_instr : 0)) << tpt_log2;
   run_ring(p, n, uni(A->stages), d, (OUTER * CS::ST) << tpt_log2);
 }
@@ -1221,6 +1243,15 @@ struct KernelEntry {
   ACP_GEN(OPC, kF32, kF32, 2, __VA_ARGS__), ACP_G1(OPC, kF32, kF32, 2, 1, 1, __VA_ARGS__), \
       ACP_G1(OPC, kF32, kF32, 2, 2, 1, __VA_ARGS__), ACP_G1(OPC, kF32, kF32, 2, 4, 1, __VA_ARGS__), \
       ACP_G1(OPC, kF32, kF32, 2, 8, 1, __VA_ARGS__)
+// two-tensor stream ops (mode key 6): variant 1 both operands on the ring,
+// variant 2 the second one staged synchronously
+#define ACP_GB1(OPC, T, OUTER, V, ...)                                                 \
+  KernelEntry{KernelKey{OPC, T, T, 16, 6, OUTER, 0, V},                              \
+              reinterpret_cast<const void*>(&dev::gen_kernel_t<__VA_ARGS__, 2, OUTER, false, (V == 2)>)}
+#define ACP_GEN_BIN(OPC, T, ...)                                                                       \
+  ACP_GB1(OPC, T, 1, 1, __VA_ARGS__), ACP_GB1(OPC, T, 2, 1, __VA_ARGS__), ACP_GB1(OPC, T, 4, 1, __VA_ARGS__), \
+      ACP_GB1(OPC, T, 8, 1, __VA_ARGS__), ACP_GB1(OPC, T, 1, 2, __VA_ARGS__), ACP_GB1(OPC, T, 2, 2, __VA_ARGS__), \
+      ACP_GB1(OPC, T, 4, 2, __VA_ARGS__), ACP_GB1(OPC, T, 8, 2, __VA_ARGS__)
 #define ACP_LIN_ROW(OPC, ...)                                                                              \
   ACP_LIN(OPC, kF32, kF32, __VA_ARGS__), ACP_L(OPC, kF32, kF32, 1, 1, __VA_ARGS__),                          \
       ACP_L(OPC, kF32, kF32, 2, 1, __VA_ARGS__), ACP_L(OPC, kF32, kF32, 4, 1, __VA_ARGS__), \
@@ -1231,7 +1262,7 @@ template <size_t N>
 const void* find_entry(const KernelEntry (&table)[N], const KernelKey& k) {
   for (const KernelEntry& e : table)
     if (e.key.op == k.op && e.key.tin == k.tin && e.key.tout == k.tout && e.key.vec_bytes == k.vec_bytes &&
-        e.key.mode == k.mode && e.key.outer == k.outer && e.key.srow == k.srow)
+        e.key.mode == k.mode && e.key.outer == k.outer && e.key.srow == k.srow && e.key.variant == k.variant)
       return e.fn;
   return nullptr;
 }

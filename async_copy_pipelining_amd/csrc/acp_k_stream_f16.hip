@@ -22,6 +22,9 @@ const KernelEntry kTable[] = {
     ACP_GEN(kOpSqrt, kF16, kF16, 2, Op<kOpSqrt, kF16, kF16>),
     ACP_GEN(kOpExp, kF16, kF32, 2, Op<kOpExp, kF16, kF32>),
     ACP_GEN(kOpExp, kF16, kF16, 2, Op<kOpExp, kF16, kF16>),
+    // two streamed tensors
+    ACP_GEN_BIN(kOpAdd, kF16, Op<kOpAdd, kF16, kF16>),
+    ACP_GEN_BIN(kOpMul, kF16, Op<kOpMul, kF16, kF16>),
 };
 }  // namespace
 const void* lookup_stream_f16(const KernelKey& k) { return find_entry(kTable, k); }

@@ -31,6 +31,9 @@ const KernelEntry kTable[] = {
     ACP_GEN_ROW(kOpAdd, RowOp<kOpAdd>),
     ACP_GEN_ROW(kOpMul, RowOp<kOpMul>),
     ACP_GEN_ROW(kOpFma, RowOp<kOpFma>),
+    // two streamed tensors
+    ACP_GEN_BIN(kOpAdd, kF32, Op<kOpAdd, kF32, kF32>),
+    ACP_GEN_BIN(kOpMul, kF32, Op<kOpMul, kF32, kF32>),
 };
 }  // namespace
 const void* lookup_stream_f32(const KernelKey& k) { return find_entry(kTable, k); }

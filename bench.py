@@ -60,12 +60,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4", choices=["c2", "c3", "c4", "c5", "calib", "copy_ref"],
+    ap.add_argument("--workload", default="c4", choices=["c2", "c3", "c4", "c5", "calib", "copy_ref", "pointwise"],
                     help="c4: the streamed fma (default); c2/c3/c5: the other workloads; "
                          "calib: torch's copy of 256 MiB, the known-size kernel that scales HBM counters; "
                          "copy_ref: the library's register-path reference copy of the c4 tensor "
                          "(the plain 1:1 read/write ceiling)")
     ap.add_argument("--stages", type=int, default=4)
+    ap.add_argument("--z-staging", default="ring", choices=["ring", "set"],
+                    help="pointwise: how the second tensor reaches the ring")
     ap.add_argument("--rows", type=int, default=2, help="rows per ring stage (c4)")
     ap.add_argument("--threads", type=int, default=256)
     ap.add_argument("--workgroups", type=int, default=0, help="persistent workgroups (0: 256 x --wg-per-cu)")
@@ -157,6 +159,27 @@ def main():
         bytes_per, dtype = x.nbytes * 2, "f16"
         config = {"workload": "tile copy, [128,500,1024] f16, 128x32 tiles, 128 threads"}
         key = "tile_copy_f16_128x500x1024"
+    elif wl == "pointwise":
+        # y = x + z over two [128,500,1024] f32 tensors, both streamed
+        shape = (128, 500, 1024)
+        stage = (1, args.rows, 1024)
+        rng = np.random.default_rng(6)
+        x = rng.standard_normal(shape, dtype=np.float32)
+        z = rng.standard_normal(shape, dtype=np.float32)
+        G = args.workgroups or 256 * args.wg_per_cu
+        for s in range(args.sets):
+            xd, zd = to_dev(x), to_dev(z)
+            yd = torch.empty(x.nbytes, dtype=torch.uint8, device=dev)
+            xdesc = acp.acp_encode_tiled("f32", xd, shape, packed(shape), stage)
+            zdesc = acp.acp_encode_tiled("f32", zd, shape, packed(shape), stage)
+            ydesc = acp.acp_encode_tiled("f32", yd, shape, packed(shape), stage)
+            launches.append(lambda xdesc=xdesc, zdesc=zdesc, ydesc=ydesc, keep=(xd, zd, yd):
+                            acp.acp_stream_binary("add", ydesc, xdesc, zdesc, stage, args.stages, args.threads, G,
+                                                  args.z_staging, stream))
+        bytes_per, dtype = 3 * x.nbytes, "f32"
+        config = {"workload": f"two-tensor stream y = x + z, [128,500,1024] f32, {args.stages}-stage LDS ring, "
+                              f"stage (1,{args.rows},1024), z staged '{args.z_staging}'", "workgroups": G}
+        key = f"stream_add2_f32_128x500x1024_s{args.stages}_r{args.rows}_{args.z_staging}"
     elif wl == "copy_ref":
         n = 128 * 500 * 1024 * 4
         G = args.workgroups or 256 * args.wg_per_cu

@@ -202,6 +202,30 @@ acp_status acp_stream_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_
                             const float* row_a, const float* row_b, const int32_t* stage_box,
                             int stages, int threads, int workgroups, void* hip_stream);
 
+/* How the second tensor of a two-tensor stream reaches its ring slot
+ * ([cb] "Testing Setup", Pointwise: one tensor on the asynchronous ring,
+ * the other "Set", i.e. loaded by ordinary loads and stored into the
+ * circular buffer; PointwiseCpAsync: both asynchronous). */
+typedef enum { ACP_STAGE_RING = 0, ACP_STAGE_SET = 1 } acp_staging;
+
+/* Stream out = x OP z (op ADD or MUL) through an LDS ring of `stages`
+ * (2..4) buffers, as acp_stream_ewise does for one tensor.  x is staged by
+ * direct-to-LDS loads; z with ACP_STAGE_RING the same way (both loads of a
+ * trip in flight together), with ACP_STAGE_SET by ordinary loads into
+ * registers, a wait for all of the wave's outstanding loads, and a store
+ * into z's image in the slot.
+ *   x, z        float16 or float32, one layout (dtype, shape, strides, box,
+ *               swizzle); x's box is the workgroup tile
+ *   out         same dtype, shape and box; any strides; not x or z
+ *   stage_box   sub-box of the tile staged per trip (divides it per dim)
+ *   workgroups  0: one workgroup per tile; G > 0: G persistent workgroups
+ * Results are the IEEE sum or product of each element pair, rounded once
+ * to the operand type.  ACP_ERR_UNSUPPORTED unless the plan has 16-byte
+ * rounds and 1, 2, 4 or 8 rounds per thread. */
+acp_status acp_stream_binary(acp_op op, const acp_tile_desc* out, const acp_tile_desc* x, const acp_tile_desc* z,
+                             const int32_t* stage_box, int stages, int threads, int workgroups,
+                             acp_staging z_staging, void* hip_stream);
+
 /* Test export: the raw LDS bytes of tile `tile_index` of `src` after its
  * direct-to-LDS load, written to `out_bytes` (device, tile_bytes long). */
 acp_status acp_debug_lds_image(const acp_tile_desc* src, int64_t tile_index, int threads,

@@ -182,3 +182,46 @@ def test_widening_stream_pieces_ragged(threads, stage_box, mode):
     x = W.strided_view(storage, shape, strides)
     ref = REF.ewise("sqrt", [x], np.float32)
     assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+
+
+def _binary_case(op, dt, shape, box, stage_box, stages, threads, workgroups, staging, swizzle=0, seed=41):
+    npdt = {"f16": np.float16, "f32": np.float32}[dt]
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape).astype(npdt)
+    z = rng.standard_normal(shape).astype(npdt)
+    xd, zd = dev(x), dev(z)
+    yd = empty_bytes(x.nbytes)
+    st = packed_strides(shape)
+    xdesc = encode(dt, xd, shape, st, box, swizzle)
+    zdesc = encode(dt, zd, shape, st, box, swizzle)
+    ydesc = encode(dt, yd, shape, st, box)
+    acp.acp_stream_binary(op, ydesc, xdesc, zdesc, stage_box, stages, threads, workgroups, staging, stream())
+    return x, z, host(yd, npdt, shape)
+
+
+@pytest.mark.parametrize("staging", ["ring", "set"])
+@pytest.mark.parametrize("op,dt,shape,box,stage_box,stages,threads,workgroups,swz", [
+    ("add", "f32", (3, 37, 1024), (1, 12, 1024), (1, 4, 1024), 4, 256, 0, 0),   # cut last stage
+    ("mul", "f32", (3, 37, 1024), (1, 4, 1024), (1, 4, 1024), 3, 256, 5, 0),    # persistent, uneven
+    ("add", "f16", (2, 70, 256), (1, 8, 256), (1, 4, 128), 2, 64, 0, 3),        # swizzled, two loads per trip
+    ("mul", "f16", (4, 33, 512), (1, 16, 256), (1, 16, 64), 4, 128, 7, 2),      # 64-byte swizzle, sub-stages
+])
+def test_two_tensor_stream_matches_oracle(staging, op, dt, shape, box, stage_box, stages, threads, workgroups, swz):
+    say(f"two-tensor stream {op} {dt} {shape} box {box} stage {stage_box} S={stages} wg={workgroups} "
+        f"z={staging} swizzle {swz}")
+    x, z, y = _binary_case(op, dt, shape, box, stage_box, stages, threads, workgroups, staging, swz)
+    ref = REF.ewise(op, [x, z], y.dtype)
+    bits = np.uint16 if dt == "f16" else np.uint32
+    assert np.array_equal(y.view(bits), ref.view(bits))
+
+
+@pytest.mark.parametrize("staging", ["ring", "set"])
+def test_two_tensor_stream_full_size_sampled(staging):
+    shape, stage_box = (128, 500, 1024), (1, 2, 1024)
+    say(f"two-tensor stream add {shape} stage {stage_box} S=4, 256 workgroups, z={staging}")
+    x, z, y = _binary_case("add", "f32", shape, stage_box, stage_box, 4, 256, 256, staging, seed=42)
+    rng = np.random.default_rng(43)
+    i0, i1 = rng.integers(0, 128, 2000), rng.integers(0, 500, 2000)
+    ref = REF.ewise("add", [x[i0, i1], z[i0, i1]], np.float32)
+    assert np.array_equal(y[i0, i1].view(np.uint32), ref.view(np.uint32))
+    assert not np.any(y.view(np.uint32) == 0xA5A5A5A5)
