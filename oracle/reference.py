@@ -9,6 +9,16 @@
 * streamed elementwise with per-row scalars: for a tensor x whose rows are
   its innermost runs, y[r, c] = op(a[r], x[r, c], b[r]) with
   fma = a*x + b, add = x + b, mul = a*x; unary ops ignore a and b.
+* store with reduce-add ("copy_async -> tma", "How inputs change the
+  algorithm": a shared -> global copy with a reduce op, e.g. add): every
+  staged element is added into the destination element it maps to.  With
+  a destination of extent 1 along some dims, every source element along
+  those dims adds into the same destination element:
+  dst'[j] = dst[j] + sum of src[i] over the i that map to j.  Integers wrap
+  modulo 2**32.  For floats the page fixes no order of the additions;
+  reading adopted: the sum is the exact one rounded once, which every
+  order of IEEE additions reproduces when each partial sum is exactly
+  representable (and always with a single contribution).
 """
 from __future__ import annotations
 
@@ -47,3 +57,25 @@ def stream_ewise(op: str, x: np.ndarray, a=None, b=None, out_dtype=np.float32) -
     if op == "mul":
         return ops.mul(a_b, x, out_dtype)
     raise ValueError(f"unknown op {op}")
+
+
+def tile_reduce_add(dst: np.ndarray, src: np.ndarray) -> np.ndarray:
+    """dst + src summed over the dims where dst has extent 1 and src more."""
+    dst = np.asarray(dst)
+    src = np.asarray(src)
+    if dst.ndim != src.ndim:
+        raise ValueError("dst and src must have the same rank")
+    axes = []
+    for d, (m, n) in enumerate(zip(dst.shape, src.shape)):
+        if m == n:
+            continue
+        if m != 1:
+            raise ValueError("dst extents must equal src's or be 1")
+        axes.append(d)
+    if dst.dtype == np.uint32:
+        total = src.astype(np.uint64).sum(axis=tuple(axes), keepdims=True) + dst.astype(np.uint64)
+        return (total % (1 << 32)).astype(np.uint32)
+    if dst.dtype in (np.float16, np.float32):
+        total = src.astype(np.float64).sum(axis=tuple(axes), keepdims=True) + dst.astype(np.float64)
+        return total.astype(dst.dtype)
+    raise ValueError("reduce-add takes uint32, float16 or float32")
