@@ -95,7 +95,7 @@ struct Launch {
 
 struct EngineRequest {
   int op;                      // acp_op
-  int mode;                    // 0 copy, 1 tile ewise, 2 stream
+  int mode;                    // 0 copy, 1 tile ewise, 2 stream, 3 store with reduce-add
   const acp::DescData* x;      // layout of every staged operand
   const acp::DescData* out;
   const void* in_ptrs[3];
@@ -183,7 +183,9 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
     const int64_t sub = x.box[d] / sb;
     const int64_t tg = (nst + sub - 1) / sub;
     xstride[d] = x.strides[d] * ei;
-    ostride[d] = o.strides[d] * eo;
+    // a reduce-add destination of extent 1 along a dim the source spans:
+    // every source stage along it adds into the same destination elements
+    ostride[d] = (q.mode == 3 && o.shape[d] == 1 && x.shape[d] > 1) ? 0 : o.strides[d] * eo;
     A.sbox[d] = static_cast<uint32_t>(sb);
     A.nst[d] = static_cast<uint32_t>(nst);
     const int64_t rem = nst ? x.shape[d] - (nst - 1) * sb : sb;
@@ -305,7 +307,7 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   }
   // any other grid with 16-byte rounds: the general lean kernel
   static const bool gen_ok = env_flag("ACP_GEN_PATH", true);
-  if (gen_ok && L->key.mode <= 2 && p.vec_bytes == 16 &&
+  if (gen_ok && L->key.mode <= 3 && p.vec_bytes == 16 &&
       (p.outer == 1 || p.outer == 2 || p.outer == 4 || p.outer == 8)) {
     acp::KernelKey gk = L->key;
     gk.mode = q.mode + 4;
@@ -321,7 +323,7 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   }
   // tile ops in the general kernel on a persistent grid: tiles per ring trip
   int tpt_log2 = 0;
-  if ((L->key.mode == 4 || L->key.mode == 5) && q.workgroups > 0 && subs == 1)
+  if ((L->key.mode == 4 || L->key.mode == 5 || L->key.mode == 7) && q.workgroups > 0 && subs == 1)
     while ((2 << tpt_log2) <= q.tiles_per_trip && tpt_log2 < 2) ++tpt_log2;
   A.tpt_log2 = static_cast<uint32_t>(tpt_log2);
 
@@ -642,6 +644,78 @@ acp_status acp_stream_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_
   Launch L;
   const acp_status st = prepare(q, &L);
   if (st != ACP_OK) return st;
+  return launch(L, hip_stream);
+}
+
+acp_status acp_tile_reduce(acp_op op, const acp_tile_desc* dst, const acp_tile_desc* src, int threads,
+                           void* hip_stream) {
+  acp::DescData s, d;
+  if (!load_desc(src, &s) || !load_desc(dst, &d)) return ret(ACP_ERR_INVALID, "not an encoded descriptor");
+  if (op != ACP_OP_ADD) return ret(ACP_ERR_INVALID, "the store reduces with add");
+  if (s.dtype != d.dtype) return ret(ACP_ERR_INVALID, "source and destination dtypes differ");
+  if (s.dtype != ACP_U32 && s.dtype != ACP_F32 && s.dtype != ACP_F16)
+    return ret(ACP_ERR_UNSUPPORTED, "reduce-add takes u32, f32 or f16");
+  if (s.rank != d.rank) return ret(ACP_ERR_INVALID, "source and destination ranks differ");
+  for (int k = 0; k < s.rank; ++k) {
+    if (s.box[k] != d.box[k]) return ret(ACP_ERR_INVALID, "source and destination boxes differ");
+    if (d.shape[k] == s.shape[k]) continue;
+    if (d.shape[k] != 1 || s.box[k] != 1)
+      return ret(ACP_ERR_INVALID, "a destination extent must equal the source's, or be 1 where the box is 1");
+  }
+  if (s.gbase == d.gbase) return ret(ACP_ERR_INVALID, "source and destination are the same tensor");
+  bool one_each = true;  // every destination element receives one contribution
+  for (int k = 0; k < s.rank; ++k) one_each = one_each && d.shape[k] == s.shape[k] && d.strides[k] == s.strides[k];
+  if (one_each && s.dtype != ACP_U32) {
+    // No two source elements meet in one destination element: dst' = src + dst
+    // needs no atomics.  Both tensors ride the ring and the sum is stored in
+    // place; every element is staged before the same lane stores it, and no
+    // other trip touches it.
+    EngineRequest q{};
+    q.op = ACP_OP_ADD;
+    q.mode = 2;
+    q.x = &s;
+    q.out = &d;
+    q.in_ptrs[0] = reinterpret_cast<const void*>(s.gbase);
+    q.in_ptrs[1] = reinterpret_cast<const void*>(d.gbase);
+    q.n_in = 2;
+    q.stage_box = s.box;
+    q.threads = threads;
+    q.copy_only = false;
+    q.binary = 1;
+    int tpt = 1;
+    acp::Plan p;
+    std::string why;
+    if (acp::plan_box(s, false, &p, &why) == acp::PlanStatus::Ok)
+      tile_schedule(p, 2, threads, 0, &q.workgroups, &q.stages, &tpt);
+    q.stages = q.workgroups > 0 ? q.stages : 2;
+    Launch L;
+    const acp_status st = prepare(q, &L);
+    if (st == ACP_OK && L.key.variant == 1) return launch(L, hip_stream);
+    if (st != ACP_OK && st != ACP_ERR_UNSUPPORTED) return st;
+    // otherwise: the atomic path below
+  }
+  EngineRequest q{};
+  q.op = ACP_OP_ADD;
+  q.mode = 3;
+  q.x = &s;
+  q.out = &d;
+  q.in_ptrs[0] = reinterpret_cast<const void*>(s.gbase);
+  q.n_in = 1;
+  q.stage_box = s.box;
+  q.threads = threads;
+  q.copy_only = false;
+  {
+    acp::Plan p;
+    std::string why;
+    if (acp::plan_box(s, false, &p, &why) == acp::PlanStatus::Ok)
+      tile_schedule(p, 1, threads, 0, &q.workgroups, &q.stages, &q.tiles_per_trip);
+    else
+      q.stages = 1;
+  }
+  Launch L;
+  const acp_status st = prepare(q, &L);
+  if (st != ACP_OK) return st;
+  if (L.key.mode != 7) return ret(ACP_ERR_UNSUPPORTED, "reduce-add needs 16-byte rounds and 1, 2, 4 or 8 rounds per thread");
   return launch(L, hip_stream);
 }
 

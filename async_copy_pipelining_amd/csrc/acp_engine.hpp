@@ -86,7 +86,8 @@ struct KernelKey {
   int tout;      // acp_dtype of the output
   int vec_bytes; // 16 or 4
   int mode;      // 0 copy, 1 tile ewise (output staged in LDS), 2 stream, 3 stream on a linear grid,
-                 // 4 / 5 / 6: copy / tile ewise / stream in the general lean kernel
+                 // 4 / 5 / 6 / 7: copy / tile ewise / stream / store with reduce-add in the
+                 // general lean kernel
   int outer;     // modes 3..6: rounds per thread (1, 2, 4 or 8); 0 otherwise
   int srow;      // modes 3 and 6, row ops: per-row scalars through the scalar cache
   int variant = 0;  // mode 6, add / mul of two streamed tensors: 1 both on the direct-to-LDS

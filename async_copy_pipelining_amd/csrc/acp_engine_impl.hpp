@@ -43,6 +43,7 @@ namespace dev {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef const EngineArgs __attribute__((address_space(4))) CArgs;
 
 constexpr int kOpZero = 0, kOpSqrt = 1, kOpExp = 2, kOpAdd = 3, kOpMul = 4, kOpFma = 5, kOpCopy = 6;
@@ -243,6 +244,25 @@ template <> struct Op<kOpFma, kF16, kF16> {
   static constexpr bool ROW = false;
   static __device__ __forceinline__ TO f(TI a, TI b, TI c, float, float) { return __builtin_fmaf16(a, b, c); }
 };
+// Store with reduce-add: the staged elements are added into the destination
+// with no-return buffer atomics (32-bit integer add, binary32 add, packed
+// binary16 pair add), 4 per 16-byte chunk.
+template <int T> struct ReduceOp {
+  typedef typename DType<T>::T TI;
+  typedef TI TO;
+  static constexpr int NIN = 1;
+  static constexpr bool ROW = false;
+  static __device__ __forceinline__ TO f(TI x, TI, TI, float, float) { return x; }
+  static __device__ __forceinline__ void add(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t w) {
+    if constexpr (T == kF32)
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(__builtin_bit_cast(float, w), rs, voff, 0, 0);
+    else if constexpr (T == kF16)
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_v2f16(__builtin_bit_cast(f16x2, w), rs, voff, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(static_cast<int>(w), rs, voff, 0, 0);
+  }
+};
+
 // Streamed x with per-row scalars (binary32): add x + b, mul a * x, fma a * x + b.
 template <int OPC> struct RowOp {
   typedef float TI;
@@ -1078,6 +1098,21 @@ struct GenPolicy {
       consume_pieces(rs, sl, beyond, last);
       return;
     }
+    if constexpr (MODE == 3) {
+      // store with reduce-add: four 4-byte atomics per staged chunk
+#pragma unroll
+      for (int f = 0; f < OUTER; ++f) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(
+            __builtin_assume_aligned(lds + sl + f * waves_kb + wave * 1024u + lane * 16u, 16));
+        const bool ok = !beyond && (oobm[f] & last) == 0;
+        const uint32_t o = ok ? ooff[f] : kOobOffset;
+        OP::add(rs, o, v.x);
+        OP::add(rs, o + 4u, v.y);
+        OP::add(rs, o + 8u, v.z);
+        OP::add(rs, o + 12u, v.w);
+      }
+      return;
+    }
     // rounds in groups whose staged operands fit in registers together
     constexpr int GRP = round_group(OUTER, NS, 16);
     static_assert(OUTER % GRP == 0, "round groups must tile the rounds");
@@ -1213,7 +1248,7 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   typedef ChunkShape<OP, 16> CS;
   constexpr int NS = GenPolicy<OP, MODE, OUTER, SROW, ZSET>::NS;
   const int d = (NS * OUTER + ((OP::ROW && !SROW) ? L.ab_instr : 0)) << tpt_log2;
-  run_ring(p, n, uni(A->stages), d, (OUTER * CS::ST) << tpt_log2);
+  run_ring(p, n, uni(A->stages), d, (OUTER * (MODE == 3 ? 4 : CS::ST)) << tpt_log2);
 }
 
 }  // namespace dev
@@ -1235,7 +1270,7 @@ struct KernelEntry {
 #define ACP_G1(OPC, TIN, TOUT, MODE, OUTER, SR, ...) \
   KernelEntry{KernelKey{OPC, TIN, TOUT, 16, (MODE) + 4, OUTER, SR}, \
               reinterpret_cast<const void*>(&dev::gen_kernel_t<__VA_ARGS__, MODE, OUTER, (SR != 0)>)}
-// general lean kernels: mode key 4 (copy), 5 (tile ewise), 6 (stream)
+// general lean kernels: mode key 4 (copy), 5 (tile ewise), 6 (stream), 7 (store with reduce-add)
 #define ACP_GEN(OPC, TIN, TOUT, MODE, ...) \
   ACP_G1(OPC, TIN, TOUT, MODE, 1, 0, __VA_ARGS__), ACP_G1(OPC, TIN, TOUT, MODE, 2, 0, __VA_ARGS__), \
       ACP_G1(OPC, TIN, TOUT, MODE, 4, 0, __VA_ARGS__), ACP_G1(OPC, TIN, TOUT, MODE, 8, 0, __VA_ARGS__)

@@ -1,4 +1,5 @@
-// Engine instantiations: tile copy (raw bytes moved as 32-bit words).
+// Engine instantiations: tile copy (raw bytes moved as 32-bit words) and the
+// store with reduce-add.
 #include "acp_engine_impl.hpp"
 
 namespace acp {
@@ -8,6 +9,10 @@ const KernelEntry kTable[] = {
     ACP_BOTH(kOpCopy, kU32, kU32, 0, Op<kOpCopy, kU32, kU32>),
     // general lean kernel
     ACP_GEN(kOpCopy, kU32, kU32, 0, Op<kOpCopy, kU32, kU32>),
+    // store with reduce-add
+    ACP_GEN(kOpAdd, kU32, kU32, 3, ReduceOp<kU32>),
+    ACP_GEN(kOpAdd, kF32, kF32, 3, ReduceOp<kF32>),
+    ACP_GEN(kOpAdd, kF16, kF16, 3, ReduceOp<kF16>),
 };
 }  // namespace
 const void* lookup_copy(const KernelKey& k) { return find_entry(kTable, k); }

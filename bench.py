@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4", choices=["c2", "c3", "c4", "c5", "calib", "copy_ref", "pointwise"],
+    ap.add_argument("--workload", default="c4", choices=["c2", "c3", "c4", "c5", "calib", "copy_ref", "pointwise", "reduce"],
                     help="c4: the streamed fma (default); c2/c3/c5: the other workloads; "
                          "calib: torch's copy of 256 MiB, the known-size kernel that scales HBM counters; "
                          "copy_ref: the library's register-path reference copy of the c4 tensor "
@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--stages", type=int, default=4)
     ap.add_argument("--z-staging", default="ring", choices=["ring", "set"],
                     help="pointwise: how the second tensor reaches the ring")
+    ap.add_argument("--reduce-over-batch", action="store_true",
+                    help="reduce: add all 128 slabs into one [500,1024] destination (else slab by slab)")
     ap.add_argument("--rows", type=int, default=2, help="rows per ring stage (c4)")
     ap.add_argument("--threads", type=int, default=256)
     ap.add_argument("--workgroups", type=int, default=0, help="persistent workgroups (0: 256 x --wg-per-cu)")
@@ -180,6 +182,27 @@ def main():
         config = {"workload": f"two-tensor stream y = x + z, [128,500,1024] f32, {args.stages}-stage LDS ring, "
                               f"stage (1,{args.rows},1024), z staged '{args.z_staging}'", "workgroups": G}
         key = f"stream_add2_f32_128x500x1024_s{args.stages}_r{args.rows}_{args.z_staging}"
+    elif wl == "reduce":
+        # store with reduce-add of a [128,500,1024] f32 tensor in (1,R,1024)
+        # tiles: into a same-shape destination (one contribution per element)
+        # or into one [1,500,1024] slab (128 contributions per element)
+        shape = (128, 500, 1024)
+        dshape = (1, 500, 1024) if args.reduce_over_batch else shape
+        box = (1, args.rows, 1024)
+        rng = np.random.default_rng(7)
+        x = rng.standard_normal(shape, dtype=np.float32)
+        for s in range(args.sets):
+            xd = to_dev(x)
+            yd = torch.zeros(int(np.prod(dshape)) * 4, dtype=torch.uint8, device=dev)
+            xdesc = acp.acp_encode_tiled("f32", xd, shape, packed(shape), box)
+            ydesc = acp.acp_encode_tiled("f32", yd, dshape, packed(dshape), box)
+            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
+                            acp.acp_tile_reduce("add", ydesc, xdesc, args.threads, stream))
+        # algorithmic bytes: the source once, the destination read and written once
+        bytes_per, dtype = x.nbytes + 2 * int(np.prod(dshape)) * 4, "f32"
+        config = {"workload": f"store with reduce-add, [128,500,1024] f32 tiles (1,{args.rows},1024) into "
+                              f"{list(dshape)}"}
+        key = f"tile_reduce_f32_128x500x1024_r{args.rows}_{'batch' if args.reduce_over_batch else 'slab'}"
     elif wl == "copy_ref":
         n = 128 * 500 * 1024 * 4
         G = args.workgroups or 256 * args.wg_per_cu

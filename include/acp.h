@@ -202,6 +202,28 @@ acp_status acp_stream_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_
                             const float* row_a, const float* row_b, const int32_t* stage_box,
                             int stages, int threads, int workgroups, void* hip_stream);
 
+/* Store with reduce-add ([tma] "How inputs change the algorithm": a shared
+ * -> global copy with a reduce op, e.g. add): every tile of `src` is staged
+ * in LDS by direct-to-LDS loads and added element by element into `dst`
+ * with no-return buffer atomics.
+ *   op    ACP_OP_ADD
+ *   src   u32, f32 or f16
+ *   dst   same dtype, rank and box; each extent equal to src's, or 1 where
+ *         src's box is 1: every source tile along such a dim adds into the
+ *         same destination elements (a sum over that dim)
+ * dst'[j] = dst[j] + sum of the src elements mapped to j; u32 wraps modulo
+ * 2^32.  Floating-point additions land in no fixed order: the result is
+ * the exactly rounded sum whenever every partial sum is representable (in
+ * particular with one contribution per element).  Tile counts above the
+ * persistent grid walk tiles w, w+G, ... as acp_tile_copy does.  When dst
+ * has src's shape and strides (one contribution per element) and the dtype
+ * is a float, no atomics are needed: both tensors ride the LDS ring and the
+ * sum is stored into dst in place.
+ * ACP_ERR_UNSUPPORTED unless the plan has 16-byte rounds and 1, 2, 4 or 8
+ * rounds per thread. */
+acp_status acp_tile_reduce(acp_op op, const acp_tile_desc* dst, const acp_tile_desc* src, int threads,
+                           void* hip_stream);
+
 /* How the second tensor of a two-tensor stream reaches its ring slot
  * ([cb] "Testing Setup", Pointwise: one tensor on the asynchronous ring,
  * the other "Set", i.e. loaded by ordinary loads and stored into the

@@ -133,6 +133,18 @@ def test_status_codes_and_reasons():
         acp.acp_tile_copy(x, acp.acp_encode_tiled("f16", FAKE_BASE, (4, 8, 256), (2048, 256, 1), (1, 4, 256)), 256)
     assert e.value.status == acp.ACP_ERR_INVALID and "valid copy" in e.value.reason
     assert acp.acp_last_error() != ""
+    # reduce-add shape and dtype rules are checked on the host
+    src = acp.acp_encode_tiled("f32", FAKE_BASE, (4, 8, 256), (2048, 256, 1), (1, 4, 256))
+    for dshape, dbox, dt, why in (((2, 8, 256), (1, 4, 256), "f32", "equal the source"),
+                                  ((1, 8, 256), (1, 8, 256), "f32", "boxes differ"),
+                                  ((1, 8, 256), (1, 4, 256), "u32", "dtypes differ")):
+        d = acp.acp_encode_tiled(dt, FAKE_BASE * 5, dshape, (2048, 256, 1), dbox)
+        with pytest.raises(acp.AcpError) as e:
+            acp.acp_tile_reduce("add", d, src, 256)
+        assert e.value.status == acp.ACP_ERR_INVALID and why in e.value.reason
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_tile_reduce("mul", src, src, 256)
+    assert e.value.status == acp.ACP_ERR_INVALID
     # the reference stream copy checks its arguments before any launch
     for dst, src, n, why in ((FAKE_BASE, FAKE_BASE + 64, 128, "overlap"), (FAKE_BASE, FAKE_BASE * 8, 100, "16-byte"),
                              (FAKE_BASE, FAKE_BASE * 8, -16, "bad"), (None, FAKE_BASE, 16, "bad")):

@@ -13,6 +13,7 @@ torch = pytest.importorskip("torch")
 import async_copy_pipelining_amd as acp  # noqa: E402
 import workloads as W  # noqa: E402
 from oracle import plan as P  # noqa: E402
+from oracle import reference as REF  # noqa: E402
 from oracle import tiles as T  # noqa: E402
 from tests.gpu_util import dev, empty_bytes, encode, host, packed_strides, stream  # noqa: E402
 
@@ -201,3 +202,41 @@ def test_reference_stream_copy_is_bit_identical(nbytes, workgroups):
     y = host(yd, np.uint8)
     assert np.array_equal(y[:nbytes], x[:nbytes])
     assert np.all(y[nbytes:] == 0x5A)      # nothing written past the end
+
+
+def _reduce_case(dt, src_shape, dst_shape, box, threads, values, swz=0, seed=51):
+    npdt = {"u32": np.uint32, "f32": np.float32, "f16": np.float16}[dt]
+    rng = np.random.default_rng(seed)
+    if values == "wide":
+        src = rng.integers(0, 2**32, size=src_shape, dtype=np.uint64).astype(np.uint32)
+        dst = rng.integers(0, 2**32, size=dst_shape, dtype=np.uint64).astype(np.uint32)
+    elif values == "normal":
+        src = rng.standard_normal(src_shape).astype(npdt)
+        dst = rng.standard_normal(dst_shape).astype(npdt)
+    else:                                   # small integers: every partial sum exact
+        src = rng.integers(-values, values + 1, size=src_shape).astype(npdt)
+        dst = rng.integers(-values, values + 1, size=dst_shape).astype(npdt)
+    sd, dd = dev(src), dev(dst)
+    sdesc = encode(dt, sd, src_shape, packed_strides(src_shape), box, swz)
+    ddesc = encode(dt, dd, dst_shape, packed_strides(dst_shape), box)
+    acp.acp_tile_reduce("add", ddesc, sdesc, threads, stream())
+    got = host(dd, npdt, dst_shape)
+    want = REF.tile_reduce_add(dst, src)
+    bits = {np.uint32: np.uint32, np.float32: np.uint32, np.float16: np.uint16}[npdt]
+    return got.view(bits), want.view(bits)
+
+
+@pytest.mark.parametrize("dt,src_shape,dst_shape,box,threads,values,swz", [
+    ("u32", (6, 40, 256), (1, 40, 256), (1, 8, 256), 128, "wide", 0),        # wraps modulo 2**32; cut rows
+    ("f32", (3, 37, 128), (3, 37, 128), (1, 8, 128), 64, "normal", 0),       # one contribution: IEEE add (ring path)
+    ("f16", (700, 8, 64), (700, 8, 64), (1, 8, 64), 64, "normal", 2),        # one contribution, persistent, swizzled
+    ("u32", (3, 37, 128), (3, 37, 128), (1, 8, 128), 64, "wide", 0),         # one contribution, integer: atomics
+    ("f32", (16, 33, 64), (1, 33, 64), (1, 8, 64), 64, 100, 3),              # 16 contributions, swizzled staging
+    ("f16", (8, 20, 128), (1, 20, 128), (1, 4, 128), 64, 8, 0),              # packed f16 pairs
+    ("f32", (600, 16, 64), (1, 16, 64), (1, 16, 64), 64, 4, 0),              # 600 tiles into one: persistent grid
+    ("u32", (4, 5, 16, 64), (1, 1, 16, 64), (1, 1, 16, 64), 64, "wide", 0),  # two reduced dims
+])
+def test_store_with_reduce_add(dt, src_shape, dst_shape, box, threads, values, swz):
+    say(f"reduce-add {dt} {src_shape} -> {dst_shape} box {box} threads {threads} swizzle {swz}")
+    got, want = _reduce_case(dt, src_shape, dst_shape, box, threads, values, swz)
+    assert np.array_equal(got, want)
