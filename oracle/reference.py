@@ -19,8 +19,17 @@
   reading adopted: the sum is the exact one rounded once, which every
   order of IEEE additions reproduces when each partial sum is exactly
   representable (and always with a single contribution).
+* row reduction ("Add TMA support for circular buffering pass", "Testing
+  Setup": the Reduction and InnerPersistent schedules over circular-
+  buffered loads): y[row] = sum of x[row, c] over the innermost dim, the
+  exact sum rounded once to binary32.  Reading adopted: the page names the
+  schedule, not an accumulation order; the exact sum is the one definition
+  every order approximates (the GPU's fixed order is compared against it
+  within the textbook bound for recursive summation).
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -79,3 +88,22 @@ def tile_reduce_add(dst: np.ndarray, src: np.ndarray) -> np.ndarray:
         total = src.astype(np.float64).sum(axis=tuple(axes), keepdims=True) + dst.astype(np.float64)
         return total.astype(dst.dtype)
     raise ValueError("reduce-add takes uint32, float16 or float32")
+
+
+def reduce_rows(x: np.ndarray) -> np.ndarray:
+    """Exact sum of every innermost row, rounded once to float32."""
+    x = np.asarray(x)
+    n_rows = int(np.prod(x.shape[:-1]))
+    rows = x.reshape(n_rows, x.shape[-1]).astype(np.float64)
+    out = np.array([math.fsum(r) for r in rows], dtype=np.float64)
+    return out.astype(np.float32).reshape(x.shape[:-1])
+
+
+def recursive_sum_bound(x: np.ndarray, n_adds: int) -> np.ndarray:
+    """Per-row bound on |computed - exact| for any order of n_adds binary32
+    additions of the row's values: gamma_n * sum |x|, gamma_n = n u / (1 - n u),
+    u = 2**-24 (recursive summation, Higham, Accuracy and Stability of
+    Numerical Algorithms, section 4.2)."""
+    u = 2.0 ** -24
+    g = n_adds * u / (1 - n_adds * u)
+    return g * np.abs(np.asarray(x, dtype=np.float64)).sum(axis=-1)

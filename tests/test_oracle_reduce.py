@@ -58,3 +58,41 @@ def test_reduce_rejects_bad_shapes():
         REF.tile_reduce_add(np.zeros((2, 3), np.float32), np.zeros((4, 3), np.float32))
     with pytest.raises(ValueError):
         REF.tile_reduce_add(np.zeros((3,), np.float32), np.zeros((4, 3), np.float32))
+
+
+def test_reduce_rows_exact_then_rounded_once():
+    from fractions import Fraction
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((7, 33)) * 10.0 ** rng.integers(-6, 7, (7, 33))).astype(np.float32)
+    got = REF.reduce_rows(x)
+    for r in range(7):
+        exact = sum(Fraction(float(v)) for v in x[r])
+        # float32(exact) by round-to-nearest: compare against both neighbours
+        f = np.float32(float(exact))
+        assert got[r] == f
+        lo, hi = np.nextafter(f, np.float32(-np.inf)), np.nextafter(f, np.float32(np.inf))
+        assert abs(Fraction(float(f)) - exact) <= abs(Fraction(float(lo)) - exact)
+        assert abs(Fraction(float(f)) - exact) <= abs(Fraction(float(hi)) - exact)
+
+
+def test_reduce_rows_closed_forms():
+    n = 1000
+    x = np.arange(1, n + 1, dtype=np.float32)[None, :]
+    assert REF.reduce_rows(x)[0] == n * (n + 1) // 2
+    # cancellation: plain float32 left-to-right loses the 1, the exact sum keeps it
+    y = np.array([[1e8, 1.0, -1e8]], np.float32)
+    assert REF.reduce_rows(y)[0] == 1.0
+    assert REF.reduce_rows(np.zeros((3, 0), np.float32)).tolist() == [0.0, 0.0, 0.0]
+    h = np.full((2, 2048), 0.5, np.float16)
+    assert REF.reduce_rows(h).tolist() == [1024.0, 1024.0]
+
+
+def test_recursive_sum_bound_holds_for_left_to_right_sums():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((50, 1024)).astype(np.float32)
+    ltr = np.zeros(50, np.float32)
+    for c in range(1024):
+        ltr = ltr + x[:, c]                       # binary32 left to right
+    err = np.abs(ltr.astype(np.float64) - REF.reduce_rows(x).astype(np.float64))
+    ulp = np.spacing(np.abs(REF.reduce_rows(x)))
+    assert np.all(err <= REF.recursive_sum_bound(x, 1023) + ulp)
