@@ -86,6 +86,7 @@ _SIGS = {
     "acp_tile_ewise": ([_I, _DESC_P, ctypes.POINTER(_DESC_P), _I, _I, _P], _I),
     "acp_stream_ewise": ([_I, _DESC_P, _DESC_P, _P, _P, ctypes.POINTER(ctypes.c_int32), _I, _I, _I, _P], _I),
     "acp_tile_reduce": ([_I, _DESC_P, _DESC_P, _I, _P], _I),
+    "acp_stream_reduce_rows": ([_I, _P, _DESC_P, ctypes.POINTER(ctypes.c_int32), _I, _I, _I, _P], _I),
     "acp_stream_binary": ([_I, _DESC_P, _DESC_P, _DESC_P, ctypes.POINTER(ctypes.c_int32), _I, _I, _I, _I, _P], _I),
     "acp_debug_lds_image": ([_DESC_P, ctypes.c_int64, _I, _P, _P], _I),
     "acp_debug_ring_trace": ([_I, _I, _I, _I, _P, _P], _I),
@@ -172,6 +173,14 @@ def acp_stream_ewise(op, out: acp_tile_desc, x: acp_tile_desc, row_a, row_b, sta
 def acp_tile_reduce(op, dst: acp_tile_desc, src: acp_tile_desc, threads: int, stream=None) -> None:
     opc = OPS[op] if isinstance(op, str) else int(op)
     _check(_lib.acp_tile_reduce(opc, ctypes.byref(dst), ctypes.byref(src), int(threads), _stream(stream)))
+
+
+def acp_stream_reduce_rows(op, out, x: acp_tile_desc, stage_box, stages: int, threads: int, workgroups: int = 0,
+                           stream=None) -> None:
+    opc = OPS[op] if isinstance(op, str) else int(op)
+    sb = (ctypes.c_int32 * len(stage_box))(*stage_box)
+    _check(_lib.acp_stream_reduce_rows(opc, _ptr(out), ctypes.byref(x), sb, int(stages), int(threads),
+                                       int(workgroups), _stream(stream)))
 
 
 STAGING = {"ring": 0, "set": 1}

@@ -95,7 +95,7 @@ struct Launch {
 
 struct EngineRequest {
   int op;                      // acp_op
-  int mode;                    // 0 copy, 1 tile ewise, 2 stream, 3 store with reduce-add
+  int mode;                    // 0 copy, 1 tile ewise, 2 stream, 3 store with reduce-add, 4 row reduction
   const acp::DescData* x;      // layout of every staged operand
   const acp::DescData* out;
   const void* in_ptrs[3];
@@ -186,6 +186,7 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
     // a reduce-add destination of extent 1 along a dim the source spans:
     // every source stage along it adds into the same destination elements
     ostride[d] = (q.mode == 3 && o.shape[d] == 1 && x.shape[d] > 1) ? 0 : o.strides[d] * eo;
+    if (q.mode == 4) ostride[d] = 0;  // row sums are addressed by row index, not by the stage grid
     A.sbox[d] = static_cast<uint32_t>(sb);
     A.nst[d] = static_cast<uint32_t>(nst);
     const int64_t rem = nst ? x.shape[d] - (nst - 1) * sb : sb;
@@ -282,6 +283,7 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
     A.ax_os[k] = static_cast<uint32_t>(axes[k].step * ostride[d]);
     A.ax_rs[k] = d < r - 1 ? static_cast<uint32_t>(axes[k].step * srow[d]) : 0u;
     A.ax_pslot[k] = A.pslot_of_dim[d];
+    if (d == r - 1) A.ax_inner_mask |= 1u << k;
   }
   A.esize_log2 = log2i(ei);
   A.outer = p.outer;
@@ -293,7 +295,8 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   // whole number of such blocks and nothing permutes it
   A.row_uniform = (q.row_ops && A.swizzle == 0 && (axes.back().count * ei) % (64 * p.vec_bytes) == 0) ? 1 : 0;
   L->key = acp::KernelKey{q.op, q.mode == 0 ? ACP_U32 : static_cast<int>(x.dtype),
-                          q.mode == 0 ? ACP_U32 : static_cast<int>(o.dtype), p.vec_bytes, q.mode, 0, 0};
+                          q.mode == 0 ? ACP_U32 : (q.mode == 4 ? ACP_F32 : static_cast<int>(o.dtype)), p.vec_bytes,
+                          q.mode, 0, 0};
   // streaming on a linear grid with 16-byte rounds: the lean kernel
   static const bool fast_ok = env_flag("ACP_FAST_PATH", true);
   if (fast_ok && q.mode == 2 && A.lin && p.vec_bytes == 16 && q.n_in == 1 &&
@@ -307,7 +310,7 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   }
   // any other grid with 16-byte rounds: the general lean kernel
   static const bool gen_ok = env_flag("ACP_GEN_PATH", true);
-  if (gen_ok && L->key.mode <= 3 && p.vec_bytes == 16 &&
+  if (gen_ok && L->key.mode <= 4 && p.vec_bytes == 16 &&
       (p.outer == 1 || p.outer == 2 || p.outer == 4 || p.outer == 8)) {
     acp::KernelKey gk = L->key;
     gk.mode = q.mode + 4;
@@ -350,7 +353,41 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   // lane writes its chunks there and reads the same bytes back before its
   // store, so trips can share it and it costs no ring slot.
   A.out_image_off = static_cast<uint32_t>(slot * A.stages);
-  const int64_t lds = slot * A.stages + out_img;
+  int64_t lds = slot * A.stages + out_img;
+  if (q.mode == 4) {
+    // row reduction: whole rows per stage, partial sums double-buffered after the ring
+    const int64_t row_bytes = x.shape[r - 1] * ei;
+    A.row_chunks = static_cast<uint32_t>(row_bytes / 16);
+    A.red_rows = static_cast<uint32_t>(n_rows);
+    A.part_bytes = static_cast<uint32_t>(n_rows * (row_bytes / 16) * 4);
+    A.part_off = static_cast<uint32_t>(lds);
+    lds += 2 * static_cast<int64_t>(A.part_bytes);
+    for (int d = 0; d + 1 < r; ++d) A.rowstr[d] = static_cast<uint32_t>(rowstride[d]);
+    // Wave-local reduction when every 1 KiB wave block lies in one row and
+    // every row's blocks belong to one wave (block b goes to wave b % waves).
+    auto row_of = [&](int64_t e) {  // stage-packed row of image element e
+      int64_t row = 0;
+      for (size_t k = axes.size(); k-- > 0;) {
+        const int64_t idx = e % axes[k].count;
+        e /= axes[k].count;
+        if (axes[k].dim < r - 1) row += idx * axes[k].step * srow[axes[k].dim];
+      }
+      return row;
+    };
+    bool local = row_bytes % 1024 == 0;
+    std::vector<int> wave_of_row(static_cast<size_t>(n_rows), -1);
+    const int64_t blocks = p.tile_bytes() / 1024;
+    for (int64_t b = 0; local && b < blocks; ++b) {
+      const int64_t r0 = row_of(b * 1024 / ei);
+      for (int c = 1; c < 64 && local; ++c) local = row_of((b * 1024 + c * 16) / ei) == r0;
+      const int w = static_cast<int>(b % A.waves);
+      if (!local || r0 >= n_rows) break;
+      if (wave_of_row[r0] < 0) wave_of_row[r0] = w;
+      else if (wave_of_row[r0] != w) local = false;
+    }
+    static const bool local_ok = env_flag("ACP_REDUCE_LOCAL", true);
+    A.red_local = (local && local_ok) ? 1 : 0;
+  }
   const int limit = device_lds_limit();
   if (lds > limit)
     return ret(ACP_ERR_LDS, "ring needs " + std::to_string(lds) + " bytes of LDS, device allows " +
@@ -716,6 +753,49 @@ acp_status acp_tile_reduce(acp_op op, const acp_tile_desc* dst, const acp_tile_d
   const acp_status st = prepare(q, &L);
   if (st != ACP_OK) return st;
   if (L.key.mode != 7) return ret(ACP_ERR_UNSUPPORTED, "reduce-add needs 16-byte rounds and 1, 2, 4 or 8 rounds per thread");
+  return launch(L, hip_stream);
+}
+
+acp_status acp_stream_reduce_rows(acp_op op, float* out, const acp_tile_desc* x, const int32_t* stage_box, int stages,
+                                  int threads, int workgroups, void* hip_stream) {
+  acp::DescData xd;
+  if (!load_desc(x, &xd)) return ret(ACP_ERR_INVALID, "not an encoded descriptor");
+  if (op != ACP_OP_ADD) return ret(ACP_ERR_INVALID, "rows reduce with add");
+  if (!out) return ret(ACP_ERR_INVALID, "null output");
+  if (!stage_box) return ret(ACP_ERR_INVALID, "null stage box");
+  if (stages < 2 || stages > 4) return ret(ACP_ERR_INVALID, "stages must be 2, 3 or 4");
+  if (workgroups < 0) return ret(ACP_ERR_INVALID, "workgroups must be >= 0");
+  if (xd.dtype != ACP_F32 && xd.dtype != ACP_F16) return ret(ACP_ERR_UNSUPPORTED, "row reduction takes f16 or f32");
+  const int r = xd.rank;
+  if (r < 2) return ret(ACP_ERR_INVALID, "row reduction needs rank >= 2");
+  for (int d = 0; d < r; ++d)
+    if (stage_box[d] < 1) return ret(ACP_ERR_INVALID, "stage box must be >= 1");
+  if (xd.box[r - 1] != xd.shape[r - 1] || stage_box[r - 1] != xd.shape[r - 1])
+    return ret(ACP_ERR_INVALID, "tiles and stages must hold whole rows (innermost box = innermost extent)");
+  int64_t rows = 1;
+  for (int d = 0; d + 1 < r; ++d) rows *= xd.shape[d];
+  if (rows >= (int64_t(1) << 29)) return ret(ACP_ERR_UNSUPPORTED, "too many rows");
+  EngineRequest q{};
+  q.op = ACP_OP_ADD;
+  q.mode = 4;
+  q.x = &xd;
+  q.out = &xd;  // same shape; the output is the packed row array `out`
+  q.in_ptrs[0] = reinterpret_cast<const void*>(xd.gbase);
+  q.n_in = 1;
+  q.stage_box = stage_box;
+  q.stages = stages;
+  q.threads = threads;
+  q.workgroups = workgroups;
+  q.copy_only = false;
+  Launch L;
+  const acp_status st = prepare(q, &L);
+  if (st != ACP_OK) return st;
+  if (L.key.mode != 8)
+    return ret(ACP_ERR_UNSUPPORTED, "row reduction needs 16-byte rounds and 1, 2, 4 or 8 rounds per thread");
+  if (L.args.red_rows > 64u * static_cast<uint32_t>(L.args.waves))
+    return ret(ACP_ERR_UNSUPPORTED, "row reduction stages hold at most 64 rows per wave");
+  L.args.out = reinterpret_cast<char*>(out);
+  L.args.out_span = static_cast<uint64_t>(rows) * 4u;
   return launch(L, hip_stream);
 }
 

@@ -77,6 +77,13 @@ struct EngineArgs {
   // the slot), so tiles that share cache lines at their edges are loaded
   // back to back.  Workgroup w takes tile groups w, w+G, ...
   uint32_t tpt_log2;
+  // Row reduction: the innermost dim's image axes (bit k for axis k), the
+  // 16-byte chunks of one row, rows per stage, the packed row stride of
+  // each outer dim, and the LDS double buffer of per-chunk partial sums.
+  uint32_t ax_inner_mask;
+  uint32_t row_chunks, red_rows, part_off, part_bytes;
+  int32_t red_local;         // every wave block lies in one row and every row in one wave
+  uint32_t rowstr[kDims];
 };
 
 // Which kernel variant a launch needs.
@@ -86,8 +93,8 @@ struct KernelKey {
   int tout;      // acp_dtype of the output
   int vec_bytes; // 16 or 4
   int mode;      // 0 copy, 1 tile ewise (output staged in LDS), 2 stream, 3 stream on a linear grid,
-                 // 4 / 5 / 6 / 7: copy / tile ewise / stream / store with reduce-add in the
-                 // general lean kernel
+                 // 4 / 5 / 6 / 7 / 8: copy / tile ewise / stream / store with reduce-add /
+                 // row reduction in the general lean kernel
   int outer;     // modes 3..6: rounds per thread (1, 2, 4 or 8); 0 otherwise
   int srow;      // modes 3 and 6, row ops: per-row scalars through the scalar cache
   int variant = 0;  // mode 6, add / mul of two streamed tensors: 1 both on the direct-to-LDS

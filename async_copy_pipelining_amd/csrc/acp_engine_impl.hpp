@@ -263,6 +263,45 @@ template <int T> struct ReduceOp {
   }
 };
 
+// Sum over the 64 lanes of a wave in a fixed order, with DPP moves: shift-
+// and-add within each row of 16 lanes (lane 15 of a row ends with the row's
+// sum), then lane 15 of rows 0 and 2 is broadcast into rows 1 and 3, and
+// lane 31 into rows 2 and 3.  Lane 63 holds the total, read as a scalar.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_shift(float v) {
+  // lanes shifted in from outside a row, and rows outside the mask, read 0
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_shift<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_shift<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_shift<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_shift<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_shift<0x142, 0xa>(v);  // row_bcast:15
+  v += dpp_shift<0x143, 0xc>(v);  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Row reduction: the staged elements are summed (in binary32) per row.
+template <int T> struct ReduceRowsOp {
+  typedef typename DType<T>::T TI;
+  typedef float TO;
+  static constexpr int NIN = 1;
+  static constexpr bool ROW = false;
+  static __device__ __forceinline__ TO f(TI x, TI, TI, float, float) { return to_f(x); }
+  // sum of one 16-byte chunk, as a fixed pairwise tree
+  static __device__ __forceinline__ float chunk(u32x4 v) {
+    TI e[16 / sizeof(TI)];
+    __builtin_memcpy(e, &v, 16);
+    if constexpr (sizeof(TI) == 4) {
+      return (to_f(e[0]) + to_f(e[1])) + (to_f(e[2]) + to_f(e[3]));
+    } else {
+      return ((to_f(e[0]) + to_f(e[1])) + (to_f(e[2]) + to_f(e[3]))) +
+             ((to_f(e[4]) + to_f(e[5])) + (to_f(e[6]) + to_f(e[7])));
+    }
+  }
+};
+
 // Streamed x with per-row scalars (binary32): add x + b, mul a * x, fma a * x + b.
 template <int OPC> struct RowOp {
   typedef float TI;
@@ -294,7 +333,7 @@ struct LaneMap {
 // from the stage origin, its stage row (row ops) and the partial slots along
 // which it lies past the edge.
 struct ByteMap {
-  uint32_t lb, xo, oo, row, ob;
+  uint32_t lb, xo, oo, row, ob, col;  // col: coordinate along the innermost dim (elements)
 };
 
 __device__ __forceinline__ ByteMap map_byte(CArgs* A, uint32_t pb, int n_axes, int swz_mask, int es_log2) {
@@ -305,6 +344,8 @@ __device__ __forceinline__ ByteMap map_byte(CArgs* A, uint32_t pb, int n_axes, i
   r.xo = sub_byte;
   r.oo = sub_byte;
   r.row = 0;
+  r.col = 0;
+  const uint32_t inner = A->ax_inner_mask;
   uint32_t rel[kPartial] = {0, 0, 0, 0};
 #pragma nounroll
   for (int k = n_axes - 1; k >= 0; --k) {
@@ -314,6 +355,7 @@ __device__ __forceinline__ ByteMap map_byte(CArgs* A, uint32_t pb, int n_axes, i
     r.xo += idx * A->ax_xs[k];
     r.oo += idx * A->ax_os[k];
     r.row += idx * A->ax_rs[k];
+    if ((inner >> k) & 1u) r.col += idx * A->ax_step[k];
     const int ps = A->ax_pslot[k];
 #pragma unroll
     for (int s2 = 0; s2 < kPartial; ++s2)
@@ -928,6 +970,15 @@ struct GenPolicy {
   uint64_t in_span, out_span, total_rows;
   uint32_t lds0, slot_bytes, in_image_bytes, out_image_off, ab_base, waves_kb, wg, grid, tile0, subs, subs_mag, subs_sh;
   uint32_t tpt_log2, tile_lds;  // tiles per trip (log2) and LDS bytes of one tile's images in a slot
+  // row reduction (MODE 4): each round's partial-sum index (row * row_chunks
+  // + chunk of the row), and the reduction geometry
+  uint32_t pidx[OUTER];
+  uint32_t row_chunks, red_rows, part_off, part_bytes, waves;
+  uint32_t red_off, red_bad;  // lane k: packed-row offset and cut-edge slots of the wave's k-th row
+  // wave-local rows: lane k holds the wave's k-th distinct row (in round
+  // order; ~0 for none), its packed-row offset and cut-edge slots
+  bool red_local;
+  uint32_t lrow, loff, lbad;
   int wave, lane, rank, ab_instr, swizzle, esize_log2;
   bool load_nt, store_nt;
   uint32_t xoff[OUTER], ooff[OUTER], oobm[OUTER], lpos[OUTER], abo[OUTER];
@@ -1080,6 +1131,67 @@ struct GenPolicy {
     }
   }
 
+  // Row reduction of one staged trip.  Each lane sums its chunks and puts
+  // the partials into LDS at (row, chunk of the row); after a workgroup
+  // barrier each wave reduces whole rows: lane-strided sums over the row's
+  // chunks, then a DPP sum across the 64 lanes, in a fixed order.  Lane 0
+  // stores the row's sum.  Partials alternate between two buffers, so the
+  // next trip's writes never meet this trip's reads (every wave passes the
+  // next barrier only after finishing them).
+  // Rows that a single wave holds entirely (each 1 KiB wave block inside one
+  // row): the wave sums each block (chunk sums, then a DPP sum over the 64
+  // lanes); lane k accumulates the blocks of the wave's k-th row in round
+  // order, and one store instruction writes every row total of the trip.
+  // No other wave is involved, so there is no barrier.
+  __device__ __forceinline__ void reduce_rows_local(uint32_t sl, const T& t, __amdgpu_buffer_rsrc_t rs) {
+    float acc = 0.f;
+#pragma unroll
+    for (int f = 0; f < OUTER; ++f) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(
+          __builtin_assume_aligned(lds + sl + f * waves_kb + wave * 1024u + lane * 16u, 16));
+      const float s = wave_sum(OP::chunk(v));
+      acc += (lrow == row_of[f]) ? s : 0.f;
+    }
+    const bool ok = (t.flags & 0x100u) == 0 && lrow != ~0u && (lbad & t.flags & 0xFFu) == 0;
+    const uint64_t g = t.rb + loff;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc), rs,
+                                          ok ? static_cast<uint32_t>(g * 4u) : kOobOffset, 0, 0);
+  }
+
+  __device__ __forceinline__ void reduce_rows_trip(int i, uint32_t sl, const T& t, __amdgpu_buffer_rsrc_t rs) {
+    if (red_local) {
+      reduce_rows_local(sl, t, rs);
+      return;
+    }
+    const uint32_t buf = part_off + (static_cast<uint32_t>(i) & 1u) * part_bytes;
+#pragma unroll
+    for (int f = 0; f < OUTER; ++f) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(
+          __builtin_assume_aligned(lds + sl + f * waves_kb + wave * 1024u + lane * 16u, 16));
+      *reinterpret_cast<float*>(lds + buf + pidx[f] * 4u) = OP::chunk(v);
+    }
+    // only LDS traffic is waited for: the ring's loads stay in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const bool beyond = (t.flags & 0x100u) != 0;
+    const uint32_t last = t.flags & 0xFFu;
+    uint32_t k = 0;
+#pragma nounroll
+    for (uint32_t r = static_cast<uint32_t>(wave); r < red_rows; r += waves, ++k) {
+      float acc = 0.f;
+      for (uint32_t c = static_cast<uint32_t>(lane); c < row_chunks; c += 64u)
+        acc += *reinterpret_cast<const float*>(lds + buf + (r * row_chunks + c) * 4u);
+      acc = wave_sum(acc);
+      // the row's place in the tensor and the cut edges it lies past (lane k
+      // of the wave holds them for the wave's k-th row)
+      const uint32_t roff = rdl(red_off, k), rbad = rdl(red_bad, k);
+      const bool ok = !beyond && (rbad & last) == 0;
+      const uint64_t g = t.rb + roff;
+      if (lane == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc), rs,
+                                              ok ? static_cast<uint32_t>(g * 4u) : kOobOffset, 0, 0);
+    }
+  }
+
   __device__ __forceinline__ void consume(int i, int slot) {
     const int e0 = i << tpt_log2;
 #pragma nounroll
@@ -1096,6 +1208,10 @@ struct GenPolicy {
     const __amdgpu_buffer_rsrc_t rs = rsrc_store(out + t.ob, range_from(out_span, t.ob));
     if constexpr (SPLIT) {
       consume_pieces(rs, sl, beyond, last);
+      return;
+    }
+    if constexpr (MODE == 4) {
+      reduce_rows_trip(i, sl, t, rs);
       return;
     }
     if constexpr (MODE == 3) {
@@ -1243,12 +1359,73 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   }
   if constexpr (GenPolicy<OP, MODE, OUTER, SROW, ZSET>::SPLIT)
     build_pieces(A, wave, lane, OUTER, p.pooff, p.poobm, p.plpos);
+  int red_stores = 0;  // row reduction: rows this wave stores per trip
+  if constexpr (MODE == 4) {
+    p.row_chunks = uni(A->row_chunks);
+    p.red_rows = uni(A->red_rows);
+    p.part_off = uni(A->part_off);
+    p.part_bytes = uni(A->part_bytes);
+    p.waves = static_cast<uint32_t>(L.waves);
+    const int n_axes = uni(A->n_axes), swz_mask = uni(A->swizzle), es_log2 = uni(A->esize_log2);
+#pragma unroll
+    for (int f = 0; f < OUTER; ++f) {
+      const ByteMap b = map_byte(A, ((f * L.waves + wave) * 64u + lane) * 16u, n_axes, swz_mask, es_log2);
+      p.pidx[f] = b.row * p.row_chunks + ((b.col << es_log2) >> 4);
+    }
+    red_stores = static_cast<uint32_t>(wave) < p.red_rows
+                     ? static_cast<int>((p.red_rows - wave + p.waves - 1) / p.waves) : 0;
+    // lane k: the wave's k-th row r = wave + k * waves of a stage (at most
+    // 64 per wave): its packed-row offset from the stage's first row and the
+    // partial slots along which it lies past the edge of a cut stage
+    const uint32_t r = static_cast<uint32_t>(wave) + static_cast<uint32_t>(lane) * p.waves;
+    uint32_t rr = r < p.red_rows ? r : 0u, off = 0, bad = 0;
+    for (int dd = p.rank - 2; dd >= 0; --dd) {
+      const uint32_t sb = A->sbox[dd];
+      const uint32_t rel = rr % sb;
+      rr /= sb;
+      off += rel * A->rowstr[dd];
+      const int ps = A->pslot_of_dim[dd];
+      if (ps >= 0 && rel >= A->prem[ps]) bad |= 1u << ps;
+    }
+    p.red_off = off;
+    p.red_bad = bad;
+    p.red_local = uni(A->red_local) != 0;
+    p.lrow = ~0u;
+    p.loff = p.lbad = 0;
+    if (p.red_local) {
+      // the wave's distinct block rows in round order; lane k takes the k-th
+      uint32_t n_local = 0;
+#pragma unroll
+      for (int f = 0; f < OUTER; ++f) {
+        bool seen = false;
+#pragma unroll
+        for (int g = 0; g < f; ++g) seen = seen || (p.row_of[g] == p.row_of[f]);
+        if (!seen) {
+          if (static_cast<uint32_t>(lane) == n_local) p.lrow = p.row_of[f];
+          ++n_local;
+        }
+      }
+      uint32_t rr2 = p.lrow != ~0u ? p.lrow : 0u, off2 = 0, bad2 = 0;
+      for (int dd = p.rank - 2; dd >= 0; --dd) {
+        const uint32_t sb = A->sbox[dd];
+        const uint32_t rel = rr2 % sb;
+        rr2 /= sb;
+        off2 += rel * A->rowstr[dd];
+        const int ps = A->pslot_of_dim[dd];
+        if (ps >= 0 && rel >= A->prem[ps]) bad2 |= 1u << ps;
+      }
+      p.loff = off2;
+      p.lbad = bad2;
+      red_stores = 1;  // one store instruction per trip
+    }
+  }
   p.tab1 = TripRow{0, 0, 0, 0, 0, 0};
   p.fill(0, 0u);
   typedef ChunkShape<OP, 16> CS;
   constexpr int NS = GenPolicy<OP, MODE, OUTER, SROW, ZSET>::NS;
   const int d = (NS * OUTER + ((OP::ROW && !SROW) ? L.ab_instr : 0)) << tpt_log2;
-  run_ring(p, n, uni(A->stages), d, (OUTER * (MODE == 3 ? 4 : CS::ST)) << tpt_log2);
+  const int st = MODE == 4 ? red_stores : OUTER * (MODE == 3 ? 4 : CS::ST);
+  run_ring(p, n, uni(A->stages), d, st << tpt_log2);
 }
 
 }  // namespace dev

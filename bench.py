@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4", choices=["c2", "c3", "c4", "c5", "calib", "copy_ref", "pointwise", "reduce"],
+    ap.add_argument("--workload", default="c4", choices=["c2", "c3", "c4", "c5", "calib", "copy_ref", "pointwise", "reduce", "rowsum"],
                     help="c4: the streamed fma (default); c2/c3/c5: the other workloads; "
                          "calib: torch's copy of 256 MiB, the known-size kernel that scales HBM counters; "
                          "copy_ref: the library's register-path reference copy of the c4 tensor "
@@ -203,6 +203,24 @@ def main():
         config = {"workload": f"store with reduce-add, [128,500,1024] f32 tiles (1,{args.rows},1024) into "
                               f"{list(dshape)}"}
         key = f"tile_reduce_f32_128x500x1024_r{args.rows}_{'batch' if args.reduce_over_batch else 'slab'}"
+    elif wl == "rowsum":
+        # y[i, j] = sum over k of x[i, j, k], [128,500,1024] f32 -> [128,500]
+        shape = (128, 500, 1024)
+        stage = (1, args.rows, 1024)
+        rng = np.random.default_rng(8)
+        x = rng.standard_normal(shape, dtype=np.float32)
+        G = args.workgroups or 256 * args.wg_per_cu
+        for s in range(args.sets):
+            xd = to_dev(x)
+            yd = torch.empty(128 * 500 * 4, dtype=torch.uint8, device=dev)
+            xdesc = acp.acp_encode_tiled("f32", xd, shape, packed(shape), stage)
+            launches.append(lambda xdesc=xdesc, keep=(xd, yd):
+                            acp.acp_stream_reduce_rows("add", keep[1], xdesc, stage, args.stages, args.threads, G,
+                                                       stream))
+        bytes_per, dtype = x.nbytes + 128 * 500 * 4, "f32"
+        config = {"workload": f"row sums of [128,500,1024] f32 -> [128,500], {args.stages}-stage LDS ring, "
+                              f"stage (1,{args.rows},1024)", "workgroups": G}
+        key = f"stream_rowsum_f32_128x500x1024_s{args.stages}_r{args.rows}"
     elif wl == "copy_ref":
         n = 128 * 500 * 1024 * 4
         G = args.workgroups or 256 * args.wg_per_cu

@@ -224,6 +224,25 @@ acp_status acp_stream_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_
 acp_status acp_tile_reduce(acp_op op, const acp_tile_desc* dst, const acp_tile_desc* src, int threads,
                            void* hip_stream);
 
+/* Row reduction over ring-staged tiles ([cb] "Testing Setup": the
+ * Reduction and InnerPersistent schedules; a stage may need several loads):
+ * out[row] = sum of x[row, :] over the innermost dim, every row of x.
+ *   op          ACP_OP_ADD
+ *   out         device float32 array over x's outer dims (shape[:-1],
+ *               packed row-major), written (not accumulated)
+ *   x           float16 or float32, rank >= 2; its box and `stage_box` hold
+ *               whole rows (innermost box = innermost extent)
+ *   stages      2..4; workgroups as for acp_stream_ewise
+ * Each lane sums its 16-byte chunks (fixed pairwise order, binary32), the
+ * chunk partials go through LDS, and after a workgroup barrier each wave
+ * reduces whole rows (lane-strided sums, then a 64-lane butterfly).  The
+ * order is fixed, so results are deterministic; their error against the
+ * exact sum is within the recursive-summation bound for the row length.
+ * ACP_ERR_UNSUPPORTED unless the plan has 16-byte rounds and 1, 2, 4 or 8
+ * rounds per thread. */
+acp_status acp_stream_reduce_rows(acp_op op, float* out, const acp_tile_desc* x, const int32_t* stage_box, int stages,
+                                  int threads, int workgroups, void* hip_stream);
+
 /* How the second tensor of a two-tensor stream reaches its ring slot
  * ([cb] "Testing Setup", Pointwise: one tensor on the asynchronous ring,
  * the other "Set", i.e. loaded by ordinary loads and stored into the

@@ -225,3 +225,58 @@ def test_two_tensor_stream_full_size_sampled(staging):
     ref = REF.ewise("add", [x[i0, i1], z[i0, i1]], np.float32)
     assert np.array_equal(y[i0, i1].view(np.uint32), ref.view(np.uint32))
     assert not np.any(y.view(np.uint32) == 0xA5A5A5A5)
+
+
+def _reduce_rows_case(dt, shape, box, stage_box, stages, threads, workgroups, ints=False, swz=0, pitch=None, seed=61):
+    npdt = {"f16": np.float16, "f32": np.float32}[dt]
+    rng = np.random.default_rng(seed)
+    if ints:
+        x = rng.integers(-50, 51, size=shape).astype(npdt)
+    else:
+        x = (rng.standard_normal(shape) * 4).astype(npdt)
+    st = packed_strides(shape)
+    if pitch:                                   # padded rows
+        store = np.zeros(shape[:-1] + (pitch,), npdt)
+        store[..., :shape[-1]] = x
+        xd = dev(store)
+        st = packed_strides(shape[:-1] + (pitch,))
+    else:
+        xd = dev(x)
+    rows = int(np.prod(shape[:-1]))
+    yd = empty_bytes(rows * 4 + 64)
+    xdesc = encode(dt, xd, shape, st, box, swz)
+    acp.acp_stream_reduce_rows("add", yd, xdesc, stage_box, stages, threads, workgroups, stream())
+    y = host(yd, np.float32)
+    assert np.all(y.view(np.uint8)[rows * 4:] == 0xA5)          # nothing written past the rows
+    return x, y[:rows].reshape(shape[:-1])
+
+
+def _assert_within_sum_bound(x, y):
+    ref = REF.reduce_rows(x).astype(np.float64)
+    bound = REF.recursive_sum_bound(x, x.shape[-1] - 1) + np.spacing(np.abs(ref.astype(np.float32))).astype(np.float64)
+    err = np.abs(y.astype(np.float64) - ref)
+    assert np.all(err <= bound), float((err - bound).max())
+
+
+@pytest.mark.parametrize("dt,shape,box,stage_box,stages,threads,workgroups,swz,pitch", [
+    ("f32", (3, 37, 1024), (1, 12, 1024), (1, 4, 1024), 4, 256, 0, 0, None),   # 4 loads per stage, cut stage
+    ("f32", (3, 37, 1024), (1, 4, 1024), (1, 4, 1024), 2, 256, 5, 0, None),    # persistent, uneven
+    ("f16", (2, 70, 256), (1, 8, 256), (1, 8, 256), 3, 64, 5, 3, None),        # swizzled f16, 8 rows per stage
+    ("f32", (5, 64, 64), (1, 16, 64), (1, 16, 64), 4, 64, 0, 0, None),         # 16 rows per wave block
+    ("f32", (4, 33, 96), (1, 8, 96), (1, 8, 96), 3, 192, 0, 0, 104),           # padded rows, 6 chunks per row, 3 waves
+])
+def test_row_reduction_matches_oracle(dt, shape, box, stage_box, stages, threads, workgroups, swz, pitch):
+    say(f"row reduction {dt} {shape} box {box} stage {stage_box} S={stages} wg={workgroups} swz {swz} pitch {pitch}")
+    # integer inputs: every partial sum exact, so the result is the exact sum
+    x, y = _reduce_rows_case(dt, shape, box, stage_box, stages, threads, workgroups, True, swz, pitch)
+    assert np.array_equal(y, REF.reduce_rows(x))
+    # real-valued inputs: within the recursive-summation bound of the exact sum
+    x, y = _reduce_rows_case(dt, shape, box, stage_box, stages, threads, workgroups, False, swz, pitch, seed=62)
+    _assert_within_sum_bound(x, y)
+
+
+def test_row_reduction_full_size():
+    shape, stage_box = (128, 500, 1024), (1, 2, 1024)
+    say(f"row reduction f32 {shape} stage {stage_box} S=4, 256 workgroups")
+    x, y = _reduce_rows_case("f32", shape, stage_box, stage_box, 4, 256, 256, False, seed=63)
+    _assert_within_sum_bound(x, y)
