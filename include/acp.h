@@ -165,7 +165,10 @@ acp_status acp_plan_query(const acp_tile_desc* desc, int threads, int copy_only,
 /* Copy every tile of `src` to the same coordinates of `dst` through LDS:
  * direct-to-LDS loads (16 or 4 bytes per lane, swizzled per `src`), a
  * per-wave completion wait, then LDS reads and coalesced stores
- * ([tma] and [ldgsts] "Demonstration program").  One workgroup per tile.
+ * ([tma] and [ldgsts] "Demonstration program").  One workgroup per tile
+ * while the tiles fit one grid of one workgroup per CU; beyond that a
+ * persistent grid (one workgroup per CU, environment ACP_TILE_WG_PER_CU)
+ * walks tiles w, w+G, ... through a 2-slot ring (ACP_TILE_STAGES).
  * `src` and `dst` must have equal dtype, shape and box ([tma]
  * validate_copy_op); `dst` may have other strides.  Overlapping src/dst
  * memory is not supported. */
@@ -177,7 +180,9 @@ acp_status acp_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, int
  * ([smem]).  n_in: ZERO 0 or 1, SQRT/EXP 1, ADD/MUL 2, FMA 3.  All inputs
  * share dtype, shape, strides, box and swizzle (one anchor layout); `out`
  * has the same shape and box.  Types: SQRT/EXP f16|f32 -> f16|f32;
- * ADD/MUL/FMA inputs and output one of f16|f32; ZERO -> f16|f32. */
+ * ADD/MUL/FMA inputs and output one of f16|f32; ZERO -> f16|f32.  Large
+ * tile counts run on a persistent grid whose ring trips stage 1, 2 or 4
+ * consecutive tiles (about 16 KiB per trip; ACP_TILES_PER_TRIP). */
 acp_status acp_tile_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_desc* const* in,
                           int n_in, int threads, void* hip_stream);
 
