@@ -108,6 +108,8 @@ struct EngineRequest {
   bool copy_only;
   int tiles_per_trip = 1;      // tile ops on a persistent grid: 1, 2 or 4
   int binary = 0;              // stream of two tensors: 1 both on the ring, 2 the second one "Set"
+  int64_t red_group = 0;       // reduce-add over batch dims: contributions per destination tile
+  int64_t red_per_wg = 0;      // ... and tiles per workgroup (a multiple of red_group)
 };
 
 acp_status prepare(const EngineRequest& q, Launch* L) {
@@ -317,7 +319,7 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
     gk.outer = p.outer;
     static const bool srow_ok = env_flag("ACP_SCALAR_ROWS", true);
     gk.srow = (q.mode == 2 && A.row_uniform && srow_ok) ? 1 : 0;
-    gk.variant = q.binary;
+    gk.variant = q.mode == 3 ? (q.red_group > 0 ? 1 : 0) : q.binary;
     if (acp::engine_kernel(gk)) L->key = gk;
   }
   if (q.binary && L->key.variant != q.binary) {
@@ -393,6 +395,33 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
     return ret(ACP_ERR_LDS, "ring needs " + std::to_string(lds) + " bytes of LDS, device allows " +
                                 std::to_string(limit));
 
+  if (q.mode == 3 && q.red_group > 0) {
+    // List the summed dims last (fastest) in the per-dim tile arrays, so
+    // that consecutive tiles are the contributions to one destination tile;
+    // workgroups take contiguous runs of whole groups.
+    int order[acp::kDims], n = 0;
+    for (int d = 0; d < r; ++d)
+      if (!(o.shape[d] == 1 && x.shape[d] > 1)) order[n++] = d;
+    for (int d = 0; d < r; ++d)
+      if (o.shape[d] == 1 && x.shape[d] > 1) order[n++] = d;
+    const acp::EngineArgs B = A;
+    for (int k = 0; k < r; ++k) {
+      const int d = order[k];
+      A.tgrid[k] = B.tgrid[d];
+      A.tg_mag[k] = B.tg_mag[d];
+      A.tg_sh[k] = B.tg_sh[d];
+      A.sub[k] = B.sub[d];
+      A.sub_mag[k] = B.sub_mag[d];
+      A.sub_sh[k] = B.sub_sh[d];
+      A.nst[k] = B.nst[d];
+      A.pslot_of_dim[k] = B.pslot_of_dim[d];
+      A.xstep[k] = B.xstep[d];
+      A.ostep[k] = B.ostep[d];
+      A.rstep[k] = B.rstep[d];
+    }
+    A.red_group = static_cast<uint32_t>(q.red_group);
+    A.per_wg = static_cast<uint32_t>(q.red_per_wg);
+  }
   unsigned grid = static_cast<unsigned>(n_tiles);
   if (q.workgroups > 0) grid = static_cast<unsigned>(q.workgroups);
   // consecutive tiles (which often share cache lines at their edges) run on
@@ -744,10 +773,35 @@ acp_status acp_tile_reduce(acp_op op, const acp_tile_desc* dst, const acp_tile_d
   {
     acp::Plan p;
     std::string why;
-    if (acp::plan_box(s, false, &p, &why) == acp::PlanStatus::Ok)
+    if (acp::plan_box(s, false, &p, &why) == acp::PlanStatus::Ok) {
       tile_schedule(p, 1, threads, 0, &q.workgroups, &q.stages, &q.tiles_per_trip);
-    else
+      // Sums over batch dims: each workgroup owns whole destination tiles,
+      // sums their contributions in registers and adds once per element.
+      int64_t group = 1;
+      for (int k = 0; k < s.rank; ++k)
+        if (d.shape[k] == 1 && s.shape[k] > 1) group *= s.shape[k];
+      static const bool grouped_ok = env_flag("ACP_REDUCE_GROUPED", true);
+      const int64_t n_tiles = p.n_tiles();
+      if (grouped_ok && group > 1 && n_tiles > 0) {
+        const int64_t dst_tiles = n_tiles / group;
+        const int64_t want = static_cast<int64_t>(device_cu_count()) * 4;
+        // few destination tiles: split each one's contributions over k
+        // workgroups (k atomic adds per element instead of one)
+        int64_t k = 1;
+        while (dst_tiles * k * 2 <= want && group % (k * 2) == 0) k *= 2;
+        const int64_t sub = group / k;                 // contributions summed per workgroup group
+        const int64_t groups = dst_tiles * k;
+        const int64_t g = std::min<int64_t>(groups, want);
+        const int64_t per = (groups + g - 1) / g;      // groups per workgroup
+        q.red_group = sub;
+        q.red_per_wg = per * sub;
+        q.workgroups = static_cast<int>((groups + per - 1) / per);
+        q.stages = 2;
+        q.tiles_per_trip = 1;
+      }
+    } else {
       q.stages = 1;
+    }
   }
   Launch L;
   const acp_status st = prepare(q, &L);

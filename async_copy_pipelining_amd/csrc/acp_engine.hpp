@@ -83,6 +83,12 @@ struct EngineArgs {
   uint32_t ax_inner_mask;
   uint32_t row_chunks, red_rows, part_off, part_bytes;
   int32_t red_local;         // every wave block lies in one row and every row in one wave
+  // Store with reduce-add over batch dims: workgroup w takes the contiguous
+  // tiles w * per_wg ... (the per-dim tile arrays list the summed dims
+  // last, so consecutive tiles are the red_group contributions to one
+  // destination tile); the contributions are summed in registers and added
+  // to the destination once per group.  0: round-robin tiles, no grouping.
+  uint32_t per_wg, red_group;
   uint32_t rowstr[kDims];
 };
 

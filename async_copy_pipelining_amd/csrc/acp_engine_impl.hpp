@@ -44,6 +44,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef const EngineArgs __attribute__((address_space(4))) CArgs;
 
 constexpr int kOpZero = 0, kOpSqrt = 1, kOpExp = 2, kOpAdd = 3, kOpMul = 4, kOpFma = 5, kOpCopy = 6;
@@ -247,12 +248,62 @@ template <> struct Op<kOpFma, kF16, kF16> {
 // Store with reduce-add: the staged elements are added into the destination
 // with no-return buffer atomics (32-bit integer add, binary32 add, packed
 // binary16 pair add), 4 per 16-byte chunk.
+// Running sums of a store with reduce-add: u32 and f32 chunks sum in their
+// own type; f16 chunks sum in binary32 (8 lanes of a float vector) and are
+// rounded once when the group is added to the destination.
+struct Acc4 {
+  uint32_t w[4];
+};
+struct Acc8 {
+  float v[8];
+};
+template <int T> struct ReduceOp;
+template <class OP, int MODE> struct AccOf { typedef Acc4 T; };
+template <int MODE> struct AccOf<ReduceOp<kF16>, MODE> { typedef Acc8 T; };
+
 template <int T> struct ReduceOp {
   typedef typename DType<T>::T TI;
   typedef TI TO;
   static constexpr int NIN = 1;
   static constexpr bool ROW = false;
   static __device__ __forceinline__ TO f(TI x, TI, TI, float, float) { return x; }
+  typedef typename AccOf<ReduceOp<T>, 3>::T Acc;
+  static __device__ __forceinline__ Acc zero_acc() { return Acc{}; }
+  static __device__ __forceinline__ Acc accumulate(Acc a, u32x4 v) {
+    if constexpr (T == kU32) {
+      a.w[0] += v.x;
+      a.w[1] += v.y;
+      a.w[2] += v.z;
+      a.w[3] += v.w;
+    } else if constexpr (T == kF32) {
+      // through memcpy: a bit cast of a vector element (v.y) was compiled
+      // as a cast of element 0
+      float x[4], s[4];
+      __builtin_memcpy(x, &v, 16);
+      __builtin_memcpy(s, a.w, 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] += x[e];
+      __builtin_memcpy(a.w, s, 16);
+    } else {
+      _Float16 h[8];
+      __builtin_memcpy(h, &v, 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a.v[e] += static_cast<float>(h[e]);
+    }
+    return a;
+  }
+  static __device__ __forceinline__ u32x4 finish(Acc a) {
+    if constexpr (T == kF16) {
+      _Float16 h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(a.v[e]);
+      u32x4 w;
+      __builtin_memcpy(&w, h, 16);
+      return w;
+    } else {
+      return u32x4{a.w[0], a.w[1], a.w[2], a.w[3]};
+    }
+  }
   static __device__ __forceinline__ void add(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t w) {
     if constexpr (T == kF32)
       __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(__builtin_bit_cast(float, w), rs, voff, 0, 0);
@@ -917,7 +968,9 @@ __device__ __forceinline__ TripRow trip_lane(CArgs* A, uint32_t wg, uint32_t gri
                                              uint32_t j) {
   const uint32_t tl = mdiv(j, subs_mag, subs_sh);
   uint32_t sub = j - tl * subs;
-  uint32_t tile = tile0 + (((wg + (tl >> tpt_log2) * grid) << tpt_log2) | (tl & ((1u << tpt_log2) - 1u)));
+  const uint32_t per_wg = A->per_wg;
+  uint32_t tile = per_wg ? tile0 + wg * per_wg + tl
+                         : tile0 + (((wg + (tl >> tpt_log2) * grid) << tpt_log2) | (tl & ((1u << tpt_log2) - 1u)));
   uint64_t xb = 0, ob = 0, rb = 0;
   uint32_t flags = 0;
   // rolled: the per-dim parameters are read on each refill (once per 64
@@ -949,7 +1002,7 @@ __device__ __forceinline__ uint32_t rdl(uint32_t v, uint32_t lane) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), static_cast<int>(lane)));
 }
 
-template <class OP, int MODE, int OUTER, bool SROW, int ZSET = 0>
+template <class OP, int MODE, int OUTER, bool SROW, int ZSET = 0, bool GROUP = false>
 struct GenPolicy {
   static constexpr bool STAGE_OUT = (MODE == 1);
   // staged operands: every input of a tile op or of a two-tensor stream op;
@@ -975,6 +1028,10 @@ struct GenPolicy {
   uint32_t pidx[OUTER];
   uint32_t row_chunks, red_rows, part_off, part_bytes, waves;
   uint32_t red_off, red_bad;  // lane k: packed-row offset and cut-edge slots of the wave's k-th row
+  // store with reduce-add over batch dims: trips per destination tile, the
+  // trips summed so far and the lane's running sums
+  uint32_t red_group, rcount;
+  typename AccOf<OP, MODE>::T racc[GROUP ? OUTER : 1];
   // wave-local rows: lane k holds the wave's k-th distinct row (in round
   // order; ~0 for none), its packed-row offset and cut-edge slots
   bool red_local;
@@ -1215,6 +1272,32 @@ struct GenPolicy {
       return;
     }
     if constexpr (MODE == 3) {
+      if constexpr (GROUP) {
+        // sum the group's contributions in registers; the group's last trip
+        // adds the sums into the destination (past-the-end chunks were
+        // staged as zeros and add nothing)
+#pragma unroll
+        for (int f = 0; f < OUTER; ++f) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(
+              __builtin_assume_aligned(lds + sl + f * waves_kb + wave * 1024u + lane * 16u, 16));
+          racc[f] = OP::accumulate(racc[f], v);
+        }
+        if (++rcount == red_group) {
+          rcount = 0;
+#pragma unroll
+          for (int f = 0; f < OUTER; ++f) {
+            const bool ok = !beyond && (oobm[f] & last) == 0;
+            const uint32_t o = ok ? ooff[f] : kOobOffset;
+            const u32x4 w = OP::finish(racc[f]);
+            OP::add(rs, o, w.x);
+            OP::add(rs, o + 4u, w.y);
+            OP::add(rs, o + 8u, w.z);
+            OP::add(rs, o + 12u, w.w);
+            racc[f] = OP::zero_acc();
+          }
+        }
+        return;
+      }
       // store with reduce-add: four 4-byte atomics per staged chunk
 #pragma unroll
       for (int f = 0; f < OUTER; ++f) {
@@ -1290,7 +1373,7 @@ struct GenPolicy {
   }
 };
 
-template <class OP, int MODE, int OUTER, bool SROW, int ZSET = 0>
+template <class OP, int MODE, int OUTER, bool SROW, int ZSET = 0, bool GROUP = false>
 __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
   CArgs* A = kargs();
@@ -1301,7 +1384,10 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   if (A->xcd_remap) wg = (wg & 7u) * (grid >> 3) + (wg >> 3);
   const uint32_t tpt_log2 = uni(A->tpt_log2);
   const uint32_t groups = (A->n_tiles + (1u << tpt_log2) - 1u) >> tpt_log2;
-  const uint32_t mine = wg < groups ? (groups - wg + grid - 1) / grid : 0;
+  const uint32_t per_wg = uni(A->per_wg);
+  const uint32_t first = wg * per_wg;
+  const uint32_t mine = per_wg ? (first < A->n_tiles ? min(per_wg, A->n_tiles - first) : 0u)
+                               : (wg < groups ? (groups - wg + grid - 1) / grid : 0);
   const int n = static_cast<int>(mine * A->subs);  // ring trips
   if (n == 0) return;
   LaneMap m;
@@ -1310,7 +1396,7 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   uint32_t row_bad[2] = {~0u, ~0u};
   if constexpr (OP::ROW && !SROW) build_rows(A, lane, row_ptr, row_bad);
   const Loc L = load_loc(A);
-  GenPolicy<OP, MODE, OUTER, SROW, ZSET> p;
+  GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP> p;
   p.tpt_log2 = tpt_log2;
   p.tile_lds = L.slot_bytes >> tpt_log2;
   p.A = A;
@@ -1357,8 +1443,14 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
     p.row_of[f] = (abo >> 8) * 32u + (abo & 255u) / 4u;
     p.sa[f] = p.sb[f] = 0.f;
   }
-  if constexpr (GenPolicy<OP, MODE, OUTER, SROW, ZSET>::SPLIT)
+  if constexpr (GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP>::SPLIT)
     build_pieces(A, wave, lane, OUTER, p.pooff, p.poobm, p.plpos);
+  if constexpr (GROUP) {
+    p.red_group = uni(A->red_group);
+    p.rcount = 0;
+#pragma unroll
+    for (int f = 0; f < OUTER; ++f) p.racc[f] = OP::zero_acc();
+  }
   int red_stores = 0;  // row reduction: rows this wave stores per trip
   if constexpr (MODE == 4) {
     p.row_chunks = uni(A->row_chunks);
@@ -1422,9 +1514,11 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   p.tab1 = TripRow{0, 0, 0, 0, 0, 0};
   p.fill(0, 0u);
   typedef ChunkShape<OP, 16> CS;
-  constexpr int NS = GenPolicy<OP, MODE, OUTER, SROW, ZSET>::NS;
+  constexpr int NS = GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP>::NS;
   const int d = (NS * OUTER + ((OP::ROW && !SROW) ? L.ab_instr : 0)) << tpt_log2;
-  const int st = MODE == 4 ? red_stores : OUTER * (MODE == 3 ? 4 : CS::ST);
+  // grouped reduce-add stores only on a group's last trip: counting none
+  // per trip only makes the waits stronger
+  const int st = MODE == 4 ? red_stores : (MODE == 3 ? (GROUP ? 0 : OUTER * 4) : OUTER * CS::ST);
   run_ring(p, n, uni(A->stages), d, st << tpt_log2);
 }
 
@@ -1464,6 +1558,12 @@ struct KernelEntry {
   ACP_GB1(OPC, T, 1, 1, __VA_ARGS__), ACP_GB1(OPC, T, 2, 1, __VA_ARGS__), ACP_GB1(OPC, T, 4, 1, __VA_ARGS__), \
       ACP_GB1(OPC, T, 8, 1, __VA_ARGS__), ACP_GB1(OPC, T, 1, 2, __VA_ARGS__), ACP_GB1(OPC, T, 2, 2, __VA_ARGS__), \
       ACP_GB1(OPC, T, 4, 2, __VA_ARGS__), ACP_GB1(OPC, T, 8, 2, __VA_ARGS__)
+// store with reduce-add summing batch dims in registers (mode key 7, variant 1)
+#define ACP_GG1(OPC, T, OUTER, ...)                       \
+  KernelEntry{KernelKey{OPC, T, T, 16, 7, OUTER, 0, 1}, \
+              reinterpret_cast<const void*>(&dev::gen_kernel_t<__VA_ARGS__, 3, OUTER, false, 0, true>)}
+#define ACP_GEN_GROUP(OPC, T, ...) \
+  ACP_GG1(OPC, T, 1, __VA_ARGS__), ACP_GG1(OPC, T, 2, __VA_ARGS__), ACP_GG1(OPC, T, 4, __VA_ARGS__), ACP_GG1(OPC, T, 8, __VA_ARGS__)
 #define ACP_LIN_ROW(OPC, ...)                                                                              \
   ACP_LIN(OPC, kF32, kF32, __VA_ARGS__), ACP_L(OPC, kF32, kF32, 1, 1, __VA_ARGS__),                          \
       ACP_L(OPC, kF32, kF32, 2, 1, __VA_ARGS__), ACP_L(OPC, kF32, kF32, 4, 1, __VA_ARGS__), \

@@ -13,6 +13,9 @@ const KernelEntry kTable[] = {
     ACP_GEN(kOpAdd, kU32, kU32, 3, ReduceOp<kU32>),
     ACP_GEN(kOpAdd, kF32, kF32, 3, ReduceOp<kF32>),
     ACP_GEN(kOpAdd, kF16, kF16, 3, ReduceOp<kF16>),
+    ACP_GEN_GROUP(kOpAdd, kU32, ReduceOp<kU32>),
+    ACP_GEN_GROUP(kOpAdd, kF32, ReduceOp<kF32>),
+    ACP_GEN_GROUP(kOpAdd, kF16, ReduceOp<kF16>),
 };
 }  // namespace
 const void* lookup_copy(const KernelKey& k) { return find_entry(kTable, k); }

@@ -235,6 +235,9 @@ def _reduce_case(dt, src_shape, dst_shape, box, threads, values, swz=0, seed=51)
     ("f16", (8, 20, 128), (1, 20, 128), (1, 4, 128), 64, 8, 0),              # packed f16 pairs
     ("f32", (600, 16, 64), (1, 16, 64), (1, 16, 64), 64, 4, 0),              # 600 tiles into one: persistent grid
     ("u32", (4, 5, 16, 64), (1, 1, 16, 64), (1, 1, 16, 64), 64, "wide", 0),  # two reduced dims
+    ("u32", (3, 7, 40, 64), (3, 1, 40, 64), (1, 1, 8, 64), 64, "wide", 0),   # a middle dim reduced
+    ("f32", (2, 2048, 8, 64), (1, 2048, 8, 64), (1, 1, 8, 64), 64, 1000, 0), # more destination tiles than workgroups
+    ("f16", (5, 3, 24, 128), (1, 3, 24, 128), (1, 1, 8, 128), 64, 8, 3),     # f16 sums in binary32 registers
 ])
 def test_store_with_reduce_add(dt, src_shape, dst_shape, box, threads, values, swz):
     say(f"reduce-add {dt} {src_shape} -> {dst_shape} box {box} threads {threads} swizzle {swz}")
