@@ -79,6 +79,7 @@ _DESC_P = ctypes.POINTER(acp_tile_desc)
 _SIGS = {
     "acp_abi_version": ([], _I),
     "acp_last_error": ([], ctypes.c_char_p),
+    "acp_last_kernel": ([], ctypes.c_char_p),
     "acp_encode_tiled": ([_DESC_P, _I, _I, _P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
                           ctypes.POINTER(ctypes.c_int32), _I, _I], _I),
     "acp_plan_query": ([_DESC_P, _I, _I, ctypes.POINTER(acp_plan_info)], _I),
@@ -119,6 +120,10 @@ def _stream(s) -> int | None:
 def _check(status: int) -> None:
     if status != ACP_OK:
         raise AcpError(status, _lib.acp_last_error().decode())
+
+
+def acp_last_kernel() -> str:
+    return _lib.acp_last_kernel().decode()
 
 
 def acp_abi_version() -> int:

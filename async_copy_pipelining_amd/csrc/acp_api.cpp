@@ -18,6 +18,7 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local std::string g_last_kernel;
 
 acp_status ret(acp_status s, const std::string& why = std::string()) {
   g_last_error = (s == ACP_OK) ? std::string() : why;
@@ -301,6 +302,7 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
                           q.mode, 0, 0};
   // streaming on a linear grid with 16-byte rounds: the lean kernel
   static const bool fast_ok = env_flag("ACP_FAST_PATH", true);
+  bool fast = false;
   if (fast_ok && q.mode == 2 && A.lin && p.vec_bytes == 16 && q.n_in == 1 &&
       (p.outer == 1 || p.outer == 2 || p.outer == 4 || p.outer == 8)) {
     acp::KernelKey fk = L->key;
@@ -308,11 +310,14 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
     fk.outer = p.outer;
     static const bool srow_ok = env_flag("ACP_SCALAR_ROWS", true);
     fk.srow = (A.row_uniform && srow_ok) ? 1 : 0;
-    if (acp::engine_kernel(fk)) L->key = fk;
+    if (acp::engine_kernel(fk)) {
+      L->key = fk;
+      fast = true;
+    }
   }
   // any other grid with 16-byte rounds: the general lean kernel
   static const bool gen_ok = env_flag("ACP_GEN_PATH", true);
-  if (gen_ok && L->key.mode <= 4 && p.vec_bytes == 16 &&
+  if (gen_ok && !fast && p.vec_bytes == 16 &&
       (p.outer == 1 || p.outer == 2 || p.outer == 4 || p.outer == 8)) {
     acp::KernelKey gk = L->key;
     gk.mode = q.mode + 4;
@@ -439,6 +444,14 @@ acp_status launch(const Launch& L, void* stream) {
   if (!k) return ret(ACP_ERR_UNSUPPORTED, "op / dtype combination is not in the registry");
   const hipError_t e = acp::engine_launch(k, L.args, L.grid, L.block, L.lds, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  static const char* const kinds[] = {"engine copy",        "engine tile ewise", "engine stream",
+                                      "stream linear grid", "general copy",      "general tile ewise",
+                                      "general stream",     "general reduce-add", "general row reduction"};
+  const int m = L.key.mode;
+  g_last_kernel = std::string(m >= 0 && m <= 8 ? kinds[m] : "?") + " vec " + std::to_string(L.key.vec_bytes) +
+                  " rounds " + std::to_string(L.args.outer) + " srow " + std::to_string(L.key.srow) + " variant " +
+                  std::to_string(L.key.variant) + " grid " + std::to_string(L.grid) + " threads " +
+                  std::to_string(L.block) + " slots " + std::to_string(L.args.stages) + " lds " + std::to_string(L.lds);
   return ret(ACP_OK);
 }
 
@@ -513,6 +526,8 @@ extern "C" {
 int acp_abi_version(void) { return ACP_ABI_VERSION; }
 
 const char* acp_last_error(void) { return g_last_error.c_str(); }
+
+const char* acp_last_kernel(void) { return g_last_kernel.c_str(); }
 
 acp_status acp_encode_tiled(acp_tile_desc* out, acp_dtype dtype, int rank, const void* gbase,
                             const int64_t* shape, const int64_t* strides, const int32_t* box,

@@ -139,6 +139,12 @@ int acp_abi_version(void);
  * pointer stays valid until the thread's next acp_* call. */
 const char* acp_last_error(void);
 
+/* The kernel and launch shape of this thread's last successful launch, as
+ * text ("stream linear grid vec 16 rounds 2 srow 1 variant 0 grid 256 ...");
+ * empty before the first.  Owned by the library; valid until the thread's
+ * next launch. */
+const char* acp_last_kernel(void);
+
 /* Encode a descriptor for tiles of `box` over a tensor at `gbase`
  * ([tma] "Algorithm" step 3; "Generated TIRx IR" shows the worked call).
  *   out      caller-owned descriptor to fill

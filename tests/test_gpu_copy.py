@@ -220,6 +220,11 @@ def _reduce_case(dt, src_shape, dst_shape, box, threads, values, swz=0, seed=51)
     sdesc = encode(dt, sd, src_shape, packed_strides(src_shape), box, swz)
     ddesc = encode(dt, dd, dst_shape, packed_strides(dst_shape), box)
     acp.acp_tile_reduce("add", ddesc, sdesc, threads, stream())
+    kernel = acp.acp_last_kernel()
+    if src_shape == dst_shape and dt != "u32":
+        assert kernel.startswith("general stream") and " variant 1 " in kernel      # ring path, no atomics
+    elif src_shape != dst_shape:
+        assert kernel.startswith("general reduce-add"), kernel
     got = host(dd, npdt, dst_shape)
     want = REF.tile_reduce_add(dst, src)
     bits = {np.uint32: np.uint32, np.float32: np.uint32, np.float16: np.uint16}[npdt]

@@ -84,6 +84,7 @@ def test_c4_full_size_bench_config_sampled():
     shape, stage_box = (128, 500, 1024), (1, 4, 1024)
     say("C4 full fma [128,500,1024] stage (1,4,1024) S=4 persistent 512 workgroups")
     x, a, b, y = _fma_case(shape, stage_box, stage_box, 4, 256, 512)
+    assert acp.acp_last_kernel().startswith("stream linear grid vec 16 rounds 4 srow 1")
     rng = np.random.default_rng(44)
     i0 = rng.integers(0, 128, 3000)
     i1 = rng.integers(0, 500, 3000)
@@ -210,6 +211,8 @@ def test_two_tensor_stream_matches_oracle(staging, op, dt, shape, box, stage_box
     say(f"two-tensor stream {op} {dt} {shape} box {box} stage {stage_box} S={stages} wg={workgroups} "
         f"z={staging} swizzle {swz}")
     x, z, y = _binary_case(op, dt, shape, box, stage_box, stages, threads, workgroups, staging, swz)
+    assert acp.acp_last_kernel().startswith("general stream")
+    assert f" variant {1 if staging == 'ring' else 2} " in acp.acp_last_kernel()
     ref = REF.ewise(op, [x, z], y.dtype)
     bits = np.uint16 if dt == "f16" else np.uint32
     assert np.array_equal(y.view(bits), ref.view(bits))
@@ -269,6 +272,7 @@ def test_row_reduction_matches_oracle(dt, shape, box, stage_box, stages, threads
     say(f"row reduction {dt} {shape} box {box} stage {stage_box} S={stages} wg={workgroups} swz {swz} pitch {pitch}")
     # integer inputs: every partial sum exact, so the result is the exact sum
     x, y = _reduce_rows_case(dt, shape, box, stage_box, stages, threads, workgroups, True, swz, pitch)
+    assert acp.acp_last_kernel().startswith("general row reduction")
     assert np.array_equal(y, REF.reduce_rows(x))
     # real-valued inputs: within the recursive-summation bound of the exact sum
     x, y = _reduce_rows_case(dt, shape, box, stage_box, stages, threads, workgroups, False, swz, pitch, seed=62)
