@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4", choices=["c2", "c3", "c4", "c5", "calib", "copy_ref", "pointwise", "reduce", "rowsum"],
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "calib", "copy_ref", "pointwise", "reduce", "rowsum"],
                     help="c4: the streamed fma (default); c2/c3/c5: the other workloads; "
                          "calib: torch's copy of 256 MiB, the known-size kernel that scales HBM counters; "
                          "copy_ref: the library's register-path reference copy of the c4 tensor "
@@ -135,6 +135,23 @@ def main():
                               f"stage (1,{args.rows},1024)", "shape": list(shape), "stages": args.stages,
                   "stage_box": list(stage), "threads": args.threads, "workgroups": G}
         key = f"stream_fma_f32_128x500x1024_s{args.stages}_r{args.rows}"
+    elif wl == "c1":
+        # one 8x256 f16 tile through the 128-byte swizzled LDS image and back,
+        # 64 threads: latency-bound, so the figure that matters is the launch
+        # time (ms_per_step), not the GB/s
+        x = W.tile_bits_f16((8, 256), seed=1)
+        shape = x.shape
+        for s in range(args.sets):
+            xd = to_dev(x)
+            yd = torch.empty(x.nbytes, dtype=torch.uint8, device=dev)
+            xdesc = acp.acp_encode_tiled("f16", xd, shape, packed(shape), shape, acp.ACP_SWIZZLE_128B)
+            ydesc = acp.acp_encode_tiled("f16", yd, shape, packed(shape), shape, acp.ACP_SWIZZLE_128B)
+            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
+                            acp.acp_tile_copy(xdesc, ydesc, 64, stream))
+        bytes_per, dtype = x.nbytes * 2, "f16"
+        config = {"workload": "swizzled tile copy, one 8x256 f16 tile (128-byte swizzle), 64 threads "
+                              "(latency-bound: read ms_per_step)"}
+        key = "tile_copy_f16_8x256_swizzle128"
     elif wl == "c2":
         x = W.sqrt_tiles_f32(65536, seed=2)
         shape = x.shape
@@ -332,6 +349,7 @@ def main():
         result["ring_stages"] = {"unit": "GB/s", **ring}
     if not args.no_cpu_baseline and wl == "c4":
         result["cpu_baseline"] = cpu_baseline_c4(args.cpu_seconds)
+        result["cpu_baseline_all_cores"] = cpu_baseline_c4_parallel(args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
@@ -357,6 +375,56 @@ def cpu_baseline_c4(budget_s: float):
     return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} [500,1024] f32 slabs of the streamed-fma workload ({done / 128:.2f} passes "
                       f"over the 128 slabs) in {el:.1f} s, numpy single thread"}
+
+
+_start_barrier = None
+
+
+def _cpu_worker_init(barrier):
+    global _start_barrier
+    _start_barrier = barrier
+
+
+def _cpu_worker(job):
+    """One process of the parallel oracle baseline: slabs wid, wid + P, ...
+    of the same workload until the budget is spent, timed from a barrier
+    that every worker reaches after drawing the input."""
+    wid, nproc, budget_s = job
+    import numpy as np
+
+    import workloads as W
+    from oracle import reference as REF
+
+    x, a, b = W.fma_rows_f32((128, 500, 1024), seed=4)
+    _start_barrier.wait()
+    done, t0 = 0, time.perf_counter()
+    while True:
+        k = (wid + done * nproc) % 128
+        REF.stream_ewise("fma", x[k], a[k], b[k], np.float32)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            return done, el
+
+
+def cpu_baseline_c4_parallel(budget_s: float):
+    """The same oracle over the host's cores: one process per core (at most
+    16), each on its own slabs of the workload; aggregate bytes over the
+    longest worker's time."""
+    import multiprocessing as mp
+    import os
+
+    nproc = max(1, min(16, len(os.sched_getaffinity(0))))
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(nproc)
+    with ctx.Pool(nproc, initializer=_cpu_worker_init, initargs=(barrier,)) as pool:
+        res = pool.map(_cpu_worker, [(i, nproc, budget_s) for i in range(nproc)])
+    done = sum(d for d, _ in res)
+    el = max(e for _, e in res)
+    nbytes = done * (500 * 1024 * 4 * 2 + 500 * 8)
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": nproc, "kind": "oracle",
+            "sample": f"{done} [500,1024] f32 slabs of the streamed-fma workload over {nproc} processes "
+                      f"in {el:.1f} s, numpy single thread each"}
 
 
 if __name__ == "__main__":
