@@ -46,6 +46,33 @@ bool same_geometry(const acp::DescData& a, const acp::DescData& b, bool strides)
   return true;
 }
 
+// bytes from a tensor's base to one past its last element (0 when empty)
+uint64_t tensor_span(const acp::DescData& t) {
+  uint64_t last = 0;
+  for (int d = 0; d < t.rank; ++d) {
+    if (t.shape[d] == 0) return 0;
+    last += static_cast<uint64_t>(t.shape[d] - 1) * static_cast<uint64_t>(t.strides[d]) * t.esize;
+  }
+  return last + t.esize;
+}
+
+// Whether [a, a + na) and [b, b + nb) share a byte.  The kernels read and
+// write different tensors from different workgroups with no ordering
+// between them, so a written tensor must not share memory with another
+// operand (strided layouts interleaved in one buffer included).
+bool overlap(uint64_t a, uint64_t na, uint64_t b, uint64_t nb) { return na && nb && a < b + nb && b < a + na; }
+
+bool overlap(const acp::DescData& a, const acp::DescData& b) {
+  return overlap(a.gbase, tensor_span(a), b.gbase, tensor_span(b));
+}
+
+// the same elements at the same addresses: an elementwise op may write its
+// result over its operand, since each element is loaded before the same
+// lane stores it and no other trip touches it
+bool same_elements(const acp::DescData& a, const acp::DescData& b) {
+  return a.gbase == b.gbase && a.esize == b.esize && same_geometry(a, b, true);
+}
+
 int log2i(int v) {
   int l = 0;
   while ((1 << l) < v) ++l;
@@ -212,17 +239,8 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
     n_tiles *= tg;
     subs *= sub;
   }
-  // bytes from each tensor's base to one past its last element
-  auto span = [&](const acp::DescData& t) -> uint64_t {
-    uint64_t last = 0;
-    for (int d = 0; d < t.rank; ++d) {
-      if (t.shape[d] == 0) return 0;
-      last += static_cast<uint64_t>(t.shape[d] - 1) * static_cast<uint64_t>(t.strides[d]) * t.esize;
-    }
-    return last + t.esize;
-  };
-  A.in_span = span(x);
-  A.out_span = span(o);
+  A.in_span = tensor_span(x);
+  A.out_span = tensor_span(o);
   A.total_rows = static_cast<uint64_t>(rs);
   if (max_x + 16 >= (int64_t(1) << 31) || max_o + 32 >= (int64_t(1) << 31))
     return ret(ACP_ERR_UNSUPPORTED, "a stage spans more than 2 GiB");
@@ -439,6 +457,7 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
 }
 
 acp_status launch(const Launch& L, void* stream) {
+  g_last_kernel = "none";
   if (L.n_tiles == 0) return ret(ACP_OK);
   const void* k = acp::engine_kernel(L.key);
   if (!k) return ret(ACP_ERR_UNSUPPORTED, "op / dtype combination is not in the registry");
@@ -606,7 +625,7 @@ acp_status acp_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, int
   // validate_copy_op: both sides laid out, equal dtype, equal extents
   if (s.dtype != d.dtype) return ret(ACP_ERR_INVALID, "not a valid copy op: dtypes differ");
   if (!same_geometry(s, d, false)) return ret(ACP_ERR_INVALID, "not a valid copy op: shapes or boxes differ");
-  if (s.gbase == d.gbase) return ret(ACP_ERR_INVALID, "source and destination are the same tensor");
+  if (overlap(s, d)) return ret(ACP_ERR_INVALID, "source and destination share memory");
   EngineRequest q{};
   q.op = ACP_OP_COPY;
   q.mode = 0;
@@ -655,6 +674,9 @@ acp_status acp_tile_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_de
   if (!is_float(ti) || !is_float(to)) return ret(ACP_ERR_UNSUPPORTED, "elementwise ops take float16 or float32");
   if ((op == ACP_OP_ADD || op == ACP_OP_MUL || op == ACP_OP_FMA || op == ACP_OP_ZERO) && ti != to)
     return ret(ACP_ERR_UNSUPPORTED, "this op keeps the operand type");
+  for (int k = 0; k < n_in; ++k)
+    if (overlap(ins[k], o) && !same_elements(ins[k], o))
+      return ret(ACP_ERR_INVALID, "the output shares memory with an operand other than element for element");
   EngineRequest q{};
   q.op = op;
   q.mode = 1;
@@ -687,7 +709,7 @@ acp_status acp_stream_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_
   if (stages < 2 || stages > 4) return ret(ACP_ERR_INVALID, "stages must be 2, 3 or 4");
   if (workgroups < 0) return ret(ACP_ERR_INVALID, "workgroups must be >= 0");
   if (!same_geometry(xd, od, false)) return ret(ACP_ERR_INVALID, "output shape or box differs from x");
-  if (xd.gbase == od.gbase) return ret(ACP_ERR_INVALID, "in-place streaming is not supported");
+  if (overlap(xd, od)) return ret(ACP_ERR_INVALID, "x and the output share memory");
   for (int d = 0; d < xd.rank; ++d)
     if (stage_box[d] < 1) return ret(ACP_ERR_INVALID, "stage box must be >= 1");
   bool row_ops = false;
@@ -707,6 +729,14 @@ acp_status acp_stream_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_
     default: return ret(ACP_ERR_INVALID, "unknown op for stream_ewise");
   }
   if (xd.rank < 2 && row_ops) return ret(ACP_ERR_INVALID, "per-row scalars need rank >= 2");
+  if (row_ops) {
+    uint64_t rows = 1;
+    for (int d = 0; d + 1 < xd.rank; ++d) rows *= static_cast<uint64_t>(xd.shape[d]);
+    const uint64_t ob = od.gbase, on = tensor_span(od);
+    if ((row_a && overlap(reinterpret_cast<uint64_t>(row_a), rows * 4, ob, on)) ||
+        (row_b && overlap(reinterpret_cast<uint64_t>(row_b), rows * 4, ob, on)))
+      return ret(ACP_ERR_INVALID, "a per-row scalar array shares memory with the output");
+  }
   EngineRequest q{};
   q.op = op;
   q.mode = 2;
@@ -743,7 +773,7 @@ acp_status acp_tile_reduce(acp_op op, const acp_tile_desc* dst, const acp_tile_d
     if (d.shape[k] != 1 || s.box[k] != 1)
       return ret(ACP_ERR_INVALID, "a destination extent must equal the source's, or be 1 where the box is 1");
   }
-  if (s.gbase == d.gbase) return ret(ACP_ERR_INVALID, "source and destination are the same tensor");
+  if (overlap(s, d)) return ret(ACP_ERR_INVALID, "source and destination share memory");
   bool one_each = true;  // every destination element receives one contribution
   for (int k = 0; k < s.rank; ++k) one_each = one_each && d.shape[k] == s.shape[k] && d.strides[k] == s.strides[k];
   if (one_each && s.dtype != ACP_U32) {
@@ -844,6 +874,9 @@ acp_status acp_stream_reduce_rows(acp_op op, float* out, const acp_tile_desc* x,
   int64_t rows = 1;
   for (int d = 0; d + 1 < r; ++d) rows *= xd.shape[d];
   if (rows >= (int64_t(1) << 29)) return ret(ACP_ERR_UNSUPPORTED, "too many rows");
+  if (reinterpret_cast<uint64_t>(out) % 4) return ret(ACP_ERR_INVALID, "output not 4-byte aligned");
+  if (overlap(reinterpret_cast<uint64_t>(out), static_cast<uint64_t>(rows) * 4, xd.gbase, tensor_span(xd)))
+    return ret(ACP_ERR_INVALID, "the output shares memory with x");
   EngineRequest q{};
   q.op = ACP_OP_ADD;
   q.mode = 4;
@@ -884,7 +917,7 @@ acp_status acp_stream_binary(acp_op op, const acp_tile_desc* out, const acp_tile
   if (!same_geometry(xd, od, false) || od.dtype != xd.dtype)
     return ret(ACP_ERR_INVALID, "output dtype, shape or box differs from x");
   if (!is_float(xd.dtype)) return ret(ACP_ERR_UNSUPPORTED, "two-tensor streams take float16 or float32");
-  if (xd.gbase == od.gbase || zd.gbase == od.gbase) return ret(ACP_ERR_INVALID, "in-place streaming is not supported");
+  if (overlap(xd, od) || overlap(zd, od)) return ret(ACP_ERR_INVALID, "the output shares memory with x or z");
   for (int d = 0; d < xd.rank; ++d)
     if (stage_box[d] < 1) return ret(ACP_ERR_INVALID, "stage box must be >= 1");
   EngineRequest q{};

@@ -139,10 +139,12 @@ int acp_abi_version(void);
  * pointer stays valid until the thread's next acp_* call. */
 const char* acp_last_error(void);
 
-/* The kernel and launch shape of this thread's last successful launch, as
- * text ("stream linear grid vec 16 rounds 2 srow 1 variant 0 grid 256 ...");
- * empty before the first.  Owned by the library; valid until the thread's
- * next launch. */
+/* The kernel and launch shape of this thread's last launch attempt of a
+ * pipelined entry point, as text ("stream linear grid vec 16 rounds 2 srow
+ * 1 variant 0 grid 256 ..."): "none" when that call launched nothing (no
+ * tiles, or the launch failed), empty before the first.  Calls rejected
+ * before the launch step leave it unchanged.  Owned by the library; valid
+ * until the thread's next such call. */
 const char* acp_last_kernel(void);
 
 /* Encode a descriptor for tiles of `box` over a tensor at `gbase`
@@ -176,8 +178,8 @@ acp_status acp_plan_query(const acp_tile_desc* desc, int threads, int copy_only,
  * persistent grid (one workgroup per CU, environment ACP_TILE_WG_PER_CU)
  * walks tiles w, w+G, ... through a 2-slot ring (ACP_TILE_STAGES).
  * `src` and `dst` must have equal dtype, shape and box ([tma]
- * validate_copy_op); `dst` may have other strides.  Overlapping src/dst
- * memory is not supported. */
+ * validate_copy_op); `dst` may have other strides.  ACP_ERR_INVALID when
+ * the byte ranges of src and dst (base to last element) intersect. */
 acp_status acp_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, int threads,
                          void* hip_stream);
 
@@ -188,7 +190,10 @@ acp_status acp_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, int
  * has the same shape and box.  Types: SQRT/EXP f16|f32 -> f16|f32;
  * ADD/MUL/FMA inputs and output one of f16|f32; ZERO -> f16|f32.  Large
  * tile counts run on a persistent grid whose ring trips stage 1, 2 or 4
- * consecutive tiles (about 16 KiB per trip; ACP_TILES_PER_TRIP). */
+ * consecutive tiles (about 16 KiB per trip; ACP_TILES_PER_TRIP).  `out`
+ * may be an input element for element (same base, element size and
+ * strides: the op runs in place); any other intersection of the output's
+ * byte range with an input's is ACP_ERR_INVALID. */
 acp_status acp_tile_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_desc* const* in,
                           int n_in, int threads, void* hip_stream);
 
@@ -200,7 +205,8 @@ acp_status acp_tile_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_de
  * must divide it per dim; its planned load count may exceed one).
  *   op          ZERO, SQRT, EXP (x f16|f32 -> out f16|f32) or
  *               ADD, MUL, FMA (x and out f32, per-row scalars)
- *   out         same shape and box as x; any strides
+ *   out         same shape and box as x; any strides; its byte range must
+ *               not intersect x's or a row array's (else ACP_ERR_INVALID)
  *   row_a/row_b device float32 arrays over x's outer dims (shape[:-1],
  *               packed row-major); FMA needs both, MUL row_a, ADD row_b;
  *               NULL otherwise
@@ -221,7 +227,8 @@ acp_status acp_stream_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_
  *   src   u32, f32 or f16
  *   dst   same dtype, rank and box; each extent equal to src's, or 1 where
  *         src's box is 1: every source tile along such a dim adds into the
- *         same destination elements (a sum over that dim)
+ *         same destination elements (a sum over that dim); its byte range
+ *         must not intersect src's (else ACP_ERR_INVALID)
  * dst'[j] = dst[j] + sum of the src elements mapped to j; u32 wraps modulo
  * 2^32.  Floating-point additions land in no fixed order: the result is
  * the exactly rounded sum whenever every partial sum is representable (in
@@ -240,15 +247,19 @@ acp_status acp_tile_reduce(acp_op op, const acp_tile_desc* dst, const acp_tile_d
  * out[row] = sum of x[row, :] over the innermost dim, every row of x.
  *   op          ACP_OP_ADD
  *   out         device float32 array over x's outer dims (shape[:-1],
- *               packed row-major), written (not accumulated)
+ *               packed row-major, 4-byte aligned, not intersecting x),
+ *               written (not accumulated)
  *   x           float16 or float32, rank >= 2; its box and `stage_box` hold
  *               whole rows (innermost box = innermost extent)
  *   stages      2..4; workgroups as for acp_stream_ewise
- * Each lane sums its 16-byte chunks (fixed pairwise order, binary32), the
- * chunk partials go through LDS, and after a workgroup barrier each wave
- * reduces whole rows (lane-strided sums, then a 64-lane butterfly).  The
- * order is fixed, so results are deterministic; their error against the
- * exact sum is within the recursive-summation bound for the row length.
+ * Each lane sums its 16-byte chunks (fixed pairwise order, binary32).  When
+ * every 1 KiB wave block of a stage lies in one row and every row in one
+ * wave, the wave sums its blocks with cross-lane moves and writes its rows
+ * with no barrier; otherwise the chunk partials go through LDS and, after a
+ * workgroup barrier, each wave reduces whole rows (lane-strided sums, then
+ * the same cross-lane sum).  The order is fixed, so results are
+ * deterministic; their error against the exact sum is within the
+ * recursive-summation bound for the row length.
  * ACP_ERR_UNSUPPORTED unless the plan has 16-byte rounds and 1, 2, 4 or 8
  * rounds per thread. */
 acp_status acp_stream_reduce_rows(acp_op op, float* out, const acp_tile_desc* x, const int32_t* stage_box, int stages,
@@ -268,7 +279,8 @@ typedef enum { ACP_STAGE_RING = 0, ACP_STAGE_SET = 1 } acp_staging;
  * into z's image in the slot.
  *   x, z        float16 or float32, one layout (dtype, shape, strides, box,
  *               swizzle); x's box is the workgroup tile
- *   out         same dtype, shape and box; any strides; not x or z
+ *   out         same dtype, shape and box; any strides; its byte range must
+ *               not intersect x's or z's (else ACP_ERR_INVALID)
  *   stage_box   sub-box of the tile staged per trip (divides it per dim)
  *   workgroups  0: one workgroup per tile; G > 0: G persistent workgroups
  * Results are the IEEE sum or product of each element pair, rounded once

@@ -151,3 +151,38 @@ def test_status_codes_and_reasons():
         with pytest.raises(acp.AcpError) as e:
             acp.acp_debug_stream_copy(dst, src, n)
         assert e.value.status == acp.ACP_ERR_INVALID and why in e.value.reason
+
+
+def test_memory_shared_between_a_written_tensor_and_another_operand_is_rejected():
+    """Workgroups read and write different tensors with no ordering between
+    them, so every entry point refuses a written tensor that shares bytes
+    with another operand (checked on the host, before any launch)."""
+    shape, strides, box = (4, 8, 256), (2048, 256, 1), (1, 4, 256)
+    span = 4 * 8 * 256 * 4
+    x = acp.acp_encode_tiled("f32", FAKE_BASE, shape, strides, box)
+    near = acp.acp_encode_tiled("f32", FAKE_BASE + span - 16, shape, strides, box)   # last 16 bytes shared
+    far = acp.acp_encode_tiled("f32", FAKE_BASE + span, shape, strides, box)         # adjacent, disjoint
+    cases = [
+        (lambda: acp.acp_tile_copy(x, near, 256), "share memory"),
+        (lambda: acp.acp_tile_copy(x, x, 256), "share memory"),
+        (lambda: acp.acp_tile_ewise("sqrt", near, [x], 256), "shares memory"),
+        (lambda: acp.acp_stream_ewise("exp", near, x, None, None, box, 2, 256), "share memory"),
+        (lambda: acp.acp_stream_ewise("exp", x, x, None, None, box, 2, 256), "share memory"),
+        (lambda: acp.acp_stream_ewise("fma", far, x, FAKE_BASE + span + 64, FAKE_BASE * 8, box, 2, 256),
+         "per-row scalar"),
+        (lambda: acp.acp_stream_binary("add", near, far, far, box, 2, 256), "shares memory"),
+        (lambda: acp.acp_stream_binary("add", far, x, near, box, 2, 256), "shares memory"),
+        (lambda: acp.acp_tile_reduce("add", near, x, 256), "share memory"),
+        (lambda: acp.acp_stream_reduce_rows("add", FAKE_BASE + 64, x, (1, 4, 256), 2, 256), "shares memory"),
+        (lambda: acp.acp_stream_reduce_rows("add", FAKE_BASE * 8 + 2, x, (1, 4, 256), 2, 256), "aligned"),
+    ]
+    for call, why in cases:
+        with pytest.raises(acp.AcpError) as e:
+            call()
+        assert e.value.status == acp.ACP_ERR_INVALID and why in e.value.reason, e.value.reason
+    # a float16 output over the bytes of a float32 operand: the same base,
+    # but not element for element, so refused as well
+    h = acp.acp_encode_tiled("f16", FAKE_BASE, shape, strides, box)
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_tile_ewise("sqrt", h, [x], 256)
+    assert e.value.status == acp.ACP_ERR_INVALID

@@ -129,3 +129,25 @@ def test_persistent_grid_ragged_tile_ewise(op, dt, shape, box, threads):
     else:
         assert np.array_equal(y.view(np.uint16 if dt == "f16" else np.uint32),
                               ref.view(np.uint16 if dt == "f16" else np.uint32))
+
+
+@pytest.mark.parametrize("op,shape,box,threads", [
+    ("sqrt", (600, 32, 32), (1, 32, 32), 256),            # persistent grid, four tiles per trip
+    ("fma", (3, 70, 128), (1, 16, 128), 256),             # one workgroup per tile, ragged last tile
+])
+def test_tile_ewise_in_place(op, shape, box, threads):
+    """The output may be an operand element for element: every element is
+    staged before the same lane stores its result, and no other trip
+    touches it."""
+    say(f"in-place tile_ewise {op} {shape} box {box} threads {threads}")
+    rng = np.random.default_rng(26)
+    if op == "sqrt":
+        ins = [rng.uniform(0, 1e3, shape).astype(np.float32)]
+    else:
+        ins = [rng.standard_normal(shape).astype(np.float32) for _ in range(3)]
+    st = packed_strides(shape)
+    bufs = [dev(a) for a in ins]
+    descs = [encode("f32", b, shape, st, box) for b in bufs]
+    acp.acp_tile_ewise(op, descs[0], descs, threads, stream())
+    y = host(bufs[0], np.float32, shape)
+    assert np.array_equal(y.view(np.uint32), REF.ewise(op, ins, np.float32).view(np.uint32))
