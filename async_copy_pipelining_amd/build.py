@@ -31,6 +31,7 @@ SOURCES = [
     ("acp_k_copy.hip", True),
     ("acp_k_tile.hip", True),
     ("acp_k_tile_gen.hip", True),
+    ("acp_k_tile_lin.hip", True),
     ("acp_k_stream_f32.hip", True),
     ("acp_k_stream_f16.hip", True),
 ]

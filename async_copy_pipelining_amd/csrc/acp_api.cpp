@@ -333,6 +333,37 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
       fast = true;
     }
   }
+  // tile ewise on a linear tile grid with 16-byte rounds: the linear kernel
+  // with the output staged in LDS, the tiles of one ring trip (1, 2 or 4,
+  // dividing the tile count) forming one stage
+  static const bool lin_tile_ok = env_flag("ACP_LIN_TILE", true);
+  int lin_tiles = 0;
+  if (lin_tile_ok && !fast && q.mode == 1 && A.lin && p.vec_bytes == 16 && q.n_in >= 1) {
+    int t = 1;
+    if (q.workgroups > 0)
+      while (2 * t <= q.tiles_per_trip && 2 * t <= 4 && n_tiles % (2 * t) == 0 && 2 * t * p.outer <= acp::kMaxOuter)
+        t *= 2;
+    const int rounds = t * p.outer;
+    const bool fits = (t - 1) * A.lin_x + max_x + 16 < (int64_t(1) << 31) &&
+                      (t - 1) * A.lin_o + max_o + 32 < (int64_t(1) << 31);
+    if (fits && (rounds == 1 || rounds == 2 || rounds == 4 || rounds == 8)) {
+      acp::KernelKey tk = L->key;
+      tk.mode = 9;
+      tk.outer = rounds;
+      if (acp::engine_kernel(tk)) {
+        L->key = tk;
+        fast = true;
+        lin_tiles = t;
+        A.outer = rounds;
+        A.tile_rounds_log2 = static_cast<uint32_t>(log2i(p.outer));
+        A.tile_x = A.lin_x;
+        A.tile_o = A.lin_o;
+        A.lin_x *= t;
+        A.lin_o *= t;
+        A.n_tiles = static_cast<uint32_t>(n_tiles / t);
+      }
+    }
+  }
   // any other grid with 16-byte rounds: the general lean kernel
   static const bool gen_ok = env_flag("ACP_GEN_PATH", true);
   if (gen_ok && !fast && p.vec_bytes == 16 &&
@@ -353,11 +384,16 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   int tpt_log2 = 0;
   if ((L->key.mode == 4 || L->key.mode == 5 || L->key.mode == 7) && q.workgroups > 0 && subs == 1)
     while ((2 << tpt_log2) <= q.tiles_per_trip && tpt_log2 < 2) ++tpt_log2;
-  A.tpt_log2 = static_cast<uint32_t>(tpt_log2);
+  if (lin_tiles) tpt_log2 = log2i(lin_tiles);
+  // the linear kernel's stage already spans the trip's tiles
+  A.tpt_log2 = static_cast<uint32_t>(lin_tiles ? 0 : tpt_log2);
 
   const int64_t in_img = align_up(p.tile_bytes(), 1024);
-  const int64_t out_img = q.mode == 1 ? align_up(p.tile_elems() * eo, 1024) : 0;
-  A.in_image_bytes = static_cast<uint32_t>(in_img);
+  // linear kernel: each operand's image holds the trip's tiles back to
+  // back, and so does the output image
+  const int64_t out_img =
+      q.mode == 1 ? align_up(p.tile_elems() * eo * (lin_tiles ? lin_tiles : 1), 1024) : 0;
+  A.in_image_bytes = static_cast<uint32_t>(lin_tiles ? in_img * lin_tiles : in_img);
   A.ab_off = static_cast<uint32_t>(q.n_in * in_img);
   A.row_ops = q.row_ops ? 1 : 0;
   if (q.row_ops) {
@@ -463,11 +499,12 @@ acp_status launch(const Launch& L, void* stream) {
   if (!k) return ret(ACP_ERR_UNSUPPORTED, "op / dtype combination is not in the registry");
   const hipError_t e = acp::engine_launch(k, L.args, L.grid, L.block, L.lds, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
-  static const char* const kinds[] = {"engine copy",        "engine tile ewise", "engine stream",
-                                      "stream linear grid", "general copy",      "general tile ewise",
-                                      "general stream",     "general reduce-add", "general row reduction"};
+  static const char* const kinds[] = {"engine copy",        "engine tile ewise",  "engine stream",
+                                      "stream linear grid", "general copy",       "general tile ewise",
+                                      "general stream",     "general reduce-add", "general row reduction",
+                                      "tile linear grid"};
   const int m = L.key.mode;
-  g_last_kernel = std::string(m >= 0 && m <= 8 ? kinds[m] : "?") + " vec " + std::to_string(L.key.vec_bytes) +
+  g_last_kernel = std::string(m >= 0 && m <= 9 ? kinds[m] : "?") + " vec " + std::to_string(L.key.vec_bytes) +
                   " rounds " + std::to_string(L.args.outer) + " srow " + std::to_string(L.key.srow) + " variant " +
                   std::to_string(L.key.variant) + " grid " + std::to_string(L.grid) + " threads " +
                   std::to_string(L.block) + " slots " + std::to_string(L.args.stages) + " lds " + std::to_string(L.lds);

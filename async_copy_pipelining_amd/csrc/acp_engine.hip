@@ -7,6 +7,7 @@ namespace acp {
 const void* lookup_copy(const KernelKey& k);
 const void* lookup_tile(const KernelKey& k);
 const void* lookup_tile_gen(const KernelKey& k);
+const void* lookup_tile_lin(const KernelKey& k);
 const void* lookup_stream_f32(const KernelKey& k);
 const void* lookup_stream_f16(const KernelKey& k);
 
@@ -90,6 +91,7 @@ const void* engine_kernel(const KernelKey& k) {
   if (const void* f = lookup_copy(k)) return f;
   if (const void* f = lookup_tile(k)) return f;
   if (const void* f = lookup_tile_gen(k)) return f;
+  if (const void* f = lookup_tile_lin(k)) return f;
   if (const void* f = lookup_stream_f32(k)) return f;
   return lookup_stream_f16(k);
 }

@@ -90,6 +90,12 @@ struct EngineArgs {
   // to the destination once per group.  0: round-robin tiles, no grouping.
   uint32_t per_wg, red_group;
   uint32_t rowstr[kDims];
+  // Tile ewise on a linear tile grid (linear kernel): a stage is 2^k tiles
+  // of 2^tile_rounds_log2 rounds each; round f belongs to tile
+  // f >> tile_rounds_log2 of the stage, whose input and output start
+  // tile_x and tile_o bytes after the previous tile's.
+  uint32_t tile_rounds_log2;
+  int64_t tile_x, tile_o;
 };
 
 // Which kernel variant a launch needs.
@@ -100,8 +106,8 @@ struct KernelKey {
   int vec_bytes; // 16 or 4
   int mode;      // 0 copy, 1 tile ewise (output staged in LDS), 2 stream, 3 stream on a linear grid,
                  // 4 / 5 / 6 / 7 / 8: copy / tile ewise / stream / store with reduce-add /
-                 // row reduction in the general lean kernel
-  int outer;     // modes 3..6: rounds per thread (1, 2, 4 or 8); 0 otherwise
+                 // row reduction in the general lean kernel, 9 tile ewise on a linear grid
+  int outer;     // modes 3..9: rounds per thread (1, 2, 4 or 8); 0 otherwise
   int srow;      // modes 3 and 6, row ops: per-row scalars through the scalar cache
   int variant = 0;  // mode 6, add / mul of two streamed tensors: 1 both on the direct-to-LDS
                     // ring, 2 the second one loaded synchronously ("Set") into its slot

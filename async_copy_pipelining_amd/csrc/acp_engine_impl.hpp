@@ -781,23 +781,38 @@ __global__ __launch_bounds__(1024) void engine_kernel_t(const EngineArgs) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming fast path: a linear stage grid (one full stage per tile, row-major
-// contiguous), 16-byte rounds, one staged operand, OUTER rounds per thread
-// known at compile time.  Same ring control and wait counts as the general
-// engine; per trip only the stage base (one multiply) changes, and no chunk
-// can be out of bounds.
+// Linear stage grid (one full stage per tile, row-major contiguous), 16-byte
+// rounds, OUTER rounds per thread known at compile time.  Same ring control
+// and wait counts as the general engine; per trip only the stage base (one
+// multiply) changes, and no chunk can be out of bounds.
+// * Streaming (STAGE_OUT false): one staged operand.
+// * Tile ewise (STAGE_OUT true, "elementwise -> smem"): OP::NIN staged
+//   operands, and the result goes through the LDS output image before the
+//   store.  A stage is 2^k consecutive tiles (one ring trip), round f
+//   belonging to tile f >> tile_rounds_log2 of it.
 
-template <class OP, int OUTER, bool SROW>
+// Rounds consumed together: the largest power of two dividing `total` (a
+// power of two) whose staged operands (ns each) stay within `cap` registers'
+// worth of chunks.
+constexpr int round_group(int total, int ns, int cap) {
+  int g = total;
+  while (g > 1 && g * (ns > 0 ? ns : 1) > cap) g /= 2;
+  return g;
+}
+
+template <class OP, int OUTER, bool SROW, bool STAGE_OUT>
 struct LinPolicy {
+  // staged operands per trip
+  static constexpr int NL = STAGE_OUT ? OP::NIN : 1;
   unsigned char* lds;
-  const char* in0;
+  const char* in[3];
   char* out;
   uint64_t in_span, out_span;
   uint64_t lin_x, lin_o, lin_r, total_rows;
-  uint32_t lds0, slot_bytes, ab_base, wg, grid, waves_kb;  // waves_kb: LDS bytes of one round
-  int wave, lane, ab_instr;
+  uint32_t lds0, slot_bytes, in_image_bytes, out_image_off, ab_base, wg, grid, waves_kb;  // waves_kb: LDS bytes of one round
+  int wave, lane, ab_instr, swizzle, esize_log2;
   bool load_nt, store_nt;
-  uint32_t xoff[OUTER], ooff[OUTER], abo[OUTER];
+  uint32_t xoff[OUTER], ooff[OUTER], abo[OUTER], lpos[OUTER];
   const uint64_t* row_ptr;   // [0] lane's array, [1 + q] row byte offset in the stage
   const uint32_t* row_ok;    // lane has a row in load q
   // SROW: this wave's row (relative to the stage) of each round, and the
@@ -812,10 +827,14 @@ struct LinPolicy {
   __device__ __forceinline__ void load(int j, int slot) {
     const uint64_t s = stage(j);
     const uint64_t xb = s * lin_x;
-    const v4i rs = rsrc_v4(in0 + xb, range_from(in_span, xb));
+    const uint32_t range = range_from(in_span, xb);
     const uint32_t base = lds0 + slot * slot_bytes + wave * 1024u;
 #pragma unroll
-    for (int f = 0; f < OUTER; ++f) dma_b128(rs, xoff[f], base + f * waves_kb, load_nt);
+    for (int k = 0; k < NL; ++k) {
+      const v4i rs = rsrc_v4(in[k] + xb, range);
+#pragma unroll
+      for (int f = 0; f < OUTER; ++f) dma_b128(rs, xoff[f], base + k * in_image_bytes + f * waves_kb, load_nt);
+    }
     if constexpr (OP::ROW && !SROW) {
       const uint64_t rb = s * lin_r;
 #pragma unroll
@@ -850,36 +869,64 @@ struct LinPolicy {
     const uint64_t ob = s * lin_o;
     const __amdgpu_buffer_rsrc_t rs = rsrc_store(out + ob, range_from(out_span, ob));
     const uint32_t sl = slot * slot_bytes;
-    u32x4 v[OUTER];
-    float ra[OUTER], rb[OUTER];
+    // rounds in groups whose staged operands fit in registers together
+    constexpr int GRP = round_group(OUTER, NL, 16);
+    static_assert(OUTER % GRP == 0, "round groups must tile the rounds");
 #pragma unroll
-    for (int f = 0; f < OUTER; ++f) {
-      v[f] = *reinterpret_cast<const u32x4*>(__builtin_assume_aligned(lds + sl + f * waves_kb + wave * 1024u + lane * 16u, 16));
-      if constexpr (OP::ROW && SROW) {
-        ra[f] = sa[f];
-        rb[f] = sb[f];
-      } else if constexpr (OP::ROW) {
-        ra[f] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f]);
-        rb[f] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f] + 128u);
-      } else {
-        ra[f] = rb[f] = 0.f;
+    for (int g0 = 0; g0 < OUTER; g0 += GRP) {
+      u32x4 v[NL > 0 ? NL : 1][GRP];
+      float ra[GRP], rb[GRP];
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const int f = g0 + u;
+#pragma unroll
+        for (int k = 0; k < NL; ++k)
+          v[k][u] = *reinterpret_cast<const u32x4*>(
+              __builtin_assume_aligned(lds + sl + k * in_image_bytes + f * waves_kb + wave * 1024u + lane * 16u, 16));
+        if constexpr (NL == 0) v[0][u] = u32x4{0, 0, 0, 0};
+        if constexpr (OP::ROW && SROW) {
+          ra[u] = sa[f];
+          rb[u] = sb[f];
+        } else if constexpr (OP::ROW) {
+          ra[u] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f]);
+          rb[u] = *reinterpret_cast<const float*>(lds + sl + ab_base + abo[f] + 128u);
+        } else {
+          ra[u] = rb[u] = 0.f;
+        }
       }
-    }
 #pragma unroll
-    for (int f = 0; f < OUTER; ++f) {
-      TI in[CS::NE];
-      __builtin_memcpy(in, &v[f], 16);
-      TO res[CS::NE];
+      for (int u = 0; u < GRP; ++u) {
+        const int f = g0 + u;
+        TI in0[CS::NE], in1[CS::NE], in2[CS::NE];
+        __builtin_memcpy(in0, &v[0][u], 16);
+        __builtin_memcpy(in1, &v[NL > 1 ? 1 : 0][u], 16);
+        __builtin_memcpy(in2, &v[NL > 2 ? 2 : 0][u], 16);
+        TO res[CS::NE];
 #pragma unroll
-      for (int e = 0; e < CS::NE; ++e) res[e] = OP::f(in[e], in[e], in[e], ra[f], rb[f]);
-      uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      __builtin_memcpy(words, res, CS::OB);
-      store_chunk<CS::OB>(rs, ooff[f], words, store_nt);
+        for (int e = 0; e < CS::NE; ++e) res[e] = OP::f(in0[e], in1[e], in2[e], ra[u], rb[u]);
+        uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        __builtin_memcpy(words, res, CS::OB);
+        if constexpr (STAGE_OUT) {
+          // the output tile is LDS-resident ("elementwise -> smem") and is
+          // copied out from there; the lane reads back the bytes it wrote
+          const uint32_t lo = (lpos[f] >> esize_log2) * CS::EO;
+          constexpr int P = (CS::OB + 15) / 16;
+          constexpr int PB = CS::OB < 16 ? CS::OB : 16;
+#pragma unroll
+          for (int piece = 0; piece < P; ++piece)
+            __builtin_memcpy(lds + out_image_off + swz(lo + piece * 16, swizzle), words + piece * 4, PB);
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int piece = 0; piece < P; ++piece)
+            __builtin_memcpy(words + piece * 4, lds + out_image_off + swz(lo + piece * 16, swizzle), PB);
+        }
+        store_chunk<CS::OB>(rs, ooff[f], words, store_nt);
+      }
     }
   }
 };
 
-template <class OP, int OUTER, bool SROW>
+template <class OP, int OUTER, bool SROW, bool STAGE_OUT = false>
 __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
   CArgs* A = kargs();
@@ -898,9 +945,9 @@ __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
   if constexpr (OP::ROW && !SROW) build_rows(A, lane, row_ptr, row_bad);
   uint32_t row_ok[2] = {row_bad[0] == 0u, row_bad[1] == 0u};
   const Loc L = load_loc(A);
-  LinPolicy<OP, OUTER, SROW> p;
+  LinPolicy<OP, OUTER, SROW, STAGE_OUT> p;
   p.lds = lds;
-  p.in0 = L.in[0];
+  for (int k = 0; k < 3; ++k) p.in[k] = L.in[k];
   p.out = L.out;
   p.in_span = L.in_span;
   p.out_span = L.out_span;
@@ -910,20 +957,30 @@ __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
   p.total_rows = L.total_rows;
   p.lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   p.slot_bytes = L.slot_bytes;
+  p.in_image_bytes = L.in_image_bytes;
+  p.out_image_off = L.out_image_off;
   p.ab_base = L.ab_off + wave * L.ab_wave_bytes;
   p.wg = wg;
   p.grid = grid;
   p.wave = wave;
   p.lane = lane;
   p.ab_instr = L.ab_instr;
+  p.swizzle = uni(A->swizzle);
+  p.esize_log2 = uni(A->esize_log2);
   p.load_nt = L.load_nt != 0;
   p.store_nt = L.store_nt != 0;
   p.waves_kb = static_cast<uint32_t>(L.waves) * 1024u;
+  // tile ewise: round f lies in tile f >> tile_rounds_log2 of the stage
+  const uint32_t trl = STAGE_OUT ? uni(A->tile_rounds_log2) : 0u;
+  const uint64_t tx = STAGE_OUT ? uni64(static_cast<uint64_t>(A->tile_x)) : 0u;
+  const uint64_t to = STAGE_OUT ? uni64(static_cast<uint64_t>(A->tile_o)) : 0u;
 #pragma unroll
   for (int f = 0; f < OUTER; ++f) {
-    p.xoff[f] = m.xoff[f];
-    p.ooff[f] = m.ooff[f];
+    const uint32_t t = static_cast<uint32_t>(f) >> trl;
+    p.xoff[f] = m.xoff[f] + static_cast<uint32_t>(t * tx);
+    p.ooff[f] = m.ooff[f] + static_cast<uint32_t>(t * to);
     p.abo[f] = m.abo[f];
+    p.lpos[f] = m.lpos[f];
   }
   p.row_ptr = row_ptr;
   p.row_ok = row_ok;
@@ -937,7 +994,7 @@ __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
     p.sa[f] = p.sb[f] = 0.f;
   }
   typedef ChunkShape<OP, 16> CS;
-  const int d = OUTER + ((OP::ROW && !SROW) ? L.ab_instr : 0);
+  const int d = LinPolicy<OP, OUTER, SROW, STAGE_OUT>::NL * OUTER + ((OP::ROW && !SROW) ? L.ab_instr : 0);
   run_ring(p, n, uni(A->stages), d, OUTER * CS::ST);
 }
 
@@ -949,15 +1006,6 @@ __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
 // with vector arithmetic, and each trip reads its row with v_readlane.  Two
 // table sets alternate so that the load cursor (up to S-1 trips ahead) can
 // enter the next batch while the consume cursor finishes the current one.
-
-// Rounds consumed together: the largest power of two dividing `total` (a
-// power of two) whose staged operands (ns each) stay within `cap` registers'
-// worth of chunks.
-constexpr int round_group(int total, int ns, int cap) {
-  int g = total;
-  while (g > 1 && g * (ns > 0 ? ns : 1) > cap) g /= 2;
-  return g;
-}
 
 struct TripRow {
   uint32_t xlo, xhi, olo, ohi, rlo, flags;  // flags: bits 0..3 last-stage slots, bit 8 out of range
@@ -1568,6 +1616,13 @@ struct KernelEntry {
   ACP_LIN(OPC, kF32, kF32, __VA_ARGS__), ACP_L(OPC, kF32, kF32, 1, 1, __VA_ARGS__),                          \
       ACP_L(OPC, kF32, kF32, 2, 1, __VA_ARGS__), ACP_L(OPC, kF32, kF32, 4, 1, __VA_ARGS__), \
       ACP_L(OPC, kF32, kF32, 8, 1, __VA_ARGS__)
+// tile ewise on a linear tile grid (mode key 9): the linear kernel with the output staged in LDS
+#define ACP_LT1(OPC, TIN, TOUT, OUTER, ...)                \
+  KernelEntry{KernelKey{OPC, TIN, TOUT, 16, 9, OUTER, 0}, \
+              reinterpret_cast<const void*>(&dev::stream_lin_kernel_t<__VA_ARGS__, OUTER, false, true>)}
+#define ACP_LIN_TILE(OPC, TIN, TOUT, ...)                                                \
+  ACP_LT1(OPC, TIN, TOUT, 1, __VA_ARGS__), ACP_LT1(OPC, TIN, TOUT, 2, __VA_ARGS__),       \
+      ACP_LT1(OPC, TIN, TOUT, 4, __VA_ARGS__), ACP_LT1(OPC, TIN, TOUT, 8, __VA_ARGS__)
 #define ACP_BOTH(OPC, TIN, TOUT, MODE, ...) ACP_K(OPC, TIN, TOUT, 16, MODE, __VA_ARGS__), ACP_K(OPC, TIN, TOUT, 4, MODE, __VA_ARGS__)
 
 template <size_t N>

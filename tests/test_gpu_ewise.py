@@ -43,6 +43,7 @@ def test_c2_full_size_sqrt():
     say("C2 sqrt 65536 tiles of 32x32 f32, 256 threads")
     x = W.sqrt_tiles_f32(tiles=65536, seed=2)
     y = run_tile_ewise("sqrt", [x], "f32", "f32", x.shape, (1, 32, 32), 256)
+    assert acp.acp_last_kernel().startswith("tile linear grid vec 16 rounds 4 ")   # 4 tiles per stage
     ref = REF.ewise("sqrt", [x], np.float32)
     d = ulp_diff(y.reshape(-1), ref.reshape(-1))
     assert d.max() <= 1
@@ -151,3 +152,35 @@ def test_tile_ewise_in_place(op, shape, box, threads):
     acp.acp_tile_ewise(op, descs[0], descs, threads, stream())
     y = host(bufs[0], np.float32, shape)
     assert np.array_equal(y.view(np.uint32), REF.ewise(op, ins, np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("op,n_in,idt,odt,shape,box,threads,swz,rounds", [
+    ("fma", 3, "f32", "f32", (4, 64, 128), (1, 16, 128), 256, 0, 2),      # one workgroup per tile
+    ("exp", 1, "f16", "f32", (2, 64, 256), (1, 8, 256), 128, 3, 2),       # widening, swizzled
+    ("sqrt", 1, "f32", "f16", (4, 64, 128), (1, 16, 128), 256, 0, 2),     # narrowing
+    ("add", 2, "f16", "f16", (8, 32, 64), (1, 32, 64), 64, 2, 4),         # 64-byte swizzle
+    ("mul", 2, "f32", "f32", (2048, 32, 32), (1, 32, 32), 256, 0, 2),     # persistent, 2 tiles per stage
+    ("exp", 1, "f16", "f32", (1024, 32, 64), (1, 32, 64), 256, 3, 4),     # persistent, 4 tiles per stage
+    ("sqrt", 1, "f32", "f32", (1026, 32, 32), (1, 32, 32), 256, 0, 2),    # 1026 tiles: 2 per stage
+    ("sqrt", 1, "f16", "f16", (32, 65536), (32, 64), 256, 1, 4),          # tiles 128 B apart in memory
+])
+def test_tile_ewise_on_a_linear_tile_grid(op, n_in, idt, odt, shape, box, threads, swz, rounds):
+    """Full tiles on a row-major tile grid run the linear kernel: the tiles
+    of a ring trip form one stage, the output goes through the LDS image."""
+    say(f"linear-grid tile_ewise {op} {idt}->{odt} {shape} box {box} threads {threads} swizzle {swz}")
+    rng = np.random.default_rng(27)
+    if op == "exp":
+        ins = [rng.uniform(-8, 8, shape).astype(NP[idt])]
+    elif op == "sqrt":
+        ins = [rng.uniform(0, 1e3, shape).astype(NP[idt])]
+    else:
+        ins = [rng.standard_normal(shape).astype(NP[idt]) for _ in range(n_in)]
+    y = run_tile_ewise(op, ins, idt, odt, shape, box, threads, swz)
+    kernel = acp.acp_last_kernel()
+    assert kernel.startswith(f"tile linear grid vec 16 rounds {rounds} "), kernel
+    ref = REF.ewise(op, ins, NP[odt])
+    if op == "exp":
+        assert ulp_diff(y.reshape(-1), ref.reshape(-1)).max() <= 1
+    else:
+        bits = np.uint32 if odt == "f32" else np.uint16
+        assert np.array_equal(y.view(bits), ref.view(bits))
