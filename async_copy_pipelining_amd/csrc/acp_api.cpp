@@ -507,7 +507,8 @@ acp_status launch(const Launch& L, void* stream) {
   g_last_kernel = std::string(m >= 0 && m <= 9 ? kinds[m] : "?") + " vec " + std::to_string(L.key.vec_bytes) +
                   " rounds " + std::to_string(L.args.outer) + " srow " + std::to_string(L.key.srow) + " variant " +
                   std::to_string(L.key.variant) + " grid " + std::to_string(L.grid) + " threads " +
-                  std::to_string(L.block) + " slots " + std::to_string(L.args.stages) + " lds " + std::to_string(L.lds);
+                  std::to_string(L.block) + " slots " + std::to_string(L.args.stages) + " lds " + std::to_string(L.lds) +
+                  (m == 8 ? std::string(L.args.red_local ? " wave-local" : " lds partials") : std::string());
   return ret(ACP_OK);
 }
 

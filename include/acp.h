@@ -142,7 +142,8 @@ const char* acp_last_error(void);
 /* The kernel and launch shape of this thread's last launch attempt of a
  * pipelined entry point, as text ("stream linear grid vec 16 rounds 2 srow
  * 1 variant 0 grid 256 ..."): "none" when that call launched nothing (no
- * tiles, or the launch failed), empty before the first.  Calls rejected
+ * tiles, or the launch failed), empty before the first.  A row reduction
+ * ends in "wave-local" or "lds partials", the path its stage layout takes.  Calls rejected
  * before the launch step leave it unchanged.  Owned by the library; valid
  * until the thread's next such call. */
 const char* acp_last_kernel(void);

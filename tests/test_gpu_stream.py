@@ -261,26 +261,44 @@ def _assert_within_sum_bound(x, y):
     assert np.all(err <= bound), float((err - bound).max())
 
 
-@pytest.mark.parametrize("dt,shape,box,stage_box,stages,threads,workgroups,swz,pitch", [
-    ("f32", (3, 37, 1024), (1, 12, 1024), (1, 4, 1024), 4, 256, 0, 0, None),   # 4 loads per stage, cut stage
-    ("f32", (3, 37, 1024), (1, 4, 1024), (1, 4, 1024), 2, 256, 5, 0, None),    # persistent, uneven
-    ("f16", (2, 70, 256), (1, 8, 256), (1, 8, 256), 3, 64, 5, 3, None),        # swizzled f16, 8 rows per stage
-    ("f32", (5, 64, 64), (1, 16, 64), (1, 16, 64), 4, 64, 0, 0, None),         # 16 rows per wave block
-    ("f32", (4, 33, 96), (1, 8, 96), (1, 8, 96), 3, 192, 0, 0, 104),           # padded rows, 6 chunks per row, 3 waves
+@pytest.mark.parametrize("dt,shape,box,stage_box,stages,threads,workgroups,swz,pitch,local", [
+    # The stage image is issue-major (rows wider than 256 elements load as
+    # 256-element segments), so 1 KiB block b of a (1, R, 1024) f32 stage is
+    # segment b // R of row b % R and goes to wave b % waves: with R equal
+    # to the wave count (or one wave) every row's blocks meet in one wave,
+    # which then reduces its rows alone ("wave-local"); otherwise the chunk
+    # partials go through LDS behind a workgroup barrier.
+    ("f32", (3, 37, 1024), (1, 12, 1024), (1, 4, 1024), 4, 256, 0, 0, None, True),    # 4 loads per stage, cut stage
+    ("f32", (3, 37, 1024), (1, 4, 1024), (1, 4, 1024), 2, 256, 5, 0, None, True),     # persistent, uneven
+    ("f32", (3, 37, 1024), (1, 4, 1024), (1, 2, 1024), 3, 256, 0, 0, None, False),    # 2 rows over 4 waves
+    ("f16", (2, 70, 256), (1, 8, 256), (1, 8, 256), 3, 64, 5, 3, None, False),        # swizzled f16, 8 rows per stage
+    ("f32", (5, 64, 64), (1, 16, 64), (1, 16, 64), 4, 64, 0, 0, None, False),         # 16 rows per wave block
+    ("f32", (4, 33, 96), (1, 8, 96), (1, 8, 96), 3, 192, 0, 0, 104, False),           # padded rows, 3 waves
+    ("f32", (3, 37, 1024), (1, 4, 1024), (1, 1, 1024), 3, 64, 0, 0, None, True),      # one wave, 4 stages per tile
+    ("f32", (3, 37, 1024), (1, 2, 1024), (1, 2, 1024), 2, 64, 7, 0, None, True),      # one wave, persistent
+    ("f16", (2, 50, 2048), (1, 5, 2048), (1, 1, 2048), 4, 64, 0, 3, None, True),      # swizzled f16 rows of 4 KiB
+    ("f32", (4, 20, 512), (1, 4, 512), (1, 2, 512), 2, 64, 0, 0, None, True),         # 2 KiB rows, two blocks each
 ])
-def test_row_reduction_matches_oracle(dt, shape, box, stage_box, stages, threads, workgroups, swz, pitch):
+def test_row_reduction_matches_oracle(dt, shape, box, stage_box, stages, threads, workgroups, swz, pitch, local):
     say(f"row reduction {dt} {shape} box {box} stage {stage_box} S={stages} wg={workgroups} swz {swz} pitch {pitch}")
     # integer inputs: every partial sum exact, so the result is the exact sum
     x, y = _reduce_rows_case(dt, shape, box, stage_box, stages, threads, workgroups, True, swz, pitch)
-    assert acp.acp_last_kernel().startswith("general row reduction")
+    kernel = acp.acp_last_kernel()
+    assert kernel.startswith("general row reduction") and kernel.endswith("wave-local" if local else "lds partials"), kernel
     assert np.array_equal(y, REF.reduce_rows(x))
     # real-valued inputs: within the recursive-summation bound of the exact sum
     x, y = _reduce_rows_case(dt, shape, box, stage_box, stages, threads, workgroups, False, swz, pitch, seed=62)
     _assert_within_sum_bound(x, y)
 
 
-def test_row_reduction_full_size():
-    shape, stage_box = (128, 500, 1024), (1, 2, 1024)
-    say(f"row reduction f32 {shape} stage {stage_box} S=4, 256 workgroups")
-    x, y = _reduce_rows_case("f32", shape, stage_box, stage_box, 4, 256, 256, False, seed=63)
+@pytest.mark.parametrize("stage_box,stages,threads,workgroups,local", [
+    ((1, 2, 1024), 4, 256, 256, False),
+    ((1, 4, 1024), 2, 256, 512, True),        # the bench shape
+    ((1, 1, 1024), 2, 64, 2048, True),
+])
+def test_row_reduction_full_size(stage_box, stages, threads, workgroups, local):
+    shape = (128, 500, 1024)
+    say(f"row reduction f32 {shape} stage {stage_box} S={stages}, {threads} threads, {workgroups} workgroups")
+    x, y = _reduce_rows_case("f32", shape, stage_box, stage_box, stages, threads, workgroups, False, seed=63)
+    assert acp.acp_last_kernel().endswith("wave-local" if local else "lds partials")
     _assert_within_sum_bound(x, y)
