@@ -1083,6 +1083,7 @@ struct GenPolicy {
   // wave-local rows: lane k holds the wave's k-th distinct row (in round
   // order; ~0 for none), its packed-row offset and cut-edge slots
   bool red_local;
+  bool one_row;      // wave-local: all of the wave's blocks lie in one row
   uint32_t lrow, loff, lbad;
   int wave, lane, rank, ab_instr, swizzle, esize_log2;
   bool load_nt, store_nt;
@@ -1249,13 +1250,27 @@ struct GenPolicy {
   // order, and one store instruction writes every row total of the trip.
   // No other wave is involved, so there is no barrier.
   __device__ __forceinline__ void reduce_rows_local(uint32_t sl, const T& t, __amdgpu_buffer_rsrc_t rs) {
-    float acc = 0.f;
+    float part[OUTER];
 #pragma unroll
     for (int f = 0; f < OUTER; ++f) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(
           __builtin_assume_aligned(lds + sl + f * waves_kb + wave * 1024u + lane * 16u, 16));
-      const float s = wave_sum(OP::chunk(v));
-      acc += (lrow == row_of[f]) ? s : 0.f;
+      part[f] = OP::chunk(v);
+    }
+    float acc = 0.f;
+    if (one_row) {
+      // every block of the wave lies in one row: each lane adds its chunk
+      // partials in round order, then one cross-lane sum
+      float p = part[0];
+#pragma unroll
+      for (int f = 1; f < OUTER; ++f) p += part[f];
+      acc = wave_sum(p);
+    } else {
+#pragma unroll
+      for (int f = 0; f < OUTER; ++f) {
+        const float s = wave_sum(part[f]);
+        acc += (lrow == row_of[f]) ? s : 0.f;
+      }
     }
     const bool ok = (t.flags & 0x100u) == 0 && lrow != ~0u && (lbad & t.flags & 0xFFu) == 0;
     const uint64_t g = t.rb + loff;
@@ -1530,6 +1545,9 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
     p.red_off = off;
     p.red_bad = bad;
     p.red_local = uni(A->red_local) != 0;
+    p.one_row = true;
+#pragma unroll
+    for (int f = 1; f < OUTER; ++f) p.one_row = p.one_row && p.row_of[f] == p.row_of[0];
     p.lrow = ~0u;
     p.loff = p.lbad = 0;
     if (p.red_local) {
