@@ -260,7 +260,7 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
       prev = d;
       lx = A.xstep[d];
       lo = A.ostep[d];
-      if (q.row_ops) {
+      if (q.row_ops || q.mode == 4) {
         if (d == r - 1) {
           lin = false;  // stages split rows: the row index is not linear in t
         } else {
@@ -315,6 +315,33 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   // every 1 KiB wave block inside one row: the innermost image run holds a
   // whole number of such blocks and nothing permutes it
   A.row_uniform = (q.row_ops && A.swizzle == 0 && (axes.back().count * ei) % (64 * p.vec_bytes) == 0) ? 1 : 0;
+  if (q.mode == 4) {
+    const int64_t row_bytes = x.shape[r - 1] * ei;
+    // Wave-local reduction when every 1 KiB wave block lies in one row and
+    // every row's blocks belong to one wave (block b goes to wave b % waves).
+    auto row_of = [&](int64_t e) {  // stage-packed row of image element e
+      int64_t row = 0;
+      for (size_t k = axes.size(); k-- > 0;) {
+        const int64_t idx = e % axes[k].count;
+        e /= axes[k].count;
+        if (axes[k].dim < r - 1) row += idx * axes[k].step * srow[axes[k].dim];
+      }
+      return row;
+    };
+    bool local = row_bytes % 1024 == 0;
+    std::vector<int> wave_of_row(static_cast<size_t>(n_rows), -1);
+    const int64_t blocks = p.tile_bytes() / 1024;
+    for (int64_t b = 0; local && b < blocks; ++b) {
+      const int64_t r0 = row_of(b * 1024 / ei);
+      for (int c = 1; c < 64 && local; ++c) local = row_of((b * 1024 + c * 16) / ei) == r0;
+      const int w = static_cast<int>(b % A.waves);
+      if (!local || r0 >= n_rows) break;
+      if (wave_of_row[r0] < 0) wave_of_row[r0] = w;
+      else if (wave_of_row[r0] != w) local = false;
+    }
+    static const bool local_ok = env_flag("ACP_REDUCE_LOCAL", true);
+    A.red_local = (local && local_ok) ? 1 : 0;
+  }
   L->key = acp::KernelKey{q.op, q.mode == 0 ? ACP_U32 : static_cast<int>(x.dtype),
                           q.mode == 0 ? ACP_U32 : (q.mode == 4 ? ACP_F32 : static_cast<int>(o.dtype)), p.vec_bytes,
                           q.mode, 0, 0};
@@ -362,6 +389,18 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
         A.lin_o *= t;
         A.n_tiles = static_cast<uint32_t>(n_tiles / t);
       }
+    }
+  }
+  // wave-local row reduction on a linear stage grid with 16-byte rounds
+  static const bool lin_rows_ok = env_flag("ACP_LIN_ROWS", true);
+  if (lin_rows_ok && !fast && q.mode == 4 && A.lin && A.red_local && p.vec_bytes == 16 &&
+      (p.outer == 1 || p.outer == 2 || p.outer == 4 || p.outer == 8)) {
+    acp::KernelKey rk = L->key;
+    rk.mode = 10;
+    rk.outer = p.outer;
+    if (acp::engine_kernel(rk)) {
+      L->key = rk;
+      fast = true;
     }
   }
   // any other grid with 16-byte rounds: the general lean kernel
@@ -422,32 +461,8 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
     A.red_rows = static_cast<uint32_t>(n_rows);
     A.part_bytes = static_cast<uint32_t>(n_rows * (row_bytes / 16) * 4);
     A.part_off = static_cast<uint32_t>(lds);
-    lds += 2 * static_cast<int64_t>(A.part_bytes);
+    if (!A.red_local) lds += 2 * static_cast<int64_t>(A.part_bytes);  // the wave-local path needs none
     for (int d = 0; d + 1 < r; ++d) A.rowstr[d] = static_cast<uint32_t>(rowstride[d]);
-    // Wave-local reduction when every 1 KiB wave block lies in one row and
-    // every row's blocks belong to one wave (block b goes to wave b % waves).
-    auto row_of = [&](int64_t e) {  // stage-packed row of image element e
-      int64_t row = 0;
-      for (size_t k = axes.size(); k-- > 0;) {
-        const int64_t idx = e % axes[k].count;
-        e /= axes[k].count;
-        if (axes[k].dim < r - 1) row += idx * axes[k].step * srow[axes[k].dim];
-      }
-      return row;
-    };
-    bool local = row_bytes % 1024 == 0;
-    std::vector<int> wave_of_row(static_cast<size_t>(n_rows), -1);
-    const int64_t blocks = p.tile_bytes() / 1024;
-    for (int64_t b = 0; local && b < blocks; ++b) {
-      const int64_t r0 = row_of(b * 1024 / ei);
-      for (int c = 1; c < 64 && local; ++c) local = row_of((b * 1024 + c * 16) / ei) == r0;
-      const int w = static_cast<int>(b % A.waves);
-      if (!local || r0 >= n_rows) break;
-      if (wave_of_row[r0] < 0) wave_of_row[r0] = w;
-      else if (wave_of_row[r0] != w) local = false;
-    }
-    static const bool local_ok = env_flag("ACP_REDUCE_LOCAL", true);
-    A.red_local = (local && local_ok) ? 1 : 0;
   }
   const int limit = device_lds_limit();
   if (lds > limit)
@@ -502,13 +517,13 @@ acp_status launch(const Launch& L, void* stream) {
   static const char* const kinds[] = {"engine copy",        "engine tile ewise",  "engine stream",
                                       "stream linear grid", "general copy",       "general tile ewise",
                                       "general stream",     "general reduce-add", "general row reduction",
-                                      "tile linear grid"};
+                                      "tile linear grid",   "row reduction linear grid"};
   const int m = L.key.mode;
-  g_last_kernel = std::string(m >= 0 && m <= 9 ? kinds[m] : "?") + " vec " + std::to_string(L.key.vec_bytes) +
+  g_last_kernel = std::string(m >= 0 && m <= 10 ? kinds[m] : "?") + " vec " + std::to_string(L.key.vec_bytes) +
                   " rounds " + std::to_string(L.args.outer) + " srow " + std::to_string(L.key.srow) + " variant " +
                   std::to_string(L.key.variant) + " grid " + std::to_string(L.grid) + " threads " +
                   std::to_string(L.block) + " slots " + std::to_string(L.args.stages) + " lds " + std::to_string(L.lds) +
-                  (m == 8 ? std::string(L.args.red_local ? " wave-local" : " lds partials") : std::string());
+                  (m == 8 || m == 10 ? std::string(L.args.red_local ? " wave-local" : " lds partials") : std::string());
   return ret(ACP_OK);
 }
 
@@ -930,7 +945,7 @@ acp_status acp_stream_reduce_rows(acp_op op, float* out, const acp_tile_desc* x,
   Launch L;
   const acp_status st = prepare(q, &L);
   if (st != ACP_OK) return st;
-  if (L.key.mode != 8)
+  if (L.key.mode != 8 && L.key.mode != 10)
     return ret(ACP_ERR_UNSUPPORTED, "row reduction needs 16-byte rounds and 1, 2, 4 or 8 rounds per thread");
   if (L.args.red_rows > 64u * static_cast<uint32_t>(L.args.waves))
     return ret(ACP_ERR_UNSUPPORTED, "row reduction stages hold at most 64 rows per wave");

@@ -106,8 +106,9 @@ struct KernelKey {
   int vec_bytes; // 16 or 4
   int mode;      // 0 copy, 1 tile ewise (output staged in LDS), 2 stream, 3 stream on a linear grid,
                  // 4 / 5 / 6 / 7 / 8: copy / tile ewise / stream / store with reduce-add /
-                 // row reduction in the general lean kernel, 9 tile ewise on a linear grid
-  int outer;     // modes 3..9: rounds per thread (1, 2, 4 or 8); 0 otherwise
+                 // row reduction in the general lean kernel, 9 tile ewise on a linear grid,
+                 // 10 wave-local row reduction on a linear grid
+  int outer;     // modes 3..10: rounds per thread (1, 2, 4 or 8); 0 otherwise
   int srow;      // modes 3 and 6, row ops: per-row scalars through the scalar cache
   int variant = 0;  // mode 6, add / mul of two streamed tensors: 1 both on the direct-to-LDS
                     // ring, 2 the second one loaded synchronously ("Set") into its slot

@@ -70,9 +70,15 @@ __device__ __forceinline__ uint32_t uni(uint32_t v) {
 
 // Range of a buffer resource starting `off` bytes into a tensor of `span`
 // bytes: it ends at the tensor's end (and below the out-of-bounds offset).
+// Both values lie below 2^63, so span - off read as a signed number tells
+// whether off is past the span; the clamp works on 32-bit halves, which
+// keeps the whole computation in scalar instructions.
 __device__ __forceinline__ uint32_t range_from(uint64_t span, uint64_t off) {
-  const uint64_t left = span > off ? span - off : 0;
-  return static_cast<uint32_t>(left < kOobOffset ? left : kOobOffset - 16u);
+  const uint64_t d = span - off;
+  const uint32_t hi = static_cast<uint32_t>(d >> 32), lo = static_cast<uint32_t>(d);
+  if (static_cast<int32_t>(hi) < 0) return 0u;
+  if (hi != 0u || lo >= kOobOffset) return kOobOffset - 16u;
+  return lo;
 }
 
 // Buffer resource for the asm loads: raw (stride 0), 32-bit data format.
@@ -999,6 +1005,127 @@ __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
 }
 
 // ---------------------------------------------------------------------------
+// Row reduction on a linear stage grid whose wave blocks each lie in one row
+// and whose rows each lie in one wave (the wave-local case): the linear
+// kernel's lean trip (stage base = one multiply) with the wave-local
+// reduction of the general kernel.  Stage s holds rows s * lin_r + (the
+// packed offsets of its rows); lane k of a wave owns the wave's k-th
+// distinct row.
+
+template <class OP, int OUTER>
+struct LinRowsPolicy {
+  unsigned char* lds;
+  const char* in0;
+  __amdgpu_buffer_rsrc_t out_rs;  // the whole row array
+  uint64_t in_span, lin_x, lin_r;
+  uint32_t lds0, slot_bytes, wg, grid, waves_kb;
+  int wave, lane;
+  bool load_nt, one_row;
+  uint32_t xoff[OUTER], row_of[OUTER];
+  uint32_t lrow, loff;  // this lane's row of the stage (~0: none) and its packed offset
+
+  __device__ __forceinline__ uint64_t stage(int j) const { return wg + static_cast<uint64_t>(j) * grid; }
+
+  __device__ __forceinline__ void load(int j, int slot) {
+    const uint64_t xb = stage(j) * lin_x;
+    const v4i rs = rsrc_v4(in0 + xb, range_from(in_span, xb));
+    const uint32_t base = lds0 + slot * slot_bytes + wave * 1024u;
+#pragma unroll
+    for (int f = 0; f < OUTER; ++f) dma_b128(rs, xoff[f], base + f * waves_kb, load_nt);
+  }
+  __device__ __forceinline__ void wait(int, int, int k) { wait_vmcnt(k); }
+
+  __device__ __forceinline__ void consume(int i, int slot) {
+    const uint32_t sl = slot * slot_bytes;
+    float part[OUTER];
+#pragma unroll
+    for (int f = 0; f < OUTER; ++f) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(
+          __builtin_assume_aligned(lds + sl + f * waves_kb + wave * 1024u + lane * 16u, 16));
+      part[f] = OP::chunk(v);
+    }
+    float acc = 0.f;
+    if (one_row) {
+      float p = part[0];
+#pragma unroll
+      for (int f = 1; f < OUTER; ++f) p += part[f];
+      acc = wave_sum(p);
+    } else {
+#pragma unroll
+      for (int f = 0; f < OUTER; ++f) {
+        const float s = wave_sum(part[f]);
+        acc += (lrow == row_of[f]) ? s : 0.f;
+      }
+    }
+    const uint64_t g = stage(i) * lin_r + loff;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc), out_rs,
+                                          lrow != ~0u ? static_cast<uint32_t>(g * 4u) : kOobOffset, 0, 0);
+  }
+};
+
+template <class OP, int OUTER>
+__global__ __launch_bounds__(1024) void rows_lin_kernel_t(const EngineArgs) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+  CArgs* A = kargs();
+  const int lane = threadIdx.x & 63;
+  const int wave = uni(static_cast<int>(threadIdx.x >> 6));
+  const uint32_t grid = gridDim.x;
+  uint32_t wg = blockIdx.x;
+  if (A->xcd_remap) wg = (wg & 7u) * (grid >> 3) + (wg >> 3);
+  const uint32_t n_tiles = A->n_tiles;
+  const int n = static_cast<int>(wg < n_tiles ? (n_tiles - wg + grid - 1) / grid : 0);
+  if (n == 0) return;
+  LaneMap m;
+  build_map<16>(A, wave, lane, m);
+  const Loc L = load_loc(A);
+  LinRowsPolicy<OP, OUTER> p;
+  p.lds = lds;
+  p.in0 = L.in[0];
+  p.out_rs = rsrc_store(L.out, range_from(L.out_span, 0));
+  p.in_span = L.in_span;
+  p.lin_x = static_cast<uint64_t>(L.lin_x);
+  p.lin_r = static_cast<uint64_t>(L.lin_r);
+  p.lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  p.slot_bytes = L.slot_bytes;
+  p.wg = wg;
+  p.grid = grid;
+  p.waves_kb = static_cast<uint32_t>(L.waves) * 1024u;
+  p.wave = wave;
+  p.lane = lane;
+  p.load_nt = L.load_nt != 0;
+#pragma unroll
+  for (int f = 0; f < OUTER; ++f) {
+    p.xoff[f] = m.xoff[f];
+    const uint32_t abo = uni(m.abo[f]);
+    p.row_of[f] = (abo >> 8) * 32u + (abo & 255u) / 4u;
+  }
+  p.one_row = true;
+#pragma unroll
+  for (int f = 1; f < OUTER; ++f) p.one_row = p.one_row && p.row_of[f] == p.row_of[0];
+  // the wave's distinct rows in round order; lane k takes the k-th
+  p.lrow = ~0u;
+  uint32_t n_local = 0;
+#pragma unroll
+  for (int f = 0; f < OUTER; ++f) {
+    bool seen = false;
+#pragma unroll
+    for (int g = 0; g < f; ++g) seen = seen || (p.row_of[g] == p.row_of[f]);
+    if (!seen) {
+      if (static_cast<uint32_t>(lane) == n_local) p.lrow = p.row_of[f];
+      ++n_local;
+    }
+  }
+  uint32_t rr = p.lrow != ~0u ? p.lrow : 0u, off = 0;
+  for (int dd = uni(A->rank) - 2; dd >= 0; --dd) {
+    const uint32_t sb = A->sbox[dd];
+    off += (rr % sb) * A->rowstr[dd];
+    rr /= sb;
+  }
+  p.loff = off;
+  run_ring(p, n, uni(A->stages), OUTER, 1);
+}
+
+// ---------------------------------------------------------------------------
 // General lean kernel: any stage grid (partial and out-of-range stages,
 // sub-stages inside a workgroup tile, persistent grids), 16-byte rounds,
 // OUTER rounds per thread known at compile time.  Trip geometry lives in a
@@ -1641,6 +1768,11 @@ struct KernelEntry {
 #define ACP_LIN_TILE(OPC, TIN, TOUT, ...)                                                \
   ACP_LT1(OPC, TIN, TOUT, 1, __VA_ARGS__), ACP_LT1(OPC, TIN, TOUT, 2, __VA_ARGS__),       \
       ACP_LT1(OPC, TIN, TOUT, 4, __VA_ARGS__), ACP_LT1(OPC, TIN, TOUT, 8, __VA_ARGS__)
+// row reduction on a linear stage grid, wave-local (mode key 10)
+#define ACP_LR1(T, OUTER)                                           \
+  KernelEntry{KernelKey{kOpAdd, T, kF32, 16, 10, OUTER, 0},         \
+              reinterpret_cast<const void*>(&dev::rows_lin_kernel_t<dev::ReduceRowsOp<T>, OUTER>)}
+#define ACP_LIN_ROWS(T) ACP_LR1(T, 1), ACP_LR1(T, 2), ACP_LR1(T, 4), ACP_LR1(T, 8)
 #define ACP_BOTH(OPC, TIN, TOUT, MODE, ...) ACP_K(OPC, TIN, TOUT, 16, MODE, __VA_ARGS__), ACP_K(OPC, TIN, TOUT, 4, MODE, __VA_ARGS__)
 
 template <size_t N>

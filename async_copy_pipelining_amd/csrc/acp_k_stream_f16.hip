@@ -27,6 +27,7 @@ const KernelEntry kTable[] = {
     ACP_GEN_BIN(kOpMul, kF16, Op<kOpMul, kF16, kF16>),
     // row reduction
     ACP_GEN(kOpAdd, kF16, kF32, 4, ReduceRowsOp<kF16>),
+    ACP_LIN_ROWS(kF16),
 };
 }  // namespace
 const void* lookup_stream_f16(const KernelKey& k) { return find_entry(kTable, k); }

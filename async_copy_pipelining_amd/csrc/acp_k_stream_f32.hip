@@ -36,6 +36,7 @@ const KernelEntry kTable[] = {
     ACP_GEN_BIN(kOpMul, kF32, Op<kOpMul, kF32, kF32>),
     // row reduction
     ACP_GEN(kOpAdd, kF32, kF32, 4, ReduceRowsOp<kF32>),
+    ACP_LIN_ROWS(kF32),
 };
 }  // namespace
 const void* lookup_stream_f32(const KernelKey& k) { return find_entry(kTable, k); }

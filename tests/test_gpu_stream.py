@@ -261,44 +261,61 @@ def _assert_within_sum_bound(x, y):
     assert np.all(err <= bound), float((err - bound).max())
 
 
-@pytest.mark.parametrize("dt,shape,box,stage_box,stages,threads,workgroups,swz,pitch,local", [
+# kernel kinds: the linear-grid kernel (full stages on a row-major stage
+# grid, wave-local) and the general kernel, wave-local or through LDS
+LIN, LOCAL, LDS = ("row reduction linear grid", "wave-local"), ("general row reduction", "wave-local"), \
+    ("general row reduction", "lds partials")
+
+
+@pytest.mark.parametrize("dt,shape,box,stage_box,stages,threads,workgroups,swz,pitch,kind", [
     # The stage image is issue-major (rows wider than 256 elements load as
     # 256-element segments), so 1 KiB block b of a (1, R, 1024) f32 stage is
     # segment b // R of row b % R and goes to wave b % waves: with R equal
     # to the wave count (or one wave) every row's blocks meet in one wave,
     # which then reduces its rows alone ("wave-local"); otherwise the chunk
     # partials go through LDS behind a workgroup barrier.
-    ("f32", (3, 37, 1024), (1, 12, 1024), (1, 4, 1024), 4, 256, 0, 0, None, True),    # 4 loads per stage, cut stage
-    ("f32", (3, 37, 1024), (1, 4, 1024), (1, 4, 1024), 2, 256, 5, 0, None, True),     # persistent, uneven
-    ("f32", (3, 37, 1024), (1, 4, 1024), (1, 2, 1024), 3, 256, 0, 0, None, False),    # 2 rows over 4 waves
-    ("f16", (2, 70, 256), (1, 8, 256), (1, 8, 256), 3, 64, 5, 3, None, False),        # swizzled f16, 8 rows per stage
-    ("f32", (5, 64, 64), (1, 16, 64), (1, 16, 64), 4, 64, 0, 0, None, False),         # 16 rows per wave block
-    ("f32", (4, 33, 96), (1, 8, 96), (1, 8, 96), 3, 192, 0, 0, 104, False),           # padded rows, 3 waves
-    ("f32", (3, 37, 1024), (1, 4, 1024), (1, 1, 1024), 3, 64, 0, 0, None, True),      # one wave, 4 stages per tile
-    ("f32", (3, 37, 1024), (1, 2, 1024), (1, 2, 1024), 2, 64, 7, 0, None, True),      # one wave, persistent
-    ("f16", (2, 50, 2048), (1, 5, 2048), (1, 1, 2048), 4, 64, 0, 3, None, True),      # swizzled f16 rows of 4 KiB
-    ("f32", (4, 20, 512), (1, 4, 512), (1, 2, 512), 2, 64, 0, 0, None, True),         # 2 KiB rows, two blocks each
+    ("f32", (3, 37, 1024), (1, 12, 1024), (1, 4, 1024), 4, 256, 0, 0, None, LOCAL),   # 4 loads per stage, cut stage
+    ("f32", (3, 37, 1024), (1, 4, 1024), (1, 4, 1024), 2, 256, 5, 0, None, LOCAL),    # persistent, uneven
+    ("f32", (3, 37, 1024), (1, 4, 1024), (1, 2, 1024), 3, 256, 0, 0, None, LDS),      # 2 rows over 4 waves
+    ("f16", (2, 70, 256), (1, 8, 256), (1, 8, 256), 3, 64, 5, 3, None, LDS),          # swizzled f16, 8 rows per stage
+    ("f32", (5, 64, 64), (1, 16, 64), (1, 16, 64), 4, 64, 0, 0, None, LDS),           # 16 rows per wave block
+    ("f32", (4, 33, 96), (1, 8, 96), (1, 8, 96), 3, 192, 0, 0, 104, LDS),             # padded rows, 3 waves
+    ("f32", (3, 37, 1024), (1, 4, 1024), (1, 1, 1024), 3, 64, 0, 0, None, LOCAL),     # one wave, 4 stages per tile
+    ("f32", (3, 37, 1024), (1, 2, 1024), (1, 2, 1024), 2, 64, 7, 0, None, LOCAL),     # one wave, persistent
+    ("f16", (2, 50, 2048), (1, 5, 2048), (1, 1, 2048), 4, 64, 0, 3, None, LOCAL),     # swizzled f16 rows of 4 KiB
+    ("f32", (4, 20, 512), (1, 4, 512), (1, 2, 512), 2, 64, 0, 0, None, LOCAL),        # 2 KiB rows, two blocks each
+    # full stages on a row-major stage grid: the linear-grid kernel
+    ("f32", (3, 36, 1024), (1, 4, 1024), (1, 4, 1024), 2, 256, 5, 0, None, LIN),      # persistent, uneven
+    ("f32", (3, 36, 1024), (1, 2, 1024), (1, 2, 1024), 4, 64, 0, 0, None, LIN),       # one wave, 2 rows per stage
+    ("f16", (2, 50, 2048), (1, 1, 2048), (1, 1, 2048), 3, 64, 9, 3, None, LIN),       # swizzled f16 rows of 4 KiB
+    ("f32", (4, 20, 512), (1, 2, 512), (1, 2, 512), 2, 64, 0, 0, None, LIN),          # 2 KiB rows
+    # a 64-byte swizzle splits 2 KiB rows into 64-byte atoms (atom axis
+    # outermost), so every 1 KiB block spans both rows of the stage
+    ("f32", (4, 20, 512), (1, 2, 512), (1, 2, 512), 2, 64, 0, 2, None, LDS),
+    # stage rows 40 apart: the stage grid is not row-major contiguous
+    ("f32", (2, 8, 40, 1024), (1, 2, 4, 1024), (1, 2, 4, 1024), 3, 256, 11, 0, None, LOCAL),
 ])
-def test_row_reduction_matches_oracle(dt, shape, box, stage_box, stages, threads, workgroups, swz, pitch, local):
+def test_row_reduction_matches_oracle(dt, shape, box, stage_box, stages, threads, workgroups, swz, pitch, kind):
     say(f"row reduction {dt} {shape} box {box} stage {stage_box} S={stages} wg={workgroups} swz {swz} pitch {pitch}")
     # integer inputs: every partial sum exact, so the result is the exact sum
     x, y = _reduce_rows_case(dt, shape, box, stage_box, stages, threads, workgroups, True, swz, pitch)
     kernel = acp.acp_last_kernel()
-    assert kernel.startswith("general row reduction") and kernel.endswith("wave-local" if local else "lds partials"), kernel
+    assert kernel.startswith(kind[0]) and kernel.endswith(kind[1]), kernel
     assert np.array_equal(y, REF.reduce_rows(x))
     # real-valued inputs: within the recursive-summation bound of the exact sum
     x, y = _reduce_rows_case(dt, shape, box, stage_box, stages, threads, workgroups, False, swz, pitch, seed=62)
     _assert_within_sum_bound(x, y)
 
 
-@pytest.mark.parametrize("stage_box,stages,threads,workgroups,local", [
-    ((1, 2, 1024), 4, 256, 256, False),
-    ((1, 4, 1024), 2, 256, 512, True),        # the bench shape
-    ((1, 1, 1024), 2, 64, 2048, True),
+@pytest.mark.parametrize("stage_box,stages,threads,workgroups,kind", [
+    ((1, 2, 1024), 4, 256, 256, LDS),
+    ((1, 4, 1024), 2, 256, 512, LIN),          # the bench shape
+    ((1, 1, 1024), 2, 64, 2048, LIN),
 ])
-def test_row_reduction_full_size(stage_box, stages, threads, workgroups, local):
+def test_row_reduction_full_size(stage_box, stages, threads, workgroups, kind):
     shape = (128, 500, 1024)
     say(f"row reduction f32 {shape} stage {stage_box} S={stages}, {threads} threads, {workgroups} workgroups")
     x, y = _reduce_rows_case("f32", shape, stage_box, stage_box, stages, threads, workgroups, False, seed=63)
-    assert acp.acp_last_kernel().endswith("wave-local" if local else "lds partials")
+    kernel = acp.acp_last_kernel()
+    assert kernel.startswith(kind[0]) and kernel.endswith(kind[1]), kernel
     _assert_within_sum_bound(x, y)
