@@ -348,11 +348,13 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   // streaming on a linear grid with 16-byte rounds: the lean kernel
   static const bool fast_ok = env_flag("ACP_FAST_PATH", true);
   bool fast = false;
-  if (fast_ok && q.mode == 2 && A.lin && p.vec_bytes == 16 && q.n_in == 1 &&
+  // (two tensors: with both on the direct-to-LDS ring)
+  if (fast_ok && q.mode == 2 && A.lin && p.vec_bytes == 16 && (q.n_in == 1 || q.binary == 1) &&
       (p.outer == 1 || p.outer == 2 || p.outer == 4 || p.outer == 8)) {
     acp::KernelKey fk = L->key;
     fk.mode = 3;
     fk.outer = p.outer;
+    fk.variant = q.binary;
     static const bool srow_ok = env_flag("ACP_SCALAR_ROWS", true);
     fk.srow = (A.row_uniform && srow_ok) ? 1 : 0;
     if (acp::engine_kernel(fk)) {

@@ -110,7 +110,7 @@ struct KernelKey {
                  // 10 wave-local row reduction on a linear grid
   int outer;     // modes 3..10: rounds per thread (1, 2, 4 or 8); 0 otherwise
   int srow;      // modes 3 and 6, row ops: per-row scalars through the scalar cache
-  int variant = 0;  // mode 6, add / mul of two streamed tensors: 1 both on the direct-to-LDS
+  int variant = 0;  // modes 3 and 6, add / mul of two streamed tensors: 1 both on the direct-to-LDS
                     // ring, 2 the second one loaded synchronously ("Set") into its slot
 };
 

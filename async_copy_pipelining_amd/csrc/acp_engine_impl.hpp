@@ -808,8 +808,8 @@ constexpr int round_group(int total, int ns, int cap) {
 
 template <class OP, int OUTER, bool SROW, bool STAGE_OUT>
 struct LinPolicy {
-  // staged operands per trip
-  static constexpr int NL = STAGE_OUT ? OP::NIN : 1;
+  // staged operands per trip (a stream stages x, and z for two-tensor ops)
+  static constexpr int NL = STAGE_OUT ? OP::NIN : (OP::NIN > 1 ? OP::NIN : 1);
   unsigned char* lds;
   const char* in[3];
   char* out;
@@ -1761,6 +1761,12 @@ struct KernelEntry {
   ACP_LIN(OPC, kF32, kF32, __VA_ARGS__), ACP_L(OPC, kF32, kF32, 1, 1, __VA_ARGS__),                          \
       ACP_L(OPC, kF32, kF32, 2, 1, __VA_ARGS__), ACP_L(OPC, kF32, kF32, 4, 1, __VA_ARGS__), \
       ACP_L(OPC, kF32, kF32, 8, 1, __VA_ARGS__)
+// two streamed tensors on a linear grid, both on the direct-to-LDS ring (mode key 3, variant 1)
+#define ACP_LB1(OPC, T, OUTER, ...)                          \
+  KernelEntry{KernelKey{OPC, T, T, 16, 3, OUTER, 0, 1}, \
+              reinterpret_cast<const void*>(&dev::stream_lin_kernel_t<__VA_ARGS__, OUTER, false>)}
+#define ACP_LIN_BIN(OPC, T, ...) \
+  ACP_LB1(OPC, T, 1, __VA_ARGS__), ACP_LB1(OPC, T, 2, __VA_ARGS__), ACP_LB1(OPC, T, 4, __VA_ARGS__), ACP_LB1(OPC, T, 8, __VA_ARGS__)
 // tile ewise on a linear tile grid (mode key 9): the linear kernel with the output staged in LDS
 #define ACP_LT1(OPC, TIN, TOUT, OUTER, ...)                \
   KernelEntry{KernelKey{OPC, TIN, TOUT, 16, 9, OUTER, 0}, \

@@ -25,6 +25,8 @@ const KernelEntry kTable[] = {
     // two streamed tensors
     ACP_GEN_BIN(kOpAdd, kF16, Op<kOpAdd, kF16, kF16>),
     ACP_GEN_BIN(kOpMul, kF16, Op<kOpMul, kF16, kF16>),
+    ACP_LIN_BIN(kOpAdd, kF16, Op<kOpAdd, kF16, kF16>),
+    ACP_LIN_BIN(kOpMul, kF16, Op<kOpMul, kF16, kF16>),
     // row reduction
     ACP_GEN(kOpAdd, kF16, kF32, 4, ReduceRowsOp<kF16>),
     ACP_LIN_ROWS(kF16),

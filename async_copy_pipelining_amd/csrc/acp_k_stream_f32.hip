@@ -34,6 +34,8 @@ const KernelEntry kTable[] = {
     // two streamed tensors
     ACP_GEN_BIN(kOpAdd, kF32, Op<kOpAdd, kF32, kF32>),
     ACP_GEN_BIN(kOpMul, kF32, Op<kOpMul, kF32, kF32>),
+    ACP_LIN_BIN(kOpAdd, kF32, Op<kOpAdd, kF32, kF32>),
+    ACP_LIN_BIN(kOpMul, kF32, Op<kOpMul, kF32, kF32>),
     // row reduction
     ACP_GEN(kOpAdd, kF32, kF32, 4, ReduceRowsOp<kF32>),
     ACP_LIN_ROWS(kF32),

@@ -65,20 +65,33 @@ def parse():
                          "calib: torch's copy of 256 MiB, the known-size kernel that scales HBM counters; "
                          "copy_ref: the library's register-path reference copy of the c4 tensor "
                          "(the plain 1:1 read/write ceiling)")
-    ap.add_argument("--stages", type=int, default=4)
+    ap.add_argument("--stages", type=int, default=None,
+                    help="ring slots (default: the measured best per workload; c4 and c5: 4)")
     ap.add_argument("--z-staging", default="ring", choices=["ring", "set"],
                     help="pointwise: how the second tensor reaches the ring")
     ap.add_argument("--reduce-over-batch", action="store_true",
                     help="reduce: add all 128 slabs into one [500,1024] destination (else slab by slab)")
-    ap.add_argument("--rows", type=int, default=2, help="rows per ring stage (c4)")
+    ap.add_argument("--rows", type=int, default=None,
+                    help="rows per ring stage or tile (default per workload: c4 2, pointwise / reduce / rowsum 4, "
+                         "reduce --reduce-over-batch 1)")
     ap.add_argument("--threads", type=int, default=256)
-    ap.add_argument("--workgroups", type=int, default=0, help="persistent workgroups (0: 256 x --wg-per-cu)")
+    ap.add_argument("--workgroups", type=int, default=None,
+                    help="persistent workgroups (default 256 x --wg-per-cu; rowsum 512)")
     ap.add_argument("--wg-per-cu", type=int, default=1)
     ap.add_argument("--sets", type=int, default=3, help="rotated buffer sets")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ring-sweep", action="store_true", help="c4: skip the 2/3-stage report (profiling runs)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    # defaults: the best launch shapes measured on MI355X for each workload
+    wl = args.workload
+    if args.rows is None:
+        args.rows = {"c4": 2, "pointwise": 4, "rowsum": 4}.get(wl, 1 if args.reduce_over_batch else 4)
+    if args.stages is None:
+        args.stages = 2 if wl in ("pointwise", "rowsum") else 4
+    if args.workgroups is None:
+        args.workgroups = 512 if wl == "rowsum" else 0
+    return args
 
 
 def main():

@@ -221,8 +221,8 @@ def _reduce_case(dt, src_shape, dst_shape, box, threads, values, swz=0, seed=51)
     ddesc = encode(dt, dd, dst_shape, packed_strides(dst_shape), box)
     acp.acp_tile_reduce("add", ddesc, sdesc, threads, stream())
     kernel = acp.acp_last_kernel()
-    if src_shape == dst_shape and dt != "u32":
-        assert kernel.startswith("general stream") and " variant 1 " in kernel      # ring path, no atomics
+    if src_shape == dst_shape and dt != "u32":                                   # ring path, no atomics
+        assert kernel.startswith(("general stream", "stream linear grid")) and " variant 1 " in kernel
     elif src_shape != dst_shape:
         assert kernel.startswith("general reduce-add"), kernel
     got = host(dd, npdt, dst_shape)

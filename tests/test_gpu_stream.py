@@ -206,13 +206,18 @@ def _binary_case(op, dt, shape, box, stage_box, stages, threads, workgroups, sta
     ("mul", "f32", (3, 37, 1024), (1, 4, 1024), (1, 4, 1024), 3, 256, 5, 0),    # persistent, uneven
     ("add", "f16", (2, 70, 256), (1, 8, 256), (1, 4, 128), 2, 64, 0, 3),        # swizzled, two loads per trip
     ("mul", "f16", (4, 33, 512), (1, 16, 256), (1, 16, 64), 4, 128, 7, 2),      # 64-byte swizzle, sub-stages
+    # full stages on a row-major stage grid: both tensors on the ring run the linear-grid kernel
+    ("add", "f32", (3, 36, 1024), (1, 4, 1024), (1, 4, 1024), 3, 256, 5, 0),    # persistent, uneven
+    ("mul", "f16", (4, 32, 512), (1, 8, 512), (1, 8, 512), 2, 128, 0, 3),       # swizzled, one tile per workgroup
 ])
 def test_two_tensor_stream_matches_oracle(staging, op, dt, shape, box, stage_box, stages, threads, workgroups, swz):
     say(f"two-tensor stream {op} {dt} {shape} box {box} stage {stage_box} S={stages} wg={workgroups} "
         f"z={staging} swizzle {swz}")
     x, z, y = _binary_case(op, dt, shape, box, stage_box, stages, threads, workgroups, staging, swz)
-    assert acp.acp_last_kernel().startswith("general stream")
-    assert f" variant {1 if staging == 'ring' else 2} " in acp.acp_last_kernel()
+    kernel = acp.acp_last_kernel()
+    linear = box == stage_box and shape[1] % box[1] == 0
+    assert kernel.startswith("stream linear grid" if linear and staging == "ring" else "general stream"), kernel
+    assert f" variant {1 if staging == 'ring' else 2} " in kernel
     ref = REF.ewise(op, [x, z], y.dtype)
     bits = np.uint16 if dt == "f16" else np.uint32
     assert np.array_equal(y.view(bits), ref.view(bits))
@@ -223,6 +228,7 @@ def test_two_tensor_stream_full_size_sampled(staging):
     shape, stage_box = (128, 500, 1024), (1, 2, 1024)
     say(f"two-tensor stream add {shape} stage {stage_box} S=4, 256 workgroups, z={staging}")
     x, z, y = _binary_case("add", "f32", shape, stage_box, stage_box, 4, 256, 256, staging, seed=42)
+    assert acp.acp_last_kernel().startswith("stream linear grid" if staging == "ring" else "general stream")
     rng = np.random.default_rng(43)
     i0, i1 = rng.integers(0, 128, 2000), rng.integers(0, 500, 2000)
     ref = REF.ewise("add", [x[i0, i1], z[i0, i1]], np.float32)
