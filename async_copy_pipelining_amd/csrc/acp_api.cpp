@@ -100,8 +100,12 @@ int device_lds_limit() {
 // measured 3.6 against 3.1 TB/s for 128x32 float16 tiles, whose 64-byte rows
 // share each cache line with the neighbouring tile.
 //   ACP_FAST_PATH=0  no linear-grid streaming kernel
+//   ACP_LIN_TILE=0   no linear-grid kernel for tile ewise
+//   ACP_LIN_ROWS=0   no linear-grid kernel for wave-local row sums
 //   ACP_GEN_PATH=0   no general lean kernel (the rolled engine runs instead)
 //   ACP_SCALAR_ROWS=0  stage per-row scalars in LDS even when rows are uniform per wave block
+//   ACP_REDUCE_LOCAL=0, ACP_REDUCE_GROUPED=0  row sums through LDS partials only; reduce-add over
+//                    batch dims with one atomic per staged element
 bool env_flag(const char* name, bool dflt) {
   const char* e = std::getenv(name);
   if (!e || !e[0]) return dflt;
