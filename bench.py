@@ -33,11 +33,19 @@ KERNEL_SOURCES = ["acp_engine_impl.hpp", "acp_engine.hpp", "acp_k_stream_f32.hip
                   "acp_k_tile.hip", "acp_k_tile_gen.hip", "acp_k_tile_lin.hip", "acp_k_copy.hip", "acp_api.cpp"]
 
 
+def _code_only(text: str) -> str:
+    """The source with comments removed and whitespace collapsed: a change
+    to comments alone leaves the kernels, and so the hash, unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "async_copy_pipelining_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "async_copy_pipelining_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
