@@ -29,8 +29,10 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "achieved HBM GB/s (and % of peak) for pipelined tile copy+ewise, 1 MI355X"
 PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["acp_engine_impl.hpp", "acp_engine.hpp", "acp_k_stream_f32.hip", "acp_k_stream_f16.hip",
-                  "acp_k_tile.hip", "acp_k_tile_gen.hip", "acp_k_tile_lin.hip", "acp_k_copy.hip", "acp_api.cpp"]
+KERNEL_SOURCES = ["acp_dev_base.hpp", "acp_dev_ops.hpp", "acp_dev_map.hpp", "acp_dev_engine.hpp", "acp_dev_lin.hpp",
+                  "acp_dev_gen.hpp", "acp_engine_impl.hpp", "acp_engine.hpp", "acp_k_stream_f32.hip",
+                  "acp_k_stream_f16.hip", "acp_k_tile.hip", "acp_k_tile_gen.hip", "acp_k_tile_lin.hip",
+                  "acp_k_copy.hip", "acp_api.cpp"]
 
 
 def _code_only(text: str) -> str:
