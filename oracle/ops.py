@@ -6,10 +6,10 @@ taken per component) and "How inputs change the algorithm" (fma is
 a * b + c).
 
 Precision readings:
-* Every op computes in binary64 from exactly widened inputs and rounds once
-  to the output type (binary32 or binary16).  For add, mul and sqrt that one
-  extra rounding through binary64 is harmless because 53 >= 2p + 2 for
-  p = 24 and p = 11 (double rounding is innocuous for these operations).
+* add and mul compute in binary64 from exactly widened inputs (all of one
+  type) and round once to that type.  The extra rounding through binary64 is
+  harmless because 53 >= 2p + 2 for p = 24 and p = 11 (double rounding is
+  innocuous for these operations).
 * fma is fused: ONE rounding of the exact a * x + b.  The product of two
   binary32 (or binary16) values is exact in binary64; the sum is formed in
   binary64 with round-to-odd (TwoSum error term, then force the last bit odd
@@ -17,9 +17,17 @@ Precision readings:
   53 >= p + 2 bits makes the second rounding correct (Boldo & Melquiond,
   "Emulation of FMA and correctly rounded sums: proved algorithms using
   rounding to odd", IEEE TC 2008).
-* exp is exp(x) in binary64 rounded to the output type: within half an ulp
-  plus 2^-53 relative of the exact value; a result within 1 ulp of it is
-  accepted for exp.
+* sqrt and exp compute in binary32 (the unary ops of "elementwise -> smem"
+  take float16 or float32 and compute in float32; reading adopted): the
+  result is the binary32 one (sqrt correctly rounded, exp(x) in binary64
+  rounded) converted to the output type.  With binary32 or binary16 inputs
+  and a binary32 output that is one rounding.  A binary16 output of a
+  binary32 input rounds twice: a binary32 result that falls exactly halfway
+  between two binary16 values resolves to the even one, whatever side the
+  exact value lay on.  (For binary16 inputs and output the two roundings
+  equal one: 24 >= 2 * 11 + 2.)
+* exp(x) in binary64 lies within half an ulp plus 2^-53 relative of the
+  exact value; a result within 1 ulp of the oracle's is accepted for exp.
 * zero writes +0 (all bits clear).
 """
 from __future__ import annotations
@@ -32,12 +40,12 @@ def _f64(x) -> np.ndarray:
 
 
 def sqrt(x, out_dtype=np.float32) -> np.ndarray:
-    return np.sqrt(_f64(x)).astype(out_dtype)
+    return np.sqrt(_f64(x)).astype(np.float32).astype(out_dtype)
 
 
 def exp(x, out_dtype=np.float32) -> np.ndarray:
     with np.errstate(over="ignore"):
-        return np.exp(_f64(x)).astype(out_dtype)
+        return np.exp(_f64(x)).astype(np.float32).astype(out_dtype)
 
 
 def add(a, b, out_dtype=np.float32) -> np.ndarray:

@@ -109,6 +109,27 @@ def test_sqrt_closed_forms():
     assert ops.sqrt(np.float16(4.0), np.float16) == np.float16(2.0)
 
 
+def test_sqrt_of_binary32_to_binary16_rounds_through_binary32():
+    # 469.33163 as binary32 is 469.331634521484375 = 2^-15 * 15379059.  Its
+    # root lies just above 21.6640625: 21.6640625^2 = 469.33160400390625,
+    # and 21.6640625 + 2^-20 (half a binary32 ulp at 16..32) squares to
+    # 21.6640625^2 + 2 * 21.6640625 * 2^-20 + 2^-40 > 469.3316731 > x.  So
+    # the binary32 root is 21.6640625 exactly, halfway between the binary16
+    # neighbours 21.65625 (significand 0x56A, even) and 21.671875 (0x56B):
+    # the binary16 result is the even one, 21.65625, while one rounding of
+    # the exact root would give 21.671875.
+    x = np.float32(469.33163)
+    assert Fraction(float(x)) == Fraction(15379059, 2 ** 15)
+    assert Fraction(21.6640625) ** 2 < Fraction(float(x)) < (Fraction(21.6640625) + Fraction(1, 2 ** 20)) ** 2
+    assert ops.sqrt(x, np.float32) == np.float32(21.6640625)
+    assert ops.sqrt(x, np.float16) == np.float16(21.65625)
+    assert int(np.float16(21.65625).view(np.uint16)) & 0x3FF == 0x16A          # even significand
+    # binary16 inputs: the two roundings equal one (24 >= 2 * 11 + 2)
+    h = np.arange(0x3C00, 0x7C00, 7, dtype=np.uint16).view(np.float16)
+    exact = np.sqrt(h.astype(np.float64)).astype(np.float16)
+    assert np.array_equal(ops.sqrt(h, np.float16).view(np.uint16), exact.view(np.uint16))
+
+
 def test_exp_against_high_precision():
     mpmath.mp.prec = 200
     xs = np.float16(np.linspace(-4, 4, 4001)).astype(np.float32)
