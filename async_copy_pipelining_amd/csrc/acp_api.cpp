@@ -318,7 +318,15 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
 
   // every 1 KiB wave block inside one row: the innermost image run holds a
   // whole number of such blocks and nothing permutes it
-  A.row_uniform = (q.row_ops && A.swizzle == 0 && (axes.back().count * ei) % (64 * p.vec_bytes) == 0) ? 1 : 0;
+  // The scalar-cache path indexes the row arrays with the stage's first row
+  // plus the row's packed position inside the stage, so it also needs the
+  // stage's rows to be consecutive in the packed row array: along every row
+  // dim the stage spans, the stage covers all of each inner row dim.
+  bool rows_consecutive = true;
+  for (int d = 0; d + 1 < r; ++d)
+    if (q.stage_box[d] > 1 && srow[d] != rowstride[d]) rows_consecutive = false;
+  A.row_uniform = (q.row_ops && rows_consecutive && A.swizzle == 0 &&
+                   (axes.back().count * ei) % (64 * p.vec_bytes) == 0) ? 1 : 0;
   if (q.mode == 4) {
     const int64_t row_bytes = x.shape[r - 1] * ei;
     // Wave-local reduction when every 1 KiB wave block lies in one row and

@@ -71,6 +71,22 @@ def test_row_add_mul(op):
     assert np.array_equal(host(yd, np.float32, shape).view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("shape,box,stage_box,threads,workgroups,kernel", [
+    # a stage spanning two outer indices holds rows 36 (8) apart: the row
+    # scalars are staged per row (the scalar-cache path needs consecutive rows)
+    ((2, 36, 512), (2, 8, 256), (2, 2, 256), 128, 0, "general stream vec 16 rounds 2 srow 0"),
+    ((4, 8, 1024), (2, 4, 1024), (2, 4, 1024), 256, 3, "general stream vec 16 rounds 8 srow 0"),
+    # covering the inner row dim whole keeps the stage's rows consecutive
+    ((4, 8, 1024), (2, 8, 1024), (2, 8, 1024), 1024, 3, "stream linear grid vec 16 rounds 4 srow 1"),
+])
+def test_fma_stage_spanning_outer_dims(shape, box, stage_box, threads, workgroups, kernel):
+    say(f"fma {shape} box {box} stage {stage_box} threads {threads} wg={workgroups}")
+    x, a, b, y = _fma_case(shape, stage_box, box, 3, threads, workgroups, seed=7)
+    assert acp.acp_last_kernel().startswith(kernel), acp.acp_last_kernel()
+    ref = REF.stream_ewise("fma", x, a, b, np.float32)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+
+
 def test_many_rows_per_stage_and_two_scalar_loads():
     # 48 rows per stage -> two 4-byte row-scalar loads per wave
     shape, stage_box = (2, 100, 64), (1, 48, 64)
