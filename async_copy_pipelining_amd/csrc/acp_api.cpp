@@ -896,9 +896,23 @@ acp_status acp_tile_reduce(acp_op op, const acp_tile_desc* dst, const acp_tile_d
       const int64_t n_tiles = p.n_tiles();
       if (grouped_ok && group > 1 && n_tiles > 0) {
         const int64_t dst_tiles = n_tiles / group;
-        const int64_t want = static_cast<int64_t>(device_cu_count()) * 4;
-        // few destination tiles: split each one's contributions over k
-        // workgroups (k atomic adds per element instead of one)
+        static const int env_wg_per_cu = [] {
+          const char* e = std::getenv("ACP_REDUCE_WG_PER_CU");
+          return (e && std::atoi(e) > 0) ? std::atoi(e) : 0;
+        }();
+        static const int env_slots = [] {
+          const char* e = std::getenv("ACP_REDUCE_STAGES");
+          return (e && std::atoi(e) >= 2 && std::atoi(e) <= 4) ? std::atoi(e) : 3;
+        }();
+        const int64_t per_cu = env_wg_per_cu ? env_wg_per_cu : std::max<int64_t>(1, 16384 / p.tile_bytes());
+        const int64_t want = static_cast<int64_t>(device_cu_count()) * per_cu;
+        // About 16 KiB of tiles per CU in flight per ring step and 3 ring
+        // slots (ACP_REDUCE_WG_PER_CU, ACP_REDUCE_STAGES): the best of 2-8
+        // workgroups per CU x 2-4 slots x 4 or 8 KiB tiles measured on 128
+        // float32 contributions per element of [500,1024] (8 KiB tiles, two
+        // per CU: 4.8 TB/s).  Few destination tiles: split each one's
+        // contributions over k workgroups (k atomic adds per element instead
+        // of one).
         int64_t k = 1;
         while (dst_tiles * k * 2 <= want && group % (k * 2) == 0) k *= 2;
         const int64_t sub = group / k;                 // contributions summed per workgroup group
@@ -908,7 +922,7 @@ acp_status acp_tile_reduce(acp_op op, const acp_tile_desc* dst, const acp_tile_d
         q.red_group = sub;
         q.red_per_wg = per * sub;
         q.workgroups = static_cast<int>((groups + per - 1) / per);
-        q.stages = 2;
+        q.stages = env_slots;
         q.tiles_per_trip = 1;
       }
     } else {

@@ -83,7 +83,7 @@ def parse():
                     help="reduce: add all 128 slabs into one [500,1024] destination (else slab by slab)")
     ap.add_argument("--rows", type=int, default=None,
                     help="rows per ring stage or tile (default per workload: c4 2, pointwise / reduce / rowsum 4, "
-                         "reduce --reduce-over-batch 1)")
+                         "reduce --reduce-over-batch 2)")
     ap.add_argument("--threads", type=int, default=256)
     ap.add_argument("--workgroups", type=int, default=None,
                     help="persistent workgroups (default 256 x --wg-per-cu; rowsum 512)")
@@ -96,7 +96,7 @@ def parse():
     # defaults: the best launch shapes measured on MI355X for each workload
     wl = args.workload
     if args.rows is None:
-        args.rows = {"c4": 2, "pointwise": 4, "rowsum": 4}.get(wl, 1 if args.reduce_over_batch else 4)
+        args.rows = {"c4": 2, "pointwise": 4, "rowsum": 4}.get(wl, 2 if args.reduce_over_batch else 4)
     if args.stages is None:
         args.stages = 2 if wl in ("pointwise", "rowsum") else 4
     if args.workgroups is None:
