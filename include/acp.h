@@ -1,11 +1,14 @@
 /*
  * acp.h -- pipelined asynchronous tile copy + elementwise for AMD MI355X (gfx950).
  *
- * A small C ABI over three operations on multi-dimensional tiles staged in LDS:
+ * A small C ABI over operations on multi-dimensional tiles staged in LDS:
  *
- *   acp_tile_copy     global -> LDS -> global, one tile per workgroup
- *   acp_tile_ewise    elementwise op on LDS-resident operand tiles
- *   acp_stream_ewise  tiles streamed through a 2..4-stage LDS ring
+ *   acp_tile_copy           global -> LDS -> global
+ *   acp_tile_ewise          elementwise op on LDS-resident operand tiles
+ *   acp_stream_ewise        tiles streamed through a 2..4-stage LDS ring
+ *   acp_tile_reduce         staged tiles added into a destination
+ *   acp_stream_binary       two tensors streamed through one ring (add, mul)
+ *   acp_stream_reduce_rows  row sums of ring-staged tiles
  *
  * plus the host-side descriptor encoder / planner they share.  The method
  * follows four pages:
@@ -38,7 +41,8 @@
  *   borrowed.
  * Asynchrony.  Compute calls validate and plan on the host (errors return
  *   synchronously), then enqueue one kernel on `hip_stream` (a hipStream_t;
- *   NULL = the null stream) and return.  Completion is stream order; the
+ *   NULL = the null stream) and return.  Nothing is allocated and nothing
+ *   else is enqueued, so a call can be captured into a HIP graph.  Completion is stream order; the
  *   caller synchronizes.  Inside a kernel the library owns every wait: unlike
  *   the pages' copy_async (whose caller commits and waits), completion of
  *   the staged loads is tracked by the kernel itself.
@@ -143,9 +147,9 @@ const char* acp_last_error(void);
  * pipelined entry point, as text ("stream linear grid vec 16 rounds 2 srow
  * 1 variant 0 grid 256 ..."): "none" when that call launched nothing (no
  * tiles, or the launch failed), empty before the first.  A row reduction
- * ends in "wave-local" or "lds partials", the path its stage layout takes.  Calls rejected
- * before the launch step leave it unchanged.  Owned by the library; valid
- * until the thread's next such call. */
+ * ends in "wave-local" or "lds partials", the path its stage layout takes.
+ * Calls rejected before the launch step leave it unchanged.  Owned by the
+ * library; valid until the thread's next such call. */
 const char* acp_last_kernel(void);
 
 /* Encode a descriptor for tiles of `box` over a tensor at `gbase`
@@ -188,8 +192,9 @@ acp_status acp_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, int
  * in LDS and the result written to an LDS tile before it is copied out
  * ([smem]).  n_in: ZERO 0 or 1, SQRT/EXP 1, ADD/MUL 2, FMA 3.  All inputs
  * share dtype, shape, strides, box and swizzle (one anchor layout); `out`
- * has the same shape and box.  Types: SQRT/EXP f16|f32 -> f16|f32;
- * ADD/MUL/FMA inputs and output one of f16|f32; ZERO -> f16|f32.  Large
+ * has the same shape and box.  Types: SQRT/EXP f16|f32 -> f16|f32,
+ * computed in f32 and rounded to the output type; ADD/MUL/FMA inputs and
+ * output one of f16|f32; ZERO -> f16|f32.  Large
  * tile counts run on a persistent grid whose ring trips stage 1, 2 or 4
  * consecutive tiles (about 16 KiB per trip; ACP_TILES_PER_TRIP).  `out`
  * may be an input element for element (same base, element size and
