@@ -14,14 +14,16 @@ asynchronous tile copies:
 
 Modules
 -------
-``swizzle``   128-byte XOR swizzle of stage-relative LDS byte offsets.
+``swizzle``   XOR swizzles (32-, 64- and 128-byte modes) of stage-relative LDS
+              byte offsets.
 ``plan``      descriptor encode, plan search (L1 -> L2 -> L3), partition.
 ``tiles``     LDS byte image of a tile (gather, swizzle, zero fill) and the
               tiled copy / elementwise data path built from it.
 ``ops``       the elementwise ops with IEEE-754 round-to-nearest-even results
-              (exact fma via round-to-odd, correctly rounded sqrt).
+              (exact fma via round-to-odd; sqrt and exp computed in binary32).
 ``ring``      the circular-buffer event schedule with per-wait counters.
-``reference`` the plain definitions every result must equal.
+``reference`` the plain definitions every result must equal (copy,
+              elementwise, streamed fma, store with reduce-add, row sums).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  It shares no code with the HIP path
