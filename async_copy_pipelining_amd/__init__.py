@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libacp.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m async_copy_pipelining_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python async_copy_pipelining_amd/build.py` "
         "(the HIP library is the only implementation)")
 
 try:

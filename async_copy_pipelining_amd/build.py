@@ -1,6 +1,7 @@
 """Build ``libacp.so`` (the C-ABI library) in-tree with hipcc for gfx950.
 
-Usage: ``python -m async_copy_pipelining_amd.build`` (or ``build()``).  Always
+Usage: ``python async_copy_pipelining_amd/build.py`` (run as a script: importing
+the package needs the library it builds), or ``__graft_entry__.build()``.  Always
 recompiles.  Device code is built with packed-fp32 instructions disabled and
 without fast-math, so fp32 results keep IEEE rounding and denormals.
 """
