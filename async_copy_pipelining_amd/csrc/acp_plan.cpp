@@ -210,7 +210,7 @@ PlanStatus plan_box_with(const DescData& dd, const int32_t* boxp, bool copy_only
     }
   }
 
-  // L2: segments for boxes over 256
+  // L3: segments for boxes over 256 (issue axes)
   for (size_t k = 0; k < dims.size(); ++k) {
     DescDim& d = dims[k];
     if (d.box <= kMaxBox) continue;
