@@ -139,6 +139,12 @@ __device__ __forceinline__ void wait_vmcnt(int k) {
   }
 }
 
+// Compile-time form of the same wait.
+template <int K>
+__device__ __forceinline__ void wait_vmcnt_c() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K < 63 ? K : 63) : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Ring control ("Add TMA support for circular buffering pass", "Loop
 // Structure" and "Detailed Pseudo-Code"): the prologue loads min(S-1, N)
@@ -148,6 +154,10 @@ __device__ __forceinline__ void wait_vmcnt(int k) {
 // after the last load of trip i when its wait executes: the loads of trips
 // i+1..min(i+S-1, N-1) (d each) and the stores of every consume since trip
 // i's load (st each).  With S == 1 the ring is load, wait, consume.
+//
+// A policy provides load(j, slot), pre_wait(i, slot, k) (called just before
+// trip i's wait with the count k it allows: the place for scalar loads whose
+// latency then hides behind the wait) and consume(i, slot).
 
 __device__ __forceinline__ int allowed(int i, int n, int s, int d, int st) {
   int ahead = n - 1 - i;
@@ -165,13 +175,65 @@ __device__ __forceinline__ void run_ring(P& p, int n, int s, int d, int st) {
   int i = 0;
   for (; i < nmain; ++i) {
     p.load(i + s - 1, ld);
-    p.wait(i, cur, allowed(i, n, s, d, st));
+    const int k = allowed(i, n, s, d, st);
+    p.pre_wait(i, cur, k);
+    wait_vmcnt(k);
     p.consume(i, cur);
     cur = (cur + 1 == s) ? 0 : cur + 1;
     ld = (ld + 1 == s) ? 0 : ld + 1;
   }
   for (; i < n; ++i) {
-    p.wait(i, cur, allowed(i, n, s, d, st));
+    const int k = allowed(i, n, s, d, st);
+    p.pre_wait(i, cur, k);
+    wait_vmcnt(k);
+    p.consume(i, cur);
+    cur = (cur + 1 == s) ? 0 : cur + 1;
+  }
+}
+
+// Steady state of the ring with a compile-time wait count K.
+template <int K, class P>
+__device__ __forceinline__ void ring_steady(P& p, int& i, int nmain, int s, int& cur, int& ld) {
+  for (; i < nmain; ++i) {
+    p.load(i + s - 1, ld);
+    p.pre_wait(i, cur, K);
+    wait_vmcnt_c<K>();
+    p.consume(i, cur);
+    cur = (cur + 1 == s) ? 0 : cur + 1;
+    ld = (ld + 1 == s) ? 0 : ld + 1;
+  }
+}
+
+// The same ring for per-trip counts D and ST known at compile time.  Past
+// the first S-1 trips of the main loop the allowed count is the constant
+// (S-1)(D+ST), so each slot count (2, 3 or 4) gets a steady-state loop with
+// its wait fixed at compile time; the first trips and the epilogue take the
+// general wait.
+template <int D, int ST, class P>
+__device__ __forceinline__ void run_ring_fixed(P& p, int n, int s) {
+  const int pro = n < s - 1 ? n : s - 1;
+  for (int j = 0; j < pro; ++j) p.load(j, j);
+  const int nmain = n - (s - 1) > 0 ? n - (s - 1) : 0;
+  const int warm = nmain < s - 1 ? nmain : s - 1;
+  int cur = 0, ld = s - 1;
+  int i = 0;
+  for (; i < warm; ++i) {
+    p.load(i + s - 1, ld);
+    const int k = allowed(i, n, s, D, ST);
+    p.pre_wait(i, cur, k);
+    wait_vmcnt(k);
+    p.consume(i, cur);
+    cur = (cur + 1 == s) ? 0 : cur + 1;
+    ld = (ld + 1 == s) ? 0 : ld + 1;
+  }
+  if (s == 4) ring_steady<3 * (D + ST)>(p, i, nmain, s, cur, ld);
+  else if (s == 3) ring_steady<2 * (D + ST)>(p, i, nmain, s, cur, ld);
+  else if (s == 2) ring_steady<D + ST>(p, i, nmain, s, cur, ld);
+  else ring_steady<0>(p, i, nmain, s, cur, ld);
+  for (; i < n; ++i) {
+    const int k = allowed(i, n, s, D, ST);
+    p.pre_wait(i, cur, k);
+    wait_vmcnt(k);
     p.consume(i, cur);
     cur = (cur + 1 == s) ? 0 : cur + 1;
   }

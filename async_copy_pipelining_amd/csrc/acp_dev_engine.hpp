@@ -121,7 +121,7 @@ struct EnginePolicy {
     const Trip t = trip_geometry(A, L, wg, grid, j);
     issue_loads<VB>(L, m, t, lds0 + slot * L.slot_bytes, wave, row_ptr, row_bad);
   }
-  __device__ __forceinline__ void wait(int, int, int k) { wait_vmcnt(k); }
+  __device__ __forceinline__ void pre_wait(int, int, int) {}
   __device__ __forceinline__ void consume(int i, int slot) {
     const Trip t = trip_geometry(A, L, wg, grid, i);
     consume_trip<OP, VB, STAGE_OUT>(L, esize_log2, swizzle, m, t, lds, slot * L.slot_bytes, wave, lane);

@@ -186,7 +186,7 @@ struct GenPolicy {
     }
   }
 
-  __device__ __forceinline__ void wait(int i, int, int k) {
+  __device__ __forceinline__ void pre_wait(int i, int, int) {
     if constexpr (OP::ROW && SROW) {
       // rows of a cut stage may lie past the tensor: their results are
       // never stored, and they read row 0 instead of memory past the arrays
@@ -199,7 +199,6 @@ struct GenPolicy {
         sb[f] = cb[r];
       }
     }
-    wait_vmcnt(k);
   }
 
   // Widening ops: 8 input bytes per lane and piece, 16 output bytes.

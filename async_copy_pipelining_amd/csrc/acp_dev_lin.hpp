@@ -9,16 +9,17 @@ namespace dev {
 
 // ---------------------------------------------------------------------------
 // Linear stage grid (one full stage per tile, row-major contiguous), 16-byte
-// rounds, OUTER rounds per thread known at compile time.  Same ring control
-// and wait counts as the general engine; per trip only the stage base (one
-// multiply) changes, and no chunk can be out of bounds.
+// rounds, OUTER rounds per thread known at compile time.  Same ring schedule
+// and wait counts as the general engine, the per-trip counts fixed at compile
+// time; per trip only the stage bases change (by one grid stride), and no
+// chunk can be out of bounds.
 // * Streaming (STAGE_OUT false): one staged operand (x and z for two-tensor ops).
 // * Tile ewise (STAGE_OUT true, "elementwise -> smem"): OP::NIN staged
 //   operands, and the result goes through the LDS output image before the
 //   store.  A stage is 2^k consecutive tiles (one ring trip), round f
 //   belonging to tile f >> tile_rounds_log2 of it.
 
-template <class OP, int OUTER, bool SROW, bool STAGE_OUT>
+template <class OP, int OUTER, bool SROW, bool STAGE_OUT, bool NT>
 struct LinPolicy {
   // staged operands per trip (a stream stages x, and z for two-tensor ops)
   static constexpr int NL = STAGE_OUT ? OP::NIN : (OP::NIN > 1 ? OP::NIN : 1);
@@ -29,7 +30,8 @@ struct LinPolicy {
   uint64_t lin_x, lin_o, lin_r, total_rows;
   uint32_t lds0, slot_bytes, in_image_bytes, out_image_off, ab_base, wg, grid, waves_kb;  // waves_kb: LDS bytes of one round
   int wave, lane, ab_instr, swizzle, esize_log2;
-  bool load_nt, store_nt;
+  bool load_nt, store_nt;     // NT: both known to be set
+  uint64_t ld_xb, ld_rb, step_x, step_r;  // byte and row offsets of the next stage loaded
   uint32_t xoff[OUTER], ooff[OUTER], abo[OUTER], lpos[OUTER];
   const uint64_t* row_ptr;   // [0] lane's array, [1 + q] row byte offset in the stage
   const uint32_t* row_ok;    // lane has a row in load q
@@ -41,20 +43,25 @@ struct LinPolicy {
   float sa[OUTER], sb[OUTER];
 
   __device__ __forceinline__ uint64_t stage(int j) const { return wg + static_cast<uint64_t>(j) * grid; }
+  __device__ __forceinline__ bool lnt() const { return NT || load_nt; }
+  __device__ __forceinline__ bool snt() const { return NT || store_nt; }
 
-  __device__ __forceinline__ void load(int j, int slot) {
-    const uint64_t s = stage(j);
-    const uint64_t xb = s * lin_x;
+  // the ring loads trips 0, 1, 2, ... in order: the stage offsets advance by
+  // one grid stride per load
+  __device__ __forceinline__ void load(int, int slot) {
+    const uint64_t xb = ld_xb;
+    ld_xb += step_x;
     const uint32_t range = range_from(in_span, xb);
     const uint32_t base = lds0 + slot * slot_bytes + wave * 1024u;
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
       const v4i rs = rsrc_v4(in[k] + xb, range);
 #pragma unroll
-      for (int f = 0; f < OUTER; ++f) dma_b128(rs, xoff[f], base + k * in_image_bytes + f * waves_kb, load_nt);
+      for (int f = 0; f < OUTER; ++f) dma_b128(rs, xoff[f], base + k * in_image_bytes + f * waves_kb, lnt());
     }
     if constexpr (OP::ROW && !SROW) {
-      const uint64_t rb = s * lin_r;
+      const uint64_t rb = ld_rb;
+      ld_rb += step_r;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         if (q >= ab_instr) continue;
@@ -65,7 +72,7 @@ struct LinPolicy {
       }
     }
   }
-  __device__ __forceinline__ void wait(int i, int, int k) {
+  __device__ __forceinline__ void pre_wait(int i, int, int) {
     if constexpr (OP::ROW && SROW) {
       // scalar loads of trip i's rows go out before the stage wait, so their
       // latency hides behind it
@@ -76,7 +83,6 @@ struct LinPolicy {
         sb[f] = cb[rb + row_of[f]];
       }
     }
-    wait_vmcnt(k);
   }
 
   __device__ __forceinline__ void consume(int i, int slot) {
@@ -138,16 +144,14 @@ struct LinPolicy {
           for (int piece = 0; piece < P; ++piece)
             __builtin_memcpy(words + piece * 4, lds + out_image_off + swz(lo + piece * 16, swizzle), PB);
         }
-        store_chunk<CS::OB>(rs, ooff[f], words, store_nt);
+        store_chunk<CS::OB>(rs, ooff[f], words, snt());
       }
     }
   }
 };
 
-template <class OP, int OUTER, bool SROW, bool STAGE_OUT = false>
-__global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
-  extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
-  CArgs* A = kargs();
+template <class OP, int OUTER, bool SROW, bool STAGE_OUT, bool NT>
+__device__ __forceinline__ void stream_lin_body(CArgs* A, unsigned char* lds) {
   const int lane = threadIdx.x & 63;
   const int wave = uni(static_cast<int>(threadIdx.x >> 6));
   const uint32_t grid = gridDim.x;
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
   if constexpr (OP::ROW && !SROW) build_rows(A, lane, row_ptr, row_bad);
   uint32_t row_ok[2] = {row_bad[0] == 0u, row_bad[1] == 0u};
   const Loc L = load_loc(A);
-  LinPolicy<OP, OUTER, SROW, STAGE_OUT> p;
+  LinPolicy<OP, OUTER, SROW, STAGE_OUT, NT> p;
   p.lds = lds;
   for (int k = 0; k < 3; ++k) p.in[k] = L.in[k];
   p.out = L.out;
@@ -187,6 +191,10 @@ __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
   p.esize_log2 = uni(A->esize_log2);
   p.load_nt = L.load_nt != 0;
   p.store_nt = L.store_nt != 0;
+  p.ld_xb = static_cast<uint64_t>(wg) * p.lin_x;
+  p.ld_rb = static_cast<uint64_t>(wg) * p.lin_r;
+  p.step_x = static_cast<uint64_t>(grid) * p.lin_x;
+  p.step_r = static_cast<uint64_t>(grid) * p.lin_r;
   p.waves_kb = static_cast<uint32_t>(L.waves) * 1024u;
   // tile ewise: round f lies in tile f >> tile_rounds_log2 of the stage
   const uint32_t trl = STAGE_OUT ? uni(A->tile_rounds_log2) : 0u;
@@ -212,19 +220,35 @@ __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
     p.sa[f] = p.sb[f] = 0.f;
   }
   typedef ChunkShape<OP, 16> CS;
-  const int d = LinPolicy<OP, OUTER, SROW, STAGE_OUT>::NL * OUTER + ((OP::ROW && !SROW) ? L.ab_instr : 0);
-  run_ring(p, n, uni(A->stages), d, OUTER * CS::ST);
+  constexpr int DL = LinPolicy<OP, OUTER, SROW, STAGE_OUT, NT>::NL * OUTER;
+  if constexpr (OP::ROW && !SROW)
+    run_ring(p, n, uni(A->stages), DL + L.ab_instr, OUTER * CS::ST);
+  else
+    run_ring_fixed<DL, OUTER * CS::ST>(p, n, uni(A->stages));
+}
+
+// Non-temporal loads and stores (the default for contiguous stages) get a
+// body with the cache policy fixed at compile time, so the trip carries no
+// branch on it.
+template <class OP, int OUTER, bool SROW, bool STAGE_OUT = false>
+__global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+  CArgs* A = kargs();
+  if (A->load_nt && A->store_nt)
+    stream_lin_body<OP, OUTER, SROW, STAGE_OUT, true>(A, lds);
+  else
+    stream_lin_body<OP, OUTER, SROW, STAGE_OUT, false>(A, lds);
 }
 
 // ---------------------------------------------------------------------------
 // Row reduction on a linear stage grid whose wave blocks each lie in one row
 // and whose rows each lie in one wave (the wave-local case): the linear
-// kernel's lean trip (stage base = one multiply) with the wave-local
+// kernel's lean trip (stage base advanced by one grid stride) with the wave-local
 // reduction of the general kernel.  Stage s holds rows s * lin_r + (the
 // packed offsets of its rows); lane k of a wave owns the wave's k-th
 // distinct row.
 
-template <class OP, int OUTER>
+template <class OP, int OUTER, bool NT>
 struct LinRowsPolicy {
   unsigned char* lds;
   const char* in0;
@@ -232,20 +256,23 @@ struct LinRowsPolicy {
   uint64_t in_span, lin_x, lin_r;
   uint32_t lds0, slot_bytes, wg, grid, waves_kb;
   int wave, lane;
-  bool load_nt, one_row;
+  bool load_nt, one_row;  // NT: load_nt known to be set
+  uint64_t ld_xb, step_x;  // byte offset of the next stage loaded
   uint32_t xoff[OUTER], row_of[OUTER];
   uint32_t lrow, loff;  // this lane's row of the stage (~0: none) and its packed offset
 
   __device__ __forceinline__ uint64_t stage(int j) const { return wg + static_cast<uint64_t>(j) * grid; }
 
-  __device__ __forceinline__ void load(int j, int slot) {
-    const uint64_t xb = stage(j) * lin_x;
+  // trips load in order: the stage offset advances by one grid stride
+  __device__ __forceinline__ void load(int, int slot) {
+    const uint64_t xb = ld_xb;
+    ld_xb += step_x;
     const v4i rs = rsrc_v4(in0 + xb, range_from(in_span, xb));
     const uint32_t base = lds0 + slot * slot_bytes + wave * 1024u;
 #pragma unroll
-    for (int f = 0; f < OUTER; ++f) dma_b128(rs, xoff[f], base + f * waves_kb, load_nt);
+    for (int f = 0; f < OUTER; ++f) dma_b128(rs, xoff[f], base + f * waves_kb, NT || load_nt);
   }
-  __device__ __forceinline__ void wait(int, int, int k) { wait_vmcnt(k); }
+  __device__ __forceinline__ void pre_wait(int, int, int) {}
 
   __device__ __forceinline__ void consume(int i, int slot) {
     const uint32_t sl = slot * slot_bytes;
@@ -275,10 +302,8 @@ struct LinRowsPolicy {
   }
 };
 
-template <class OP, int OUTER>
-__global__ __launch_bounds__(1024) void rows_lin_kernel_t(const EngineArgs) {
-  extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
-  CArgs* A = kargs();
+template <class OP, int OUTER, bool NT>
+__device__ __forceinline__ void rows_lin_body(CArgs* A, unsigned char* lds) {
   const int lane = threadIdx.x & 63;
   const int wave = uni(static_cast<int>(threadIdx.x >> 6));
   const uint32_t grid = gridDim.x;
@@ -290,7 +315,7 @@ __global__ __launch_bounds__(1024) void rows_lin_kernel_t(const EngineArgs) {
   LaneMap m;
   build_map<16>(A, wave, lane, m);
   const Loc L = load_loc(A);
-  LinRowsPolicy<OP, OUTER> p;
+  LinRowsPolicy<OP, OUTER, NT> p;
   p.lds = lds;
   p.in0 = L.in[0];
   p.out_rs = rsrc_store(L.out, range_from(L.out_span, 0));
@@ -305,6 +330,8 @@ __global__ __launch_bounds__(1024) void rows_lin_kernel_t(const EngineArgs) {
   p.wave = wave;
   p.lane = lane;
   p.load_nt = L.load_nt != 0;
+  p.ld_xb = static_cast<uint64_t>(wg) * p.lin_x;
+  p.step_x = static_cast<uint64_t>(grid) * p.lin_x;
 #pragma unroll
   for (int f = 0; f < OUTER; ++f) {
     p.xoff[f] = m.xoff[f];
@@ -334,7 +361,17 @@ __global__ __launch_bounds__(1024) void rows_lin_kernel_t(const EngineArgs) {
     rr /= sb;
   }
   p.loff = off;
-  run_ring(p, n, uni(A->stages), OUTER, 1);
+  run_ring_fixed<OUTER, 1>(p, n, uni(A->stages));
+}
+
+template <class OP, int OUTER>
+__global__ __launch_bounds__(1024) void rows_lin_kernel_t(const EngineArgs) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+  CArgs* A = kargs();
+  if (A->load_nt)
+    rows_lin_body<OP, OUTER, true>(A, lds);
+  else
+    rows_lin_body<OP, OUTER, false>(A, lds);
 }
 
 }  // namespace dev

@@ -48,14 +48,21 @@ struct TracePolicy {
     ++pos;
   }
   __device__ void load(int j, int s) { put(0, j, s, 0); }
-  __device__ void wait(int i, int s, int k) { put(1, i, s, k); }
+  __device__ void pre_wait(int i, int s, int k) { put(1, i, s, k); }
   __device__ void consume(int i, int s) { put(2, i, s, 0); }
 };
 
+// Per-trip counts that the linear-grid kernels fix at compile time run the
+// ring with those counts; any other pair runs the general ring.
 __global__ void ring_trace_kernel(int n, int s, int loads, int stores, int32_t* out) {
   if (threadIdx.x != 0) return;
   TracePolicy p{out, 0};
-  run_ring(p, n, s, loads, stores);
+  if (loads == 1 && stores == 1) run_ring_fixed<1, 1>(p, n, s);
+  else if (loads == 2 && stores == 1) run_ring_fixed<2, 1>(p, n, s);
+  else if (loads == 2 && stores == 2) run_ring_fixed<2, 2>(p, n, s);
+  else if (loads == 4 && stores == 1) run_ring_fixed<4, 1>(p, n, s);
+  else if (loads == 4 && stores == 4) run_ring_fixed<4, 4>(p, n, s);
+  else run_ring(p, n, s, loads, stores);
 }
 
 // Measurement reference: a plain register-path copy (no LDS, no ring).

@@ -305,7 +305,10 @@ acp_status acp_debug_lds_image(const acp_tile_desc* src, int64_t tile_index, int
  * `n_iters` trips, `stages` buffers, `loads` and `stores` memory operations
  * per trip, recording 3 * n_iters events of 4 int32 each
  * (kind 0 load / 1 wait / 2 consume, trip, stage, outstanding-op count
- * allowed at the wait) into device memory `out_events`. */
+ * allowed at the wait) into device memory `out_events`.  The pairs
+ * (loads, stores) = (1,1), (2,1), (2,2), (4,1), (4,4) run the ring form whose
+ * per-trip counts are compile-time constants (the one the linear-grid kernels
+ * use), any other pair the general form; both follow the same schedule. */
 acp_status acp_debug_ring_trace(int n_iters, int stages, int loads, int stores, int32_t* out_events,
                                 void* hip_stream);
 

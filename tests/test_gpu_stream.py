@@ -22,7 +22,8 @@ def say(msg):
 def test_ring_trace_matches_oracle_schedule(stages):
     say(f"ring trace stages {stages}")
     for n in range(0, 17):
-        for loads, stores in ((1, 0), (5, 4), (9, 8), (2, 1)):
+        # (1,1), (2,1), (2,2), (4,1), (4,4): the compile-time-count ring; the rest the general one
+        for loads, stores in ((1, 0), (5, 4), (9, 8), (2, 1), (1, 1), (2, 2), (4, 1), (4, 4)):
             ev = RING.schedule(n, stages, loads, stores)
             out = torch.full((max(1, 3 * n) * 4,), -1, dtype=torch.int32, device="cuda:0")
             acp.acp_debug_ring_trace(n, stages, loads, stores, out, stream())
@@ -96,11 +97,17 @@ def test_many_rows_per_stage_and_two_scalar_loads():
     assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
 
 
-def test_c4_full_size_bench_config_sampled():
-    shape, stage_box = (128, 500, 1024), (1, 4, 1024)
-    say("C4 full fma [128,500,1024] stage (1,4,1024) S=4 persistent 512 workgroups")
-    x, a, b, y = _fma_case(shape, stage_box, stage_box, 4, 256, 512)
-    assert acp.acp_last_kernel().startswith("stream linear grid vec 16 rounds 4 srow 1")
+@pytest.mark.parametrize("stage_box,stages,threads,workgroups,rounds", [
+    ((1, 1, 1024), 4, 128, 256, 2),   # the bench's launch
+    ((1, 1, 1024), 3, 128, 256, 2),   # its 3- and 2-stage rings (bench "ring_stages")
+    ((1, 1, 1024), 2, 128, 256, 2),
+    ((1, 4, 1024), 4, 256, 512, 4),
+])
+def test_c4_full_size_bench_config_sampled(stage_box, stages, threads, workgroups, rounds):
+    shape = (128, 500, 1024)
+    say(f"C4 full fma [128,500,1024] stage {stage_box} S={stages} {threads} threads, {workgroups} workgroups")
+    x, a, b, y = _fma_case(shape, stage_box, stage_box, stages, threads, workgroups)
+    assert acp.acp_last_kernel().startswith(f"stream linear grid vec 16 rounds {rounds} srow 1")
     rng = np.random.default_rng(44)
     i0 = rng.integers(0, 128, 3000)
     i1 = rng.integers(0, 500, 3000)
