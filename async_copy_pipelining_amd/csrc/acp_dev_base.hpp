@@ -54,6 +54,21 @@ __device__ __forceinline__ CArgs* kargs() {
   return (CArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
 }
 
+// The argument block (over 1 KiB) is read through the scalar cache, and a
+// kernel's set-up reads it in dependent rounds (a field, a branch on it, the
+// next field), each of which can miss on a new 64-byte line and wait for
+// L2 or HBM.  Reading one word of every line first, all in one batch behind
+// a single wait, leaves the later reads to hit the scalar cache.
+__device__ __forceinline__ void prefetch_kargs() {
+  typedef const uint32_t __attribute__((address_space(4))) CWord;
+  CWord* w = (CWord*)(__builtin_amdgcn_kernarg_segment_ptr());
+  constexpr int kWords = static_cast<int>(sizeof(EngineArgs) / 4);
+  uint32_t x = w[kWords - 1];
+#pragma unroll
+  for (int k = 0; k < kWords; k += 16) x ^= w[k];
+  asm volatile("" ::"s"(x));
+}
+
 // XOR swizzle of a stage-relative LDS byte offset: the 16-byte chunk index
 // within its span takes the 128-byte row index modulo the span's chunk
 // count (mask 1, 3, 7 for the 32-, 64-, 128-byte modes; 0 is no swizzle).

@@ -133,6 +133,7 @@ struct EnginePolicy {
 template <class OP, int VB, bool STAGE_OUT>
 __global__ __launch_bounds__(1024) void engine_kernel_t(const EngineArgs) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+  prefetch_kargs();
   CArgs* A = kargs();
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   const int lane = threadIdx.x & 63;

@@ -446,6 +446,7 @@ struct GenPolicy {
 template <class OP, int MODE, int OUTER, bool SROW, int ZSET = 0, bool GROUP = false>
 __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+  prefetch_kargs();
   CArgs* A = kargs();
   const int lane = threadIdx.x & 63;
   const int wave = uni(static_cast<int>(threadIdx.x >> 6));

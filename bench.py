@@ -86,7 +86,7 @@ def parse():
                          "reduce --reduce-over-batch 2)")
     ap.add_argument("--threads", type=int, default=None, help="threads per workgroup (default: c4 128, else 256)")
     ap.add_argument("--workgroups", type=int, default=None,
-                    help="persistent workgroups (default 256 x --wg-per-cu; rowsum 512)")
+                    help="persistent workgroups (default 256 x --wg-per-cu)")
     ap.add_argument("--wg-per-cu", type=int, default=1)
     ap.add_argument("--sets", type=int, default=3, help="rotated buffer sets")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
@@ -102,7 +102,7 @@ def parse():
     if args.stages is None:
         args.stages = 2 if wl in ("pointwise", "rowsum") else 4
     if args.workgroups is None:
-        args.workgroups = 512 if wl == "rowsum" else 0
+        args.workgroups = 0
     return args
 
 
