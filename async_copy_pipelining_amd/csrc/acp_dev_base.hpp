@@ -33,6 +33,8 @@
 //   space 4): scalar loads, no per-lane copy of the argument block.
 #pragma once
 
+#include <cstddef>
+
 #include <hip/hip_runtime.h>
 
 #include "acp_engine.hpp"
@@ -57,15 +59,31 @@ __device__ __forceinline__ CArgs* kargs() {
 // The argument block (over 1 KiB) is read through the scalar cache, and a
 // kernel's set-up reads it in dependent rounds (a field, a branch on it, the
 // next field), each of which can miss on a new 64-byte line and wait for
-// L2 or HBM.  Reading one word of every line first, all in one batch behind
-// a single wait, leaves the later reads to hit the scalar cache.
+// L2 or HBM.  Reading one word of every line the kernel uses first, in one
+// batch behind a single wait, leaves the later reads to hit the scalar
+// cache.  At most 15 scalar loads can be outstanding, so a mask of up to 15
+// lines costs one round trip.
+constexpr int kArgLines = static_cast<int>((sizeof(EngineArgs) + 63) / 64);
+constexpr uint32_t arg_lines(size_t lo, size_t hi) {  // lines of bytes [lo, hi)
+  uint32_t m = 0;
+  for (size_t l = lo / 64; l * 64 < hi; ++l) m |= 1u << l;
+  return m;
+}
+constexpr uint32_t kAllArgLines = arg_lines(0, sizeof(EngineArgs));
+// the linear kernels: pointers, stage box, the image axes and everything after
+constexpr uint32_t kLinArgLines = arg_lines(0, offsetof(EngineArgs, xstep)) |
+                                  arg_lines(offsetof(EngineArgs, sbox), offsetof(EngineArgs, nst)) |
+                                  arg_lines(offsetof(EngineArgs, ax_count), sizeof(EngineArgs));
+static_assert(__builtin_popcount(kLinArgLines) <= 15, "one batch of scalar loads");
+
+template <uint32_t LINES = kAllArgLines>
 __device__ __forceinline__ void prefetch_kargs() {
   typedef const uint32_t __attribute__((address_space(4))) CWord;
   CWord* w = (CWord*)(__builtin_amdgcn_kernarg_segment_ptr());
-  constexpr int kWords = static_cast<int>(sizeof(EngineArgs) / 4);
-  uint32_t x = w[kWords - 1];
+  uint32_t x = 0;
 #pragma unroll
-  for (int k = 0; k < kWords; k += 16) x ^= w[k];
+  for (int k = 0; k < kArgLines; ++k)
+    if ((LINES >> k) & 1u) x ^= w[k * 16];
   asm volatile("" ::"s"(x));
 }
 

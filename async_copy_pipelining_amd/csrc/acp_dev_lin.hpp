@@ -233,7 +233,7 @@ __device__ __forceinline__ void stream_lin_body(CArgs* A, unsigned char* lds) {
 template <class OP, int OUTER, bool SROW, bool STAGE_OUT = false>
 __global__ __launch_bounds__(1024) void stream_lin_kernel_t(const EngineArgs) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
-  prefetch_kargs();
+  prefetch_kargs<kLinArgLines>();
   CArgs* A = kargs();
   if (A->load_nt && A->store_nt)
     stream_lin_body<OP, OUTER, SROW, STAGE_OUT, true>(A, lds);
@@ -368,7 +368,7 @@ __device__ __forceinline__ void rows_lin_body(CArgs* A, unsigned char* lds) {
 template <class OP, int OUTER>
 __global__ __launch_bounds__(1024) void rows_lin_kernel_t(const EngineArgs) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
-  prefetch_kargs();
+  prefetch_kargs<kLinArgLines>();
   CArgs* A = kargs();
   if (A->load_nt)
     rows_lin_body<OP, OUTER, true>(A, lds);
