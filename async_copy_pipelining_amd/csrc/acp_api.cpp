@@ -562,12 +562,17 @@ int device_cu_count() {
 //   about 32 KiB of loads in flight per CU (ACP_TILE_WG_PER_CU), within 32
 //   waves per CU and the LDS (32x32 float32 sqrt: 5.0-5.4 TB/s with 4 tiles
 //   per trip against 4.5-4.9 with one).
-void tile_schedule(const acp::Plan& p, int n_in, int threads, int64_t out_image, int* workgroups, int* stages,
-                   int* tiles_per_trip) {
-  static const int env_per_cu = [] {
+int tile_wg_per_cu_env() {
+  static const int v = [] {
     const char* e = std::getenv("ACP_TILE_WG_PER_CU");
     return (e && std::atoi(e) > 0) ? std::atoi(e) : 0;
   }();
+  return v;
+}
+
+void tile_schedule(const acp::Plan& p, int n_in, int threads, int64_t out_image, int* workgroups, int* stages,
+                   int* tiles_per_trip) {
+  const int env_per_cu = tile_wg_per_cu_env();
   static const int slots = [] {
     const char* e = std::getenv("ACP_TILE_STAGES");
     return (e && std::atoi(e) > 0 && std::atoi(e) <= 4) ? std::atoi(e) : 2;
@@ -762,8 +767,18 @@ acp_status acp_tile_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_de
     else q.stages = 1;
   }
   Launch L;
-  const acp_status st = prepare(q, &L);
+  acp_status st = prepare(q, &L);
   if (st != ACP_OK) return st;
+  // The linear tile kernel streams best with one workgroup per CU (32x32
+  // float32 sqrt: 6.00-6.03 against 5.87-5.88 TB/s with two); the general
+  // kernel keeps the schedule's count, whose extra waves cover the LDS round
+  // trip of its output image.
+  const int cus = device_cu_count();
+  if (L.key.mode == 9 && tile_wg_per_cu_env() == 0 && q.workgroups > cus) {
+    q.workgroups = cus;
+    st = prepare(q, &L);
+    if (st != ACP_OK) return st;
+  }
   return launch(L, hip_stream);
 }
 
