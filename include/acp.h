@@ -196,7 +196,9 @@ acp_status acp_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, int
  * computed in f32 and rounded to the output type; ADD/MUL/FMA inputs and
  * output one of f16|f32; ZERO -> f16|f32.  Large
  * tile counts run on a persistent grid whose ring trips stage 1, 2 or 4
- * consecutive tiles (about 16 KiB per trip; ACP_TILES_PER_TRIP).  `out`
+ * consecutive tiles (about 16 KiB per trip; ACP_TILES_PER_TRIP): one
+ * workgroup per CU when the tiles form a linear grid, else about 32 KiB of
+ * loads in flight per CU (ACP_TILE_WG_PER_CU overrides both).  `out`
  * may be an input element for element (same base, element size and
  * strides: the op runs in place); any other intersection of the output's
  * byte range with an input's is ACP_ERR_INVALID. */
