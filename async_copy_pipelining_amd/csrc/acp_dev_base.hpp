@@ -240,8 +240,9 @@ __device__ __forceinline__ void ring_steady(P& p, int& i, int nmain, int s, int&
 // The same ring for per-trip counts D and ST known at compile time.  Past
 // the first S-1 trips of the main loop the allowed count is the constant
 // (S-1)(D+ST), so each slot count (2, 3 or 4) gets a steady-state loop with
-// its wait fixed at compile time; the first trips and the epilogue take the
-// general wait.
+// its wait fixed at compile time (with one slot, or any other count, the
+// steady state waits for everything: exact for S = 1, stronger otherwise);
+// the first trips and the epilogue take the general wait.
 template <int D, int ST, class P>
 __device__ __forceinline__ void run_ring_fixed(P& p, int n, int s) {
   const int pro = n < s - 1 ? n : s - 1;
