@@ -161,7 +161,7 @@ __device__ __forceinline__ void stream_lin_body(CArgs* A, unsigned char* lds) {
   const int n = static_cast<int>(wg < n_tiles ? (n_tiles - wg + grid - 1) / grid : 0);
   if (n == 0) return;
   LaneMap m;
-  build_map<16>(A, wave, lane, m);
+  build_map_c<16, OUTER>(A, wave, lane, m);
   uint64_t row_ptr[3] = {0, 0, 0};
   uint32_t row_bad[2] = {~0u, ~0u};
   if constexpr (OP::ROW && !SROW) build_rows(A, lane, row_ptr, row_bad);
@@ -314,7 +314,7 @@ __device__ __forceinline__ void rows_lin_body(CArgs* A, unsigned char* lds) {
   const int n = static_cast<int>(wg < n_tiles ? (n_tiles - wg + grid - 1) / grid : 0);
   if (n == 0) return;
   LaneMap m;
-  build_map<16>(A, wave, lane, m);
+  build_map_c<16, OUTER>(A, wave, lane, m);
   const Loc L = load_loc(A);
   LinRowsPolicy<OP, OUTER, NT> p;
   p.lds = lds;

@@ -82,6 +82,60 @@ __device__ __forceinline__ void build_map(CArgs* A, int wave, int lane, LaneMap&
   }
 }
 
+// The same map for a round count known at compile time (the linear
+// kernels): the axes run in the outer loop and the rounds in the inner one,
+// so each axis' parameters are read once rather than once per round.  The
+// fields equal build_map's: map_byte's walk, round by round.
+template <int VB, int OUTER>
+__device__ __forceinline__ void build_map_c(CArgs* A, int wave, int lane, LaneMap& m) {
+  static_assert(OUTER >= 1 && OUTER <= kMaxOuter, "round count");
+  const int waves = A->waves, n_axes = A->n_axes;
+  const uint32_t swz_mask = static_cast<uint32_t>(A->swizzle);
+  const int es_log2 = A->esize_log2;
+#pragma unroll
+  for (int g = 0; g < kMaxOuter; ++g) m.xoff[g] = m.ooff[g] = m.oobm[g] = m.lpos[g] = m.abo[g] = 0;
+  uint32_t e[OUTER], row[OUTER], rel[OUTER][kPartial];
+#pragma unroll
+  for (int f = 0; f < OUTER; ++f) {
+    const uint32_t lb = swz(((static_cast<uint32_t>(f) * waves + wave) * 64u + lane) * VB, swz_mask);
+    const uint32_t sub_byte = lb & ((1u << es_log2) - 1u);
+    e[f] = lb >> es_log2;
+    m.lpos[f] = lb;
+    m.xoff[f] = sub_byte;
+    m.ooff[f] = sub_byte;
+    row[f] = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < kPartial; ++s2) rel[f][s2] = 0;
+  }
+#pragma nounroll
+  for (int k = n_axes - 1; k >= 0; --k) {
+    const uint32_t mag = A->ax_mag[k], sh = A->ax_sh[k], cnt = A->ax_count[k];
+    const uint32_t xs = A->ax_xs[k], os = A->ax_os[k], rs = A->ax_rs[k], step = A->ax_step[k];
+    const int ps = A->ax_pslot[k];
+#pragma unroll
+    for (int f = 0; f < OUTER; ++f) {
+      const uint32_t q = mdiv(e[f], mag, sh);
+      const uint32_t idx = e[f] - q * cnt;
+      e[f] = q;
+      m.xoff[f] += idx * xs;
+      m.ooff[f] += idx * os;
+      row[f] += idx * rs;
+#pragma unroll
+      for (int s2 = 0; s2 < kPartial; ++s2)
+        if (ps == s2) rel[f][s2] += idx * step;
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < OUTER; ++f) {
+    uint32_t ob = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < kPartial; ++s2)
+      if (rel[f][s2] >= A->prem[s2]) ob |= 1u << s2;
+    m.oobm[f] = ob;
+    m.abo[f] = (row[f] >> 5) * 256u + (row[f] & 31u) * 4u;
+  }
+}
+
 // Consumer pieces of a widening op: every 16-byte round of a wave (1 KiB of
 // LDS) is consumed as two halves of 512 B, lane l taking the 8 bytes at
 // 8 * l of each half.  Eight input bytes widen to 16 output bytes, so every
