@@ -462,7 +462,12 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   const int n = static_cast<int>(mine * A->subs);  // ring trips
   if (n == 0) return;
   LaneMap m;
-  build_map<16>(A, wave, lane, m);
+  // the lane map with the axes outside the rounds (store with reduce-add
+  // keeps the per-round walk: measured 1.6 % faster there)
+  if constexpr (MODE == 3)
+    build_map<16>(A, wave, lane, m);
+  else
+    build_map_c<16, OUTER>(A, wave, lane, m);
   uint64_t row_ptr[3] = {0, 0, 0};
   uint32_t row_bad[2] = {~0u, ~0u};
   if constexpr (OP::ROW && !SROW) build_rows(A, lane, row_ptr, row_bad);
@@ -514,8 +519,14 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
     p.row_of[f] = (abo >> 8) * 32u + (abo & 255u) / 4u;
     p.sa[f] = p.sb[f] = 0.f;
   }
-  if constexpr (GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP>::SPLIT)
-    build_pieces(A, wave, lane, OUTER, p.pooff, p.poobm, p.plpos);
+  if constexpr (GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP>::SPLIT) {
+    // the piece map with the axes outside the pieces, up to 8 pieces (above
+    // that the per-piece walk keeps the register count down)
+    if constexpr (2 * OUTER <= 8 && GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP>::NP == 2 * OUTER)
+      build_pieces_c(A, wave, lane, p.pooff, p.poobm, p.plpos);
+    else
+      build_pieces(A, wave, lane, OUTER, p.pooff, p.poobm, p.plpos);
+  }
   if constexpr (GROUP) {
     p.red_group = uni(A->red_group);
     p.rcount = 0;

@@ -163,6 +163,52 @@ __device__ __forceinline__ void build_pieces(CArgs* A, int wave, int lane, int o
   }
 }
 
+// build_pieces for a piece count known at compile time (N = 2 * rounds): the
+// axes in the outer loop, as in build_map_c.
+template <int N>
+__device__ __forceinline__ void build_pieces_c(CArgs* A, int wave, int lane, uint32_t (&oo)[N], uint32_t (&ob)[N],
+                                               uint32_t (&lp)[N]) {
+  const int waves = A->waves, n_axes = A->n_axes;
+  const uint32_t swz_mask = static_cast<uint32_t>(A->swizzle);
+  const int es_log2 = A->esize_log2;
+  uint32_t e[N], rel[N][kPartial];
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const uint32_t f = static_cast<uint32_t>(q) >> 1, h = static_cast<uint32_t>(q) & 1u;
+    const uint32_t lb = swz((f * waves + wave) * 1024u + h * 512u + lane * 8u, swz_mask);
+    const uint32_t sub_byte = lb & ((1u << es_log2) - 1u);
+    e[q] = lb >> es_log2;
+    lp[q] = lb;
+    oo[q] = sub_byte;
+#pragma unroll
+    for (int s2 = 0; s2 < kPartial; ++s2) rel[q][s2] = 0;
+  }
+#pragma nounroll
+  for (int k = n_axes - 1; k >= 0; --k) {
+    const uint32_t mag = A->ax_mag[k], sh = A->ax_sh[k], cnt = A->ax_count[k];
+    const uint32_t os = A->ax_os[k], step = A->ax_step[k];
+    const int ps = A->ax_pslot[k];
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const uint32_t d = mdiv(e[q], mag, sh);
+      const uint32_t idx = e[q] - d * cnt;
+      e[q] = d;
+      oo[q] += idx * os;
+#pragma unroll
+      for (int s2 = 0; s2 < kPartial; ++s2)
+        if (ps == s2) rel[q][s2] += idx * step;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    uint32_t b = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < kPartial; ++s2)
+      if (rel[q][s2] >= A->prem[s2]) b |= 1u << s2;
+    ob[q] = b;
+  }
+}
+
 // Launch values the ring touches every trip, read from the argument block
 // once: they then live in registers across the asm statements (whose memory
 // clobbers would otherwise force a reload of every argument per trip).
