@@ -600,6 +600,14 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   p.fill(0, 0u);
   typedef ChunkShape<OP, 16> CS;
   constexpr int NS = GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP>::NS;
+  // streams with one tile per trip take the ring whose steady-state wait is a
+  // compile-time count (the per-trip counts are known here)
+  if constexpr (MODE == 2 && !(OP::ROW && !SROW)) {
+    if (tpt_log2 == 0) {
+      run_ring_fixed<NS * OUTER, OUTER * CS::ST>(p, n, uni(A->stages));
+      return;
+    }
+  }
   const int d = (NS * OUTER + ((OP::ROW && !SROW) ? L.ab_instr : 0)) << tpt_log2;
   // grouped reduce-add stores only on a group's last trip: counting none
   // per trip only makes the waits stronger
