@@ -2,8 +2,8 @@
 """Throughput of the pipelined tile copy + elementwise path on one MI355X.
 
 Default workload: y = a[row] * x + b[row] over a [128, 500, 1024] float32
-tensor streamed through a 4-stage LDS ring (stage = one 1024-element row,
-128 threads, one persistent workgroup per CU), the configuration the HBM-roofline target is
+tensor streamed through a 4-stage LDS ring (stage = two 1024-element rows,
+256 threads, one persistent workgroup per CU), the configuration the HBM-roofline target is
 quoted on.  One step = one launch of acp_stream_ewise over the whole tensor.
 The same line also reports the 2- and 3-stage rings ("ring_stages").  Inputs are seeded synthetic
 tensors resident in HBM; three buffer sets are rotated so that consecutive
@@ -82,9 +82,9 @@ def parse():
     ap.add_argument("--reduce-over-batch", action="store_true",
                     help="reduce: add all 128 slabs into one [500,1024] destination (else slab by slab)")
     ap.add_argument("--rows", type=int, default=None,
-                    help="rows per ring stage or tile (default per workload: c4 1, pointwise / reduce / rowsum 4, "
+                    help="rows per ring stage or tile (default per workload: c4 2, pointwise / reduce / rowsum 4, "
                          "reduce --reduce-over-batch 2)")
-    ap.add_argument("--threads", type=int, default=None, help="threads per workgroup (default: c4 128, else 256)")
+    ap.add_argument("--threads", type=int, default=256, help="threads per workgroup")
     ap.add_argument("--workgroups", type=int, default=None,
                     help="persistent workgroups (default 256 x --wg-per-cu)")
     ap.add_argument("--wg-per-cu", type=int, default=1)
@@ -96,9 +96,7 @@ def parse():
     # defaults: the best launch shapes measured on MI355X for each workload
     wl = args.workload
     if args.rows is None:
-        args.rows = {"c4": 1, "pointwise": 4, "rowsum": 4}.get(wl, 2 if args.reduce_over_batch else 4)
-    if args.threads is None:
-        args.threads = 128 if wl == "c4" else 256
+        args.rows = {"c4": 2, "pointwise": 4, "rowsum": 4}.get(wl, 2 if args.reduce_over_batch else 4)
     if args.stages is None:
         args.stages = 2 if wl in ("pointwise", "rowsum") else 4
     if args.workgroups is None:

@@ -98,9 +98,10 @@ def test_many_rows_per_stage_and_two_scalar_loads():
 
 
 @pytest.mark.parametrize("stage_box,stages,threads,workgroups,rounds", [
-    ((1, 1, 1024), 4, 128, 256, 2),   # the bench's launch
-    ((1, 1, 1024), 3, 128, 256, 2),   # its 3- and 2-stage rings (bench "ring_stages")
-    ((1, 1, 1024), 2, 128, 256, 2),
+    ((1, 2, 1024), 4, 256, 256, 2),   # the bench's launch
+    ((1, 2, 1024), 3, 256, 256, 2),   # its 3- and 2-stage rings (bench "ring_stages")
+    ((1, 2, 1024), 2, 256, 256, 2),
+    ((1, 1, 1024), 4, 128, 256, 2),
     ((1, 4, 1024), 4, 256, 512, 4),
 ])
 def test_c4_full_size_bench_config_sampled(stage_box, stages, threads, workgroups, rounds):
