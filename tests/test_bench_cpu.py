@@ -1,0 +1,40 @@
+"""bench.py without a GPU: the one-GPU contract and the rocprofv3 summaries it
+reads its HBM traffic from."""
+import json
+import os
+import re
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_profile_summaries_name_their_commands_and_kernel_sources():
+    names = sorted(f for f in os.listdir(PROFILES) if f.endswith(".md"))
+    assert names
+    for name in names:
+        text = open(os.path.join(PROFILES, name), encoding="utf-8").read()
+        assert re.search(r"^kernel_source_hash: [0-9a-f]{16}$", text, re.M), name
+        cmds = re.findall(r"^\s+rocprofv3 .* -- python3 \$R/bench\.py .*$", text, re.M)
+        assert cmds, name
+        for c in cmds:
+            # only committed files run: the bench itself, no helper scripts
+            assert "_work" not in c, c
+            assert ("gpurun_out/prof" in c) or ("gpurun_out/c1" in c), c
+
+
+def test_headline_profile_matches_the_bench_default():
+    # the default workload (streamed fma, 4 slots, stage (1,2,1024)) reads its
+    # traffic from this summary
+    src = open(os.path.join(ROOT, "bench.py"), encoding="utf-8").read()
+    assert '"c4": 2' in src
+    assert os.path.exists(os.path.join(PROFILES, "stream_fma_f32_128x500x1024_s4_r2.md"))
