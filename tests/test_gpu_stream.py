@@ -118,6 +118,19 @@ def test_c4_full_size_bench_config_sampled(stage_box, stages, threads, workgroup
     assert not np.any(y.view(np.uint32) == 0xA5A5A5A5)
 
 
+@pytest.mark.parametrize("stages", [2, 3, 4])
+@pytest.mark.parametrize("rows,workgroups", [(1, 8), (2, 8), (3, 1), (5, 2), (17, 4), (64, 3)])
+def test_linear_ring_short_and_long_trip_counts(stages, rows, workgroups):
+    # one row per stage on a linear grid: workgroups get 0..22 trips, so the
+    # ring runs with no steady state, exactly S-1 trips, and past its warm-up
+    shape, stage = (1, rows, 1024), (1, 1, 1024)
+    say(f"linear fma {shape} stage {stage} S={stages} workgroups {workgroups}")
+    x, a, b, y = _fma_case(shape, stage, stage, stages, 256, workgroups, seed=rows)
+    assert acp.acp_last_kernel().startswith("stream linear grid"), acp.acp_last_kernel()
+    ref = REF.stream_ewise("fma", x, a, b, np.float32)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+
+
 def _exp_table_on_gpu():
     """GPU exp of every float16 in [-4, 4] (34818 values: U(-4, 4) rounded to
     float16 reaches +4.0 as well) through the C5 path."""
