@@ -131,6 +131,35 @@ def test_linear_ring_short_and_long_trip_counts(stages, rows, workgroups):
     assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("stages", [2, 3, 4])
+@pytest.mark.parametrize("k", [2, 3, 5, 9])
+def test_general_stream_short_and_long_trip_counts(stages, k):
+    # float16 -> float32 sqrt on padded rows with a gap between the outer
+    # slices, so the stage grid is not linear and the general kernel runs:
+    # each of the two workgroups streams its box's k stages, so the ring runs
+    # with no steady state, exactly S-1 trips, and past its warm-up
+    shape, pitch, gap = (2, k, 64, 128), 136, 512
+    strides = (k * 64 * pitch + gap, 64 * pitch, pitch, 1)
+    box, stage = (1, k, 64, 128), (1, 1, 64, 128)
+    say(f"general widening stream sqrt {shape} strides {strides} stage {stage} S={stages}")
+    rng = np.random.default_rng(20 + k)
+    n_store = (shape[0] - 1) * strides[0] + (k - 1) * strides[1] + 63 * pitch + 128
+    storage = np.zeros(n_store, np.float16)
+    fill = np.lib.stride_tricks.as_strided(storage, shape=shape, strides=tuple(2 * st for st in strides))
+    fill[...] = np.abs(rng.standard_normal(shape)).astype(np.float16)
+    x = W.strided_view(storage, shape, strides)
+    xd = dev(storage)
+    n = int(np.prod(shape))
+    yd = empty_bytes(n * 4)
+    xdesc = encode("f16", xd, shape, strides, box)
+    ydesc = encode("f32", yd, shape, packed_strides(shape), box)
+    acp.acp_stream_ewise("sqrt", ydesc, xdesc, None, None, stage, stages, 256, 0, stream())
+    assert acp.acp_last_kernel().startswith("general stream"), acp.acp_last_kernel()
+    y = host(yd, np.float32, shape)
+    ref = REF.ewise("sqrt", [np.ascontiguousarray(x)], np.float32)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+
+
 def _exp_table_on_gpu():
     """GPU exp of every float16 in [-4, 4] (34818 values: U(-4, 4) rounded to
     float16 reaches +4.0 as well) through the C5 path."""
