@@ -326,6 +326,19 @@ def _reduce_rows_case(dt, shape, box, stage_box, stages, threads, workgroups, in
     return x, y[:rows].reshape(shape[:-1])
 
 
+@pytest.mark.parametrize("stages", [2, 3, 4])
+@pytest.mark.parametrize("n_stages,workgroups", [(1, 8), (2, 8), (3, 1), (5, 2), (17, 4), (40, 3)])
+def test_linear_row_sums_short_and_long_trip_counts(stages, n_stages, workgroups):
+    # wave-local row sums on a linear grid with 0..17 trips per workgroup:
+    # no steady state, exactly S-1 trips, and past the ring's warm-up
+    shape = (1, 4 * n_stages, 1024)
+    say(f"linear row sums {shape} stage (1,4,1024) S={stages} workgroups {workgroups}")
+    x, y = _reduce_rows_case("f32", shape, (1, 4, 1024), (1, 4, 1024), stages, 256, workgroups, ints=True,
+                             seed=70 + n_stages)
+    assert acp.acp_last_kernel().startswith("row reduction linear grid"), acp.acp_last_kernel()
+    assert np.array_equal(y, REF.reduce_rows(x))
+
+
 def _assert_within_sum_bound(x, y):
     ref = REF.reduce_rows(x).astype(np.float64)
     bound = REF.recursive_sum_bound(x, x.shape[-1] - 1) + np.spacing(np.abs(ref.astype(np.float32))).astype(np.float64)
