@@ -302,6 +302,20 @@ def test_two_tensor_stream_full_size_sampled(staging):
     assert not np.any(y.view(np.uint32) == 0xA5A5A5A5)
 
 
+@pytest.mark.parametrize("stages", [2, 3, 4])
+@pytest.mark.parametrize("rows,workgroups", [(1, 8), (3, 1), (5, 2), (17, 4)])
+def test_linear_two_tensor_short_and_long_trip_counts(stages, rows, workgroups):
+    # x + z with both tensors on the ring (two loads per round) on a linear
+    # grid with 0..17 trips per workgroup
+    shape, stage = (1, rows, 1024), (1, 1, 1024)
+    say(f"linear two-tensor add {shape} stage {stage} S={stages} workgroups {workgroups}")
+    x, z, y = _binary_case("add", "f32", shape, stage, stage, stages, 256, workgroups, "ring", seed=80 + rows)
+    assert acp.acp_last_kernel().startswith("stream linear grid"), acp.acp_last_kernel()
+    assert " variant 1 " in acp.acp_last_kernel()
+    ref = REF.ewise("add", [x, z], np.float32)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+
+
 def _reduce_rows_case(dt, shape, box, stage_box, stages, threads, workgroups, ints=False, swz=0, pitch=None, seed=61):
     npdt = {"f16": np.float16, "f32": np.float32}[dt]
     rng = np.random.default_rng(seed)
