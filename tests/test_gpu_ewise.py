@@ -184,3 +184,20 @@ def test_tile_ewise_on_a_linear_tile_grid(op, n_in, idt, odt, shape, box, thread
     else:
         bits = np.uint32 if odt == "f32" else np.uint16
         assert np.array_equal(y.view(bits), ref.view(bits))
+
+
+@pytest.mark.parametrize("tiles", [516, 1028, 2052, 5124])
+def test_linear_tile_sqrt_short_and_long_trip_counts(tiles):
+    # a persistent linear tile grid (4 tiles per stage, one workgroup per CU)
+    # with 0..6 trips per workgroup
+    x = W.sqrt_tiles_f32(tiles=tiles, seed=tiles)
+    shape, box = x.shape, (1, 32, 32)
+    say(f"linear tile sqrt {shape}")
+    xd = dev(x)
+    yd = empty_bytes(x.nbytes)
+    st = packed_strides(shape)
+    acp.acp_tile_ewise("sqrt", encode("f32", yd, shape, st, box), [encode("f32", xd, shape, st, box)], 256, stream())
+    assert acp.acp_last_kernel().startswith("tile linear grid"), acp.acp_last_kernel()
+    y = host(yd, np.float32, shape)
+    ref = REF.ewise("sqrt", [x], np.float32)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
