@@ -23,7 +23,7 @@ Sources
   aligned width, and the table of vec / cp_size / outer for 4096 elements over
   128 threads.
 
-Readings where the pages are silent (each restated in the design doc):
+Readings where the pages are silent:
 * The atom axis produced by the swizzle split is the OUTERMOST descriptor
   dimension: that is the only order that reproduces the worked example's
   strides (512 then 128 bytes innermost-first).
