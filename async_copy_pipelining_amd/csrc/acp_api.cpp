@@ -28,6 +28,7 @@ acp_status ret(acp_status s, const std::string& why = std::string()) {
 acp_status from_plan(acp::PlanStatus s, const std::string& why) {
   if (s == acp::PlanStatus::Invalid) return ret(ACP_ERR_INVALID, why);
   if (s == acp::PlanStatus::Declined) return ret(ACP_ERR_DECLINED, why);
+  if (s == acp::PlanStatus::Unsupported) return ret(ACP_ERR_UNSUPPORTED, why);
   return ACP_OK;
 }
 

@@ -10,19 +10,25 @@
 //  L2  Under a swizzle an innermost box wider than the mode's atom (16 << mode
 //      bytes: 32, 64 or 128) is split into atoms; the atom axis becomes the
 //      outermost descriptor dim (the only order that gives the worked 8x256
-//      float16 example's byte strides 512, 128).  Otherwise the inner box must
-//      be a whole number of 16-byte chunks.
+//      float16 example's byte strides 512, 128).  When that box, or the
+//      tensor row, is no whole number of atoms, the box is shrunk instead:
+//      cut into equal segments (the largest divisor whose bytes fit the atom
+//      and are a whole number of 16-byte chunks), the quotient an issue axis.
 //  L3  Adjacent dims merge when the inner one is fully boxed and contiguous
 //      with the outer one and the merged box stays <= 256 (copies may merge
 //      the innermost pair beyond 256 when promotion then fixes it; under the
 //      swizzle the innermost box stays within one atom; atom axes never merge).
-//      A copy's innermost box over 256 promotes the element 1 -> 2 -> 4 -> 8
-//      bytes.  Any box still over 256 is cut into equal segments (largest
-//      divisor <= 256; for the innermost dim preferably a 16-byte multiple,
-//      else a 4-byte one); the quotient is an issue axis (several loads).
-//      While the descriptor is deeper than 5, its outermost dim leaves it and
-//      becomes issue axes.  More than 256 loads per tile, or more than 12
-//      image axes, declines.
+//      A merge joins whole boxes; a merged dim is not cut again.  Under a
+//      swizzle the innermost box must now be a whole number of 16-byte
+//      chunks, else the plan declines.  A copy's innermost box over 256
+//      promotes the element 1 -> 2 -> 4 -> 8 bytes.  Any box still over 256
+//      is cut into equal segments (largest divisor <= 256; for the innermost
+//      dim preferably a 16-byte multiple, else a 4-byte one, else any); the
+//      quotient is an issue axis (several loads).  While the descriptor is
+//      deeper than 5, its outermost dim leaves it and becomes issue axes, so
+//      the shrink always succeeds.  More than 256 loads per tile, or more
+//      than 12 image axes, exceed what the kernels index: Unsupported (not
+//      a decline: a legal descriptor exists).
 //  Partition: vec_bytes is the widest of {16, 4} (the gfx950 direct-to-LDS
 //      sizes; the page's 8-byte form does not exist there) that divides the
 //      innermost LDS run, the tensor's inner extent and every stride (bytes),
@@ -145,9 +151,18 @@ PlanStatus plan_box_with(const DescData& dd, const int32_t* boxp, bool copy_only
   if (dd.swizzle != 0) {
     DescDim inner = dims.back();
     const int64_t ib = inner.box * es;
-    if (ib > atom_bytes) {
-      if (ib % atom_bytes != 0 || (inner.extent * es) % atom_bytes != 0)
-        return fail(reason, PlanStatus::Declined, "no swizzle-atom-aligned innermost box");
+    if (ib > atom_bytes && ib % 16 != 0) {
+      return fail(reason, PlanStatus::Declined, "innermost box is not a whole number of 16-byte swizzle chunks");
+    } else if (ib > atom_bytes && (ib % atom_bytes != 0 || (inner.extent * es) % atom_bytes != 0)) {
+      // shrink: equal segments within one atom, the quotient an issue axis
+      const int64_t seg = largest_divisor_upto(inner.box, atom_bytes / es, es, 16);
+      DescDim& d = dims.back();
+      const Axis part = d.parts[0];
+      d.segmented = true;
+      d.seg = Axis{d.box / seg, part.dim, part.step * seg};
+      d.parts[0] = Axis{seg, part.dim, part.step};
+      d.box = seg;
+    } else if (ib > atom_bytes) {
       const int64_t w = atom_bytes / es;
       const int dim = inner.parts[0].dim;
       DescDim atom;
@@ -163,9 +178,6 @@ PlanStatus plan_box_with(const DescData& dd, const int32_t* boxp, bool copy_only
       in2.parts.push_back(Axis{w, dim, 1});
       dims.back() = in2;
       dims.insert(dims.begin(), atom);
-    } else if (ib % 16 != 0) {
-      return fail(reason, PlanStatus::Declined,
-                  "innermost box is not a whole number of 16-byte swizzle chunks");
     }
   }
 
@@ -175,7 +187,7 @@ PlanStatus plan_box_with(const DescData& dd, const int32_t* boxp, bool copy_only
     for (size_t k = dims.size() - 1; k >= 1; --k) {
       const DescDim& o = dims[k - 1];
       const DescDim& i = dims[k];
-      if (o.atom || i.atom) continue;
+      if (o.atom || i.atom || o.segmented || i.segmented) continue;
       if (i.box != i.extent || o.stride != i.extent * i.stride) continue;
       DescDim m;
       m.extent = o.extent * i.extent;
@@ -195,6 +207,10 @@ PlanStatus plan_box_with(const DescData& dd, const int32_t* boxp, bool copy_only
       break;
     }
   }
+
+  // under a swizzle the innermost box (merged rows included) is whole chunks
+  if (dd.swizzle != 0 && (dims.back().box * p.desc_esize) % 16 != 0)
+    return fail(reason, PlanStatus::Declined, "innermost box is not a whole number of 16-byte swizzle chunks");
 
   // promotion of a copy's innermost box
   if (copy_only && dims.back().box > kMaxBox) {
@@ -219,7 +235,7 @@ PlanStatus plan_box_with(const DescData& dd, const int32_t* boxp, bool copy_only
     if (k + 1 == dims.size()) {
       seg = largest_divisor_upto(d.box, kMaxBox, p.desc_esize, 16);
       if (!seg) seg = largest_divisor_upto(d.box, kMaxBox, p.desc_esize, 4);
-      if (!seg) return fail(reason, PlanStatus::Declined, "no legal innermost box segment");
+      if (!seg) seg = largest_divisor_upto(d.box, kMaxBox, 1, 1);
     } else {
       seg = largest_divisor_upto(d.box, kMaxBox, 1, 1);
     }
@@ -244,7 +260,8 @@ PlanStatus plan_box_with(const DescData& dd, const int32_t* boxp, bool copy_only
     if (d.segmented) p.issue_axes.push_back(d.seg);
   p.dims = dims;
   if (p.issues() > kMaxIssues || static_cast<int>(p.image_axes().size()) > kMaxImageAxes)
-    return fail(reason, PlanStatus::Declined, "rank > 5 after shrinking");
+    return fail(reason, PlanStatus::Unsupported,
+                "the shrunk plan needs more than 256 loads per tile or 12 image axes (kernel limits)");
   *out = p;
   return PlanStatus::Ok;
 }

@@ -18,11 +18,11 @@ namespace acp {
 constexpr int kMaxInputRank = 8;
 constexpr int kMaxRank = 5;
 constexpr int64_t kMaxBox = 256;
-constexpr int64_t kMaxIssues = 256;
-constexpr int kMaxImageAxes = 12;
+constexpr int64_t kMaxIssues = 256;   // loads per tile the kernels index (a library limit)
+constexpr int kMaxImageAxes = 12;     // axes of a tile's LDS image the kernels index (a library limit)
 constexpr uint32_t kDescMagic = 0x44504341u;  // "ACPD"
 
-enum class PlanStatus { Ok, Invalid, Declined };
+enum class PlanStatus { Ok, Invalid, Declined, Unsupported };
 
 // Contents of acp_tile_desc::opaque.
 struct DescData {

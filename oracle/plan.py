@@ -33,11 +33,22 @@ Readings where the pages are silent:
   most 128 bytes.  Atom axes never merge.
 * A box > 256 that promotion cannot fix is cut into equal segments: the
   largest divisor <= 256 (for the innermost dim, one whose bytes are a
-  multiple of 16 if possible, else of 4).  The quotient becomes an issue axis.
+  multiple of 16 if possible, else of 4, else any).  The quotient becomes an
+  issue axis.
+* Under a swizzle, an innermost box wider than one atom that is not a whole
+  number of atoms (or over a tensor row that is not) is shrunk the same
+  way: cut into equal segments, the largest divisor whose bytes fit the atom
+  and are a whole number of 16-byte chunks, the quotient an issue axis.  An
+  innermost box within one atom may merge with whole rows (up to the atom);
+  the plan declines when the final innermost box is no whole number of
+  16-byte chunks.
+* A merge joins whole boxes, and a merged dim is never cut into several
+  loads again.
 * "Shrinking the chain prefix": while the descriptor has more than 5 dims,
   the outermost dim leaves the descriptor and its box becomes issue axes.
-  The plan declines ("rank > 5 after shrinking") if that needs more than
-  MAX_ISSUES loads per tile or more than MAX_IMAGE_AXES image axes.
+  Under this reading the shrink always reaches rank <= 5, so the page's
+  "rank > 5 after shrinking" decline cannot occur; the pages set no limit on
+  the number of loads per tile.
 * The stage's LDS image is issue-major, then box-dense row-major over the
   descriptor dims (each load writes one dense box), then swizzled.
 * The element-count rule of the ldgsts page is read as: threads * vec must
@@ -55,8 +66,6 @@ from . import swizzle as _swz
 MAX_RANK = 5            # descriptor rank limit
 MAX_BOX = 256           # per-dimension box limit
 MAX_INPUT_RANK = 8      # rank of the tensor handed to the encoder
-MAX_ISSUES = 256        # loads per tile the shrink step may create
-MAX_IMAGE_AXES = 12     # axes of the LDS image (issue axes + box parts)
 SWIZZLE_NONE = 0
 SWIZZLE_32B = 1
 SWIZZLE_64B = 2
@@ -212,20 +221,26 @@ def plan_box(esize: int, shape, strides, box, swizzle: int = SWIZZLE_NONE,
 
     # L2: a swizzle splits an inner box wider than one atom (16 << mode
     # bytes) into atoms; the atom axis becomes the outermost descriptor dim.
+    # An inner box that is no whole number of atoms is shrunk into equal
+    # segments that fit one atom (issue axis).
     if swizzle != SWIZZLE_NONE:
         inner = dims[-1]
         inner_bytes = inner.box * esize
-        if inner_bytes > atom_bytes:
-            if inner_bytes % atom_bytes or (inner.extent * esize) % atom_bytes:
-                raise Declined("no swizzle-atom-aligned innermost box")
+        if inner_bytes > atom_bytes and inner_bytes % 16:
+            raise Declined("innermost box is not a whole number of 16-byte swizzle chunks")
+        if inner_bytes > atom_bytes and (inner_bytes % atom_bytes or (inner.extent * esize) % atom_bytes):
+            seg = _largest_divisor_at_most(inner.box, atom_bytes // esize, lambda s: (s * esize) % 16 == 0)
+            part = inner.parts[0]
+            inner.seg_issue = Axis(inner.box // seg, part.dim, part.step * seg)
+            inner.parts = [Axis(seg, part.dim, part.step)]
+            inner.box = seg
+        elif inner_bytes > atom_bytes:
             w = atom_bytes // esize
             d_in = inner.parts[0].dim
             atom = DescDim(extent=inner.extent // w, stride=atom_bytes, box=inner.box // w,
                            parts=[Axis(inner.box // w, d_in, w)], atom=True)
             dims[-1] = DescDim(extent=w, stride=esize, box=w, parts=[Axis(w, d_in, 1)])
             dims.insert(0, atom)
-        elif inner_bytes % 16:
-            raise Declined("innermost box is not a whole number of 16-byte swizzle chunks")
 
     desc_esize = esize
 
@@ -235,7 +250,7 @@ def plan_box(esize: int, shape, strides, box, swizzle: int = SWIZZLE_NONE,
         changed = False
         for k in range(len(dims) - 1, 0, -1):
             o, i = dims[k - 1], dims[k]
-            if o.atom or i.atom:
+            if o.atom or i.atom or o.seg_issue is not None or i.seg_issue is not None:
                 continue
             if i.box != i.extent or o.stride != i.extent * i.stride:
                 continue
@@ -252,6 +267,11 @@ def plan_box(esize: int, shape, strides, box, swizzle: int = SWIZZLE_NONE,
             dims[k - 1:k + 1] = [merged]
             changed = True
             break
+
+    # Under a swizzle the innermost box (merged rows included) must be a whole
+    # number of 16-byte chunks.
+    if swizzle != SWIZZLE_NONE and (dims[-1].box * desc_esize) % 16:
+        raise Declined("innermost box is not a whole number of 16-byte swizzle chunks")
 
     # Promotion of the innermost dim (copies only): box > 256 -> wider element.
     promoted = False
@@ -277,7 +297,7 @@ def plan_box(esize: int, shape, strides, box, swizzle: int = SWIZZLE_NONE,
             if not seg:
                 seg = _largest_divisor_at_most(d.box, MAX_BOX, lambda s: (s * desc_esize) % 4 == 0)
             if not seg:
-                raise Declined("no legal innermost box segment")
+                seg = _largest_divisor_at_most(d.box, MAX_BOX)
         else:
             seg = _largest_divisor_at_most(d.box, MAX_BOX)
         d.seg_issue = Axis(d.box // seg, part.dim, part.step * seg)
@@ -298,11 +318,8 @@ def plan_box(esize: int, shape, strides, box, swizzle: int = SWIZZLE_NONE,
         if d.seg_issue is not None:
             issue_axes.append(d.seg_issue)
 
-    p = Plan(esize=esize, desc_esize=desc_esize, shape=shape, strides=strides, box=box,
-             swizzle=swizzle, dims=dims, issue_axes=issue_axes, promoted=promoted)
-    if p.issues > MAX_ISSUES or len(p.image_axes) > MAX_IMAGE_AXES:
-        raise Declined("rank > 5 after shrinking")
-    return p
+    return Plan(esize=esize, desc_esize=desc_esize, shape=shape, strides=strides, box=box,
+                swizzle=swizzle, dims=dims, issue_axes=issue_axes, promoted=promoted)
 
 
 def partition(p: Plan, threads: int, vec_candidates=GFX950_VEC_BYTES, base_addr: int = 0) -> Plan:

@@ -16,9 +16,10 @@
   those dims adds into the same destination element:
   dst'[j] = dst[j] + sum of src[i] over the i that map to j.  Integers wrap
   modulo 2**32.  For floats the page fixes no order of the additions;
-  reading adopted: the sum is the exact one rounded once, which every
-  order of IEEE additions reproduces when each partial sum is exactly
-  representable (and always with a single contribution).
+  reading adopted: the sum is the exact one rounded once to the
+  destination type, which every order of IEEE additions reproduces when
+  each partial sum is exactly representable (and always with a single
+  contribution).
 * row reduction ("Add TMA support for circular buffering pass", "Testing
   Setup": the Reduction and InnerPersistent schedules over circular-
   buffered loads): y[row] = sum of x[row, c] over the innermost dim, the
@@ -29,11 +30,57 @@
 """
 from __future__ import annotations
 
+import itertools
 import math
+import struct
 
 import numpy as np
 
 from . import ops
+
+
+def _odd_neighbour(t: float, away: float) -> float:
+    """Of t and its binary64 neighbour in the direction ``away`` (away from
+    zero), the one whose significand is odd."""
+    bits = struct.unpack("<q", struct.pack("<d", t))[0]
+    return t if bits & 1 else math.nextafter(t, away)
+
+
+def _sum_to_odd(values) -> float:
+    """The exact sum of finite binary64 ``values`` rounded to binary64 with
+    round-to-odd: truncated toward zero to 53 bits, and when that dropped
+    anything, the odd one of the two neighbours enclosing the exact sum.
+    A binary64 round-to-odd result rounded to nearest into a format of at most
+    51 significand bits gives the exact value rounded once to nearest in that
+    format (Boldo and Melquiond, "Emulation of FMA and correctly rounded sums:
+    proved algorithms using rounding to odd", IEEE Trans. Computers 2008).
+
+    ``math.fsum`` gives s, the exact sum rounded to nearest binary64; a second
+    ``fsum`` of the values and -s gives the sign of the exact residual
+    (exact - s), which is a nonzero multiple of 2**-1074 whenever the sum
+    was inexact, so it never rounds to zero."""
+    vals = values if isinstance(values, list) else list(values)
+    s = math.fsum(vals)
+    if not math.isfinite(s) or s == 0.0:
+        return s
+    r = math.fsum(itertools.chain(vals, (-s,)))
+    if r == 0.0:
+        return s
+    away = math.inf if s > 0 else -math.inf
+    # truncation toward zero: s itself when the exact sum lies beyond it
+    # (further from zero), else the neighbour of s toward zero
+    t = s if (r > 0) == (s > 0) else math.nextafter(s, 0.0)
+    return _odd_neighbour(t, away)
+
+
+def sum_rounded_once(rows: np.ndarray, out_dtype) -> np.ndarray:
+    """Exact sum of each row of ``rows`` (a 2-D array of binary16/32/64
+    values), rounded once to nearest-even in ``out_dtype`` (binary16 or
+    binary32)."""
+    rows = np.asarray(rows, dtype=np.float64)
+    ro = np.array([_sum_to_odd(r) for r in rows.tolist()], dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return ro.astype(out_dtype)
 
 
 def tile_copy(x: np.ndarray) -> np.ndarray:
@@ -85,8 +132,12 @@ def tile_reduce_add(dst: np.ndarray, src: np.ndarray) -> np.ndarray:
         total = src.astype(np.uint64).sum(axis=tuple(axes), keepdims=True) + dst.astype(np.uint64)
         return (total % (1 << 32)).astype(np.uint32)
     if dst.dtype in (np.float16, np.float32):
-        total = src.astype(np.float64).sum(axis=tuple(axes), keepdims=True) + dst.astype(np.float64)
-        return total.astype(dst.dtype)
+        # contributions to each destination element: the summed dims moved
+        # last, then the destination's own value
+        kept = [d for d in range(src.ndim) if d not in axes]
+        contrib = np.transpose(src, kept + axes).reshape(dst.size, -1).astype(np.float64)
+        rows = np.concatenate([contrib, dst.reshape(dst.size, 1).astype(np.float64)], axis=1)
+        return sum_rounded_once(rows, dst.dtype).reshape(dst.shape)
     raise ValueError("reduce-add takes uint32, float16 or float32")
 
 
@@ -95,8 +146,7 @@ def reduce_rows(x: np.ndarray) -> np.ndarray:
     x = np.asarray(x)
     n_rows = int(np.prod(x.shape[:-1]))
     rows = x.reshape(n_rows, x.shape[-1]).astype(np.float64)
-    out = np.array([math.fsum(r) for r in rows], dtype=np.float64)
-    return out.astype(np.float32).reshape(x.shape[:-1])
+    return sum_rounded_once(rows, np.float32).reshape(x.shape[:-1])
 
 
 def recursive_sum_bound(x: np.ndarray, n_adds: int) -> np.ndarray:

@@ -69,10 +69,3 @@ def schedule(n_iters: int, stages: int, loads: int = 1, stores: int = 0):
         wait_and_consume(i)
     return events
 
-
-def page_stage_formulas(i: int, stages: int):
-    """The main loop's (current_stage, load_stage) exactly as the page writes them."""
-    stage_depth = stages
-    current_stage = i % stage_depth
-    load_stage = (i + (stage_depth - 1)) % stage_depth
-    return current_stage, load_stage

@@ -24,10 +24,25 @@ def test_library_exports_every_declared_symbol():
     assert acp.acp_abi_version() == 1
 
 
+# kernel limits of the library (not rules of the pages): loads per tile and
+# LDS-image axes its kernels index; beyond them it answers UNSUPPORTED
+LIB_MAX_ISSUES = 256
+LIB_MAX_IMAGE_AXES = 12
+
+
+class _Unsupported(Exception):
+    pass
+
+
 def _cmp(dt, shape, strides, box, swz, threads, copy_only, base=FAKE_BASE):
     """Run both planners; return (oracle outcome, library outcome)."""
     try:
-        p = P.plan(dt, shape, strides, box, swz, threads=threads, copy_only=copy_only, base_addr=base)
+        p = P.plan_box(P.ESIZE[dt], shape, strides, box, swz, copy_only, base)
+        if p.issues > LIB_MAX_ISSUES or len(p.image_axes) > LIB_MAX_IMAGE_AXES:
+            # a legal plan beyond what the library's kernels index
+            raise _Unsupported()
+        if threads:
+            P.partition(p, threads, base_addr=base)
         o = ("ok", p.rank, [d.extent for d in reversed(p.dims)], [d.stride for d in reversed(p.dims)],
              [d.box for d in reversed(p.dims)], p.issues, len(p.image_axes), p.promoted,
              p.vec, p.vec_bytes, p.outer, p.tile_bytes)
@@ -35,6 +50,8 @@ def _cmp(dt, shape, strides, box, swz, threads, copy_only, base=FAKE_BASE):
         o = ("declined",)
     except P.Invalid:
         o = ("invalid",)
+    except _Unsupported:
+        o = ("unsupported",)
     try:
         # encode checks the box with promotion allowed; the query then plans
         # with the requested mode and thread count
@@ -43,7 +60,8 @@ def _cmp(dt, shape, strides, box, swz, threads, copy_only, base=FAKE_BASE):
         c = ("ok", q["rank"], q["dims"], q["strides"], q["box"], q["issues"], q["n_image_axes"], q["promoted"],
              q["vec"], q["vec_bytes"], q["outer"], q["tile_bytes"])
     except acp.AcpError as e:
-        c = {acp.ACP_ERR_DECLINED: ("declined",), acp.ACP_ERR_INVALID: ("invalid",)}[e.status]
+        c = {acp.ACP_ERR_DECLINED: ("declined",), acp.ACP_ERR_INVALID: ("invalid",),
+             acp.ACP_ERR_UNSUPPORTED: ("unsupported",)}[e.status]
     return o, c
 
 
@@ -111,8 +129,20 @@ def test_status_codes_and_reasons():
         acp.acp_encode_tiled("f16", 0, (8, 256), (256, 1), (8, 256))
     assert e.value.status == acp.ACP_ERR_INVALID
     with pytest.raises(acp.AcpError) as e:
-        acp.acp_encode_tiled("f16", FAKE_BASE, (8, 96), (96, 1), (8, 96), acp.ACP_SWIZZLE_128B)
-    assert e.value.status == acp.ACP_ERR_DECLINED and "swizzle-atom" in e.value.reason
+        acp.acp_encode_tiled("f16", FAKE_BASE, (8, 12), (12, 1), (8, 12), acp.ACP_SWIZZLE_128B)
+    assert e.value.status == acp.ACP_ERR_DECLINED and "16-byte" in e.value.reason
+    # a 192-byte inner box under the 128-byte swizzle is shrunk into two loads
+    d = acp.acp_encode_tiled("f16", FAKE_BASE, (8, 96), (96, 1), (8, 96), acp.ACP_SWIZZLE_128B)
+    assert acp.acp_plan_query(d, 64)["issues"] == 2
+    # legal, but deeper than the kernels index: unsupported, not declined
+    shape = (7, 7, 7, 7, 7, 7, 7, 64)
+    strides, st = [], 1
+    for ext in reversed(shape):
+        strides.append(st)
+        st *= ext + 1
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_encode_tiled("f32", FAKE_BASE, shape, tuple(reversed(strides)), shape)
+    assert e.value.status == acp.ACP_ERR_UNSUPPORTED and "kernel limits" in e.value.reason
     d = acp.acp_encode_tiled("f16", FAKE_BASE, (8, 256), (256, 1), (8, 256))
     with pytest.raises(acp.AcpError) as e:
         acp.acp_plan_query(d, 96)

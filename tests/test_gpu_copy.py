@@ -119,6 +119,36 @@ def test_narrow_swizzle_images_and_copies(mode, dt, shape, box, threads):
         assert _lds_image(src, t, threads, p.tile_bytes) == T.lds_image(elems, p, t)
 
 
+@pytest.mark.parametrize("mode,dt,shape,box,threads", [
+    (3, "f16", (16, 96), (16, 96), 64),      # 192-byte rows: shrunk into two 96-byte loads
+    (3, "f16", (20, 200), (8, 128), 128),    # 256-byte box over 400-byte rows: two 128-byte loads
+    (1, "f16", (16, 24), (16, 24), 64),      # 48-byte rows under the 32-byte mode: three 16-byte loads
+    (2, "f32", (32, 36), (16, 36), 192),     # 144-byte rows under the 64-byte mode: three 48-byte loads
+    (3, "f16", (8, 4, 12), (8, 4, 12), 64),  # 24-byte rows: four merge into 96 bytes of whole chunks
+])
+def test_swizzle_shrunk_inner_box(mode, dt, shape, box, threads):
+    # "copy_async -> tma", "Algorithm" step 2: an innermost box that does not
+    # fit the swizzle atom is shrunk (cut into loads that do) instead of
+    # declined; rows narrower than 16 bytes merge up to whole chunks
+    say(f"swizzle mode {mode} shrink {dt} {shape} box {box} threads {threads}")
+    rng = np.random.default_rng(13)
+    es = P.ESIZE[dt]
+    x = rng.integers(0, 256, size=int(np.prod(shape)) * es, dtype=np.uint8)
+    xd, yd = dev(x), empty_bytes(x.nbytes)
+    st = packed_strides(shape)
+    src = encode(dt, xd, shape, st, box, mode)
+    dst = encode(dt, yd, shape, st, box, mode)
+    p = P.plan(dt, shape, st, box, mode, threads=threads)
+    info = acp.acp_plan_query(src, threads)
+    assert (info["issues"], info["vec_bytes"], info["outer"]) == (p.issues, p.vec_bytes, p.outer)
+    acp.acp_tile_copy(src, dst, threads, stream())
+    assert np.array_equal(host(yd, np.uint8), x)
+    elems = x.view({1: np.uint8, 2: np.uint16, 4: np.uint32}[es])
+    n = int(np.prod(P.tile_grid(shape, box)))
+    for t in sorted({0, n // 2, n - 1}):
+        assert _lds_image(src, t, threads, p.tile_bytes) == T.lds_image(elems, p, t)
+
+
 @pytest.mark.parametrize("misalign", [4, 8])
 def test_four_byte_path_when_only_4_or_8_aligned(misalign):
     shape, box = (64, 256), (64, 32)

@@ -60,19 +60,102 @@ def test_reduce_rejects_bad_shapes():
         REF.tile_reduce_add(np.zeros((3,), np.float32), np.zeros((4, 3), np.float32))
 
 
-def test_reduce_rows_exact_then_rounded_once():
+def _round_exact(q, dt):
+    """Rational q rounded to nearest in numpy float type dt, ties to even,
+    decided by exact rational distances (no intermediate binary64 rounding
+    can decide it: the binary64 guess only picks the three candidates)."""
     from fractions import Fraction
+    f = dt(float(q))
+    cands = [np.nextafter(f, dt(-np.inf)), f, np.nextafter(f, dt(np.inf))]
+    cands = [c for c in cands if np.isfinite(c)]
+    best = min(abs(Fraction(float(c)) - q) for c in cands)
+    ties = [c for c in cands if abs(Fraction(float(c)) - q) == best]
+    if len(ties) == 1:
+        return ties[0]
+    bits = np.dtype(dt).type
+    ui = np.uint16 if dt == np.float16 else np.uint32
+    return [c for c in ties if int(np.array(c, dt).view(ui)) % 2 == 0][0]
+
+
+def _exact_sum(values):
+    from fractions import Fraction
+    return sum((Fraction(float(v)) for v in values), Fraction(0))
+
+
+def test_reduce_rows_exact_then_rounded_once():
     rng = np.random.default_rng(6)
     x = (rng.standard_normal((7, 33)) * 10.0 ** rng.integers(-6, 7, (7, 33))).astype(np.float32)
     got = REF.reduce_rows(x)
     for r in range(7):
-        exact = sum(Fraction(float(v)) for v in x[r])
-        # float32(exact) by round-to-nearest: compare against both neighbours
-        f = np.float32(float(exact))
-        assert got[r] == f
-        lo, hi = np.nextafter(f, np.float32(-np.inf)), np.nextafter(f, np.float32(np.inf))
-        assert abs(Fraction(float(f)) - exact) <= abs(Fraction(float(lo)) - exact)
-        assert abs(Fraction(float(f)) - exact) <= abs(Fraction(float(hi)) - exact)
+        assert got[r] == _round_exact(_exact_sum(x[r]), np.float32)
+
+
+def test_reduce_rows_single_rounding_at_a_binary64_sticky_bit():
+    # 1 + 2**-24 is the binary32 midpoint between 1 and 1 + 2**-23; the
+    # 2**-80 term puts the exact sum just above it, so it rounds up.  Summing
+    # into binary64 first drops the 2**-80 (half an ulp of binary64 is
+    # 2**-53) and the tie then goes to the even neighbour, 1.
+    x = np.array([[1.0, 2.0 ** -24, 2.0 ** -80]], np.float32)
+    assert REF.reduce_rows(x)[0] == np.float32(1 + 2.0 ** -23)
+    # the same below the midpoint
+    x = np.array([[1.0, 2.0 ** -24, -(2.0 ** -80)]], np.float32)
+    assert REF.reduce_rows(x)[0] == np.float32(1.0)
+    # and for negative sums (truncation toward zero mirrors)
+    x = np.array([[-1.0, -(2.0 ** -24), -(2.0 ** -80)]], np.float32)
+    assert REF.reduce_rows(x)[0] == np.float32(-(1 + 2.0 ** -23))
+    # an exact tie stays a tie: ties to even
+    x = np.array([[1.0, 2.0 ** -24]], np.float32)
+    assert REF.reduce_rows(x)[0] == np.float32(1.0)
+    x = np.array([[1.0 + 2.0 ** -23, 2.0 ** -24]], np.float32)
+    assert REF.reduce_rows(x)[0] == np.float32(1.0 + 2.0 ** -22)
+
+
+def test_reduce_rows_random_near_ties_against_exact_rounding():
+    # rows built around binary32 midpoints with tiny residues far below the
+    # binary64 precision of the sum: every one needs the single rounding
+    rng = np.random.default_rng(11)
+    rows = []
+    for _ in range(300):
+        big = np.float32(rng.uniform(1, 2)) * np.float32(2.0 ** int(rng.integers(-4, 5)))
+        half_ulp = np.spacing(big) / 2
+        tail = float(rng.choice([-1, 1])) * 2.0 ** -int(rng.integers(60, 120))
+        extra = [float(v) for v in rng.standard_normal(int(rng.integers(0, 4))).astype(np.float32) * 2.0 ** -40]
+        rows.append([float(big), float(half_ulp), tail] + extra + [0.0] * (6 - 3 - len(extra)))
+    x = np.array(rows, dtype=np.float32)
+    got = REF.reduce_rows(x)
+    for r in range(len(rows)):
+        assert got[r] == _round_exact(_exact_sum(x[r]), np.float32), x[r]
+
+
+def test_reduce_add_float_single_rounding():
+    # store with reduce-add into float32: dst 1, contributions 2**-24 and
+    # 2**-80: the exact sum lies just above the binary32 midpoint
+    dst = np.array([[1.0]], np.float32)
+    src = np.array([[2.0 ** -24], [2.0 ** -80]], np.float32)
+    assert REF.tile_reduce_add(dst, src)[0, 0] == np.float32(1 + 2.0 ** -23)
+    # float16: 1 + 2**-11 is the binary16 midpoint between 1 and 1 + 2**-10;
+    # the subnormal 2**-24 puts the exact sum above it.  Rounding the partial
+    # sum 1 + 2**-11 to binary16 first would give 1 (ties to even), and 1 +
+    # 2**-24 rounds to 1 again.
+    dst16 = np.zeros((1, 1), np.float16)
+    src16 = np.array([[1.0], [2.0 ** -11], [2.0 ** -24]], np.float16)
+    assert REF.tile_reduce_add(dst16, src16)[0, 0] == np.float16(1 + 2.0 ** -10)
+    h = np.float16(1.0)
+    for v in src16[1:, 0]:
+        h = np.float16(h + v)
+    assert h == np.float16(1.0)
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float16])
+def test_reduce_add_random_against_exact_rounding(dt):
+    rng = np.random.default_rng(12)
+    src = (rng.standard_normal((9, 3, 5)) * 2.0 ** rng.integers(-12, 12, (9, 3, 5))).astype(dt)
+    dst = rng.standard_normal((1, 3, 5)).astype(dt)
+    got = REF.tile_reduce_add(dst, src)
+    for j in range(3):
+        for k in range(5):
+            want = _round_exact(_exact_sum(list(src[:, j, k]) + [dst[0, j, k]]), dt)
+            assert got[0, j, k] == want
 
 
 def test_reduce_rows_closed_forms():

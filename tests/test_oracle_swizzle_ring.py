@@ -102,16 +102,21 @@ def test_ring_bruteforce(stages):
                 assert e.iteration - consumed <= stages - 1
 
 
-def test_ring_page_formulas():
-    # main-loop stage indices of the page equal j % S for the load of j = i + S - 1
+def test_ring_main_loop_slot_order():
+    # "Detailed Pseudo-Code" of the circular-buffering page: in the main loop
+    # the stage being consumed advances one slot per iteration starting from
+    # slot 0, and the stage being loaded runs S - 1 slots ahead of it (mod S).
+    # Checked on the schedule's events: the k-th main-loop load goes to the
+    # slot that is S - 1 past the slot of the k-th consume.
     for stages in (2, 3, 4):
         for n in range(stages, 20):
             ev = R.schedule(n, stages)
-            main = [e for e in ev if e.kind == R.LOAD][stages - 1:]
-            for i, e in enumerate(main):
-                cur, ld = R.page_stage_formulas(i, stages)
-                assert ld == e.stage and e.iteration == i + stages - 1
-                assert cur == i % stages
+            main_loads = [e for e in ev if e.kind == R.LOAD][stages - 1:]
+            cons = [e for e in ev if e.kind == R.CONSUME]
+            for k, ld in enumerate(main_loads):
+                assert cons[k].stage == k % stages
+                assert ld.stage == (cons[k].stage + stages - 1) % stages
+                assert ld.iteration == cons[k].iteration + stages - 1
 
 
 def test_ring_wait_counts_hand_derived():
