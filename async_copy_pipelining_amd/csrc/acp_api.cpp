@@ -7,6 +7,7 @@
 // kernel on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -82,12 +83,29 @@ int log2i(int v) {
 
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-int device_lds_limit() {
-  int dev = 0, v = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 65536;
-  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) return 65536;
+// Device attributes, read from the runtime once per device and kept.
+constexpr int kMaxDevices = 64;
+
+int current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  return dev;
+}
+
+int device_attr(hipDeviceAttribute_t attr, std::atomic<int>* cache, int dflt) {
+  const int dev = current_device();
+  if (dev < 0) return dflt;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, attr, dev) != hipSuccess || v <= 0) return dflt;
+  cache[dev].store(v, std::memory_order_relaxed);
   return v;
 }
+
+std::atomic<int> g_lds_limit[kMaxDevices];
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int device_lds_limit() { return device_attr(hipDeviceAttributeMaxSharedMemoryPerBlock, g_lds_limit, 65536); }
 
 // Launch knobs read once from the environment (measurement aids; the
 // defaults are the measured best on MI355X):
@@ -124,6 +142,8 @@ struct Launch {
   acp::KernelKey key;
   unsigned grid = 0, block = 0, lds = 0;
   int64_t n_tiles = 0;
+  const void* kernel = nullptr;  // resolved from `key` when the launch is cached
+  std::string desc;              // acp_last_kernel text of this launch
 };
 
 struct EngineRequest {
@@ -522,34 +542,117 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   return ACP_OK;
 }
 
-acp_status launch(const Launch& L, void* stream) {
-  g_last_kernel = "none";
-  if (L.n_tiles == 0) return ret(ACP_OK);
-  const void* k = acp::engine_kernel(L.key);
-  if (!k) return ret(ACP_ERR_UNSUPPORTED, "op / dtype combination is not in the registry");
-  const hipError_t e = acp::engine_launch(k, L.args, L.grid, L.block, L.lds, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+std::string describe(const Launch& L) {
   static const char* const kinds[] = {"engine copy",        "engine tile ewise",  "engine stream",
                                       "stream linear grid", "general copy",       "general tile ewise",
                                       "general stream",     "general reduce-add", "general row reduction",
                                       "tile linear grid",   "row reduction linear grid"};
   const int m = L.key.mode;
-  g_last_kernel = std::string(m >= 0 && m <= 10 ? kinds[m] : "?") + " vec " + std::to_string(L.key.vec_bytes) +
-                  " rounds " + std::to_string(L.args.outer) + " srow " + std::to_string(L.key.srow) + " variant " +
-                  std::to_string(L.key.variant) + " grid " + std::to_string(L.grid) + " threads " +
-                  std::to_string(L.block) + " slots " + std::to_string(L.args.stages) + " lds " + std::to_string(L.lds) +
-                  (m == 8 || m == 10 ? std::string(L.args.red_local ? " wave-local" : " lds partials") : std::string());
+  return std::string(m >= 0 && m <= 10 ? kinds[m] : "?") + " vec " + std::to_string(L.key.vec_bytes) +
+         " rounds " + std::to_string(L.args.outer) + " srow " + std::to_string(L.key.srow) + " variant " +
+         std::to_string(L.key.variant) + " grid " + std::to_string(L.grid) + " threads " +
+         std::to_string(L.block) + " slots " + std::to_string(L.args.stages) + " lds " + std::to_string(L.lds) +
+         (m == 8 || m == 10 ? std::string(L.args.red_local ? " wave-local" : " lds partials") : std::string());
+}
+
+// Resolve the kernel and the description of a prepared launch (done once,
+// when the launch enters the cache).
+acp_status finalize(Launch* L) {
+  if (L->n_tiles == 0) return ACP_OK;
+  L->kernel = acp::engine_kernel(L->key);
+  if (!L->kernel) return ret(ACP_ERR_UNSUPPORTED, "op / dtype combination is not in the registry");
+  L->desc = describe(*L);
+  return ACP_OK;
+}
+
+acp_status launch(const Launch& L, void* stream) {
+  g_last_kernel = "none";
+  if (L.n_tiles == 0) return ret(ACP_OK);
+  const hipError_t e = acp::engine_launch(L.kernel, L.args, L.grid, L.block, L.lds, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  g_last_kernel = L.desc;
   return ret(ACP_OK);
+}
+
+// Prepared launches, per thread: the host plan and the kernel arguments of a
+// call depend only on its arguments (descriptors by value, scalars, device
+// addresses) and on the device, so a repeated call reuses them ("copy_async
+// -> tma", "Algorithm" step 3: the host descriptor is emitted once, keyed by
+// a cache).  A key is those bytes; a small round-robin table of recent keys
+// per thread.
+struct CallKey {
+  unsigned char b[4 * sizeof(acp::DescData) + 256];
+  size_t n = 0;
+  bool ok = true;
+  explicit CallKey(int entry) {
+    add(&entry, sizeof(entry));
+    const int dev = current_device();
+    add(&dev, sizeof(dev));
+  }
+  void add(const void* p, size_t k) {
+    if (n + k > sizeof(b)) { ok = false; return; }
+    std::memcpy(b + n, p, k);
+    n += k;
+  }
+  template <class T>
+  void val(const T& v) { add(&v, sizeof(v)); }
+  void desc(const acp_tile_desc* d) {
+    if (!d) { val(-1); return; }
+    add(d->opaque, sizeof(acp::DescData));
+  }
+  void ints(const int32_t* v, int k) {
+    if (!v) { val(-1); return; }
+    add(v, sizeof(int32_t) * static_cast<size_t>(k));
+  }
+};
+
+// rank of an encoded descriptor (0 if it is not one): the length of the
+// stage box a call passes
+int desc_rank(const acp_tile_desc* d) {
+  acp::DescData dd;
+  return load_desc(d, &dd) ? dd.rank : 0;
+}
+
+constexpr int kCacheEntries = 16;
+struct CacheEntry {
+  std::string key;
+  Launch L;
+};
+thread_local CacheEntry g_cache[kCacheEntries];
+thread_local int g_cache_next = 0;
+
+const Launch* cache_find(const CallKey& k) {
+  if (!k.ok) return nullptr;
+  for (const CacheEntry& e : g_cache)
+    if (e.key.size() == k.n && std::memcmp(e.key.data(), k.b, k.n) == 0) return &e.L;
+  return nullptr;
+}
+
+const Launch* cache_put(const CallKey& k, const Launch& L) {
+  if (!k.ok) return nullptr;
+  CacheEntry& e = g_cache[g_cache_next];
+  g_cache_next = (g_cache_next + 1) % kCacheEntries;
+  e.key.assign(reinterpret_cast<const char*>(k.b), k.n);
+  e.L = L;
+  return &e.L;
+}
+
+// Launch the cached launch for `k`, or build, finalize, cache and launch it.
+template <class Build>
+acp_status run_cached(const CallKey& k, Build&& build, void* stream) {
+  if (const Launch* c = cache_find(k)) return launch(*c, stream);
+  Launch L;
+  acp_status st = build(&L);
+  if (st != ACP_OK) return st;
+  st = finalize(&L);
+  if (st != ACP_OK) return st;
+  const Launch* c = cache_put(k, L);
+  return launch(c ? *c : L, stream);
 }
 
 bool is_float(int dt) { return dt == ACP_F16 || dt == ACP_F32; }
 
-int device_cu_count() {
-  int dev = 0, v = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 256;
-  return v;
-}
+int device_cu_count() { return device_attr(hipDeviceAttributeMultiprocessorCount, g_cu_count, 256); }
 
 // Tile copy and tile elementwise: the result of a tile does not depend on
 // which workgroup moves it, so large tile counts run on a persistent grid
@@ -609,6 +712,359 @@ void tile_schedule(const acp::Plan& p, int n_in, int threads, int64_t out_image,
     *stages = 1;
     *tiles_per_trip = 1;
   }
+}
+
+// The compute entry points, without the launch: validate and prepare (no
+// HIP calls besides device attributes).  The exported functions cache the
+// result and launch it.
+acp_status keep(Launch* res, Launch& L) {
+  *res = std::move(L);
+  return ACP_OK;
+}
+
+acp_status build_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, int threads, Launch* res) {
+  acp::DescData s, d;
+  if (!load_desc(src, &s) || !load_desc(dst, &d)) return ret(ACP_ERR_INVALID, "not an encoded descriptor");
+  // validate_copy_op: both sides laid out, equal dtype, equal extents
+  if (s.dtype != d.dtype) return ret(ACP_ERR_INVALID, "not a valid copy op: dtypes differ");
+  if (!same_geometry(s, d, false)) return ret(ACP_ERR_INVALID, "not a valid copy op: shapes or boxes differ");
+  if (overlap(s, d)) return ret(ACP_ERR_INVALID, "source and destination share memory");
+  EngineRequest q{};
+  q.op = ACP_OP_COPY;
+  q.mode = 0;
+  q.x = &s;
+  q.out = &d;
+  q.in_ptrs[0] = reinterpret_cast<const void*>(s.gbase);
+  q.n_in = 1;
+  q.stage_box = s.box;
+  q.threads = threads;
+  q.copy_only = true;
+  {
+    acp::Plan p;
+    std::string why;
+    if (acp::plan_box(s, true, &p, &why) == acp::PlanStatus::Ok) tile_schedule(p, 1, threads, 0, &q.workgroups, &q.stages, &q.tiles_per_trip);
+    else q.stages = 1;
+  }
+  Launch L;
+  const acp_status st = prepare(q, &L);
+  if (st != ACP_OK) return st;
+  return keep(res, L);
+}
+
+acp_status build_tile_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_desc* const* in, int n_in,
+                          int threads, Launch* res) {
+  acp::DescData o;
+  if (!load_desc(out, &o)) return ret(ACP_ERR_INVALID, "not an encoded output descriptor");
+  int need = -1;
+  switch (op) {
+    case ACP_OP_ZERO: need = n_in <= 1 ? n_in : -1; break;
+    case ACP_OP_SQRT: case ACP_OP_EXP: need = 1; break;
+    case ACP_OP_ADD: case ACP_OP_MUL: need = 2; break;
+    case ACP_OP_FMA: need = 3; break;
+    default: return ret(ACP_ERR_INVALID, "unknown op for tile_ewise");
+  }
+  if (need != n_in) return ret(ACP_ERR_INVALID, "wrong number of operands for the op");
+  if (n_in > 0 && !in) return ret(ACP_ERR_INVALID, "null operand list");
+  acp::DescData ins[3];
+  for (int k = 0; k < n_in; ++k) {
+    if (!load_desc(in[k], &ins[k])) return ret(ACP_ERR_INVALID, "not an encoded operand descriptor");
+    if (!same_geometry(ins[k], ins[0], true) || ins[k].dtype != ins[0].dtype || ins[k].swizzle != ins[0].swizzle)
+      return ret(ACP_ERR_INVALID, "operands must share one layout (dtype, shape, strides, box, swizzle)");
+  }
+  const acp::DescData& anchor = n_in ? ins[0] : o;
+  if (!same_geometry(anchor, o, false)) return ret(ACP_ERR_INVALID, "output shape or box differs from the operands");
+  const int ti = anchor.dtype, to = o.dtype;
+  if (!is_float(ti) || !is_float(to)) return ret(ACP_ERR_UNSUPPORTED, "elementwise ops take float16 or float32");
+  if ((op == ACP_OP_ADD || op == ACP_OP_MUL || op == ACP_OP_FMA || op == ACP_OP_ZERO) && ti != to)
+    return ret(ACP_ERR_UNSUPPORTED, "this op keeps the operand type");
+  for (int k = 0; k < n_in; ++k)
+    if (overlap(ins[k], o) && !same_elements(ins[k], o))
+      return ret(ACP_ERR_INVALID, "the output shares memory with an operand other than element for element");
+  EngineRequest q{};
+  q.op = op;
+  q.mode = 1;
+  q.x = &anchor;
+  q.out = &o;
+  for (int k = 0; k < n_in; ++k) q.in_ptrs[k] = reinterpret_cast<const void*>(ins[k].gbase);
+  q.n_in = n_in;
+  q.stage_box = anchor.box;
+  q.threads = threads;
+  q.copy_only = false;
+  {
+    acp::Plan p;
+    std::string why;
+    if (acp::plan_box(anchor, false, &p, &why) == acp::PlanStatus::Ok)
+      tile_schedule(p, n_in, threads, p.tile_elems() * o.esize, &q.workgroups, &q.stages, &q.tiles_per_trip);
+    else q.stages = 1;
+  }
+  Launch L;
+  acp_status st = prepare(q, &L);
+  if (st != ACP_OK) return st;
+  // The linear tile kernel streams best with one workgroup per CU (32x32
+  // float32 sqrt: 6.00-6.03 against 5.87-5.88 TB/s with two); the general
+  // kernel keeps the schedule's count, whose extra waves cover the LDS round
+  // trip of its output image.
+  const int cus = device_cu_count();
+  if (L.key.mode == 9 && tile_wg_per_cu_env() == 0 && q.workgroups > cus) {
+    q.workgroups = cus;
+    st = prepare(q, &L);
+    if (st != ACP_OK) return st;
+  }
+  return keep(res, L);
+}
+
+acp_status build_stream_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_desc* x, const float* row_a,
+                            const float* row_b, const int32_t* stage_box, int stages, int threads, int workgroups,
+                            Launch* res) {
+  acp::DescData xd, od;
+  if (!load_desc(x, &xd) || !load_desc(out, &od)) return ret(ACP_ERR_INVALID, "not an encoded descriptor");
+  if (!stage_box) return ret(ACP_ERR_INVALID, "null stage box");
+  if (stages < 2 || stages > 4) return ret(ACP_ERR_INVALID, "stages must be 2, 3 or 4");
+  if (workgroups < 0) return ret(ACP_ERR_INVALID, "workgroups must be >= 0");
+  if (!same_geometry(xd, od, false)) return ret(ACP_ERR_INVALID, "output shape or box differs from x");
+  if (overlap(xd, od)) return ret(ACP_ERR_INVALID, "x and the output share memory");
+  for (int d = 0; d < xd.rank; ++d)
+    if (stage_box[d] < 1) return ret(ACP_ERR_INVALID, "stage box must be >= 1");
+  bool row_ops = false;
+  switch (op) {
+    case ACP_OP_ZERO: case ACP_OP_SQRT: case ACP_OP_EXP:
+      if (!is_float(xd.dtype) || !is_float(od.dtype))
+        return ret(ACP_ERR_UNSUPPORTED, "elementwise ops take float16 or float32");
+      if (op == ACP_OP_ZERO && xd.dtype != od.dtype) return ret(ACP_ERR_UNSUPPORTED, "zero keeps the type");
+      break;
+    case ACP_OP_ADD: case ACP_OP_MUL: case ACP_OP_FMA:
+      if (xd.dtype != ACP_F32 || od.dtype != ACP_F32)
+        return ret(ACP_ERR_UNSUPPORTED, "per-row ops take float32 x and output");
+      if ((op != ACP_OP_ADD && !row_a) || (op != ACP_OP_MUL && !row_b))
+        return ret(ACP_ERR_INVALID, "missing per-row scalar array");
+      row_ops = true;
+      break;
+    default: return ret(ACP_ERR_INVALID, "unknown op for stream_ewise");
+  }
+  if (xd.rank < 2 && row_ops) return ret(ACP_ERR_INVALID, "per-row scalars need rank >= 2");
+  if (row_ops) {
+    uint64_t rows = 1;
+    for (int d = 0; d + 1 < xd.rank; ++d) rows *= static_cast<uint64_t>(xd.shape[d]);
+    const uint64_t ob = od.gbase, on = tensor_span(od);
+    if ((row_a && overlap(reinterpret_cast<uint64_t>(row_a), rows * 4, ob, on)) ||
+        (row_b && overlap(reinterpret_cast<uint64_t>(row_b), rows * 4, ob, on)))
+      return ret(ACP_ERR_INVALID, "a per-row scalar array shares memory with the output");
+  }
+  EngineRequest q{};
+  q.op = op;
+  q.mode = 2;
+  q.x = &xd;
+  q.out = &od;
+  q.in_ptrs[0] = reinterpret_cast<const void*>(xd.gbase);
+  q.n_in = 1;
+  q.stage_box = stage_box;
+  q.stages = stages;
+  q.threads = threads;
+  q.workgroups = workgroups;
+  q.row_a = row_a;
+  q.row_b = row_b;
+  q.row_ops = row_ops;
+  q.copy_only = false;
+  Launch L;
+  const acp_status st = prepare(q, &L);
+  if (st != ACP_OK) return st;
+  return keep(res, L);
+}
+
+acp_status build_tile_reduce(acp_op op, const acp_tile_desc* dst, const acp_tile_desc* src, int threads,
+                           Launch* res) {
+  acp::DescData s, d;
+  if (!load_desc(src, &s) || !load_desc(dst, &d)) return ret(ACP_ERR_INVALID, "not an encoded descriptor");
+  if (op != ACP_OP_ADD) return ret(ACP_ERR_INVALID, "the store reduces with add");
+  if (s.dtype != d.dtype) return ret(ACP_ERR_INVALID, "source and destination dtypes differ");
+  if (s.dtype != ACP_U32 && s.dtype != ACP_F32 && s.dtype != ACP_F16)
+    return ret(ACP_ERR_UNSUPPORTED, "reduce-add takes u32, f32 or f16");
+  if (s.rank != d.rank) return ret(ACP_ERR_INVALID, "source and destination ranks differ");
+  for (int k = 0; k < s.rank; ++k) {
+    if (s.box[k] != d.box[k]) return ret(ACP_ERR_INVALID, "source and destination boxes differ");
+    if (d.shape[k] == s.shape[k]) continue;
+    if (d.shape[k] != 1 || s.box[k] != 1)
+      return ret(ACP_ERR_INVALID, "a destination extent must equal the source's, or be 1 where the box is 1");
+  }
+  if (overlap(s, d)) return ret(ACP_ERR_INVALID, "source and destination share memory");
+  bool one_each = true;  // every destination element receives one contribution
+  for (int k = 0; k < s.rank; ++k) one_each = one_each && d.shape[k] == s.shape[k] && d.strides[k] == s.strides[k];
+  if (one_each && s.dtype != ACP_U32) {
+    // No two source elements meet in one destination element: dst' = src + dst
+    // needs no atomics.  Both tensors ride the ring and the sum is stored in
+    // place; every element is staged before the same lane stores it, and no
+    // other trip touches it.
+    EngineRequest q{};
+    q.op = ACP_OP_ADD;
+    q.mode = 2;
+    q.x = &s;
+    q.out = &d;
+    q.in_ptrs[0] = reinterpret_cast<const void*>(s.gbase);
+    q.in_ptrs[1] = reinterpret_cast<const void*>(d.gbase);
+    q.n_in = 2;
+    q.stage_box = s.box;
+    q.threads = threads;
+    q.copy_only = false;
+    q.binary = 1;
+    int tpt = 1;
+    acp::Plan p;
+    std::string why;
+    if (acp::plan_box(s, false, &p, &why) == acp::PlanStatus::Ok)
+      tile_schedule(p, 2, threads, 0, &q.workgroups, &q.stages, &tpt);
+    q.stages = q.workgroups > 0 ? q.stages : 2;
+    Launch L;
+    const acp_status st = prepare(q, &L);
+    if (st == ACP_OK && L.key.variant == 1) return keep(res, L);
+    if (st != ACP_OK && st != ACP_ERR_UNSUPPORTED) return st;
+    // otherwise: the atomic path below
+  }
+  EngineRequest q{};
+  q.op = ACP_OP_ADD;
+  q.mode = 3;
+  q.x = &s;
+  q.out = &d;
+  q.in_ptrs[0] = reinterpret_cast<const void*>(s.gbase);
+  q.n_in = 1;
+  q.stage_box = s.box;
+  q.threads = threads;
+  q.copy_only = false;
+  {
+    acp::Plan p;
+    std::string why;
+    if (acp::plan_box(s, false, &p, &why) == acp::PlanStatus::Ok) {
+      tile_schedule(p, 1, threads, 0, &q.workgroups, &q.stages, &q.tiles_per_trip);
+      // Sums over batch dims: each workgroup owns whole destination tiles,
+      // sums their contributions in registers and adds once per element.
+      int64_t group = 1;
+      for (int k = 0; k < s.rank; ++k)
+        if (d.shape[k] == 1 && s.shape[k] > 1) group *= s.shape[k];
+      static const bool grouped_ok = env_flag("ACP_REDUCE_GROUPED", true);
+      const int64_t n_tiles = p.n_tiles();
+      if (grouped_ok && group > 1 && n_tiles > 0) {
+        const int64_t dst_tiles = n_tiles / group;
+        static const int env_wg_per_cu = [] {
+          const char* e = std::getenv("ACP_REDUCE_WG_PER_CU");
+          return (e && std::atoi(e) > 0) ? std::atoi(e) : 0;
+        }();
+        static const int env_slots = [] {
+          const char* e = std::getenv("ACP_REDUCE_STAGES");
+          return (e && std::atoi(e) >= 2 && std::atoi(e) <= 4) ? std::atoi(e) : 3;
+        }();
+        const int64_t per_cu = env_wg_per_cu ? env_wg_per_cu : std::max<int64_t>(1, 16384 / p.tile_bytes());
+        const int64_t want = static_cast<int64_t>(device_cu_count()) * per_cu;
+        // About 16 KiB of tiles per CU in flight per ring step and 3 ring
+        // slots (ACP_REDUCE_WG_PER_CU, ACP_REDUCE_STAGES): the best of 2-8
+        // workgroups per CU x 2-4 slots x 4 or 8 KiB tiles measured on 128
+        // float32 contributions per element of [500,1024] (8 KiB tiles, two
+        // per CU: 4.8 TB/s).  Few destination tiles: split each one's
+        // contributions over k workgroups (k atomic adds per element instead
+        // of one).
+        int64_t k = 1;
+        while (dst_tiles * k * 2 <= want && group % (k * 2) == 0) k *= 2;
+        const int64_t sub = group / k;                 // contributions summed per workgroup group
+        const int64_t groups = dst_tiles * k;
+        const int64_t g = std::min<int64_t>(groups, want);
+        const int64_t per = (groups + g - 1) / g;      // groups per workgroup
+        q.red_group = sub;
+        q.red_per_wg = per * sub;
+        q.workgroups = static_cast<int>((groups + per - 1) / per);
+        q.stages = env_slots;
+        q.tiles_per_trip = 1;
+      }
+    } else {
+      q.stages = 1;
+    }
+  }
+  Launch L;
+  const acp_status st = prepare(q, &L);
+  if (st != ACP_OK) return st;
+  if (L.key.mode != 7) return ret(ACP_ERR_UNSUPPORTED, "reduce-add needs 16-byte rounds and 1, 2, 4 or 8 rounds per thread");
+  return keep(res, L);
+}
+
+acp_status build_stream_reduce_rows(acp_op op, float* out, const acp_tile_desc* x, const int32_t* stage_box, int stages,
+                                  int threads, int workgroups, Launch* res) {
+  acp::DescData xd;
+  if (!load_desc(x, &xd)) return ret(ACP_ERR_INVALID, "not an encoded descriptor");
+  if (op != ACP_OP_ADD) return ret(ACP_ERR_INVALID, "rows reduce with add");
+  if (!out) return ret(ACP_ERR_INVALID, "null output");
+  if (!stage_box) return ret(ACP_ERR_INVALID, "null stage box");
+  if (stages < 2 || stages > 4) return ret(ACP_ERR_INVALID, "stages must be 2, 3 or 4");
+  if (workgroups < 0) return ret(ACP_ERR_INVALID, "workgroups must be >= 0");
+  if (xd.dtype != ACP_F32 && xd.dtype != ACP_F16) return ret(ACP_ERR_UNSUPPORTED, "row reduction takes f16 or f32");
+  const int r = xd.rank;
+  if (r < 2) return ret(ACP_ERR_INVALID, "row reduction needs rank >= 2");
+  for (int d = 0; d < r; ++d)
+    if (stage_box[d] < 1) return ret(ACP_ERR_INVALID, "stage box must be >= 1");
+  if (xd.box[r - 1] != xd.shape[r - 1] || stage_box[r - 1] != xd.shape[r - 1])
+    return ret(ACP_ERR_INVALID, "tiles and stages must hold whole rows (innermost box = innermost extent)");
+  int64_t rows = 1;
+  for (int d = 0; d + 1 < r; ++d) rows *= xd.shape[d];
+  if (rows >= (int64_t(1) << 29)) return ret(ACP_ERR_UNSUPPORTED, "too many rows");
+  if (reinterpret_cast<uint64_t>(out) % 4) return ret(ACP_ERR_INVALID, "output not 4-byte aligned");
+  if (overlap(reinterpret_cast<uint64_t>(out), static_cast<uint64_t>(rows) * 4, xd.gbase, tensor_span(xd)))
+    return ret(ACP_ERR_INVALID, "the output shares memory with x");
+  EngineRequest q{};
+  q.op = ACP_OP_ADD;
+  q.mode = 4;
+  q.x = &xd;
+  q.out = &xd;  // same shape; the output is the packed row array `out`
+  q.in_ptrs[0] = reinterpret_cast<const void*>(xd.gbase);
+  q.n_in = 1;
+  q.stage_box = stage_box;
+  q.stages = stages;
+  q.threads = threads;
+  q.workgroups = workgroups;
+  q.copy_only = false;
+  Launch L;
+  const acp_status st = prepare(q, &L);
+  if (st != ACP_OK) return st;
+  if (L.key.mode != 8 && L.key.mode != 10)
+    return ret(ACP_ERR_UNSUPPORTED, "row reduction needs 16-byte rounds and 1, 2, 4 or 8 rounds per thread");
+  if (L.args.red_rows > 64u * static_cast<uint32_t>(L.args.waves))
+    return ret(ACP_ERR_UNSUPPORTED, "row reduction stages hold at most 64 rows per wave");
+  L.args.out = reinterpret_cast<char*>(out);
+  L.args.out_span = static_cast<uint64_t>(rows) * 4u;
+  return keep(res, L);
+}
+
+acp_status build_stream_binary(acp_op op, const acp_tile_desc* out, const acp_tile_desc* x, const acp_tile_desc* z,
+                             const int32_t* stage_box, int stages, int threads, int workgroups, acp_staging z_staging,
+                             Launch* res) {
+  acp::DescData xd, zd, od;
+  if (!load_desc(x, &xd) || !load_desc(z, &zd) || !load_desc(out, &od))
+    return ret(ACP_ERR_INVALID, "not an encoded descriptor");
+  if (op != ACP_OP_ADD && op != ACP_OP_MUL) return ret(ACP_ERR_INVALID, "two-tensor streams are add or mul");
+  if (z_staging != ACP_STAGE_RING && z_staging != ACP_STAGE_SET) return ret(ACP_ERR_INVALID, "unknown staging");
+  if (!stage_box) return ret(ACP_ERR_INVALID, "null stage box");
+  if (stages < 2 || stages > 4) return ret(ACP_ERR_INVALID, "stages must be 2, 3 or 4");
+  if (workgroups < 0) return ret(ACP_ERR_INVALID, "workgroups must be >= 0");
+  if (!same_geometry(zd, xd, true) || zd.dtype != xd.dtype || zd.swizzle != xd.swizzle)
+    return ret(ACP_ERR_INVALID, "x and z must share one layout (dtype, shape, strides, box, swizzle)");
+  if (!same_geometry(xd, od, false) || od.dtype != xd.dtype)
+    return ret(ACP_ERR_INVALID, "output dtype, shape or box differs from x");
+  if (!is_float(xd.dtype)) return ret(ACP_ERR_UNSUPPORTED, "two-tensor streams take float16 or float32");
+  if (overlap(xd, od) || overlap(zd, od)) return ret(ACP_ERR_INVALID, "the output shares memory with x or z");
+  for (int d = 0; d < xd.rank; ++d)
+    if (stage_box[d] < 1) return ret(ACP_ERR_INVALID, "stage box must be >= 1");
+  EngineRequest q{};
+  q.op = op;
+  q.mode = 2;
+  q.x = &xd;
+  q.out = &od;
+  q.in_ptrs[0] = reinterpret_cast<const void*>(xd.gbase);
+  q.in_ptrs[1] = reinterpret_cast<const void*>(zd.gbase);
+  q.n_in = 2;
+  q.stage_box = stage_box;
+  q.stages = stages;
+  q.threads = threads;
+  q.workgroups = workgroups;
+  q.copy_only = false;
+  q.binary = z_staging == ACP_STAGE_SET ? 2 : 1;
+  Launch L;
+  const acp_status st = prepare(q, &L);
+  if (st != ACP_OK) return st;
+  return keep(res, L);
 }
 
 }  // namespace
@@ -693,348 +1149,84 @@ acp_status acp_plan_query(const acp_tile_desc* desc, int threads, int copy_only,
 }
 
 acp_status acp_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, int threads, void* hip_stream) {
-  acp::DescData s, d;
-  if (!load_desc(src, &s) || !load_desc(dst, &d)) return ret(ACP_ERR_INVALID, "not an encoded descriptor");
-  // validate_copy_op: both sides laid out, equal dtype, equal extents
-  if (s.dtype != d.dtype) return ret(ACP_ERR_INVALID, "not a valid copy op: dtypes differ");
-  if (!same_geometry(s, d, false)) return ret(ACP_ERR_INVALID, "not a valid copy op: shapes or boxes differ");
-  if (overlap(s, d)) return ret(ACP_ERR_INVALID, "source and destination share memory");
-  EngineRequest q{};
-  q.op = ACP_OP_COPY;
-  q.mode = 0;
-  q.x = &s;
-  q.out = &d;
-  q.in_ptrs[0] = reinterpret_cast<const void*>(s.gbase);
-  q.n_in = 1;
-  q.stage_box = s.box;
-  q.threads = threads;
-  q.copy_only = true;
-  {
-    acp::Plan p;
-    std::string why;
-    if (acp::plan_box(s, true, &p, &why) == acp::PlanStatus::Ok) tile_schedule(p, 1, threads, 0, &q.workgroups, &q.stages, &q.tiles_per_trip);
-    else q.stages = 1;
-  }
-  Launch L;
-  const acp_status st = prepare(q, &L);
-  if (st != ACP_OK) return st;
-  return launch(L, hip_stream);
+  CallKey k(1);
+  k.desc(src);
+  k.desc(dst);
+  k.val(threads);
+  return run_cached(k, [&](Launch* L) { return build_tile_copy(src, dst, threads, L); }, hip_stream);
 }
 
 acp_status acp_tile_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_desc* const* in, int n_in,
                           int threads, void* hip_stream) {
-  acp::DescData o;
-  if (!load_desc(out, &o)) return ret(ACP_ERR_INVALID, "not an encoded output descriptor");
-  int need = -1;
-  switch (op) {
-    case ACP_OP_ZERO: need = n_in <= 1 ? n_in : -1; break;
-    case ACP_OP_SQRT: case ACP_OP_EXP: need = 1; break;
-    case ACP_OP_ADD: case ACP_OP_MUL: need = 2; break;
-    case ACP_OP_FMA: need = 3; break;
-    default: return ret(ACP_ERR_INVALID, "unknown op for tile_ewise");
-  }
-  if (need != n_in) return ret(ACP_ERR_INVALID, "wrong number of operands for the op");
-  if (n_in > 0 && !in) return ret(ACP_ERR_INVALID, "null operand list");
-  acp::DescData ins[3];
-  for (int k = 0; k < n_in; ++k) {
-    if (!load_desc(in[k], &ins[k])) return ret(ACP_ERR_INVALID, "not an encoded operand descriptor");
-    if (!same_geometry(ins[k], ins[0], true) || ins[k].dtype != ins[0].dtype || ins[k].swizzle != ins[0].swizzle)
-      return ret(ACP_ERR_INVALID, "operands must share one layout (dtype, shape, strides, box, swizzle)");
-  }
-  const acp::DescData& anchor = n_in ? ins[0] : o;
-  if (!same_geometry(anchor, o, false)) return ret(ACP_ERR_INVALID, "output shape or box differs from the operands");
-  const int ti = anchor.dtype, to = o.dtype;
-  if (!is_float(ti) || !is_float(to)) return ret(ACP_ERR_UNSUPPORTED, "elementwise ops take float16 or float32");
-  if ((op == ACP_OP_ADD || op == ACP_OP_MUL || op == ACP_OP_FMA || op == ACP_OP_ZERO) && ti != to)
-    return ret(ACP_ERR_UNSUPPORTED, "this op keeps the operand type");
-  for (int k = 0; k < n_in; ++k)
-    if (overlap(ins[k], o) && !same_elements(ins[k], o))
-      return ret(ACP_ERR_INVALID, "the output shares memory with an operand other than element for element");
-  EngineRequest q{};
-  q.op = op;
-  q.mode = 1;
-  q.x = &anchor;
-  q.out = &o;
-  for (int k = 0; k < n_in; ++k) q.in_ptrs[k] = reinterpret_cast<const void*>(ins[k].gbase);
-  q.n_in = n_in;
-  q.stage_box = anchor.box;
-  q.threads = threads;
-  q.copy_only = false;
-  {
-    acp::Plan p;
-    std::string why;
-    if (acp::plan_box(anchor, false, &p, &why) == acp::PlanStatus::Ok)
-      tile_schedule(p, n_in, threads, p.tile_elems() * o.esize, &q.workgroups, &q.stages, &q.tiles_per_trip);
-    else q.stages = 1;
-  }
-  Launch L;
-  acp_status st = prepare(q, &L);
-  if (st != ACP_OK) return st;
-  // The linear tile kernel streams best with one workgroup per CU (32x32
-  // float32 sqrt: 6.00-6.03 against 5.87-5.88 TB/s with two); the general
-  // kernel keeps the schedule's count, whose extra waves cover the LDS round
-  // trip of its output image.
-  const int cus = device_cu_count();
-  if (L.key.mode == 9 && tile_wg_per_cu_env() == 0 && q.workgroups > cus) {
-    q.workgroups = cus;
-    st = prepare(q, &L);
-    if (st != ACP_OK) return st;
-  }
-  return launch(L, hip_stream);
+  CallKey k(2);
+  k.val(op);
+  k.desc(out);
+  k.val(n_in);
+  if (n_in < 0 || n_in > 3 || (n_in > 0 && !in)) k.ok = false;
+  for (int i = 0; k.ok && i < n_in; ++i) k.desc(in[i]);
+  k.val(threads);
+  return run_cached(k, [&](Launch* L) { return build_tile_ewise(op, out, in, n_in, threads, L); }, hip_stream);
 }
 
 acp_status acp_stream_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_desc* x, const float* row_a,
                             const float* row_b, const int32_t* stage_box, int stages, int threads, int workgroups,
                             void* hip_stream) {
-  acp::DescData xd, od;
-  if (!load_desc(x, &xd) || !load_desc(out, &od)) return ret(ACP_ERR_INVALID, "not an encoded descriptor");
-  if (!stage_box) return ret(ACP_ERR_INVALID, "null stage box");
-  if (stages < 2 || stages > 4) return ret(ACP_ERR_INVALID, "stages must be 2, 3 or 4");
-  if (workgroups < 0) return ret(ACP_ERR_INVALID, "workgroups must be >= 0");
-  if (!same_geometry(xd, od, false)) return ret(ACP_ERR_INVALID, "output shape or box differs from x");
-  if (overlap(xd, od)) return ret(ACP_ERR_INVALID, "x and the output share memory");
-  for (int d = 0; d < xd.rank; ++d)
-    if (stage_box[d] < 1) return ret(ACP_ERR_INVALID, "stage box must be >= 1");
-  bool row_ops = false;
-  switch (op) {
-    case ACP_OP_ZERO: case ACP_OP_SQRT: case ACP_OP_EXP:
-      if (!is_float(xd.dtype) || !is_float(od.dtype))
-        return ret(ACP_ERR_UNSUPPORTED, "elementwise ops take float16 or float32");
-      if (op == ACP_OP_ZERO && xd.dtype != od.dtype) return ret(ACP_ERR_UNSUPPORTED, "zero keeps the type");
-      break;
-    case ACP_OP_ADD: case ACP_OP_MUL: case ACP_OP_FMA:
-      if (xd.dtype != ACP_F32 || od.dtype != ACP_F32)
-        return ret(ACP_ERR_UNSUPPORTED, "per-row ops take float32 x and output");
-      if ((op != ACP_OP_ADD && !row_a) || (op != ACP_OP_MUL && !row_b))
-        return ret(ACP_ERR_INVALID, "missing per-row scalar array");
-      row_ops = true;
-      break;
-    default: return ret(ACP_ERR_INVALID, "unknown op for stream_ewise");
-  }
-  if (xd.rank < 2 && row_ops) return ret(ACP_ERR_INVALID, "per-row scalars need rank >= 2");
-  if (row_ops) {
-    uint64_t rows = 1;
-    for (int d = 0; d + 1 < xd.rank; ++d) rows *= static_cast<uint64_t>(xd.shape[d]);
-    const uint64_t ob = od.gbase, on = tensor_span(od);
-    if ((row_a && overlap(reinterpret_cast<uint64_t>(row_a), rows * 4, ob, on)) ||
-        (row_b && overlap(reinterpret_cast<uint64_t>(row_b), rows * 4, ob, on)))
-      return ret(ACP_ERR_INVALID, "a per-row scalar array shares memory with the output");
-  }
-  EngineRequest q{};
-  q.op = op;
-  q.mode = 2;
-  q.x = &xd;
-  q.out = &od;
-  q.in_ptrs[0] = reinterpret_cast<const void*>(xd.gbase);
-  q.n_in = 1;
-  q.stage_box = stage_box;
-  q.stages = stages;
-  q.threads = threads;
-  q.workgroups = workgroups;
-  q.row_a = row_a;
-  q.row_b = row_b;
-  q.row_ops = row_ops;
-  q.copy_only = false;
-  Launch L;
-  const acp_status st = prepare(q, &L);
-  if (st != ACP_OK) return st;
-  return launch(L, hip_stream);
+  CallKey k(3);
+  k.val(op);
+  k.desc(out);
+  k.desc(x);
+  k.val(row_a);
+  k.val(row_b);
+  k.ints(stage_box, desc_rank(x));
+  k.val(stages);
+  k.val(threads);
+  k.val(workgroups);
+  return run_cached(k, [&](Launch* L) {
+    return build_stream_ewise(op, out, x, row_a, row_b, stage_box, stages, threads, workgroups, L);
+  }, hip_stream);
 }
 
 acp_status acp_tile_reduce(acp_op op, const acp_tile_desc* dst, const acp_tile_desc* src, int threads,
                            void* hip_stream) {
-  acp::DescData s, d;
-  if (!load_desc(src, &s) || !load_desc(dst, &d)) return ret(ACP_ERR_INVALID, "not an encoded descriptor");
-  if (op != ACP_OP_ADD) return ret(ACP_ERR_INVALID, "the store reduces with add");
-  if (s.dtype != d.dtype) return ret(ACP_ERR_INVALID, "source and destination dtypes differ");
-  if (s.dtype != ACP_U32 && s.dtype != ACP_F32 && s.dtype != ACP_F16)
-    return ret(ACP_ERR_UNSUPPORTED, "reduce-add takes u32, f32 or f16");
-  if (s.rank != d.rank) return ret(ACP_ERR_INVALID, "source and destination ranks differ");
-  for (int k = 0; k < s.rank; ++k) {
-    if (s.box[k] != d.box[k]) return ret(ACP_ERR_INVALID, "source and destination boxes differ");
-    if (d.shape[k] == s.shape[k]) continue;
-    if (d.shape[k] != 1 || s.box[k] != 1)
-      return ret(ACP_ERR_INVALID, "a destination extent must equal the source's, or be 1 where the box is 1");
-  }
-  if (overlap(s, d)) return ret(ACP_ERR_INVALID, "source and destination share memory");
-  bool one_each = true;  // every destination element receives one contribution
-  for (int k = 0; k < s.rank; ++k) one_each = one_each && d.shape[k] == s.shape[k] && d.strides[k] == s.strides[k];
-  if (one_each && s.dtype != ACP_U32) {
-    // No two source elements meet in one destination element: dst' = src + dst
-    // needs no atomics.  Both tensors ride the ring and the sum is stored in
-    // place; every element is staged before the same lane stores it, and no
-    // other trip touches it.
-    EngineRequest q{};
-    q.op = ACP_OP_ADD;
-    q.mode = 2;
-    q.x = &s;
-    q.out = &d;
-    q.in_ptrs[0] = reinterpret_cast<const void*>(s.gbase);
-    q.in_ptrs[1] = reinterpret_cast<const void*>(d.gbase);
-    q.n_in = 2;
-    q.stage_box = s.box;
-    q.threads = threads;
-    q.copy_only = false;
-    q.binary = 1;
-    int tpt = 1;
-    acp::Plan p;
-    std::string why;
-    if (acp::plan_box(s, false, &p, &why) == acp::PlanStatus::Ok)
-      tile_schedule(p, 2, threads, 0, &q.workgroups, &q.stages, &tpt);
-    q.stages = q.workgroups > 0 ? q.stages : 2;
-    Launch L;
-    const acp_status st = prepare(q, &L);
-    if (st == ACP_OK && L.key.variant == 1) return launch(L, hip_stream);
-    if (st != ACP_OK && st != ACP_ERR_UNSUPPORTED) return st;
-    // otherwise: the atomic path below
-  }
-  EngineRequest q{};
-  q.op = ACP_OP_ADD;
-  q.mode = 3;
-  q.x = &s;
-  q.out = &d;
-  q.in_ptrs[0] = reinterpret_cast<const void*>(s.gbase);
-  q.n_in = 1;
-  q.stage_box = s.box;
-  q.threads = threads;
-  q.copy_only = false;
-  {
-    acp::Plan p;
-    std::string why;
-    if (acp::plan_box(s, false, &p, &why) == acp::PlanStatus::Ok) {
-      tile_schedule(p, 1, threads, 0, &q.workgroups, &q.stages, &q.tiles_per_trip);
-      // Sums over batch dims: each workgroup owns whole destination tiles,
-      // sums their contributions in registers and adds once per element.
-      int64_t group = 1;
-      for (int k = 0; k < s.rank; ++k)
-        if (d.shape[k] == 1 && s.shape[k] > 1) group *= s.shape[k];
-      static const bool grouped_ok = env_flag("ACP_REDUCE_GROUPED", true);
-      const int64_t n_tiles = p.n_tiles();
-      if (grouped_ok && group > 1 && n_tiles > 0) {
-        const int64_t dst_tiles = n_tiles / group;
-        static const int env_wg_per_cu = [] {
-          const char* e = std::getenv("ACP_REDUCE_WG_PER_CU");
-          return (e && std::atoi(e) > 0) ? std::atoi(e) : 0;
-        }();
-        static const int env_slots = [] {
-          const char* e = std::getenv("ACP_REDUCE_STAGES");
-          return (e && std::atoi(e) >= 2 && std::atoi(e) <= 4) ? std::atoi(e) : 3;
-        }();
-        const int64_t per_cu = env_wg_per_cu ? env_wg_per_cu : std::max<int64_t>(1, 16384 / p.tile_bytes());
-        const int64_t want = static_cast<int64_t>(device_cu_count()) * per_cu;
-        // About 16 KiB of tiles per CU in flight per ring step and 3 ring
-        // slots (ACP_REDUCE_WG_PER_CU, ACP_REDUCE_STAGES): the best of 2-8
-        // workgroups per CU x 2-4 slots x 4 or 8 KiB tiles measured on 128
-        // float32 contributions per element of [500,1024] (8 KiB tiles, two
-        // per CU: 4.8 TB/s).  Few destination tiles: split each one's
-        // contributions over k workgroups (k atomic adds per element instead
-        // of one).
-        int64_t k = 1;
-        while (dst_tiles * k * 2 <= want && group % (k * 2) == 0) k *= 2;
-        const int64_t sub = group / k;                 // contributions summed per workgroup group
-        const int64_t groups = dst_tiles * k;
-        const int64_t g = std::min<int64_t>(groups, want);
-        const int64_t per = (groups + g - 1) / g;      // groups per workgroup
-        q.red_group = sub;
-        q.red_per_wg = per * sub;
-        q.workgroups = static_cast<int>((groups + per - 1) / per);
-        q.stages = env_slots;
-        q.tiles_per_trip = 1;
-      }
-    } else {
-      q.stages = 1;
-    }
-  }
-  Launch L;
-  const acp_status st = prepare(q, &L);
-  if (st != ACP_OK) return st;
-  if (L.key.mode != 7) return ret(ACP_ERR_UNSUPPORTED, "reduce-add needs 16-byte rounds and 1, 2, 4 or 8 rounds per thread");
-  return launch(L, hip_stream);
+  CallKey k(4);
+  k.val(op);
+  k.desc(dst);
+  k.desc(src);
+  k.val(threads);
+  return run_cached(k, [&](Launch* L) { return build_tile_reduce(op, dst, src, threads, L); }, hip_stream);
 }
 
 acp_status acp_stream_reduce_rows(acp_op op, float* out, const acp_tile_desc* x, const int32_t* stage_box, int stages,
                                   int threads, int workgroups, void* hip_stream) {
-  acp::DescData xd;
-  if (!load_desc(x, &xd)) return ret(ACP_ERR_INVALID, "not an encoded descriptor");
-  if (op != ACP_OP_ADD) return ret(ACP_ERR_INVALID, "rows reduce with add");
-  if (!out) return ret(ACP_ERR_INVALID, "null output");
-  if (!stage_box) return ret(ACP_ERR_INVALID, "null stage box");
-  if (stages < 2 || stages > 4) return ret(ACP_ERR_INVALID, "stages must be 2, 3 or 4");
-  if (workgroups < 0) return ret(ACP_ERR_INVALID, "workgroups must be >= 0");
-  if (xd.dtype != ACP_F32 && xd.dtype != ACP_F16) return ret(ACP_ERR_UNSUPPORTED, "row reduction takes f16 or f32");
-  const int r = xd.rank;
-  if (r < 2) return ret(ACP_ERR_INVALID, "row reduction needs rank >= 2");
-  for (int d = 0; d < r; ++d)
-    if (stage_box[d] < 1) return ret(ACP_ERR_INVALID, "stage box must be >= 1");
-  if (xd.box[r - 1] != xd.shape[r - 1] || stage_box[r - 1] != xd.shape[r - 1])
-    return ret(ACP_ERR_INVALID, "tiles and stages must hold whole rows (innermost box = innermost extent)");
-  int64_t rows = 1;
-  for (int d = 0; d + 1 < r; ++d) rows *= xd.shape[d];
-  if (rows >= (int64_t(1) << 29)) return ret(ACP_ERR_UNSUPPORTED, "too many rows");
-  if (reinterpret_cast<uint64_t>(out) % 4) return ret(ACP_ERR_INVALID, "output not 4-byte aligned");
-  if (overlap(reinterpret_cast<uint64_t>(out), static_cast<uint64_t>(rows) * 4, xd.gbase, tensor_span(xd)))
-    return ret(ACP_ERR_INVALID, "the output shares memory with x");
-  EngineRequest q{};
-  q.op = ACP_OP_ADD;
-  q.mode = 4;
-  q.x = &xd;
-  q.out = &xd;  // same shape; the output is the packed row array `out`
-  q.in_ptrs[0] = reinterpret_cast<const void*>(xd.gbase);
-  q.n_in = 1;
-  q.stage_box = stage_box;
-  q.stages = stages;
-  q.threads = threads;
-  q.workgroups = workgroups;
-  q.copy_only = false;
-  Launch L;
-  const acp_status st = prepare(q, &L);
-  if (st != ACP_OK) return st;
-  if (L.key.mode != 8 && L.key.mode != 10)
-    return ret(ACP_ERR_UNSUPPORTED, "row reduction needs 16-byte rounds and 1, 2, 4 or 8 rounds per thread");
-  if (L.args.red_rows > 64u * static_cast<uint32_t>(L.args.waves))
-    return ret(ACP_ERR_UNSUPPORTED, "row reduction stages hold at most 64 rows per wave");
-  L.args.out = reinterpret_cast<char*>(out);
-  L.args.out_span = static_cast<uint64_t>(rows) * 4u;
-  return launch(L, hip_stream);
+  CallKey k(5);
+  k.val(op);
+  k.val(out);
+  k.desc(x);
+  k.ints(stage_box, desc_rank(x));
+  k.val(stages);
+  k.val(threads);
+  k.val(workgroups);
+  return run_cached(k, [&](Launch* L) {
+    return build_stream_reduce_rows(op, out, x, stage_box, stages, threads, workgroups, L);
+  }, hip_stream);
 }
 
 acp_status acp_stream_binary(acp_op op, const acp_tile_desc* out, const acp_tile_desc* x, const acp_tile_desc* z,
                              const int32_t* stage_box, int stages, int threads, int workgroups, acp_staging z_staging,
                              void* hip_stream) {
-  acp::DescData xd, zd, od;
-  if (!load_desc(x, &xd) || !load_desc(z, &zd) || !load_desc(out, &od))
-    return ret(ACP_ERR_INVALID, "not an encoded descriptor");
-  if (op != ACP_OP_ADD && op != ACP_OP_MUL) return ret(ACP_ERR_INVALID, "two-tensor streams are add or mul");
-  if (z_staging != ACP_STAGE_RING && z_staging != ACP_STAGE_SET) return ret(ACP_ERR_INVALID, "unknown staging");
-  if (!stage_box) return ret(ACP_ERR_INVALID, "null stage box");
-  if (stages < 2 || stages > 4) return ret(ACP_ERR_INVALID, "stages must be 2, 3 or 4");
-  if (workgroups < 0) return ret(ACP_ERR_INVALID, "workgroups must be >= 0");
-  if (!same_geometry(zd, xd, true) || zd.dtype != xd.dtype || zd.swizzle != xd.swizzle)
-    return ret(ACP_ERR_INVALID, "x and z must share one layout (dtype, shape, strides, box, swizzle)");
-  if (!same_geometry(xd, od, false) || od.dtype != xd.dtype)
-    return ret(ACP_ERR_INVALID, "output dtype, shape or box differs from x");
-  if (!is_float(xd.dtype)) return ret(ACP_ERR_UNSUPPORTED, "two-tensor streams take float16 or float32");
-  if (overlap(xd, od) || overlap(zd, od)) return ret(ACP_ERR_INVALID, "the output shares memory with x or z");
-  for (int d = 0; d < xd.rank; ++d)
-    if (stage_box[d] < 1) return ret(ACP_ERR_INVALID, "stage box must be >= 1");
-  EngineRequest q{};
-  q.op = op;
-  q.mode = 2;
-  q.x = &xd;
-  q.out = &od;
-  q.in_ptrs[0] = reinterpret_cast<const void*>(xd.gbase);
-  q.in_ptrs[1] = reinterpret_cast<const void*>(zd.gbase);
-  q.n_in = 2;
-  q.stage_box = stage_box;
-  q.stages = stages;
-  q.threads = threads;
-  q.workgroups = workgroups;
-  q.copy_only = false;
-  q.binary = z_staging == ACP_STAGE_SET ? 2 : 1;
-  Launch L;
-  const acp_status st = prepare(q, &L);
-  if (st != ACP_OK) return st;
-  return launch(L, hip_stream);
+  CallKey k(6);
+  k.val(op);
+  k.desc(out);
+  k.desc(x);
+  k.desc(z);
+  k.ints(stage_box, desc_rank(x));
+  k.val(stages);
+  k.val(threads);
+  k.val(workgroups);
+  k.val(z_staging);
+  return run_cached(k, [&](Launch* L) {
+    return build_stream_binary(op, out, x, z, stage_box, stages, threads, workgroups, z_staging, L);
+  }, hip_stream);
 }
 
 acp_status acp_debug_lds_image(const acp_tile_desc* src, int64_t tile_index, int threads, void* out_bytes,

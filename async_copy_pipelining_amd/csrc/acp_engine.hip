@@ -1,5 +1,7 @@
 // Kernel registry, launch helpers, the two debug kernels of the engine and the
 // register-path reference copy.
+#include <unordered_map>
+
 #include "acp_engine_impl.hpp"
 
 namespace acp {
@@ -103,9 +105,25 @@ const void* engine_kernel(const KernelKey& k) {
   return lookup_stream_f16(k);
 }
 
+// Raise a kernel's dynamic-LDS limit only when a launch needs more than any
+// earlier one on this device (per thread: the attribute is process state, so
+// a second thread setting it again is harmless).
+hipError_t ensure_lds_limit(const void* kernel, unsigned lds_bytes) {
+  thread_local std::unordered_map<uint64_t, unsigned> done;  // (kernel, device) -> limit set
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const uint64_t key = (static_cast<uint64_t>(reinterpret_cast<uintptr_t>(kernel)) << 8) ^ static_cast<uint64_t>(dev);
+  const auto it = done.find(key);
+  if (it != done.end() && it->second >= lds_bytes) return hipSuccess;
+  const hipError_t err =
+      hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_bytes));
+  if (err == hipSuccess) done[key] = lds_bytes;
+  return err;
+}
+
 hipError_t engine_launch(const void* kernel, const EngineArgs& args, unsigned grid, unsigned block,
                          unsigned lds_bytes, hipStream_t stream) {
-  hipError_t err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_bytes));
+  const hipError_t err = ensure_lds_limit(kernel, lds_bytes);
   if (err != hipSuccess) return err;
   void* params[] = {const_cast<EngineArgs*>(&args)};
   return hipLaunchKernel(kernel, dim3(grid), dim3(block), params, lds_bytes, stream);
@@ -118,7 +136,7 @@ const void* lds_image_kernel(int vec_bytes) {
 
 hipError_t lds_image_launch(const void* kernel, const EngineArgs& args, unsigned block, unsigned lds_bytes,
                             void* out_bytes, uint32_t image_bytes, hipStream_t stream) {
-  hipError_t err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_bytes));
+  const hipError_t err = ensure_lds_limit(kernel, lds_bytes);
   if (err != hipSuccess) return err;
   unsigned char* out = static_cast<unsigned char*>(out_bytes);
   void* params[] = {const_cast<EngineArgs*>(&args), &out, &image_bytes};

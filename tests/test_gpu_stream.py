@@ -97,25 +97,32 @@ def test_many_rows_per_stage_and_two_scalar_loads():
     assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
 
 
+_C4_REF = {}
+
+
+def _c4_reference(x, a, b):
+    """The oracle's streamed fma over the whole [128, 500, 1024] tensor,
+    computed once per module (about a second and a half on one core)."""
+    if "y" not in _C4_REF:
+        _C4_REF["y"] = REF.stream_ewise("fma", x, a, b, np.float32).view(np.uint32)
+    return _C4_REF["y"]
+
+
 @pytest.mark.parametrize("stage_box,stages,threads,workgroups,rounds", [
     ((1, 2, 1024), 4, 256, 256, 2),   # the bench's launch
     ((1, 2, 1024), 3, 256, 256, 2),   # its 3- and 2-stage rings (bench "ring_stages")
     ((1, 2, 1024), 2, 256, 256, 2),
     ((1, 1, 1024), 4, 128, 256, 2),
     ((1, 4, 1024), 4, 256, 512, 4),
+    ((1, 4, 1024), 2, 256, 256, 4),
 ])
-def test_c4_full_size_bench_config_sampled(stage_box, stages, threads, workgroups, rounds):
+def test_c4_full_size_bench_config(stage_box, stages, threads, workgroups, rounds):
+    # every element of the full-size streamed fma against the oracle, bit for bit
     shape = (128, 500, 1024)
     say(f"C4 full fma [128,500,1024] stage {stage_box} S={stages} {threads} threads, {workgroups} workgroups")
     x, a, b, y = _fma_case(shape, stage_box, stage_box, stages, threads, workgroups)
     assert acp.acp_last_kernel().startswith(f"stream linear grid vec 16 rounds {rounds} srow 1")
-    rng = np.random.default_rng(44)
-    i0 = rng.integers(0, 128, 3000)
-    i1 = rng.integers(0, 500, 3000)
-    ref = REF.stream_ewise("fma", x[i0, i1][:, None, :], a[i0, i1][:, None], b[i0, i1][:, None], np.float32)[:, 0]
-    assert np.array_equal(y[i0, i1].view(np.uint32), ref.view(np.uint32))
-    # every row was written (the buffer started as 0xA5A5A5A5 = -2.9e-16)
-    assert not np.any(y.view(np.uint32) == 0xA5A5A5A5)
+    assert np.array_equal(y.view(np.uint32), _c4_reference(x, a, b))
 
 
 @pytest.mark.parametrize("stages", [2, 3, 4])
@@ -290,16 +297,13 @@ def test_two_tensor_stream_matches_oracle(staging, op, dt, shape, box, stage_box
 
 
 @pytest.mark.parametrize("staging", ["ring", "set"])
-def test_two_tensor_stream_full_size_sampled(staging):
+def test_two_tensor_stream_full_size(staging):
     shape, stage_box = (128, 500, 1024), (1, 2, 1024)
     say(f"two-tensor stream add {shape} stage {stage_box} S=4, 256 workgroups, z={staging}")
     x, z, y = _binary_case("add", "f32", shape, stage_box, stage_box, 4, 256, 256, staging, seed=42)
     assert acp.acp_last_kernel().startswith("stream linear grid" if staging == "ring" else "general stream")
-    rng = np.random.default_rng(43)
-    i0, i1 = rng.integers(0, 128, 2000), rng.integers(0, 500, 2000)
-    ref = REF.ewise("add", [x[i0, i1], z[i0, i1]], np.float32)
-    assert np.array_equal(y[i0, i1].view(np.uint32), ref.view(np.uint32))
-    assert not np.any(y.view(np.uint32) == 0xA5A5A5A5)
+    ref = REF.ewise("add", [x, z], np.float32)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
 
 
 @pytest.mark.parametrize("stages", [2, 3, 4])
@@ -418,3 +422,26 @@ def test_row_reduction_full_size(stage_box, stages, threads, workgroups, kind):
     kernel = acp.acp_last_kernel()
     assert kernel.startswith(kind[0]) and kernel.endswith(kind[1]), kernel
     _assert_within_sum_bound(x, y)
+
+
+def test_repeated_calls_reuse_or_rebuild_their_launch():
+    # The library keeps each call's prepared launch, keyed by its arguments:
+    # alternating slot counts, thread counts and output buffers (more distinct
+    # calls than the per-thread table holds) must each run their own launch.
+    shape, stage = (2, 64, 1024), (1, 2, 1024)
+    say(f"repeated fma calls {shape} with changing arguments")
+    x, a, b = W.fma_rows_f32(shape, seed=21)
+    xd, ad, bd = dev(x), dev(a), dev(b)
+    st = packed_strides(shape)
+    xdesc = encode("f32", xd, shape, st, stage)
+    outs = [empty_bytes(x.nbytes) for _ in range(3)]
+    ydescs = [encode("f32", o, shape, st, stage) for o in outs]
+    ref = REF.stream_ewise("fma", x, a, b, np.float32).view(np.uint32)
+    combos = [(s, t, w, k) for s in (2, 3, 4) for t in (128, 256) for w in (4, 8, 16) for k in range(3)]
+    for rep in range(2):
+        for stages, threads, wgs, k in combos:
+            outs[k].fill_(0xA5)
+            acp.acp_stream_ewise("fma", ydescs[k], xdesc, ad, bd, stage, stages, threads, wgs, stream())
+            kern = acp.acp_last_kernel()
+            assert f" grid {wgs} threads {threads} slots {stages} " in kern, kern
+            assert np.array_equal(host(outs[k], np.uint32, shape), ref), (rep, stages, threads, wgs, k)
