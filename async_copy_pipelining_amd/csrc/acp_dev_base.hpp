@@ -224,53 +224,67 @@ __device__ __forceinline__ void run_ring(P& p, int n, int s, int d, int st) {
   }
 }
 
-// Steady state of the ring with a compile-time wait count K.
-template <int K, class P>
-__device__ __forceinline__ void ring_steady(P& p, int& i, int nmain, int s, int& cur, int& ld) {
+// The ring for per-trip counts D and ST and a slot count S known at compile
+// time: every wait is an immediate.  Trip i's allowed count is
+// ahead * D + behind * ST (see `allowed`).  In the warm-up (the first S-1
+// main-loop trips) ahead is S-1 and behind is i; in the steady state both
+// are S-1; in the epilogue ahead is the number of trips left after i (S-2
+// down to 0) and behind is S-1 once i >= S-1.  A trip of a very short ring
+// (i < S-1 in the epilogue) waits as if no store had been issued since its
+// load: a smaller count, hence a stronger wait, and still exact for pre_wait.
+template <int D, int ST, int S, class P>
+__device__ __forceinline__ void run_ring_s(P& p, int n) {
+  static_assert(S >= 1 && S <= 4, "slot count");
+  const int nmain = n - (S - 1) > 0 ? n - (S - 1) : 0;
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j)
+    if (j < n) p.load(j, j);
+  int i = 0;
+  // warm-up: load trip i + S - 1 into slot i + S - 1 (mod S), consume slot i
+  const int warm = nmain < S - 1 ? nmain : S - 1;
+  for (; i < warm; ++i) {
+    p.load(i + S - 1, (i + S - 1) % S);
+    p.pre_wait(i, i, allowed(i, n, S, D, ST));
+    if (i == 0) wait_vmcnt_c<(S - 1) * D>();
+    else if (i == 1) wait_vmcnt_c<(S - 1) * D + ST>();
+    else wait_vmcnt_c<(S - 1) * D + 2 * ST>();
+    p.consume(i, i);
+  }
+  int cur = warm % S, ld = (warm + S - 1) % S;
   for (; i < nmain; ++i) {
-    p.load(i + s - 1, ld);
-    p.pre_wait(i, cur, K);
-    wait_vmcnt_c<K>();
+    p.load(i + S - 1, ld);
+    p.pre_wait(i, cur, (S - 1) * (D + ST));
+    wait_vmcnt_c<(S - 1) * (D + ST)>();
     p.consume(i, cur);
-    cur = (cur + 1 == s) ? 0 : cur + 1;
-    ld = (ld + 1 == s) ? 0 : ld + 1;
+    cur = (cur + 1 == S) ? 0 : cur + 1;
+    ld = (ld + 1 == S) ? 0 : ld + 1;
+  }
+  // epilogue: no loads; `left` trips follow trip i
+  for (; i < n; ++i) {
+    const int left = n - 1 - i;
+    p.pre_wait(i, cur, allowed(i, n, S, D, ST));
+    if (i >= S - 1) {
+      if (left == 0) wait_vmcnt_c<(S - 1) * ST>();
+      else if (left == 1) wait_vmcnt_c<D + (S - 1) * ST>();
+      else wait_vmcnt_c<2 * D + (S - 1) * ST>();
+    } else {
+      if (left == 0) wait_vmcnt_c<0>();
+      else if (left == 1) wait_vmcnt_c<D>();
+      else wait_vmcnt_c<2 * D>();
+    }
+    p.consume(i, cur);
+    cur = (cur + 1 == S) ? 0 : cur + 1;
   }
 }
 
-// The same ring for per-trip counts D and ST known at compile time.  Past
-// the first S-1 trips of the main loop the allowed count is the constant
-// (S-1)(D+ST), so each slot count (2, 3 or 4) gets a steady-state loop with
-// its wait fixed at compile time (with one slot, or any other count, the
-// steady state waits for everything: exact for S = 1, stronger otherwise);
-// the first trips and the epilogue take the general wait.
+// The same ring for per-trip counts D and ST known at compile time and a
+// slot count s (1..4) chosen at launch: one compile-time ring per slot count.
 template <int D, int ST, class P>
 __device__ __forceinline__ void run_ring_fixed(P& p, int n, int s) {
-  const int pro = n < s - 1 ? n : s - 1;
-  for (int j = 0; j < pro; ++j) p.load(j, j);
-  const int nmain = n - (s - 1) > 0 ? n - (s - 1) : 0;
-  const int warm = nmain < s - 1 ? nmain : s - 1;
-  int cur = 0, ld = s - 1;
-  int i = 0;
-  for (; i < warm; ++i) {
-    p.load(i + s - 1, ld);
-    const int k = allowed(i, n, s, D, ST);
-    p.pre_wait(i, cur, k);
-    wait_vmcnt(k);
-    p.consume(i, cur);
-    cur = (cur + 1 == s) ? 0 : cur + 1;
-    ld = (ld + 1 == s) ? 0 : ld + 1;
-  }
-  if (s == 4) ring_steady<3 * (D + ST)>(p, i, nmain, s, cur, ld);
-  else if (s == 3) ring_steady<2 * (D + ST)>(p, i, nmain, s, cur, ld);
-  else if (s == 2) ring_steady<D + ST>(p, i, nmain, s, cur, ld);
-  else ring_steady<0>(p, i, nmain, s, cur, ld);
-  for (; i < n; ++i) {
-    const int k = allowed(i, n, s, D, ST);
-    p.pre_wait(i, cur, k);
-    wait_vmcnt(k);
-    p.consume(i, cur);
-    cur = (cur + 1 == s) ? 0 : cur + 1;
-  }
+  if (s == 4) run_ring_s<D, ST, 4>(p, n);
+  else if (s == 3) run_ring_s<D, ST, 3>(p, n);
+  else if (s == 2) run_ring_s<D, ST, 2>(p, n);
+  else run_ring_s<D, ST, 1>(p, n);
 }
 
 }  // namespace dev

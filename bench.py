@@ -86,7 +86,7 @@ def parse():
                          "reduce --reduce-over-batch 2)")
     ap.add_argument("--threads", type=int, default=256, help="threads per workgroup")
     ap.add_argument("--workgroups", type=int, default=None,
-                    help="persistent workgroups (default 256 x --wg-per-cu)")
+                    help="persistent workgroups (default 256 x --wg-per-cu; 0: one workgroup per tile)")
     ap.add_argument("--wg-per-cu", type=int, default=1)
     ap.add_argument("--sets", type=int, default=3, help="rotated buffer sets")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
@@ -99,8 +99,6 @@ def parse():
         args.rows = {"c4": 2, "pointwise": 4, "rowsum": 4}.get(wl, 2 if args.reduce_over_batch else 4)
     if args.stages is None:
         args.stages = 2 if wl in ("pointwise", "rowsum") else 4
-    if args.workgroups is None:
-        args.workgroups = 0
     return args
 
 
@@ -137,7 +135,7 @@ def main():
         shape = (128, 500, 1024)
         stage = (1, args.rows, 1024)
         x, a, b = W.fma_rows_f32(shape, seed=4)
-        G = args.workgroups or 256 * args.wg_per_cu
+        G = 256 * args.wg_per_cu if args.workgroups is None else args.workgroups
         descs, keep = [], []
         for s in range(args.sets):
             xd, ad, bd = to_dev(x), to_dev(a), to_dev(b)
@@ -208,7 +206,7 @@ def main():
         rng = np.random.default_rng(6)
         x = rng.standard_normal(shape, dtype=np.float32)
         z = rng.standard_normal(shape, dtype=np.float32)
-        G = args.workgroups or 256 * args.wg_per_cu
+        G = 256 * args.wg_per_cu if args.workgroups is None else args.workgroups
         for s in range(args.sets):
             xd, zd = to_dev(x), to_dev(z)
             yd = torch.empty(x.nbytes, dtype=torch.uint8, device=dev)
@@ -249,7 +247,7 @@ def main():
         stage = (1, args.rows, 1024)
         rng = np.random.default_rng(8)
         x = rng.standard_normal(shape, dtype=np.float32)
-        G = args.workgroups or 256 * args.wg_per_cu
+        G = 256 * args.wg_per_cu if args.workgroups is None else args.workgroups
         for s in range(args.sets):
             xd = to_dev(x)
             yd = torch.empty(128 * 500 * 4, dtype=torch.uint8, device=dev)
@@ -263,7 +261,7 @@ def main():
         key = f"stream_rowsum_f32_128x500x1024_s{args.stages}_r{args.rows}"
     elif wl == "copy_ref":
         n = 128 * 500 * 1024 * 4
-        G = args.workgroups or 256 * args.wg_per_cu
+        G = 256 * args.wg_per_cu if args.workgroups is None else args.workgroups
         for s in range(args.sets):
             xd = torch.ones(n, dtype=torch.uint8, device=dev)
             yd = torch.empty(n, dtype=torch.uint8, device=dev)

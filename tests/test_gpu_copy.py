@@ -149,6 +149,29 @@ def test_swizzle_shrunk_inner_box(mode, dt, shape, box, threads):
         assert _lds_image(src, t, threads, p.tile_bytes) == T.lds_image(elems, p, t)
 
 
+@pytest.mark.parametrize("shape,box,threads", [
+    ((40, 130, 96), (1, 64, 32), 128),       # three tiles per row: the second pair holds one tile
+    ((6, 300, 1000), (1, 128, 32), 128),     # 1000 = 31 * 32 + 8: the last tile of a row is cut
+    ((8, 64, 256), (1, 16, 16), 64),         # 32-byte rows: four tiles per trip
+])
+def test_paired_tiles_per_trip(shape, box, threads):
+    # a persistent copy of tiles narrower than a cache line stages
+    # neighbouring tiles side by side in one trip; the output is the input,
+    # and the padding of a strided destination is never written
+    say(f"paired-tile copy {shape} box {box} threads {threads}")
+    x = W.normal_f16(shape, seed=9)
+    xd = dev(x)
+    pitch = shape[-1] + 24
+    ost = (shape[1] * pitch, pitch, 1)
+    yd = empty_bytes(shape[0] * shape[1] * pitch * 2, 0x00)
+    src = encode("f16", xd, shape, packed_strides(shape), box)
+    dst = encode("f16", yd, shape, ost, box)
+    acp.acp_tile_copy(src, dst, threads, stream())
+    y = host(yd, np.uint16).reshape(shape[0], shape[1], pitch)
+    assert np.array_equal(y[:, :, :shape[-1]], x.view(np.uint16))
+    assert not np.any(y[:, :, shape[-1]:])
+
+
 @pytest.mark.parametrize("misalign", [4, 8])
 def test_four_byte_path_when_only_4_or_8_aligned(misalign):
     shape, box = (64, 256), (64, 32)
