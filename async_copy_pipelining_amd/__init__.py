@@ -92,6 +92,8 @@ _SIGS = {
     "acp_debug_lds_image": ([_DESC_P, ctypes.c_int64, _I, _P, _P], _I),
     "acp_debug_ring_trace": ([_I, _I, _I, _I, _P, _P], _I),
     "acp_debug_stream_copy": ([_P, _P, ctypes.c_int64, _I, _P], _I),
+    "acp_debug_stream_read": ([_P, ctypes.c_int64, _P, _I, _P], _I),
+    "acp_debug_stream_fill": ([_P, ctypes.c_int64, ctypes.c_uint32, _I, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -212,3 +214,12 @@ def acp_debug_ring_trace(n_iters: int, stages: int, loads: int, stores: int, out
 
 def acp_debug_stream_copy(dst, src, nbytes: int, workgroups: int = 0, stream=None) -> None:
     _check(_lib.acp_debug_stream_copy(_ptr(dst), _ptr(src), int(nbytes), int(workgroups), _stream(stream)))
+
+
+def acp_debug_stream_read(src, nbytes: int, sums, workgroups: int = 0, stream=None) -> None:
+    _check(_lib.acp_debug_stream_read(_ptr(src), int(nbytes), _ptr(sums), int(workgroups), _stream(stream)))
+
+
+def acp_debug_stream_fill(dst, nbytes: int, pattern: int, workgroups: int = 0, stream=None) -> None:
+    _check(_lib.acp_debug_stream_fill(_ptr(dst), int(nbytes), int(pattern) & 0xFFFFFFFF, int(workgroups),
+                                      _stream(stream)))

@@ -1317,4 +1317,38 @@ acp_status acp_debug_stream_copy(void* dst, const void* src, int64_t bytes, int 
   return ret(ACP_OK);
 }
 
+// grid of a reference stream: `workgroups` (0: one per compute unit), at
+// most one per 16 KiB block
+unsigned ref_grid(int64_t bytes, int workgroups) {
+  const int64_t blocks = (bytes + 16383) / 16384;
+  int64_t grid = workgroups > 0 ? workgroups : device_cu_count();
+  return static_cast<unsigned>(grid > blocks ? blocks : grid);
+}
+
+acp_status acp_debug_stream_read(const void* src, int64_t bytes, void* sums, int workgroups, void* hip_stream) {
+  if (!src || !sums || bytes < 0 || workgroups < 0) return ret(ACP_ERR_INVALID, "bad stream read arguments");
+  if (bytes % 16 != 0) return ret(ACP_ERR_INVALID, "stream read moves whole 16-byte units");
+  if (bytes >= (int64_t(1) << 40)) return ret(ACP_ERR_INVALID, "stream read size out of range");
+  if (bytes == 0) return ret(ACP_OK);
+  const unsigned grid = ref_grid(bytes, workgroups);
+  const char* s = static_cast<const char*>(src);
+  const char* o = static_cast<const char*>(sums);
+  if (o < s + bytes && s < o + 16 * static_cast<int64_t>(grid)) return ret(ACP_ERR_INVALID, "sums overlap the source");
+  const hipError_t e = acp::stream_read_launch(src, static_cast<uint64_t>(bytes), sums, grid,
+                                               static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ret(ACP_OK);
+}
+
+acp_status acp_debug_stream_fill(void* dst, int64_t bytes, uint32_t pattern, int workgroups, void* hip_stream) {
+  if (!dst || bytes < 0 || workgroups < 0) return ret(ACP_ERR_INVALID, "bad stream fill arguments");
+  if (bytes % 16 != 0) return ret(ACP_ERR_INVALID, "stream fill writes whole 16-byte units");
+  if (bytes >= (int64_t(1) << 40)) return ret(ACP_ERR_INVALID, "stream fill size out of range");
+  if (bytes == 0) return ret(ACP_OK);
+  const hipError_t e = acp::stream_fill_launch(dst, static_cast<uint64_t>(bytes), pattern, ref_grid(bytes, workgroups),
+                                               static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ret(ACP_OK);
+}
+
 }  // extern "C"

@@ -88,7 +88,61 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(const char* src, char*
   }
 }
 
+// Measurement references for one direction at a time, with the copy's walk
+// (16 KiB blocks w, w+G, ..., four non-temporal 16-byte accesses per lane):
+// a read-only stream whose lanes fold what they read into one 16-byte XOR per
+// lane (the workgroup's XOR goes to sums[w], so no load can be dropped), and
+// a write-only stream of one 32-bit pattern.
+__global__ __launch_bounds__(256) void stream_read_kernel(const char* src, uint64_t bytes, u32x4* sums) {
+  __shared__ u32x4 part[256];
+  const uint64_t blocks = (bytes + 16383u) / 16384u;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (uint64_t b = blockIdx.x; b < blocks; b += gridDim.x) {
+    const uint64_t off = b * 16384u;
+    const uint64_t left = bytes - off;
+    const int range = static_cast<int>(left < 16384u ? left : 16384u);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src) + off, 0, range, 0x00020000);
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (u * 256 + threadIdx.x) * 16, 0, 2);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u];
+  }
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (unsigned h = 128; h > 0; h >>= 1) {
+    if (threadIdx.x < h) part[threadIdx.x] ^= part[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sums[blockIdx.x] = part[0];
+}
+
+__global__ __launch_bounds__(256) void stream_fill_kernel(char* dst, uint64_t bytes, uint32_t pattern) {
+  const uint64_t blocks = (bytes + 16383u) / 16384u;
+  const u32x4 v = {pattern, pattern, pattern, pattern};
+  for (uint64_t b = blockIdx.x; b < blocks; b += gridDim.x) {
+    const uint64_t off = b * 16384u;
+    const uint64_t left = bytes - off;
+    const int range = static_cast<int>(left < 16384u ? left : 16384u);
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(dst + off, 0, range, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) __builtin_amdgcn_raw_buffer_store_b128(v, ry, (u * 256 + threadIdx.x) * 16, 0, 2);
+  }
+}
+
 }  // namespace dev
+
+hipError_t stream_read_launch(const void* src, uint64_t bytes, void* sums, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL(dev::stream_read_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const char*>(src), bytes,
+                     static_cast<dev::u32x4*>(sums));
+  return hipGetLastError();
+}
+
+hipError_t stream_fill_launch(void* dst, uint64_t bytes, uint32_t pattern, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL(dev::stream_fill_kernel, dim3(grid), dim3(256), 0, stream, static_cast<char*>(dst), bytes,
+                     pattern);
+  return hipGetLastError();
+}
 
 hipError_t stream_copy_launch(const void* src, void* dst, uint64_t bytes, unsigned grid, hipStream_t stream) {
   hipLaunchKernelGGL(dev::stream_copy_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const char*>(src),

@@ -122,6 +122,8 @@ const void* lds_image_kernel(int vec_bytes);
 hipError_t lds_image_launch(const void* kernel, const EngineArgs& args, unsigned block, unsigned lds_bytes,
                             void* out_bytes, uint32_t image_bytes, hipStream_t stream);
 hipError_t stream_copy_launch(const void* src, void* dst, uint64_t bytes, unsigned grid, hipStream_t stream);
+hipError_t stream_read_launch(const void* src, uint64_t bytes, void* sums, unsigned grid, hipStream_t stream);
+hipError_t stream_fill_launch(void* dst, uint64_t bytes, uint32_t pattern, unsigned grid, hipStream_t stream);
 hipError_t ring_trace_launch(int n_iters, int stages, int loads, int stores, int32_t* out,
                              hipStream_t stream);
 

@@ -1,26 +1,34 @@
 #!/usr/bin/env python3
 """Throughput of the pipelined tile copy + elementwise path on one MI355X.
 
-Default workload: y = a[row] * x + b[row] over a [128, 500, 1024] float32
-tensor streamed through a 4-stage LDS ring (stage = two 1024-element rows,
-256 threads, one persistent workgroup per CU), the configuration the HBM-roofline target is
-quoted on.  One step = one launch of acp_stream_ewise over the whole tensor.
-The same line also reports the 2- and 3-stage rings ("ring_stages").  Inputs are seeded synthetic
-tensors resident in HBM; three buffer sets are rotated so that consecutive
-steps never hit data left in the 256 MB last-level cache by the previous one.
+Default run: y = a[row] * x + b[row] over a [128, 500, 1024] float32 tensor
+streamed through a 4-stage LDS ring (stage = two 1024-element rows, 256
+threads, one persistent workgroup per CU), the configuration the HBM-roofline
+target is quoted on.  One step = one launch of acp_stream_ewise over the whole
+tensor.  The same line reports the 2-, 3- and 4-stage rings ("ring_stages"),
+the other workloads ("configs": the swizzled 8x256 tile copy, the 32x32 tile
+sqrt, the 128x32 tile copy and the rank-5 exp stream, each with its roofline
+figures and its own CPU-oracle baseline) and the CPU oracle of the streamed
+fma.  Inputs are seeded synthetic tensors resident in HBM; three buffer sets
+are rotated so that consecutive steps never hit data left in the 256 MB
+last-level cache by the previous one.
 
-Prints ONE JSON line (rank 0) with the metric, the roofline of the kernel
-(its average launch duration from HIP events around the timed region, on the
-stream it runs on) and the CPU oracle timed on a bounded sample of the same
-workload.
+Prints ONE JSON line with the metric, the roofline of the kernel (its average
+launch duration from HIP events around the timed region, on the stream it
+runs on) and the CPU oracle timed on a bounded sample of the same workload.
 
-Other workloads (for measurement only): --workload c2 | c3 | c5.
+Other modes (measurement aids):
+  --workload NAME   one workload alone (c1 c2 c3 c5, the references copy_ref /
+                    read_ref / write_ref, calib, and pointwise / reduce / rowsum)
+  --fixed-cost      the streamed fma and the reference copy over 1..128 slabs of
+                    the tensor: per-launch fixed cost and per-byte rate of each
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -32,7 +40,8 @@ PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["acp_dev_base.hpp", "acp_dev_ops.hpp", "acp_dev_map.hpp", "acp_dev_engine.hpp", "acp_dev_lin.hpp",
                   "acp_dev_gen.hpp", "acp_engine_impl.hpp", "acp_engine.hpp", "acp_k_stream_f32.hip",
                   "acp_k_stream_f16.hip", "acp_k_tile.hip", "acp_k_tile_gen.hip", "acp_k_tile_lin.hip",
-                  "acp_k_copy.hip", "acp_api.cpp"]
+                  "acp_k_copy.hip", "acp_engine.hip", "acp_api.cpp"]
+SLAB = (500, 1024)                       # one [500, 1024] slab of the [128, 500, 1024] workloads
 
 
 def _code_only(text: str) -> str:
@@ -51,18 +60,24 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload_key: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when absent or taken on a different kernel source."""
+def _profile_field(workload_key: str, field: str):
+    """A number from the committed rocprofv3 summary of a workload, or None
+    when absent or taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", f"{workload_key}.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     m_hash = re.search(r"kernel_source_hash:\s*(\w+)", txt)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+    m_val = re.search(rf"{field}:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_hash():
         return None
-    return float(m_bytes.group(1))
+    return float(m_val.group(1))
+
+
+def traffic_from_profiles(workload_key: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) from the
+    committed summary of the workload."""
+    return _profile_field(workload_key, "hbm_bytes_per_launch")
 
 
 def parse():
@@ -70,11 +85,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "calib", "copy_ref", "pointwise", "reduce", "rowsum"],
-                    help="c4: the streamed fma (default); c2/c3/c5: the other workloads; "
-                         "calib: torch's copy of 256 MiB, the known-size kernel that scales HBM counters; "
-                         "copy_ref: the library's register-path reference copy of the c4 tensor "
-                         "(the plain 1:1 read/write ceiling)")
+    ap.add_argument("--workload", default=None,
+                    choices=["c1", "c2", "c3", "c4", "c5", "calib", "copy_ref", "read_ref", "write_ref", "pointwise",
+                             "reduce", "rowsum"],
+                    help="measure one workload alone (default: c4 with ring_stages and configs); calib: torch's "
+                         "copy of 256 MiB, the known-size kernel that scales HBM counters; copy_ref / read_ref / "
+                         "write_ref: the library's register-path reference streams over the c4 tensor")
     ap.add_argument("--stages", type=int, default=None,
                     help="ring slots (default: the measured best per workload; c4 and c5: 4)")
     ap.add_argument("--z-staging", default="ring", choices=["ring", "set"],
@@ -84,22 +100,298 @@ def parse():
     ap.add_argument("--rows", type=int, default=None,
                     help="rows per ring stage or tile (default per workload: c4 2, pointwise / reduce / rowsum 4, "
                          "reduce --reduce-over-batch 2)")
-    ap.add_argument("--threads", type=int, default=256, help="threads per workgroup")
+    ap.add_argument("--threads", type=int, default=None, help="threads per workgroup (default 256; c3 128; c1 64)")
     ap.add_argument("--workgroups", type=int, default=None,
-                    help="persistent workgroups (default 256 x --wg-per-cu; 0: one workgroup per tile)")
+                    help="persistent workgroups (default 256 x --wg-per-cu; 0: one workgroup per tile; c5 default 0)")
     ap.add_argument("--wg-per-cu", type=int, default=1)
+    ap.add_argument("--c5-stage", default="1,1,1,64,64", help="c5: the stage box (outermost first)")
     ap.add_argument("--sets", type=int, default=3, help="rotated buffer sets")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="budget of the streamed-fma oracle sample")
+    ap.add_argument("--config-cpu-seconds", type=float, default=2.0, help="budget of each config's oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-ring-sweep", action="store_true", help="c4: skip the 2/3-stage report (profiling runs)")
+    ap.add_argument("--no-ring-sweep", action="store_true", help="c4: skip the 2/3-stage report")
+    ap.add_argument("--no-configs", action="store_true", help="default run: skip the other workloads")
+    ap.add_argument("--fixed-cost", action="store_true",
+                    help="fit launch time = fixed + bytes / rate over 1..128 slabs (streamed fma, reference copy)")
     args = ap.parse_args()
-    # defaults: the best launch shapes measured on MI355X for each workload
-    wl = args.workload
-    if args.rows is None:
-        args.rows = {"c4": 2, "pointwise": 4, "rowsum": 4}.get(wl, 2 if args.reduce_over_batch else 4)
-    if args.stages is None:
-        args.stages = 2 if wl in ("pointwise", "rowsum") else 4
     return args
+
+
+def _packed(shape):
+    st, out = 1, []
+    for e in reversed(shape):
+        out.append(st)
+        st *= e
+    return tuple(reversed(out))
+
+
+class Ctx:
+    """Device plumbing shared by the workload builders."""
+
+    def __init__(self, args):
+        import numpy as np
+        import torch
+
+        import async_copy_pipelining_amd as acp
+        import workloads as W
+        self.np, self.torch, self.acp, self.W, self.args = np, torch, acp, W, args
+        self.dev = "cuda:0"
+        torch.cuda.set_device(0)
+        self.stream = torch.cuda.current_stream()
+
+    def to_dev(self, a):
+        np = self.np
+        return self.torch.from_numpy(np.ascontiguousarray(a).view(np.uint8).reshape(-1).copy()).to(self.dev)
+
+    def empty(self, nbytes):
+        return self.torch.empty(int(nbytes), dtype=self.torch.uint8, device=self.dev)
+
+
+def build(name, ctx, stages=None):
+    """Launch callables (one per buffer set) and the accounting of one
+    workload: algorithmic bytes per launch, the compute dtype, the config and
+    the key of its committed profile summary."""
+    args, acp, W, np, stream = ctx.args, ctx.acp, ctx.W, ctx.np, ctx.stream
+    sets = args.sets
+    launches, unit = [], "GB/s"
+    wpc = args.wg_per_cu
+    G = 256 * wpc if args.workgroups is None else args.workgroups
+    if name == "c4":
+        rows = args.rows or 2
+        S = stages or args.stages or 4
+        threads = args.threads or 256
+        shape, stage = (128, 500, 1024), (1, rows, 1024)
+        x, a, b = W.fma_rows_f32(shape, seed=4)
+        for _ in range(sets):
+            xd, ad, bd, yd = ctx.to_dev(x), ctx.to_dev(a), ctx.to_dev(b), ctx.empty(x.nbytes)
+            xdesc = acp.acp_encode_tiled("f32", xd, shape, _packed(shape), stage)
+            ydesc = acp.acp_encode_tiled("f32", yd, shape, _packed(shape), stage)
+            launches.append(lambda xdesc=xdesc, ydesc=ydesc, ad=ad, bd=bd, keep=(xd, yd):
+                            acp.acp_stream_ewise("fma", ydesc, xdesc, ad, bd, stage, launches_stages[0], threads, G,
+                                                 stream))
+        launches_stages = [S]
+        out = dict(bytes=x.nbytes * 2 + a.nbytes + b.nbytes, dtype="f32",
+                   config={"workload": f"stream fma y=a[row]*x+b[row], [128,500,1024] f32, {S}-stage LDS ring, "
+                                       f"stage (1,{rows},1024)", "shape": list(shape), "stages": S,
+                           "stage_box": list(stage), "threads": threads, "workgroups": G},
+                   key=f"stream_fma_f32_128x500x1024_s{S}_r{rows}")
+        out["set_stages"] = launches_stages      # the ring sweep changes the slot count in place
+    elif name == "c1":
+        # one 8x256 f16 tile through the 128-byte swizzled LDS image and back,
+        # 64 threads: latency-bound, so the figure that matters is the launch
+        # time in microseconds
+        threads = args.threads or 64
+        x = W.tile_bits_f16((8, 256), seed=1)
+        shape = x.shape
+        for _ in range(sets):
+            xd, yd = ctx.to_dev(x), ctx.empty(x.nbytes)
+            xdesc = acp.acp_encode_tiled("f16", xd, shape, _packed(shape), shape, acp.ACP_SWIZZLE_128B)
+            ydesc = acp.acp_encode_tiled("f16", yd, shape, _packed(shape), shape, acp.ACP_SWIZZLE_128B)
+            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
+                            acp.acp_tile_copy(xdesc, ydesc, threads, stream))
+        unit = "us"
+        out = dict(bytes=x.nbytes * 2, dtype="f16",
+                   config={"workload": f"swizzled tile copy, one 8x256 f16 tile (128-byte swizzle), {threads} "
+                                       "threads (latency-bound: microseconds per launch)"},
+                   key="tile_copy_swizzled_f16_8x256")
+    elif name == "c2":
+        threads = args.threads or 256
+        x = W.sqrt_tiles_f32(65536, seed=2)
+        shape = x.shape
+        for _ in range(sets):
+            xd, yd = ctx.to_dev(x), ctx.empty(x.nbytes)
+            xdesc = acp.acp_encode_tiled("f32", xd, shape, _packed(shape), (1, 32, 32))
+            ydesc = acp.acp_encode_tiled("f32", yd, shape, _packed(shape), (1, 32, 32))
+            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
+                            acp.acp_tile_ewise("sqrt", ydesc, [xdesc], threads, stream))
+        out = dict(bytes=x.nbytes * 2, dtype="f32",
+                   config={"workload": f"tile sqrt, 65536 tiles of 32x32 f32, {threads} threads, persistent grid"},
+                   key="tile_sqrt_f32_65536x32x32")
+    elif name == "c3":
+        threads = args.threads or 128
+        shape = (128, 500, 1024)
+        x = W.normal_f16(shape, seed=3)
+        for _ in range(sets):
+            xd, yd = ctx.to_dev(x), ctx.empty(x.nbytes)
+            xdesc = acp.acp_encode_tiled("f16", xd, shape, _packed(shape), (1, 128, 32))
+            ydesc = acp.acp_encode_tiled("f16", yd, shape, _packed(shape), (1, 128, 32))
+            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
+                            acp.acp_tile_copy(xdesc, ydesc, threads, stream))
+        out = dict(bytes=x.nbytes * 2, dtype="f16",
+                   config={"workload": f"tile copy, [128,500,1024] f16, 128x32 tiles, {threads} threads"},
+                   key="tile_copy_f16_128x500x1024")
+    elif name == "c5":
+        threads = args.threads or 256
+        S = stages or args.stages or 4
+        shape, pitch = (4, 8, 64, 128, 256), 264
+        c5_stage = tuple(int(v) for v in args.c5_stage.split(","))
+        c5_wgs = 0 if args.workgroups is None else args.workgroups
+        storage, strides = W.padded_uniform_f16(shape, pitch=pitch, seed=5)
+        n = int(np.prod(shape))
+        for _ in range(sets):
+            xd, yd = ctx.to_dev(storage), ctx.empty(n * 4)
+            xdesc = acp.acp_encode_tiled("f16", xd, shape, strides, (1, 2, 16, 64, 64), acp.ACP_SWIZZLE_128B)
+            ydesc = acp.acp_encode_tiled("f32", yd, shape, _packed(shape), (1, 2, 16, 64, 64))
+            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
+                            acp.acp_stream_ewise("exp", ydesc, xdesc, None, None, c5_stage, S, threads, c5_wgs,
+                                                 stream))
+        out = dict(bytes=n * 2 + n * 4, dtype="f16->f32",
+                   config={"workload": "rank-5 exp (4,8,64,128,256) f16 pitch 264 -> f32, box (1,2,16,64,64), "
+                                       f"{S}-stage swizzled ring, stage {c5_stage}"},
+                   key=f"stream_exp_rank5_s{S}")
+    elif name == "pointwise":
+        rows, S, threads = args.rows or 4, args.stages or 2, args.threads or 256
+        shape, stage = (128, 500, 1024), (1, rows, 1024)
+        rng = np.random.default_rng(6)
+        x = rng.standard_normal(shape, dtype=np.float32)
+        z = rng.standard_normal(shape, dtype=np.float32)
+        for _ in range(sets):
+            xd, zd, yd = ctx.to_dev(x), ctx.to_dev(z), ctx.empty(x.nbytes)
+            xdesc = acp.acp_encode_tiled("f32", xd, shape, _packed(shape), stage)
+            zdesc = acp.acp_encode_tiled("f32", zd, shape, _packed(shape), stage)
+            ydesc = acp.acp_encode_tiled("f32", yd, shape, _packed(shape), stage)
+            launches.append(lambda xdesc=xdesc, zdesc=zdesc, ydesc=ydesc, keep=(xd, zd, yd):
+                            acp.acp_stream_binary("add", ydesc, xdesc, zdesc, stage, S, threads, G, args.z_staging,
+                                                  stream))
+        out = dict(bytes=3 * x.nbytes, dtype="f32",
+                   config={"workload": f"two-tensor stream y = x + z, [128,500,1024] f32, {S}-stage LDS ring, "
+                                       f"stage (1,{rows},1024), z staged '{args.z_staging}'", "workgroups": G},
+                   key=f"stream_add2_f32_128x500x1024_s{S}_r{rows}_{args.z_staging}")
+    elif name == "reduce":
+        # store with reduce-add of a [128,500,1024] f32 tensor in (1,R,1024)
+        # tiles: into a same-shape destination (one contribution per element)
+        # or into one [1,500,1024] slab (128 contributions per element)
+        threads = args.threads or 256
+        rows = args.rows or (2 if args.reduce_over_batch else 4)
+        shape = (128, 500, 1024)
+        dshape = (1, 500, 1024) if args.reduce_over_batch else shape
+        box = (1, rows, 1024)
+        rng = np.random.default_rng(7)
+        x = rng.standard_normal(shape, dtype=np.float32)
+        for _ in range(sets):
+            xd = ctx.to_dev(x)
+            yd = ctx.torch.zeros(int(np.prod(dshape)) * 4, dtype=ctx.torch.uint8, device=ctx.dev)
+            xdesc = acp.acp_encode_tiled("f32", xd, shape, _packed(shape), box)
+            ydesc = acp.acp_encode_tiled("f32", yd, dshape, _packed(dshape), box)
+            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
+                            acp.acp_tile_reduce("add", ydesc, xdesc, threads, stream))
+        # algorithmic bytes: the source once, the destination read and written once
+        out = dict(bytes=x.nbytes + 2 * int(np.prod(dshape)) * 4, dtype="f32",
+                   config={"workload": f"store with reduce-add, [128,500,1024] f32 tiles (1,{rows},1024) into "
+                                       f"{list(dshape)}"},
+                   key=f"tile_reduce_f32_128x500x1024_r{rows}_{'batch' if args.reduce_over_batch else 'slab'}")
+    elif name == "rowsum":
+        rows, S, threads = args.rows or 4, args.stages or 2, args.threads or 256
+        shape, stage = (128, 500, 1024), (1, rows, 1024)
+        rng = np.random.default_rng(8)
+        x = rng.standard_normal(shape, dtype=np.float32)
+        for _ in range(sets):
+            xd, yd = ctx.to_dev(x), ctx.empty(128 * 500 * 4)
+            xdesc = acp.acp_encode_tiled("f32", xd, shape, _packed(shape), stage)
+            launches.append(lambda xdesc=xdesc, keep=(xd, yd):
+                            acp.acp_stream_reduce_rows("add", keep[1], xdesc, stage, S, threads, G, stream))
+        out = dict(bytes=x.nbytes + 128 * 500 * 4, dtype="f32",
+                   config={"workload": f"row sums of [128,500,1024] f32 -> [128,500], {S}-stage LDS ring, "
+                                       f"stage (1,{rows},1024)", "workgroups": G},
+                   key=f"stream_rowsum_f32_128x500x1024_s{S}_r{rows}")
+    elif name in ("copy_ref", "read_ref", "write_ref"):
+        nbytes = 128 * 500 * 1024 * 4
+        for _ in range(sets):
+            xd = ctx.torch.ones(nbytes, dtype=ctx.torch.uint8, device=ctx.dev)
+            yd = ctx.empty(nbytes)
+            sums = ctx.empty(16 * 4096)
+            if name == "copy_ref":
+                launches.append(lambda xd=xd, yd=yd: acp.acp_debug_stream_copy(yd, xd, nbytes, G, stream))
+            elif name == "read_ref":
+                launches.append(lambda xd=xd, s=sums: acp.acp_debug_stream_read(xd, nbytes, s, G, stream))
+            else:
+                launches.append(lambda yd=yd: acp.acp_debug_stream_fill(yd, nbytes, 0x3F800000, G, stream))
+        what = {"copy_ref": ("copy", 2 * nbytes, "stream_copy_reference_262MB"),
+                "read_ref": ("read-only stream", nbytes, "stream_read_reference_262MB"),
+                "write_ref": ("write-only stream", nbytes, "stream_write_reference_262MB")}[name]
+        out = dict(bytes=what[1], dtype="u8",
+                   config={"workload": f"reference register-path {what[0]} of 262144000 B (the c4 tensor), "
+                                       f"{G} workgroups"},
+                   key=what[2])
+    elif name == "calib":
+        nbytes = 256 << 20
+        for _ in range(sets):
+            xd = ctx.torch.ones(nbytes, dtype=ctx.torch.uint8, device=ctx.dev)
+            yd = ctx.empty(nbytes)
+            launches.append(lambda xd=xd, yd=yd: yd.copy_(xd))
+        out = dict(bytes=2 * nbytes, dtype="u8",
+                   config={"workload": "torch copy_ of 256 MiB (counter calibration: 268435456 B read, "
+                                       "268435456 B written)"},
+                   key="calib_copy_256MiB")
+    else:
+        raise ValueError(name)
+    out["launches"] = launches
+    out["unit"] = unit
+    return out
+
+
+def time_launches(ctx, fns, steps, warmup):
+    """Average launch time (ms) of `steps` back-to-back launches after
+    `warmup` untimed ones, from one event pair on the launch stream."""
+    torch = ctx.torch
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(ctx.stream)
+    for i in range(steps):
+        fns[i % len(fns)]()
+    t1.record(ctx.stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def bracketed_median(ctx, fns, steps):
+    """Median of per-launch times, each launch between its own event pair
+    (the dispatch gap is added to every launch)."""
+    torch = ctx.torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(ctx.stream)
+        fns[i % len(fns)]()
+        ends[i].record(ctx.stream)
+    torch.cuda.synchronize()
+    v = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return v[len(v) // 2]
+
+
+def roofline(wl, avg_ms, median_ms):
+    achieved = wl["bytes"] / (avg_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic_from_profiles(wl["key"]),
+            "algorithmic_bytes_per_launch": wl["bytes"], "avg_launch_ms": round(avg_ms, 5),
+            "median_event_bracketed_launch_ms": round(median_ms, 5), "kernel_source_hash": kernel_hash()}
+
+
+def measure_config(name, ctx, steps, warmup):
+    """One of the other workloads: its throughput (microseconds per launch for
+    the latency-bound single tile), the launch the library chose, and its
+    roofline figures."""
+    wl = build(name, ctx)
+    avg = time_launches(ctx, wl["launches"], steps, warmup)
+    kernel = ctx.acp.acp_last_kernel()
+    med = bracketed_median(ctx, wl["launches"], steps)
+    rf = roofline(wl, avg, med)
+    if wl["unit"] == "us":
+        entry = {"value": round(avg * 1e3, 2), "unit": "us per launch", "back_to_back_us": round(avg * 1e3, 2),
+                 "event_bracketed_median_us": round(med * 1e3, 2),
+                 "kernel_us": _profile_field(wl["key"], "kernel_average_ns")}
+        if entry["kernel_us"] is not None:
+            entry["kernel_us"] = round(entry["kernel_us"] / 1e3, 2)
+    else:
+        entry = {"value": rf["achieved"], "unit": "GB/s", "frac": rf["frac"], "roofline": rf}
+    entry.update({"ms_per_step": round(avg, 5), "dtype": wl["dtype"], "config": {**wl["config"], "kernel": kernel}})
+    del wl
+    ctx.torch.cuda.synchronize()
+    ctx.torch.cuda.empty_cache()
+    return entry
 
 
 def main():
@@ -108,271 +400,138 @@ def main():
         print(json.dumps({"error": "this build measures one GPU only: every box has one MI355X; "
                                    "run with --gpus 1", "n_gpus": args.gpus}))
         sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    import async_copy_pipelining_amd as acp
-    import workloads as W
-
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    stream = torch.cuda.current_stream()
-
-    def to_dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.uint8).reshape(-1).copy()).to(dev)
-
-    def packed(shape):
-        st, out = 1, []
-        for e in reversed(shape):
-            out.append(st)
-            st *= e
-        return tuple(reversed(out))
-
-    wl = args.workload
-    launches = []          # one callable per buffer set
-    if wl == "c4":
-        shape = (128, 500, 1024)
-        stage = (1, args.rows, 1024)
-        x, a, b = W.fma_rows_f32(shape, seed=4)
-        G = 256 * args.wg_per_cu if args.workgroups is None else args.workgroups
-        descs, keep = [], []
-        for s in range(args.sets):
-            xd, ad, bd = to_dev(x), to_dev(a), to_dev(b)
-            yd = torch.empty(x.nbytes, dtype=torch.uint8, device=dev)
-            xdesc = acp.acp_encode_tiled("f32", xd, shape, packed(shape), stage)
-            ydesc = acp.acp_encode_tiled("f32", yd, shape, packed(shape), stage)
-            descs.append((xdesc, ydesc, ad, bd))
-            keep.append((xd, yd))
-            launches.append((lambda xdesc=xdesc, ydesc=ydesc, ad=ad, bd=bd, keep=(xd, yd):
-                             acp.acp_stream_ewise("fma", ydesc, xdesc, ad, bd, stage, args.stages,
-                                                  args.threads, G, stream)))
-        ring_launches = {st: [(lambda xdesc=xdesc, ydesc=ydesc, ad=ad, bd=bd, st=st:
-                               acp.acp_stream_ewise("fma", ydesc, xdesc, ad, bd, stage, st, args.threads, G, stream))
-                              for (xdesc, ydesc, ad, bd) in descs] for st in (2, 3, 4)}
-        bytes_per = x.nbytes * 2 + a.nbytes + b.nbytes
-        dtype = "f32"
-        config = {"workload": f"stream fma y=a[row]*x+b[row], [128,500,1024] f32, {args.stages}-stage LDS ring, "
-                              f"stage (1,{args.rows},1024)", "shape": list(shape), "stages": args.stages,
-                  "stage_box": list(stage), "threads": args.threads, "workgroups": G}
-        key = f"stream_fma_f32_128x500x1024_s{args.stages}_r{args.rows}"
-    elif wl == "c1":
-        # one 8x256 f16 tile through the 128-byte swizzled LDS image and back,
-        # 64 threads: latency-bound, so the figure that matters is the launch
-        # time (ms_per_step), not the GB/s
-        x = W.tile_bits_f16((8, 256), seed=1)
-        shape = x.shape
-        for s in range(args.sets):
-            xd = to_dev(x)
-            yd = torch.empty(x.nbytes, dtype=torch.uint8, device=dev)
-            xdesc = acp.acp_encode_tiled("f16", xd, shape, packed(shape), shape, acp.ACP_SWIZZLE_128B)
-            ydesc = acp.acp_encode_tiled("f16", yd, shape, packed(shape), shape, acp.ACP_SWIZZLE_128B)
-            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
-                            acp.acp_tile_copy(xdesc, ydesc, 64, stream))
-        bytes_per, dtype = x.nbytes * 2, "f16"
-        config = {"workload": "swizzled tile copy, one 8x256 f16 tile (128-byte swizzle), 64 threads "
-                              "(latency-bound: read ms_per_step)"}
-        key = "tile_copy_f16_8x256_swizzle128"
-    elif wl == "c2":
-        x = W.sqrt_tiles_f32(65536, seed=2)
-        shape = x.shape
-        for s in range(args.sets):
-            xd = to_dev(x)
-            yd = torch.empty(x.nbytes, dtype=torch.uint8, device=dev)
-            xdesc = acp.acp_encode_tiled("f32", xd, shape, packed(shape), (1, 32, 32))
-            ydesc = acp.acp_encode_tiled("f32", yd, shape, packed(shape), (1, 32, 32))
-            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
-                            acp.acp_tile_ewise("sqrt", ydesc, [xdesc], 256, stream))
-        bytes_per, dtype = x.nbytes * 2, "f32"
-        config = {"workload": "tile sqrt, 65536 tiles of 32x32 f32, 256 threads, persistent grid"}
-        key = "tile_sqrt_f32_65536x32x32"
-    elif wl == "c3":
-        shape = (128, 500, 1024)
-        x = W.normal_f16(shape, seed=3)
-        for s in range(args.sets):
-            xd = to_dev(x)
-            yd = torch.empty(x.nbytes, dtype=torch.uint8, device=dev)
-            xdesc = acp.acp_encode_tiled("f16", xd, shape, packed(shape), (1, 128, 32))
-            ydesc = acp.acp_encode_tiled("f16", yd, shape, packed(shape), (1, 128, 32))
-            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
-                            acp.acp_tile_copy(xdesc, ydesc, 128, stream))
-        bytes_per, dtype = x.nbytes * 2, "f16"
-        config = {"workload": "tile copy, [128,500,1024] f16, 128x32 tiles, 128 threads"}
-        key = "tile_copy_f16_128x500x1024"
-    elif wl == "pointwise":
-        # y = x + z over two [128,500,1024] f32 tensors, both streamed
-        shape = (128, 500, 1024)
-        stage = (1, args.rows, 1024)
-        rng = np.random.default_rng(6)
-        x = rng.standard_normal(shape, dtype=np.float32)
-        z = rng.standard_normal(shape, dtype=np.float32)
-        G = 256 * args.wg_per_cu if args.workgroups is None else args.workgroups
-        for s in range(args.sets):
-            xd, zd = to_dev(x), to_dev(z)
-            yd = torch.empty(x.nbytes, dtype=torch.uint8, device=dev)
-            xdesc = acp.acp_encode_tiled("f32", xd, shape, packed(shape), stage)
-            zdesc = acp.acp_encode_tiled("f32", zd, shape, packed(shape), stage)
-            ydesc = acp.acp_encode_tiled("f32", yd, shape, packed(shape), stage)
-            launches.append(lambda xdesc=xdesc, zdesc=zdesc, ydesc=ydesc, keep=(xd, zd, yd):
-                            acp.acp_stream_binary("add", ydesc, xdesc, zdesc, stage, args.stages, args.threads, G,
-                                                  args.z_staging, stream))
-        bytes_per, dtype = 3 * x.nbytes, "f32"
-        config = {"workload": f"two-tensor stream y = x + z, [128,500,1024] f32, {args.stages}-stage LDS ring, "
-                              f"stage (1,{args.rows},1024), z staged '{args.z_staging}'", "workgroups": G}
-        key = f"stream_add2_f32_128x500x1024_s{args.stages}_r{args.rows}_{args.z_staging}"
-    elif wl == "reduce":
-        # store with reduce-add of a [128,500,1024] f32 tensor in (1,R,1024)
-        # tiles: into a same-shape destination (one contribution per element)
-        # or into one [1,500,1024] slab (128 contributions per element)
-        shape = (128, 500, 1024)
-        dshape = (1, 500, 1024) if args.reduce_over_batch else shape
-        box = (1, args.rows, 1024)
-        rng = np.random.default_rng(7)
-        x = rng.standard_normal(shape, dtype=np.float32)
-        for s in range(args.sets):
-            xd = to_dev(x)
-            yd = torch.zeros(int(np.prod(dshape)) * 4, dtype=torch.uint8, device=dev)
-            xdesc = acp.acp_encode_tiled("f32", xd, shape, packed(shape), box)
-            ydesc = acp.acp_encode_tiled("f32", yd, dshape, packed(dshape), box)
-            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
-                            acp.acp_tile_reduce("add", ydesc, xdesc, args.threads, stream))
-        # algorithmic bytes: the source once, the destination read and written once
-        bytes_per, dtype = x.nbytes + 2 * int(np.prod(dshape)) * 4, "f32"
-        config = {"workload": f"store with reduce-add, [128,500,1024] f32 tiles (1,{args.rows},1024) into "
-                              f"{list(dshape)}"}
-        key = f"tile_reduce_f32_128x500x1024_r{args.rows}_{'batch' if args.reduce_over_batch else 'slab'}"
-    elif wl == "rowsum":
-        # y[i, j] = sum over k of x[i, j, k], [128,500,1024] f32 -> [128,500]
-        shape = (128, 500, 1024)
-        stage = (1, args.rows, 1024)
-        rng = np.random.default_rng(8)
-        x = rng.standard_normal(shape, dtype=np.float32)
-        G = 256 * args.wg_per_cu if args.workgroups is None else args.workgroups
-        for s in range(args.sets):
-            xd = to_dev(x)
-            yd = torch.empty(128 * 500 * 4, dtype=torch.uint8, device=dev)
-            xdesc = acp.acp_encode_tiled("f32", xd, shape, packed(shape), stage)
-            launches.append(lambda xdesc=xdesc, keep=(xd, yd):
-                            acp.acp_stream_reduce_rows("add", keep[1], xdesc, stage, args.stages, args.threads, G,
-                                                       stream))
-        bytes_per, dtype = x.nbytes + 128 * 500 * 4, "f32"
-        config = {"workload": f"row sums of [128,500,1024] f32 -> [128,500], {args.stages}-stage LDS ring, "
-                              f"stage (1,{args.rows},1024)", "workgroups": G}
-        key = f"stream_rowsum_f32_128x500x1024_s{args.stages}_r{args.rows}"
-    elif wl == "copy_ref":
-        n = 128 * 500 * 1024 * 4
-        G = 256 * args.wg_per_cu if args.workgroups is None else args.workgroups
-        for s in range(args.sets):
-            xd = torch.ones(n, dtype=torch.uint8, device=dev)
-            yd = torch.empty(n, dtype=torch.uint8, device=dev)
-            launches.append(lambda xd=xd, yd=yd: acp.acp_debug_stream_copy(yd, xd, n, G, stream))
-        bytes_per, dtype = 2 * n, "u8"
-        config = {"workload": f"reference register-path copy of 262144000 B (the c4 tensor), {G} workgroups"}
-        key = "stream_copy_reference_262MB"
-    elif wl == "calib":
-        n = 256 << 20
-        for s in range(args.sets):
-            xd = torch.ones(n, dtype=torch.uint8, device=dev)
-            yd = torch.empty(n, dtype=torch.uint8, device=dev)
-            launches.append(lambda xd=xd, yd=yd: yd.copy_(xd))
-        bytes_per, dtype = 2 * n, "u8"
-        config = {"workload": "torch copy_ of 256 MiB (counter calibration: 268435456 B read, 268435456 B written)"}
-        key = "calib_copy_256MiB"
-    else:
-        shape, pitch = (4, 8, 64, 128, 256), 264
-        storage, strides = W.padded_uniform_f16(shape, pitch=pitch, seed=5)
-        n = int(np.prod(shape))
-        for s in range(args.sets):
-            xd = to_dev(storage)
-            yd = torch.empty(n * 4, dtype=torch.uint8, device=dev)
-            xdesc = acp.acp_encode_tiled("f16", xd, shape, strides, (1, 2, 16, 64, 64), acp.ACP_SWIZZLE_128B)
-            ydesc = acp.acp_encode_tiled("f32", yd, shape, packed(shape), (1, 2, 16, 64, 64))
-            launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
-                            acp.acp_stream_ewise("exp", ydesc, xdesc, None, None, (1, 1, 1, 64, 64),
-                                                 args.stages, 256, 0, stream))
-        bytes_per, dtype = n * 2 + n * 4, "f16->f32"
-        config = {"workload": "rank-5 exp (4,8,64,128,256) f16 pitch 264 -> f32, box (1,2,16,64,64), "
-                              f"{args.stages}-stage swizzled ring, stage (1,1,1,64,64)"}
-        key = f"stream_exp_rank5_s{args.stages}"
-
-    for i in range(args.warmup):
-        launches[i % len(launches)]()
-    torch.cuda.synchronize()
-    kernel = acp.acp_last_kernel()          # the launch shape the library chose for the timed kernel
-    if kernel:
-        config = {**config, "kernel": kernel}
-
-    # Timed region: K steps back to back, bracketed by synchronize and one
-    # event pair on the launch stream.
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        launches[i % len(launches)]()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-
-    # One step is one launch of the kernel, on the stream the events were
-    # recorded on: the timed region's events give its average launch
-    # duration (the figure rocprofv3's kernel trace reports per dispatch).
-    ms_per_step = total_ms / args.steps
-    avg_launch_ms = ms_per_step
-    value = bytes_per / (ms_per_step * 1e-3) / 1e9
-    achieved = bytes_per / (avg_launch_ms * 1e-3) / 1e9
-
-    # For reference: the same K launches, each bracketed by its own event
-    # pair (this adds the dispatch gap to every launch).
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for i in range(args.steps):
-        starts[i].record(stream)
-        launches[i % len(launches)]()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    per_launch = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-
+    ctx = Ctx(args)
+    if args.fixed_cost:
+        fixed_cost(ctx)
+        return
+    name = args.workload or "c4"
+    wl = build(name, ctx)
+    fns = wl["launches"]
     ring = None
-    if wl == "c4" and not args.no_ring_sweep:
-        # the 2-, 3- and 4-stage rings, back to back like `value`
+    if name == "c4" and not args.no_ring_sweep:
+        # the 2-, 3- and 4-stage rings, back to back like `value` (measured
+        # before the headline's own warm-up and timed region)
         ring = {}
         for st in (2, 3, 4):
-            fns = ring_launches[st] if st != args.stages else launches
-            for i in range(args.warmup):
-                fns[i % len(fns)]()
-            torch.cuda.synchronize()
-            r0 = torch.cuda.Event(enable_timing=True)
-            r1 = torch.cuda.Event(enable_timing=True)
-            r0.record(stream)
-            for i in range(args.steps):
-                fns[i % len(fns)]()
-            r1.record(stream)
-            torch.cuda.synchronize()
-            ring[str(st)] = round(bytes_per / (r0.elapsed_time(r1) / args.steps * 1e-3) / 1e9, 1)
+            wl["set_stages"][0] = st
+            ring[str(st)] = round(wl["bytes"] / (time_launches(ctx, fns, args.steps, args.warmup) * 1e-3) / 1e9, 1)
+        wl["set_stages"][0] = args.stages or 4
 
-    traffic = traffic_from_profiles(key)
+    # Timed region: warm-up, then K steps back to back, bracketed by
+    # synchronize and one event pair on the launch stream.  One step is one
+    # launch of the kernel, so the event pair's time over K is the kernel's
+    # average launch duration (the figure rocprofv3's kernel trace reports per
+    # dispatch, plus the dispatch gap).
+    ms_per_step = time_launches(ctx, fns, args.steps, args.warmup)
+    kernel = ctx.acp.acp_last_kernel()
+    median = bracketed_median(ctx, fns, args.steps)
+    rf = roofline(wl, ms_per_step, median)
+    if wl["unit"] == "us":
+        value, unit = round(ms_per_step * 1e3, 3), "us"
+    else:
+        value, unit = round(wl["bytes"] / (ms_per_step * 1e-3) / 1e9, 1), "GB/s"
     result = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "metric": METRIC if unit == "GB/s" else "microseconds per launch, swizzled 8x256 f16 tile copy, 1 MI355X",
+        "value": value, "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "higher_is_better": unit == "GB/s", "scaling": "weak", "vs_baseline": None, "dtype": wl["dtype"],
         "data": "synthetic (seeded numpy draws resident in HBM, 3 rotated buffer sets)",
-        "config": config,
-        "percent_of_peak": round(100.0 * value / PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": bytes_per,
-                     "avg_launch_ms": round(avg_launch_ms, 5),
-                     "median_event_bracketed_launch_ms": round(per_launch[len(per_launch) // 2], 5),
-                     "kernel_source_hash": kernel_hash()},
+        "config": {**wl["config"], "kernel": kernel},
+        "percent_of_peak": round(100.0 * rf["achieved"] / PEAK_GBS, 2),
+        "roofline": rf,
     }
     if ring is not None:
         result["ring_stages"] = {"unit": "GB/s", **ring}
-    if not args.no_cpu_baseline and wl == "c4":
-        result["cpu_baseline"] = cpu_baseline_c4(args.cpu_seconds)
-        result["cpu_baseline_all_cores"] = cpu_baseline_c4_parallel(args.cpu_seconds)
+    del wl, fns
+    ctx.torch.cuda.empty_cache()
+    if name == "c4" and args.workload is None and not args.no_configs:
+        configs = {}
+        for c in ("c1", "c2", "c3", "c5"):
+            configs[c] = measure_config(c, ctx, args.steps, args.warmup)
+            if not args.no_cpu_baseline:
+                configs[c]["cpu_baseline"] = cpu_baseline_config(c, args.config_cpu_seconds)
+        result["configs"] = configs
+    if not args.no_cpu_baseline:
+        if name == "c4":
+            result["cpu_baseline"] = cpu_baseline_c4(args.cpu_seconds)
+            result["cpu_baseline_all_cores"] = cpu_baseline_c4_parallel(args.cpu_seconds)
+        elif name in ("c1", "c2", "c3", "c5"):
+            result["cpu_baseline"] = cpu_baseline_config(name, args.config_cpu_seconds)
     print(json.dumps(result), flush=True)
 
+
+# ---------------------------------------------------------------------------
+# Fixed cost per launch: the streamed fma (the default launch) and the
+# reference copy over 1..128 [500,1024] slabs of the same tensors.  Windows of
+# N slabs rotate through all three buffer sets so that no window is reused
+# before more than the 256 MB last-level cache has been streamed; each launch
+# is timed between its own event pair (device time: host gaps between
+# launches are not counted).  A least-squares line time = fixed + bytes /
+# rate over the slab counts gives each kernel's fixed cost and per-byte rate.
+
+def _fit(points):
+    n = len(points)
+    mx = sum(p[0] for p in points) / n
+    my = sum(p[1] for p in points) / n
+    sxx = sum((p[0] - mx) ** 2 for p in points)
+    sxy = sum((p[0] - mx) * (p[1] - my) for p in points)
+    slope = sxy / sxx
+    return my - slope * mx, slope
+
+
+def fixed_cost(ctx):
+    args, acp, W, np, torch = ctx.args, ctx.acp, ctx.W, ctx.np, ctx.torch
+    shape = (128, 500, 1024)
+    slab_b = 500 * 1024 * 4
+    x, a, b = W.fma_rows_f32(shape, seed=4)
+    bufs = [(ctx.to_dev(x), ctx.to_dev(a), ctx.to_dev(b), ctx.empty(x.nbytes)) for _ in range(3)]
+    stage = (1, 2, 1024)
+    res = {"workload": "streamed fma (stage (1,2,1024), 4 slots, 256 workgroups) and reference copy, "
+                       "1..128 slabs of [500,1024] f32", "points": {}}
+    for kind in ("ring", "copy"):
+        pts = []
+        for N in (1, 2, 4, 8, 16, 32, 64, 128):
+            n_win = max(12, 3 * (128 // N))
+            fns = []
+            for j in range(n_win):
+                xd, ad, bd, yd = bufs[j % 3]
+                s0 = ((j // 3) * N) % (128 - N + 1)
+                if kind == "ring":
+                    sh = (N, 500, 1024)
+                    xdesc = acp.acp_encode_tiled("f32", xd.data_ptr() + s0 * slab_b, sh, _packed(sh), stage)
+                    ydesc = acp.acp_encode_tiled("f32", yd.data_ptr() + s0 * slab_b, sh, _packed(sh), stage)
+                    pa, pb = ad.data_ptr() + s0 * 2000, bd.data_ptr() + s0 * 2000
+                    fns.append(lambda xdesc=xdesc, ydesc=ydesc, pa=pa, pb=pb:
+                               acp.acp_stream_ewise("fma", ydesc, xdesc, pa, pb, stage, 4, 256, 256, ctx.stream))
+                else:
+                    px, py = xd.data_ptr() + s0 * slab_b, yd.data_ptr() + s0 * slab_b
+                    fns.append(lambda px=px, py=py, nb=N * slab_b:
+                               acp.acp_debug_stream_copy(py, px, nb, 256, ctx.stream))
+            for i in range(2 * len(fns)):
+                fns[i % len(fns)]()
+            torch.cuda.synchronize()
+            steps = max(60, len(fns))
+            starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+            ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+            for i in range(steps):
+                starts[i].record(ctx.stream)
+                fns[i % len(fns)]()
+                ends[i].record(ctx.stream)
+            torch.cuda.synchronize()
+            t = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+            med_us = t[len(t) // 2] * 1e3
+            nbytes = N * (2 * slab_b + (1000 * 4 if kind == "ring" else 0))
+            pts.append((nbytes, med_us))
+            res["points"].setdefault(kind, []).append({"slabs": N, "bytes": nbytes, "median_us": round(med_us, 2)})
+        fixed, per_byte = _fit(pts)
+        res[kind] = {"fixed_us": round(fixed, 2), "rate_GBps": round(1e-3 / per_byte, 1)}
+    print(json.dumps(res), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# CPU baselines: the oracle's plain definition of each workload (as it
+# stands, not tuned), timed on the host on a bounded sample of the same
+# workload.
 
 def cpu_baseline_c4(budget_s: float):
     """The oracle's streamed fma over whole [500, 1024] slabs of the same
@@ -396,6 +555,63 @@ def cpu_baseline_c4(budget_s: float):
     return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} [500,1024] f32 slabs of the streamed-fma workload ({done / 128:.2f} passes "
                       f"over the 128 slabs) in {el:.1f} s, numpy single thread"}
+
+
+def cpu_baseline_config(name: str, budget_s: float):
+    """The oracle's plain definition on a bounded sample of workload `name`
+    (single thread): tile copy = the identity, tile sqrt and the rank-5 exp =
+    the op element by element."""
+    import numpy as np
+
+    import workloads as W
+    from oracle import reference as REF
+
+    done, t0 = 0, time.perf_counter()
+    if name == "c1":
+        x = W.tile_bits_f16((8, 256), seed=1)
+        while time.perf_counter() - t0 < budget_s:
+            REF.tile_copy(x)
+            done += 1
+        el = time.perf_counter() - t0
+        return {"value": round(el / done * 1e6, 3), "unit": "us per tile", "cores": 1, "kind": "oracle",
+                "sample": f"{done} copies of the 8x256 f16 tile in {el:.1f} s (reference.tile_copy), numpy "
+                          "single thread"}
+    if name == "c2":
+        x = W.sqrt_tiles_f32(65536, seed=2)
+        chunk = 2048
+        while time.perf_counter() - t0 < budget_s:
+            k = (done * chunk) % 65536
+            REF.ewise("sqrt", [x[k:k + chunk]], np.float32)
+            done += 1
+        el = time.perf_counter() - t0
+        nbytes = done * chunk * 1024 * 8
+        return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{done} chunks of {chunk} 32x32 f32 tiles of the tile-sqrt workload in {el:.1f} s "
+                          "(reference.ewise sqrt), numpy single thread"}
+    if name == "c3":
+        x = W.normal_f16((128, 500, 1024), seed=3)
+        while time.perf_counter() - t0 < budget_s:
+            REF.tile_copy(x[done % 128])
+            done += 1
+        el = time.perf_counter() - t0
+        nbytes = done * 500 * 1024 * 2 * 2
+        return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{done} [500,1024] f16 slabs of the tile-copy workload in {el:.1f} s "
+                          "(reference.tile_copy), numpy single thread"}
+    if name == "c5":
+        shape = (4, 8, 64, 128, 256)
+        storage, strides = W.padded_uniform_f16(shape, pitch=264, seed=5)
+        xv = W.strided_view(storage, shape, strides)
+        while time.perf_counter() - t0 < budget_s:
+            i = done % 32
+            REF.stream_ewise("exp", xv[i // 8, i % 8], out_dtype=np.float32)
+            done += 1
+        el = time.perf_counter() - t0
+        nbytes = done * 64 * 128 * 256 * 6
+        return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{done} (64,128,256) blocks of the rank-5 exp workload in {el:.1f} s "
+                          "(reference.stream_ewise exp, f16 -> f32), numpy single thread"}
+    raise ValueError(name)
 
 
 _start_barrier = None
@@ -433,7 +649,6 @@ def cpu_baseline_c4_parallel(budget_s: float):
     16), each on its own slabs of the workload; aggregate bytes over the
     longest worker's time."""
     import multiprocessing as mp
-    import os
 
     nproc = max(1, min(16, len(os.sched_getaffinity(0))))
     ctx = mp.get_context("spawn")

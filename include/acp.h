@@ -65,8 +65,8 @@ extern "C" {
 #define ACP_MAX_INPUT_RANK 8   /* rank of a tensor handed to the encoder */
 #define ACP_MAX_RANK 5         /* descriptor rank after planning ([tma] "What it accepts") */
 #define ACP_MAX_BOX 256        /* per-dimension box limit ([cb] "Lowering Details") */
-#define ACP_MAX_ISSUES 256     /* loads per tile the planner may create when shrinking */
-#define ACP_MAX_IMAGE_AXES 12  /* axes of a tile's LDS image */
+#define ACP_MAX_ISSUES 256     /* loads per tile the kernels index (a library limit) */
+#define ACP_MAX_IMAGE_AXES 12  /* axes of a tile's LDS image the kernels index (a library limit) */
 #define ACP_MAX_EWISE_INPUTS 3
 
 typedef enum {
@@ -163,9 +163,14 @@ const char* acp_last_kernel(void);
  *   box      rank tile extents >= 1 (may exceed 256: the planner splits it)
  *   swizzle  LDS layout of the staged tile
  *   oob      ACP_OOB_ZERO
- * Runs the box-level plan search and returns ACP_ERR_DECLINED when no legal
- * descriptor exists (rank > 5 after shrinking, no swizzle-atom-aligned
- * innermost box, innermost stride != 1).  Pure host code. */
+ * Runs the box-level plan search.  The search always shrinks a plan to rank
+ * <= 5 (outer dims become loads of their own) and cuts an innermost box that
+ * does not fit the swizzle atom into loads that do ([tma] "Algorithm" step
+ * 2), so it returns ACP_ERR_DECLINED only when no legal descriptor exists:
+ * innermost stride != 1, or under a swizzle an innermost box (merged rows
+ * included) that is no whole number of 16-byte chunks.  A legal plan beyond
+ * what the kernels index (more than ACP_MAX_ISSUES loads per tile or
+ * ACP_MAX_IMAGE_AXES image axes) is ACP_ERR_UNSUPPORTED.  Pure host code. */
 acp_status acp_encode_tiled(acp_tile_desc* out, acp_dtype dtype, int rank, const void* gbase,
                             const int64_t* shape, const int64_t* strides, const int32_t* box,
                             acp_swizzle swizzle, acp_oob oob);
@@ -326,6 +331,23 @@ acp_status acp_debug_ring_trace(int n_iters, int stages, int loads, int stores, 
  * a size that is negative, not a multiple of 16 or at least 2^40, or
  * overlapping buffers. */
 acp_status acp_debug_stream_copy(void* dst, const void* src, int64_t bytes, int workgroups, void* hip_stream);
+
+/* Measurement references for one direction (not part of the pipelined
+ * path), with acp_debug_stream_copy's walk: 256-thread workgroups, 16 KiB
+ * blocks w, w+G, ..., four 16-byte non-temporal accesses per lane;
+ * `workgroups` 0 takes one per compute unit (never more than the blocks).
+ * They give the bandwidth the device reaches when it only reads or only
+ * writes, the two limits a mixed read/write stream lies between.
+ *   acp_debug_stream_read   reads `bytes` from device memory `src`; each
+ *                           workgroup w writes the XOR of the 16-byte words
+ *                           it read to sums[w] (device, 16 bytes per
+ *                           workgroup, not intersecting src)
+ *   acp_debug_stream_fill   writes the 32-bit `pattern` over `bytes` of
+ *                           device memory `dst`
+ * ACP_ERR_INVALID on null pointers, a size that is negative, not a multiple
+ * of 16 or at least 2^40, or sums intersecting the source. */
+acp_status acp_debug_stream_read(const void* src, int64_t bytes, void* sums, int workgroups, void* hip_stream);
+acp_status acp_debug_stream_fill(void* dst, int64_t bytes, uint32_t pattern, int workgroups, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -36,5 +36,6 @@ def test_headline_profile_matches_the_bench_default():
     # the default workload (streamed fma, 4 slots, stage (1,2,1024)) reads its
     # traffic from this summary
     src = open(os.path.join(ROOT, "bench.py"), encoding="utf-8").read()
-    assert '"c4": 2' in src
+    c4 = src[src.index('if name == "c4":'):src.index('elif name == "c1":')]
+    assert "rows = args.rows or 2" in c4 and "S = stages or args.stages or 4" in c4
     assert os.path.exists(os.path.join(PROFILES, "stream_fma_f32_128x500x1024_s4_r2.md"))

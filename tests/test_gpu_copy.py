@@ -301,3 +301,26 @@ def test_store_with_reduce_add(dt, src_shape, dst_shape, box, threads, values, s
     say(f"reduce-add {dt} {src_shape} -> {dst_shape} box {box} threads {threads} swizzle {swz}")
     got, want = _reduce_case(dt, src_shape, dst_shape, box, threads, values, swz)
     assert np.array_equal(got, want)
+
+
+def test_reference_read_and_fill_streams():
+    # the one-direction measurement references: the read stream's per-
+    # workgroup XORs fold to the XOR of every 16-byte word of the source;
+    # the fill writes its pattern over exactly the requested bytes
+    n = (3 << 20) + 4096 + 48                     # a short last block
+    say(f"reference read / fill streams over {n} bytes")
+    rng = np.random.default_rng(31)
+    x = rng.integers(0, 2**32, size=n // 4, dtype=np.uint64).astype(np.uint32)
+    xd = dev(x)
+    for wgs in (0, 7, 300):
+        sums = empty_bytes(16 * 512, 0x00)
+        acp.acp_debug_stream_read(xd, n, sums, wgs, stream())
+        g = wgs or 256
+        g = min(g, (n + 16383) // 16384)
+        got = np.bitwise_xor.reduce(host(sums, np.uint32).reshape(-1, 4)[:g], axis=0)
+        want = np.bitwise_xor.reduce(x.reshape(-1, 4), axis=0)
+        assert np.array_equal(got, want), wgs
+    yd = empty_bytes(n + 64, 0x11)
+    acp.acp_debug_stream_fill(yd, n, 0xDEADBEEF, 5, stream())
+    y = host(yd, np.uint8)
+    assert np.all(y[:n].view(np.uint32) == 0xDEADBEEF) and np.all(y[n:] == 0x11)
