@@ -94,6 +94,7 @@ _SIGS = {
     "acp_debug_stream_copy": ([_P, _P, ctypes.c_int64, _I, _P], _I),
     "acp_debug_stream_read": ([_P, ctypes.c_int64, _P, _I, _P], _I),
     "acp_debug_stream_fill": ([_P, ctypes.c_int64, ctypes.c_uint32, _I, _P], _I),
+    "acp_debug_stream_widen": ([_P, _P, ctypes.c_int64, _I, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -223,3 +224,7 @@ def acp_debug_stream_read(src, nbytes: int, sums, workgroups: int = 0, stream=No
 def acp_debug_stream_fill(dst, nbytes: int, pattern: int, workgroups: int = 0, stream=None) -> None:
     _check(_lib.acp_debug_stream_fill(_ptr(dst), int(nbytes), int(pattern) & 0xFFFFFFFF, int(workgroups),
                                       _stream(stream)))
+
+
+def acp_debug_stream_widen(dst, src, elements: int, workgroups: int = 0, stream=None) -> None:
+    _check(_lib.acp_debug_stream_widen(_ptr(dst), _ptr(src), int(elements), int(workgroups), _stream(stream)))

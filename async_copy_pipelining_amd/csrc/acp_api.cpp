@@ -1351,4 +1351,22 @@ acp_status acp_debug_stream_fill(void* dst, int64_t bytes, uint32_t pattern, int
   return ret(ACP_OK);
 }
 
+acp_status acp_debug_stream_widen(float* dst, const void* src, int64_t elements, int workgroups, void* hip_stream) {
+  if (!dst || !src || elements < 0 || workgroups < 0) return ret(ACP_ERR_INVALID, "bad stream widen arguments");
+  if (elements % 8 != 0) return ret(ACP_ERR_INVALID, "stream widen converts whole groups of 8 elements");
+  if (elements >= (int64_t(1) << 38)) return ret(ACP_ERR_INVALID, "stream widen size out of range");
+  const int64_t in_bytes = elements * 2;
+  const char* s = static_cast<const char*>(src);
+  const char* d = reinterpret_cast<const char*>(dst);
+  if (s < d + 2 * in_bytes && d < s + in_bytes) return ret(ACP_ERR_INVALID, "source and destination overlap");
+  if (elements == 0) return ret(ACP_OK);
+  const int64_t blocks = (in_bytes + 8191) / 8192;
+  int64_t grid = workgroups > 0 ? workgroups : device_cu_count();
+  if (grid > blocks) grid = blocks;
+  const hipError_t e = acp::stream_widen_launch(src, dst, static_cast<uint64_t>(in_bytes), static_cast<unsigned>(grid),
+                                                static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ret(ACP_OK);
+}
+
 }  // extern "C"

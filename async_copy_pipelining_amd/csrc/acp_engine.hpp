@@ -124,6 +124,7 @@ hipError_t lds_image_launch(const void* kernel, const EngineArgs& args, unsigned
 hipError_t stream_copy_launch(const void* src, void* dst, uint64_t bytes, unsigned grid, hipStream_t stream);
 hipError_t stream_read_launch(const void* src, uint64_t bytes, void* sums, unsigned grid, hipStream_t stream);
 hipError_t stream_fill_launch(void* dst, uint64_t bytes, uint32_t pattern, unsigned grid, hipStream_t stream);
+hipError_t stream_widen_launch(const void* src, void* dst, uint64_t in_bytes, unsigned grid, hipStream_t stream);
 hipError_t ring_trace_launch(int n_iters, int stages, int loads, int stores, int32_t* out,
                              hipStream_t stream);
 

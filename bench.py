@@ -19,7 +19,8 @@ runs on) and the CPU oracle timed on a bounded sample of the same workload.
 
 Other modes (measurement aids):
   --workload NAME   one workload alone (c1 c2 c3 c5, the references copy_ref /
-                    read_ref / write_ref, calib, and pointwise / reduce / rowsum)
+                    read_ref / write_ref / widen_ref, calib, and pointwise /
+                    reduce / rowsum)
   --fixed-cost      the streamed fma and the reference copy over 1..128 slabs of
                     the tensor: per-launch fixed cost and per-byte rate of each
 """
@@ -86,7 +87,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None,
-                    choices=["c1", "c2", "c3", "c4", "c5", "calib", "copy_ref", "read_ref", "write_ref", "pointwise",
+                    choices=["c1", "c2", "c3", "c4", "c5", "calib", "copy_ref", "read_ref", "write_ref", "widen_ref",
+                             "pointwise",
                              "reduce", "rowsum"],
                     help="measure one workload alone (default: c4 with ring_stages and configs); calib: torch's "
                          "copy of 256 MiB, the known-size kernel that scales HBM counters; copy_ref / read_ref / "
@@ -294,6 +296,16 @@ def build(name, ctx, stages=None):
                    config={"workload": f"row sums of [128,500,1024] f32 -> [128,500], {S}-stage LDS ring, "
                                        f"stage (1,{rows},1024)", "workgroups": G},
                    key=f"stream_rowsum_f32_128x500x1024_s{S}_r{rows}")
+    elif name == "widen_ref":
+        n = 4 * 8 * 64 * 128 * 256            # the rank-5 exp workload's element count, packed
+        for _ in range(sets):
+            xd = ctx.torch.zeros(n * 2, dtype=ctx.torch.uint8, device=ctx.dev)
+            yd = ctx.empty(n * 4)
+            launches.append(lambda xd=xd, yd=yd: acp.acp_debug_stream_widen(yd, xd, n, G, stream))
+        out = dict(bytes=n * 6, dtype="f16->f32",
+                   config={"workload": f"reference register-path f16 -> f32 widening stream of {n} elements "
+                                       f"(the rank-5 exp workload's count, packed), {G} workgroups"},
+                   key="stream_widen_reference_33M")
     elif name in ("copy_ref", "read_ref", "write_ref"):
         nbytes = 128 * 500 * 1024 * 4
         for _ in range(sets):

@@ -324,3 +324,17 @@ def test_reference_read_and_fill_streams():
     acp.acp_debug_stream_fill(yd, n, 0xDEADBEEF, 5, stream())
     y = host(yd, np.uint8)
     assert np.all(y[:n].view(np.uint32) == 0xDEADBEEF) and np.all(y[n:] == 0x11)
+
+
+def test_reference_widening_stream():
+    # the widening reference converts float16 to float32 exactly and writes
+    # nothing past the output
+    n = (1 << 20) + 8 * 37                   # a short last block
+    say(f"reference widening stream over {n} elements")
+    x = W.normal_f16((n,), seed=33)
+    xd = dev(x)
+    yd = empty_bytes(n * 4 + 64, 0x11)
+    acp.acp_debug_stream_widen(yd, xd, n, 0, stream())
+    y = host(yd, np.uint8)
+    assert np.array_equal(y[:n * 4].view(np.float32), x.astype(np.float32))
+    assert np.all(y[n * 4:] == 0x11)
