@@ -132,8 +132,9 @@ __global__ __launch_bounds__(256) void stream_fill_kernel(char* dst, uint64_t by
 
 // Measurement reference for a widening stream (two bytes written per byte
 // read): float16 -> float32 conversion of a contiguous tensor, workgroup w
-// taking 8 KiB input blocks w, w+G, ...: two 16-byte non-temporal loads per
-// lane, each widened into two 16-byte stores.
+// taking 8 KiB input blocks w, w+G, ...: four 8-byte non-temporal loads per
+// lane, each widened into one 16-byte store, so every wave instruction reads
+// 512 contiguous bytes and writes 1 KiB.
 __global__ __launch_bounds__(256) void stream_widen_kernel(const char* src, char* dst, uint64_t in_bytes) {
   const uint64_t blocks = (in_bytes + 8191u) / 8192u;
   for (uint64_t b = blockIdx.x; b < blocks; b += gridDim.x) {
@@ -142,22 +143,19 @@ __global__ __launch_bounds__(256) void stream_widen_kernel(const char* src, char
     const int range = static_cast<int>(left < 8192u ? left : 8192u);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src) + off, 0, range, 0x00020000);
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(dst + 2 * off, 0, 2 * range, 0x00020000);
-    u32x4 v[2];
+    u32x2 v[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (u * 256 + threadIdx.x) * 16, 0, 2);
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b64(rx, (u * 256 + threadIdx.x) * 8, 0, 2);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      _Float16 h[8];
-      __builtin_memcpy(h, &v[u], 16);
-      float f[8];
+    for (int u = 0; u < 4; ++u) {
+      _Float16 h[4];
+      __builtin_memcpy(h, &v[u], 8);
+      float f[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = static_cast<float>(h[e]);
-      u32x4 w0, w1;
-      __builtin_memcpy(&w0, f, 16);
-      __builtin_memcpy(&w1, f + 4, 16);
-      const int o = (u * 256 + threadIdx.x) * 32;
-      __builtin_amdgcn_raw_buffer_store_b128(w0, ry, o, 0, 2);
-      __builtin_amdgcn_raw_buffer_store_b128(w1, ry, o + 16, 0, 2);
+      for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(h[e]);
+      u32x4 w;
+      __builtin_memcpy(&w, f, 16);
+      __builtin_amdgcn_raw_buffer_store_b128(w, ry, (u * 256 + threadIdx.x) * 16, 0, 2);
     }
   }
 }

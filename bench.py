@@ -29,7 +29,6 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import re
 import sys
@@ -42,7 +41,6 @@ KERNEL_SOURCES = ["acp_dev_base.hpp", "acp_dev_ops.hpp", "acp_dev_map.hpp", "acp
                   "acp_dev_gen.hpp", "acp_engine_impl.hpp", "acp_engine.hpp", "acp_k_stream_f32.hip",
                   "acp_k_stream_f16.hip", "acp_k_tile.hip", "acp_k_tile_gen.hip", "acp_k_tile_lin.hip",
                   "acp_k_copy.hip", "acp_engine.hip", "acp_api.cpp"]
-SLAB = (500, 1024)                       # one [500, 1024] slab of the [128, 500, 1024] workloads
 
 
 def _code_only(text: str) -> str:

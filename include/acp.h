@@ -353,8 +353,9 @@ acp_status acp_debug_stream_fill(void* dst, int64_t bytes, uint32_t pattern, int
  * (not part of the pipelined path): dst[i] = (float)src[i] for `elements`
  * float16 values of contiguous device memory `src` into contiguous device
  * memory `dst` (exact: every float16 is a float32).  256-thread workgroups
- * take 8 KiB input blocks w, w+G, ... (two 16-byte non-temporal loads per
- * lane, four 16-byte non-temporal stores); `workgroups` 0 takes one per
+ * take 8 KiB input blocks w, w+G, ... (four 8-byte non-temporal loads per
+ * lane, each widened into one 16-byte non-temporal store, so every wave
+ * instruction covers a contiguous span); `workgroups` 0 takes one per
  * compute unit.  ACP_ERR_INVALID on null pointers, an element count that is
  * negative, not a multiple of 8 or at least 2^38, or overlapping buffers. */
 acp_status acp_debug_stream_widen(float* dst, const void* src, int64_t elements, int workgroups, void* hip_stream);
