@@ -303,7 +303,7 @@ def build(name, ctx, stages=None):
         out = dict(bytes=n * 6, dtype="f16->f32",
                    config={"workload": f"reference register-path f16 -> f32 widening stream of {n} elements "
                                        f"(the rank-5 exp workload's count, packed), {G} workgroups"},
-                   key="stream_widen_reference_33M")
+                   key="stream_widen_reference_67M")
     elif name in ("copy_ref", "read_ref", "write_ref"):
         nbytes = 128 * 500 * 1024 * 4
         for _ in range(sets):
