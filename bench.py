@@ -517,7 +517,8 @@ def fixed_cost(ctx):
                     px, py = xd.data_ptr() + s0 * slab_b, yd.data_ptr() + s0 * slab_b
                     fns.append(lambda px=px, py=py, nb=N * slab_b:
                                acp.acp_debug_stream_copy(py, px, nb, 256, ctx.stream))
-            for i in range(2 * len(fns)):
+            warm = 2 * len(fns)
+            for i in range(warm):
                 fns[i % len(fns)]()
             torch.cuda.synchronize()
             steps = max(60, len(fns))
@@ -532,7 +533,8 @@ def fixed_cost(ctx):
             med_us = t[len(t) // 2] * 1e3
             nbytes = N * (2 * slab_b + (1000 * 4 if kind == "ring" else 0))
             pts.append((nbytes, med_us))
-            res["points"].setdefault(kind, []).append({"slabs": N, "bytes": nbytes, "median_us": round(med_us, 2)})
+            res["points"].setdefault(kind, []).append({"slabs": N, "bytes": nbytes, "median_us": round(med_us, 2),
+                                                       "warmup_launches": warm, "timed_launches": steps})
         fixed, per_byte = _fit(pts)
         res[kind] = {"fixed_us": round(fixed, 2), "rate_GBps": round(1e-3 / per_byte, 1)}
     print(json.dumps(res), flush=True)
