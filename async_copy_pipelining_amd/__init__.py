@@ -95,6 +95,7 @@ _SIGS = {
     "acp_debug_stream_read": ([_P, ctypes.c_int64, _P, _I, _P], _I),
     "acp_debug_stream_fill": ([_P, ctypes.c_int64, ctypes.c_uint32, _I, _P], _I),
     "acp_debug_stream_widen": ([_P, _P, ctypes.c_int64, _I, _P], _I),
+    "acp_debug_widen_tiles": ([_P, _P, _P, _P, _P, _P, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -228,3 +229,9 @@ def acp_debug_stream_fill(dst, nbytes: int, pattern: int, workgroups: int = 0, s
 
 def acp_debug_stream_widen(dst, src, elements: int, workgroups: int = 0, stream=None) -> None:
     _check(_lib.acp_debug_stream_widen(_ptr(dst), _ptr(src), int(elements), int(workgroups), _stream(stream)))
+
+
+def acp_debug_widen_tiles(dst, src, shape, src_strides, box, stage_box, stream=None) -> None:
+    arr64, arr32 = ctypes.c_int64 * 5, ctypes.c_int32 * 5
+    _check(_lib.acp_debug_widen_tiles(_ptr(dst), _ptr(src), arr64(*shape), arr64(*src_strides), arr32(*box),
+                                      arr32(*stage_box), _stream(stream)))

@@ -1369,4 +1369,41 @@ acp_status acp_debug_stream_widen(float* dst, const void* src, int64_t elements,
   return ret(ACP_OK);
 }
 
+acp_status acp_debug_widen_tiles(float* dst, const void* src, const int64_t* shape, const int64_t* src_strides,
+                                 const int32_t* box, const int32_t* stage_box, void* hip_stream) {
+  if (!dst || !src || !shape || !src_strides || !box || !stage_box) return ret(ACP_ERR_INVALID, "null argument");
+  if (src_strides[4] != 1) return ret(ACP_ERR_INVALID, "innermost source stride must be 1");
+  int64_t in_b[5], out_b[5], span_in = 2, n_tiles = 1, st = 4;
+  uint32_t tgrid[5], bx[5], sb[5];
+  for (int d = 4; d >= 0; --d) {
+    if (shape[d] < 1 || box[d] < 1 || stage_box[d] < 1 || src_strides[d] < 1)
+      return ret(ACP_ERR_INVALID, "extents, strides and boxes must be >= 1");
+    if (shape[d] % box[d] != 0 || box[d] % stage_box[d] != 0)
+      return ret(ACP_ERR_INVALID, "tiles and stages must be whole");
+    if (d < 3 && stage_box[d] != 1) return ret(ACP_ERR_INVALID, "a stage spans the two innermost dims only");
+    in_b[d] = src_strides[d] * 2;
+    out_b[d] = st;
+    st *= shape[d];
+    span_in += (shape[d] - 1) * in_b[d];
+    tgrid[d] = static_cast<uint32_t>(shape[d] / box[d]);
+    bx[d] = static_cast<uint32_t>(box[d]);
+    sb[d] = static_cast<uint32_t>(stage_box[d]);
+    n_tiles *= shape[d] / box[d];
+  }
+  if (stage_box[4] % 4 != 0 || static_cast<int64_t>(stage_box[3]) * stage_box[4] / 4 > 2048)
+    return ret(ACP_ERR_INVALID, "a stage row must hold whole 4-element pieces, at most 2048 per stage");
+  for (int d = 0; d < 4; ++d)
+    if (in_b[d] % 8 != 0) return ret(ACP_ERR_INVALID, "source strides must be 8-byte multiples");
+  if (reinterpret_cast<uint64_t>(src) % 8 != 0 || reinterpret_cast<uint64_t>(dst) % 16 != 0)
+    return ret(ACP_ERR_INVALID, "source must be 8-byte and destination 16-byte aligned");
+  if (n_tiles >= (int64_t(1) << 31)) return ret(ACP_ERR_INVALID, "too many tiles");
+  const char* s = static_cast<const char*>(src);
+  const char* o = reinterpret_cast<const char*>(dst);
+  if (s < o + st && o < s + span_in) return ret(ACP_ERR_INVALID, "source and destination overlap");
+  const hipError_t e = acp::widen_tiles_launch(src, dst, in_b, out_b, tgrid, bx, sb, static_cast<uint32_t>(n_tiles),
+                                               static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ret(ACP_OK);
+}
+
 }  // extern "C"

@@ -160,7 +160,111 @@ __global__ __launch_bounds__(256) void stream_widen_kernel(const char* src, char
   }
 }
 
+// Measurement reference with the walk of a tiled widening stream: tiles of a
+// rank-5 float16 tensor (any strides, innermost 1) go to float32 in a packed
+// output with no LDS and no ring.  Workgroup b takes the tile whose index is
+// b remapped so that consecutive tiles run on one XCD (as the library's
+// streams do when the tile count is a multiple of 8), and walks the tile's
+// stages in row-major order; a stage is stage_rows rows of stage_cols
+// elements (the two innermost dims).  Each lane takes 4-element pieces (up
+// to eight per stage): two stages per iteration, their 8-byte loads in
+// flight together, each piece widened into one 16-byte non-temporal store.
+// Geometry (validated on the host): stage_cols a multiple of 4, at most 2048
+// pieces per stage, every tile and stage whole, 8-byte aligned input rows.
+struct WidenTilesArgs {
+  const char* src;
+  char* dst;
+  int64_t in_stride[5], out_stride[5];  // bytes
+  uint32_t tgrid[5], box[5], sbox[5], sub[5];
+  uint32_t n_tiles, subs, remap;
+};
+
+__global__ __launch_bounds__(256) void widen_tiles_kernel(const WidenTilesArgs A) {
+  uint32_t b = blockIdx.x;
+  const uint32_t grid = gridDim.x;
+  if (A.remap) b = (b % 8u) * (grid / 8u) + b / 8u;
+  if (b >= A.n_tiles) return;
+  // tile coordinates, last dim fastest
+  uint32_t tc[5], t = b;
+  for (int d = 4; d >= 0; --d) {
+    tc[d] = t % A.tgrid[d];
+    t /= A.tgrid[d];
+  }
+  const uint32_t cols = A.sbox[4], rows = A.sbox[3];
+  const uint32_t pieces_per_row = cols / 4u;
+  const uint32_t pieces = rows * pieces_per_row;
+  for (uint32_t j0 = 0; j0 < A.subs; j0 += 2) {
+    u32x2 v[2][8];
+    int64_t ob[2];
+    uint32_t np = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t j = j0 + h;
+      if (j >= A.subs) break;
+      // stage coordinates inside the tile, last dim fastest
+      uint32_t sj = j, sc[5];
+      for (int d = 4; d >= 0; --d) {
+        sc[d] = sj % A.sub[d];
+        sj /= A.sub[d];
+      }
+      int64_t ib = 0, o = 0;
+      for (int d = 0; d < 5; ++d) {
+        const int64_t c = static_cast<int64_t>(tc[d]) * A.box[d] + static_cast<int64_t>(sc[d]) * A.sbox[d];
+        ib += c * A.in_stride[d];
+        o += c * A.out_stride[d];
+      }
+      ob[h] = o;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t p = u * 256u + threadIdx.x;
+        const uint32_t r = p / pieces_per_row, q = p % pieces_per_row;
+        if (p < pieces)
+          v[h][u] = *reinterpret_cast<const u32x2*>(A.src + ib + r * A.in_stride[3] + q * 8u);
+      }
+      ++np;
+    }
+    for (uint32_t h = 0; h < np; ++h) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t p = u * 256u + threadIdx.x;
+        if (p >= pieces) continue;
+        const uint32_t r = p / pieces_per_row, q = p % pieces_per_row;
+        _Float16 hh[4];
+        __builtin_memcpy(hh, &v[h][u], 8);
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(hh[e]);
+        u32x4 w;
+        __builtin_memcpy(&w, f, 16);
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(A.dst + ob[h] + r * A.out_stride[3] + q * 16u));
+      }
+    }
+  }
+}
+
 }  // namespace dev
+
+hipError_t widen_tiles_launch(const void* src, void* dst, const int64_t* in_stride_b, const int64_t* out_stride_b,
+                              const uint32_t* tgrid, const uint32_t* box, const uint32_t* sbox, uint32_t n_tiles,
+                              hipStream_t stream) {
+  dev::WidenTilesArgs A{};
+  A.src = static_cast<const char*>(src);
+  A.dst = static_cast<char*>(dst);
+  A.subs = 1;
+  for (int d = 0; d < 5; ++d) {
+    A.in_stride[d] = in_stride_b[d];
+    A.out_stride[d] = out_stride_b[d];
+    A.tgrid[d] = tgrid[d];
+    A.box[d] = box[d];
+    A.sbox[d] = sbox[d];
+    A.sub[d] = box[d] / sbox[d];
+    A.subs *= A.sub[d];
+  }
+  A.n_tiles = n_tiles;
+  A.remap = (n_tiles % 8 == 0 && n_tiles >= 16) ? 1u : 0u;
+  hipLaunchKernelGGL(dev::widen_tiles_kernel, dim3(n_tiles), dim3(256), 0, stream, A);
+  return hipGetLastError();
+}
 
 hipError_t stream_widen_launch(const void* src, void* dst, uint64_t in_bytes, unsigned grid, hipStream_t stream) {
   hipLaunchKernelGGL(dev::stream_widen_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const char*>(src),

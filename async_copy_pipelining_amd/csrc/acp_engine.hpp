@@ -125,6 +125,9 @@ hipError_t stream_copy_launch(const void* src, void* dst, uint64_t bytes, unsign
 hipError_t stream_read_launch(const void* src, uint64_t bytes, void* sums, unsigned grid, hipStream_t stream);
 hipError_t stream_fill_launch(void* dst, uint64_t bytes, uint32_t pattern, unsigned grid, hipStream_t stream);
 hipError_t stream_widen_launch(const void* src, void* dst, uint64_t in_bytes, unsigned grid, hipStream_t stream);
+hipError_t widen_tiles_launch(const void* src, void* dst, const int64_t* in_stride_b, const int64_t* out_stride_b,
+                              const uint32_t* tgrid, const uint32_t* box, const uint32_t* sbox, uint32_t n_tiles,
+                              hipStream_t stream);
 hipError_t ring_trace_launch(int n_iters, int stages, int loads, int stores, int32_t* out,
                              hipStream_t stream);
 

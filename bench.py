@@ -19,8 +19,8 @@ runs on) and the CPU oracle timed on a bounded sample of the same workload.
 
 Other modes (measurement aids):
   --workload NAME   one workload alone (c1 c2 c3 c5, the references copy_ref /
-                    read_ref / write_ref / widen_ref, calib, and pointwise /
-                    reduce / rowsum)
+                    read_ref / write_ref / widen_ref / widen_tiles_ref, calib,
+                    and pointwise / reduce / rowsum)
   --fixed-cost      the streamed fma and the reference copy over 1..128 slabs of
                     the tensor: per-launch fixed cost and per-byte rate of each
 """
@@ -86,7 +86,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None,
                     choices=["c1", "c2", "c3", "c4", "c5", "calib", "copy_ref", "read_ref", "write_ref", "widen_ref",
-                             "pointwise",
+                             "widen_tiles_ref", "pointwise",
                              "reduce", "rowsum"],
                     help="measure one workload alone (default: c4 with ring_stages and configs); calib: torch's "
                          "copy of 256 MiB, the known-size kernel that scales HBM counters; copy_ref / read_ref / "
@@ -304,6 +304,21 @@ def build(name, ctx, stages=None):
                    config={"workload": f"reference register-path f16 -> f32 widening stream of {n} elements "
                                        f"(the rank-5 exp workload's count, packed), {G} workgroups"},
                    key="stream_widen_reference_67M")
+    elif name == "widen_tiles_ref":
+        # the rank-5 exp workload's walk (tiles (1,2,16,64,64), stages
+        # (1,1,1,64,64), row pitch 264) as a plain register-path widening copy
+        shape, pitch = (4, 8, 64, 128, 256), 264
+        storage, strides = W.padded_uniform_f16(shape, pitch=pitch, seed=5)
+        n = int(np.prod(shape))
+        for _ in range(sets):
+            xd, yd = ctx.to_dev(storage), ctx.empty(n * 4)
+            launches.append(lambda xd=xd, yd=yd: acp.acp_debug_widen_tiles(
+                yd, xd, shape, strides, (1, 2, 16, 64, 64), (1, 1, 1, 64, 64), stream))
+        out = dict(bytes=n * 6, dtype="f16->f32",
+                   config={"workload": "reference register-path widening copy with the rank-5 exp workload's walk: "
+                                       "(4,8,64,128,256) f16 pitch 264 -> f32, tiles (1,2,16,64,64), stages "
+                                       "(1,1,1,64,64), one workgroup per tile"},
+                   key="widen_tiles_reference_rank5")
     elif name in ("copy_ref", "read_ref", "write_ref"):
         nbytes = 128 * 500 * 1024 * 4
         for _ in range(sets):

@@ -360,6 +360,23 @@ acp_status acp_debug_stream_fill(void* dst, int64_t bytes, uint32_t pattern, int
  * negative, not a multiple of 8 or at least 2^38, or overlapping buffers. */
 acp_status acp_debug_stream_widen(float* dst, const void* src, int64_t elements, int workgroups, void* hip_stream);
 
+/* Measurement reference with the walk of a tiled widening stream (not part
+ * of the pipelined path): dst = (float)src over a rank-5 float16 tensor
+ * `src` (element `src_strides`, innermost 1, 8-byte multiples in bytes) into
+ * a packed float32 tensor `dst` of the same `shape`, with no LDS and no
+ * ring.  One 256-thread workgroup per `box` tile (consecutive tiles on one
+ * XCD when the tile count is a multiple of 8) walks the tile's `stage_box`
+ * stages in row-major order; a stage spans the two innermost dims only.
+ * Each lane takes 4-element pieces of a stage (8-byte loads, two stages in
+ * flight) and writes each as one 16-byte non-temporal store.  It gives the
+ * rate a plain register-path stream reaches over the same tiles, stages and
+ * row pitch as acp_stream_ewise's widening ops.  ACP_ERR_INVALID unless
+ * every tile and stage is whole, a stage row holds whole 4-element pieces
+ * (at most 2048 per stage), src is 8-byte and dst 16-byte aligned, and the
+ * two do not overlap. */
+acp_status acp_debug_widen_tiles(float* dst, const void* src, const int64_t* shape, const int64_t* src_strides,
+                                 const int32_t* box, const int32_t* stage_box, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -338,3 +338,21 @@ def test_reference_widening_stream():
     y = host(yd, np.uint8)
     assert np.array_equal(y[:n * 4].view(np.float32), x.astype(np.float32))
     assert np.all(y[n * 4:] == 0x11)
+
+
+@pytest.mark.parametrize("shape,box,stage", [
+    ((2, 4, 16, 128, 256), (1, 2, 16, 64, 64), (1, 1, 1, 64, 64)),   # the rank-5 exp walk, reduced
+    ((1, 2, 3, 40, 96), (1, 1, 3, 20, 48), (1, 1, 1, 10, 48)),       # 12 pieces per row, 120 per stage
+])
+def test_reference_widening_tile_walk(shape, box, stage):
+    # the same-walk widening reference converts every element exactly into a
+    # packed float32 output (row pitch 264 on the input: padding never read)
+    say(f"reference tiled widening {shape} box {box} stage {stage}")
+    storage, strides = W.padded_uniform_f16(shape, pitch=shape[-1] + 8, seed=34)
+    n = int(np.prod(shape))
+    xd, yd = dev(storage), empty_bytes(n * 4 + 64, 0x11)
+    acp.acp_debug_widen_tiles(yd, xd, shape, strides, box, stage, stream())
+    y = host(yd, np.uint8)
+    want = W.strided_view(storage, shape, strides).astype(np.float32)
+    assert np.array_equal(y[:n * 4].view(np.float32).reshape(shape), want)
+    assert np.all(y[n * 4:] == 0x11)
