@@ -92,6 +92,7 @@ _SIGS = {
     "acp_debug_lds_image": ([_DESC_P, ctypes.c_int64, _I, _P, _P], _I),
     "acp_debug_ring_trace": ([_I, _I, _I, _I, _P, _P], _I),
     "acp_debug_stream_copy": ([_P, _P, ctypes.c_int64, _I, _P], _I),
+    "acp_debug_stream_copy_shape": ([_P, _P, ctypes.c_int64, _I, _I, _I, _I, _I, _P], _I),
     "acp_debug_stream_read": ([_P, ctypes.c_int64, _P, _I, _P], _I),
     "acp_debug_stream_fill": ([_P, ctypes.c_int64, ctypes.c_uint32, _I, _P], _I),
     "acp_debug_stream_widen": ([_P, _P, ctypes.c_int64, _I, _P], _I),
@@ -216,6 +217,12 @@ def acp_debug_ring_trace(n_iters: int, stages: int, loads: int, stores: int, out
 
 def acp_debug_stream_copy(dst, src, nbytes: int, workgroups: int = 0, stream=None) -> None:
     _check(_lib.acp_debug_stream_copy(_ptr(dst), _ptr(src), int(nbytes), int(workgroups), _stream(stream)))
+
+
+def acp_debug_stream_copy_shape(dst, src, nbytes: int, workgroups: int, threads: int, unroll: int,
+                                load_nt: int = 1, store_nt: int = 1, stream=None) -> None:
+    _check(_lib.acp_debug_stream_copy_shape(_ptr(dst), _ptr(src), int(nbytes), int(workgroups), int(threads),
+                                            int(unroll), int(load_nt), int(store_nt), _stream(stream)))
 
 
 def acp_debug_stream_read(src, nbytes: int, sums, workgroups: int = 0, stream=None) -> None:

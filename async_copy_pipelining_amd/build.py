@@ -35,6 +35,7 @@ SOURCES = [
     ("acp_k_tile_lin.hip", True),
     ("acp_k_stream_f32.hip", True),
     ("acp_k_stream_f16.hip", True),
+    ("acp_k_ref.hip", True),
 ]
 
 

@@ -1317,6 +1317,30 @@ acp_status acp_debug_stream_copy(void* dst, const void* src, int64_t bytes, int 
   return ret(ACP_OK);
 }
 
+acp_status acp_debug_stream_copy_shape(void* dst, const void* src, int64_t bytes, int workgroups, int threads,
+                                       int unroll, int load_nt, int store_nt, void* hip_stream) {
+  if (!dst || !src || bytes < 0 || workgroups < 0) return ret(ACP_ERR_INVALID, "bad stream copy arguments");
+  if ((load_nt != 0 && load_nt != 1) || (store_nt != 0 && store_nt != 1))
+    return ret(ACP_ERR_INVALID, "cache policies are 0 (default) or 1 (non-temporal)");
+  if (bytes % 16 != 0) return ret(ACP_ERR_INVALID, "stream copy moves whole 16-byte units");
+  if (bytes >= (int64_t(1) << 40)) return ret(ACP_ERR_INVALID, "stream copy size out of range");
+  const char* s = static_cast<const char*>(src);
+  const char* d = static_cast<const char*>(dst);
+  if (s < d + bytes && d < s + bytes) return ret(ACP_ERR_INVALID, "source and destination overlap");
+  const void* kernel = acp::copy_shape_kernel_for(threads, unroll, load_nt, store_nt);
+  if (!kernel) return ret(ACP_ERR_UNSUPPORTED, "no reference copy kernel of that shape is built");
+  if (bytes == 0) return ret(ACP_OK);
+  const int64_t block = static_cast<int64_t>(threads) * unroll * 16;
+  const int64_t blocks = (bytes + block - 1) / block;
+  int64_t grid = workgroups > 0 ? workgroups : device_cu_count();
+  if (grid > blocks) grid = blocks;
+  const hipError_t e = acp::copy_shape_launch(kernel, src, dst, static_cast<uint64_t>(bytes),
+                                              static_cast<unsigned>(grid), static_cast<unsigned>(threads),
+                                              static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ret(ACP_OK);
+}
+
 // grid of a reference stream: `workgroups` (0: one per compute unit), at
 // most one per 16 KiB block
 unsigned ref_grid(int64_t bytes, int workgroups) {

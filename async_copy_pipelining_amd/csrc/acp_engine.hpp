@@ -128,6 +128,11 @@ hipError_t stream_widen_launch(const void* src, void* dst, uint64_t in_bytes, un
 hipError_t widen_tiles_launch(const void* src, void* dst, const int64_t* in_stride_b, const int64_t* out_stride_b,
                               const uint32_t* tgrid, const uint32_t* box, const uint32_t* sbox, uint32_t n_tiles,
                               hipStream_t stream);
+// Reference copies of other shapes: the kernel for (threads, unroll, cache
+// policies), or nullptr when that combination is not built.
+const void* copy_shape_kernel_for(int threads, int unroll, int load_nt, int store_nt);
+hipError_t copy_shape_launch(const void* kernel, const void* src, void* dst, uint64_t bytes, unsigned grid,
+                             unsigned threads, hipStream_t stream);
 hipError_t ring_trace_launch(int n_iters, int stages, int loads, int stores, int32_t* out,
                              hipStream_t stream);
 

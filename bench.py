@@ -40,7 +40,7 @@ PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["acp_dev_base.hpp", "acp_dev_ops.hpp", "acp_dev_map.hpp", "acp_dev_engine.hpp", "acp_dev_lin.hpp",
                   "acp_dev_gen.hpp", "acp_engine_impl.hpp", "acp_engine.hpp", "acp_k_stream_f32.hip",
                   "acp_k_stream_f16.hip", "acp_k_tile.hip", "acp_k_tile_gen.hip", "acp_k_tile_lin.hip",
-                  "acp_k_copy.hip", "acp_engine.hip", "acp_api.cpp"]
+                  "acp_k_copy.hip", "acp_k_ref.hip", "acp_engine.hip", "acp_api.cpp"]
 
 
 def _code_only(text: str) -> str:
@@ -113,6 +113,8 @@ def parse():
     ap.add_argument("--no-configs", action="store_true", help="default run: skip the other workloads")
     ap.add_argument("--fixed-cost", action="store_true",
                     help="fit launch time = fixed + bytes / rate over 1..128 slabs (streamed fma, reference copy)")
+    ap.add_argument("--copy-sweep", action="store_true",
+                    help="plain register-path copies of 262 MB in other shapes, cache policies and grids")
     args = ap.parse_args()
     return args
 
@@ -429,6 +431,9 @@ def main():
     if args.fixed_cost:
         fixed_cost(ctx)
         return
+    if args.copy_sweep:
+        copy_sweep(ctx)
+        return
     name = args.workload or "c4"
     wl = build(name, ctx)
     fns = wl["launches"]
@@ -553,6 +558,36 @@ def fixed_cost(ctx):
         fixed, per_byte = _fit(pts)
         res[kind] = {"fixed_us": round(fixed, 2), "rate_GBps": round(1e-3 / per_byte, 1)}
     print(json.dumps(res), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Copy sweep: what a plain register-path copy of the reference copy's bytes
+# reaches in other shapes (threads x 16-byte loads per lane), cache policies
+# and grids, over the same rotated buffer sets as every workload.  The
+# reference copy's own shape is 256 x 4 with non-temporal loads and stores.
+
+COPY_SWEEP_SHAPES = ((256, 4), (256, 2), (256, 8), (512, 2), (512, 4), (512, 8), (1024, 2), (1024, 4),
+                     (128, 8), (64, 16))
+COPY_SWEEP_GRIDS = (256, 512, 1024, 4096)
+
+
+def copy_sweep(ctx):
+    args, acp, torch = ctx.args, ctx.acp, ctx.torch
+    n = 262144000
+    bufs = [(torch.full((n,), 1 + i, dtype=torch.uint8, device=ctx.dev), ctx.empty(n)) for i in range(args.sets)]
+    points = []
+    for threads, unroll in COPY_SWEEP_SHAPES:
+        policies = ((1, 1), (1, 0), (0, 1), (0, 0)) if (threads, unroll) == (256, 4) else ((1, 1),)
+        for lnt, snt in policies:
+            for G in COPY_SWEEP_GRIDS:
+                fns = [lambda x=x, y=y, G=G, t=threads, u=unroll, l=lnt, s=snt:
+                       acp.acp_debug_stream_copy_shape(y, x, n, G, t, u, l, s, ctx.stream) for x, y in bufs]
+                avg = time_launches(ctx, fns, args.steps, args.warmup)
+                points.append({"threads": threads, "unroll": unroll, "load_nt": lnt, "store_nt": snt,
+                               "workgroups": G, "avg_launch_us": round(avg * 1e3, 2),
+                               "GBps": round(2 * n / (avg * 1e-3) / 1e9, 1)})
+    print(json.dumps({"workload": "plain register-path copy of 262 144 000 B, shapes x cache policies x grids",
+                      "sets": args.sets, "steps": args.steps, "warmup": args.warmup, "points": points}), flush=True)
 
 
 # ---------------------------------------------------------------------------

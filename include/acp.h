@@ -332,6 +332,21 @@ acp_status acp_debug_ring_trace(int n_iters, int stages, int loads, int stores, 
  * overlapping buffers. */
 acp_status acp_debug_stream_copy(void* dst, const void* src, int64_t bytes, int workgroups, void* hip_stream);
 
+/* Measurement reference (not part of the pipelined path): acp_debug_stream_copy
+ * in other shapes and cache policies, so that a sweep shows what a plain
+ * register-path copy reaches on the device.  Workgroups of `threads` lanes
+ * copy blocks of threads * unroll * 16 bytes w, w+G, ... (each lane issues
+ * `unroll` 16-byte loads, then the stores); `load_nt` / `store_nt` 1 give
+ * the loads / stores the non-temporal cache policy, 0 the default one;
+ * `workgroups` 0 takes one per compute unit (never more than the blocks).
+ * Built shapes (threads x unroll): 64x16, 128x8, 256x2, 256x4, 256x8,
+ * 512x2, 512x4, 512x8, 1024x2, 1024x4, each with the four policy pairs;
+ * 256x4 with both policies non-temporal is acp_debug_stream_copy's kernel
+ * shape.  ACP_ERR_UNSUPPORTED for any other combination; ACP_ERR_INVALID as
+ * for acp_debug_stream_copy, or for policies other than 0 / 1. */
+acp_status acp_debug_stream_copy_shape(void* dst, const void* src, int64_t bytes, int workgroups, int threads,
+                                       int unroll, int load_nt, int store_nt, void* hip_stream);
+
 /* Measurement references for one direction (not part of the pipelined
  * path), with acp_debug_stream_copy's walk: 256-thread workgroups, 16 KiB
  * blocks w, w+G, ..., four 16-byte non-temporal accesses per lane;

@@ -257,6 +257,40 @@ def test_reference_stream_copy_is_bit_identical(nbytes, workgroups):
     assert np.all(y[nbytes:] == 0x5A)      # nothing written past the end
 
 
+COPY_SHAPES = [(64, 16), (128, 8), (256, 2), (256, 4), (256, 8), (512, 2), (512, 4), (512, 8), (1024, 2),
+               (1024, 4)]
+
+
+def test_reference_copy_shapes_are_bit_identical():
+    # every built shape and cache-policy pair of the copy sweep moves exactly
+    # the requested bytes: a short last block, grids below and above the
+    # block count
+    nbytes = (1 << 20) + 16 * 37
+    say(f"reference copy shapes over {nbytes} bytes")
+    rng = np.random.default_rng(32)
+    x = rng.integers(0, 256, nbytes + 64, dtype=np.uint8)
+    xd = dev(x)
+    for threads, unroll in COPY_SHAPES:
+        for lnt, snt in ((1, 1), (1, 0), (0, 1), (0, 0)):
+            for wgs in (0, 3, 4096):
+                yd = empty_bytes(nbytes + 64, 0x5A)
+                acp.acp_debug_stream_copy_shape(yd, xd, nbytes, wgs, threads, unroll, lnt, snt, stream())
+                y = host(yd, np.uint8)
+                assert np.array_equal(y[:nbytes], x[:nbytes]), (threads, unroll, lnt, snt, wgs)
+                assert np.all(y[nbytes:] == 0x5A), (threads, unroll, lnt, snt, wgs)
+
+
+def test_reference_copy_shape_rejects_unbuilt_shapes():
+    xd, yd = empty_bytes(4096, 1), empty_bytes(4096, 2)
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_debug_stream_copy_shape(yd, xd, 4096, 0, 256, 3, 1, 1, stream())
+    assert e.value.status == acp.ACP_ERR_UNSUPPORTED
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_debug_stream_copy_shape(yd, xd, 4096, 0, 256, 4, 2, 1, stream())
+    assert e.value.status == acp.ACP_ERR_INVALID
+    assert np.all(host(yd, np.uint8) == 2)
+
+
 def _reduce_case(dt, src_shape, dst_shape, box, threads, values, swz=0, seed=51):
     npdt = {"u32": np.uint32, "f32": np.float32, "f16": np.float16}[dt]
     rng = np.random.default_rng(seed)
