@@ -93,6 +93,7 @@ _SIGS = {
     "acp_debug_ring_trace": ([_I, _I, _I, _I, _P, _P], _I),
     "acp_debug_stream_copy": ([_P, _P, ctypes.c_int64, _I, _P], _I),
     "acp_debug_stream_copy_shape": ([_P, _P, ctypes.c_int64, _I, _I, _I, _I, _I, _P], _I),
+    "acp_debug_copy_tiles": ([_P, _P, _I, _P, _P, _P, _I, _I, _I, _P], _I),
     "acp_debug_stream_read": ([_P, ctypes.c_int64, _P, _I, _P], _I),
     "acp_debug_stream_fill": ([_P, ctypes.c_int64, ctypes.c_uint32, _I, _P], _I),
     "acp_debug_stream_widen": ([_P, _P, ctypes.c_int64, _I, _P], _I),
@@ -223,6 +224,14 @@ def acp_debug_stream_copy_shape(dst, src, nbytes: int, workgroups: int, threads:
                                 load_nt: int = 1, store_nt: int = 1, stream=None) -> None:
     _check(_lib.acp_debug_stream_copy_shape(_ptr(dst), _ptr(src), int(nbytes), int(workgroups), int(threads),
                                             int(unroll), int(load_nt), int(store_nt), _stream(stream)))
+
+
+def acp_debug_copy_tiles(dst, src, esize: int, shape, src_strides, box, tiles_per_trip: int = 2, threads: int = 128,
+                         workgroups: int = 0, stream=None) -> None:
+    arr64 = ctypes.c_int64 * 3
+    arr32 = ctypes.c_int32 * 3
+    _check(_lib.acp_debug_copy_tiles(_ptr(dst), _ptr(src), int(esize), arr64(*shape), arr64(*src_strides),
+                                     arr32(*box), int(tiles_per_trip), int(threads), int(workgroups), _stream(stream)))
 
 
 def acp_debug_stream_read(src, nbytes: int, sums, workgroups: int = 0, stream=None) -> None:

@@ -534,8 +534,12 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   unsigned grid = static_cast<unsigned>(n_tiles);
   if (q.workgroups > 0) grid = static_cast<unsigned>(q.workgroups);
   // consecutive tiles (which often share cache lines at their edges) run on
-  // one XCD and hence one L2: blockIdx b -> (b % 8) * (G / 8) + b / 8
-  A.xcd_remap = (grid % 8 == 0 && grid >= 16 && xcd_remap_enabled()) ? 1 : 0;
+  // one XCD and hence one L2: blockIdx b -> (b % 8) * (G / 8) + b / 8.
+  // Copies whose staged rows are whole 128-byte lines share no line with
+  // their neighbours and measured faster without it (128x32 float16 tiles
+  // in pairs over [128,500,1024]: 4.69 TB/s against 4.48).
+  const bool whole_lines = q.mode == 0 && (static_cast<int64_t>(q.stage_box[r - 1]) * ei) % 128 == 0;
+  A.xcd_remap = (grid % 8 == 0 && grid >= 16 && xcd_remap_enabled() && !whole_lines) ? 1 : 0;
   L->grid = grid;
   L->block = static_cast<unsigned>(q.threads);
   L->lds = static_cast<unsigned>(lds);
@@ -1337,6 +1341,52 @@ acp_status acp_debug_stream_copy_shape(void* dst, const void* src, int64_t bytes
   const hipError_t e = acp::copy_shape_launch(kernel, src, dst, static_cast<uint64_t>(bytes),
                                               static_cast<unsigned>(grid), static_cast<unsigned>(threads),
                                               static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ret(ACP_OK);
+}
+
+acp_status acp_debug_copy_tiles(void* dst, const void* src, int esize, const int64_t* shape,
+                                const int64_t* src_strides, const int32_t* box, int tiles_per_trip, int threads,
+                                int workgroups, void* hip_stream) {
+  if (!dst || !src || !shape || !src_strides || !box || workgroups < 0) return ret(ACP_ERR_INVALID, "null argument");
+  if (esize != 1 && esize != 2 && esize != 4 && esize != 8) return ret(ACP_ERR_INVALID, "element size 1, 2, 4 or 8");
+  if (tiles_per_trip != 1 && tiles_per_trip != 2 && tiles_per_trip != 4)
+    return ret(ACP_ERR_INVALID, "tiles per trip 1, 2 or 4");
+  if (threads != 128 && threads != 256) return ret(ACP_ERR_INVALID, "threads 128 or 256");
+  for (int d = 0; d < 3; ++d)
+    if (shape[d] < 1 || src_strides[d] < 1 || box[d] < 1)
+      return ret(ACP_ERR_INVALID, "extents, strides and boxes must be >= 1");
+  if (src_strides[2] != 1) return ret(ACP_ERR_INVALID, "innermost source stride must be 1");
+  if (box[0] != 1) return ret(ACP_ERR_INVALID, "a tile spans one index of dim 0");
+  const int64_t row_bytes = shape[2] * esize;
+  const int64_t group_bytes = static_cast<int64_t>(tiles_per_trip) * box[2] * esize;
+  if (row_bytes % 16 != 0 || group_bytes % 16 != 0)
+    return ret(ACP_ERR_INVALID, "rows and tile groups must be whole 16-byte chunks");
+  if (static_cast<int64_t>(box[1]) * (group_bytes / 16) > 8 * static_cast<int64_t>(threads))
+    return ret(ACP_ERR_INVALID, "a tile group holds at most 8 chunks of 16 bytes per lane");
+  const int64_t in_b[2] = {src_strides[0] * esize, src_strides[1] * esize};
+  const int64_t out_b[2] = {shape[1] * row_bytes, row_bytes};
+  if (in_b[0] % 16 != 0 || in_b[1] % 16 != 0) return ret(ACP_ERR_INVALID, "source strides must be 16-byte multiples");
+  if (reinterpret_cast<uint64_t>(src) % 16 != 0 || reinterpret_cast<uint64_t>(dst) % 16 != 0)
+    return ret(ACP_ERR_INVALID, "source and destination must be 16-byte aligned");
+  if ((box[1] - 1) * std::max(in_b[1], out_b[1]) + group_bytes >= (int64_t(1) << 31) || row_bytes >= (int64_t(1) << 31))
+    return ret(ACP_ERR_INVALID, "a tile group spans 2 GiB or more");
+  const int64_t tiles_1 = (shape[1] + box[1] - 1) / box[1];
+  const int64_t groups_2 = (row_bytes + group_bytes - 1) / group_bytes;
+  const int64_t n_groups = shape[0] * tiles_1 * groups_2;
+  if (n_groups >= (int64_t(1) << 31) || shape[1] >= (int64_t(1) << 31)) return ret(ACP_ERR_INVALID, "too many tiles");
+  const int64_t span_in = (shape[0] - 1) * in_b[0] + (shape[1] - 1) * in_b[1] + row_bytes;
+  const int64_t span_out = shape[0] * out_b[0];
+  const char* s = static_cast<const char*>(src);
+  const char* o = static_cast<const char*>(dst);
+  if (s < o + span_out && o < s + span_in) return ret(ACP_ERR_INVALID, "source and destination overlap");
+  int64_t grid = workgroups > 0 ? workgroups : device_cu_count();
+  if (grid > n_groups) grid = n_groups;
+  const hipError_t e = acp::copy_tiles_launch(
+      src, dst, in_b, out_b, static_cast<uint32_t>(shape[1]), static_cast<uint32_t>(row_bytes),
+      static_cast<uint32_t>(box[1]), static_cast<uint32_t>(group_bytes), static_cast<uint32_t>(tiles_1),
+      static_cast<uint32_t>(groups_2), static_cast<uint32_t>(n_groups), static_cast<unsigned>(threads),
+      static_cast<unsigned>(grid), static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return ret(ACP_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return ret(ACP_OK);
 }

@@ -58,7 +58,7 @@ __device__ __forceinline__ uint32_t rdl(uint32_t v, uint32_t lane) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), static_cast<int>(lane)));
 }
 
-template <class OP, int MODE, int OUTER, bool SROW, int ZSET = 0, bool GROUP = false>
+template <class OP, int MODE, int OUTER, bool SROW, int ZSET = 0, bool GROUP = false, bool NT = false>
 struct GenPolicy {
   static constexpr bool STAGE_OUT = (MODE == 1);
   // staged operands: every input of a tile op or of a two-tensor stream op;
@@ -94,7 +94,7 @@ struct GenPolicy {
   bool one_row;      // wave-local: all of the wave's blocks lie in one row
   uint32_t lrow, loff, lbad;
   int wave, lane, rank, ab_instr, swizzle, esize_log2;
-  bool load_nt, store_nt;
+  bool load_nt, store_nt;  // NT: both known to be set
   uint32_t xoff[OUTER], ooff[OUTER], oobm[OUTER], lpos[OUTER], abo[OUTER];
   // two table sets as separate members: a dynamically indexed array would
   // live in scratch memory, whose loads share the wave's vmcnt with the ring
@@ -155,7 +155,7 @@ struct GenPolicy {
 #pragma unroll
       for (int f = 0; f < OUTER; ++f) {
         const bool ok = !beyond && (oobm[f] & last) == 0;
-        dma_b128(rs, ok ? xoff[f] : kOobOffset, sbase + k * in_image_bytes + f * waves_kb, load_nt);
+        dma_b128(rs, ok ? xoff[f] : kOobOffset, sbase + k * in_image_bytes + f * waves_kb, NT || load_nt);
       }
     }
     if constexpr (ZSET) {
@@ -239,7 +239,7 @@ struct GenPolicy {
           __builtin_memcpy(words, lds + out_image_off + swz(lo, swizzle), 16);
         }
         const bool ok = !beyond && (poobm[q] & last) == 0;
-        store_chunk<16>(rs, ok ? pooff[q] : kOobOffset, words, store_nt);
+        store_chunk<16>(rs, ok ? pooff[q] : kOobOffset, words, NT || store_nt);
       }
     }
   }
@@ -437,17 +437,14 @@ struct GenPolicy {
           }
         }
         const bool ok = !beyond && (oobm[f] & last) == 0;
-        store_chunk<CS::OB>(rs, ok ? ooff[f] : kOobOffset, words, store_nt);
+        store_chunk<CS::OB>(rs, ok ? ooff[f] : kOobOffset, words, NT || store_nt);
       }
     }
   }
 };
 
-template <class OP, int MODE, int OUTER, bool SROW, int ZSET = 0, bool GROUP = false>
-__global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
-  extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
-  prefetch_kargs();
-  CArgs* A = kargs();
+template <class OP, int MODE, int OUTER, bool SROW, int ZSET, bool GROUP, bool NT>
+__device__ __forceinline__ void gen_body(CArgs* A, unsigned char* lds) {
   const int lane = threadIdx.x & 63;
   const int wave = uni(static_cast<int>(threadIdx.x >> 6));
   const uint32_t grid = gridDim.x;
@@ -472,7 +469,7 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   uint32_t row_bad[2] = {~0u, ~0u};
   if constexpr (OP::ROW && !SROW) build_rows(A, lane, row_ptr, row_bad);
   const Loc L = load_loc(A);
-  GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP> p;
+  GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP, NT> p;
   p.tpt_log2 = tpt_log2;
   p.tile_lds = L.slot_bytes >> tpt_log2;
   p.A = A;
@@ -519,10 +516,10 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
     p.row_of[f] = (abo >> 8) * 32u + (abo & 255u) / 4u;
     p.sa[f] = p.sb[f] = 0.f;
   }
-  if constexpr (GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP>::SPLIT) {
+  if constexpr (GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP, NT>::SPLIT) {
     // the piece map with the axes outside the pieces, up to 8 pieces (above
     // that the per-piece walk keeps the register count down)
-    if constexpr (2 * OUTER <= 8 && GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP>::NP == 2 * OUTER)
+    if constexpr (2 * OUTER <= 8 && GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP, NT>::NP == 2 * OUTER)
       build_pieces_c(A, wave, lane, p.pooff, p.poobm, p.plpos);
     else
       build_pieces(A, wave, lane, OUTER, p.pooff, p.poobm, p.plpos);
@@ -599,10 +596,10 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   p.tab1 = TripRow{0, 0, 0, 0, 0, 0};
   p.fill(0, 0u);
   typedef ChunkShape<OP, 16> CS;
-  constexpr int NS = GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP>::NS;
-  // streams with one tile per trip take the ring whose steady-state wait is a
-  // compile-time count (the per-trip counts are known here)
-  if constexpr (MODE == 2 && !(OP::ROW && !SROW)) {
+  constexpr int NS = GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP, NT>::NS;
+  // copies and streams with one tile per trip take the ring whose waits are
+  // compile-time counts (the per-trip counts are known here)
+  if constexpr ((MODE == 0 || MODE == 2) && !(OP::ROW && !SROW)) {
     if (tpt_log2 == 0) {
       run_ring_fixed<NS * OUTER, OUTER * CS::ST>(p, n, uni(A->stages));
       return;
@@ -613,6 +610,23 @@ __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   // per trip only makes the waits stronger
   const int st = MODE == 4 ? red_stores : (MODE == 3 ? (GROUP ? 0 : OUTER * 4) : OUTER * CS::ST);
   run_ring(p, n, uni(A->stages), d, st << tpt_log2);
+}
+
+// Copies with non-temporal loads and stores (the default for tile copies)
+// get a body with the cache policy fixed at compile time, so no load or
+// store of a trip branches on it.
+template <class OP, int MODE, int OUTER, bool SROW, int ZSET = 0, bool GROUP = false>
+__global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+  prefetch_kargs();
+  CArgs* A = kargs();
+  if constexpr (MODE == 0) {
+    if (A->load_nt && A->store_nt) {
+      gen_body<OP, MODE, OUTER, SROW, ZSET, GROUP, true>(A, lds);
+      return;
+    }
+  }
+  gen_body<OP, MODE, OUTER, SROW, ZSET, GROUP, false>(A, lds);
 }
 
 }  // namespace dev

@@ -133,6 +133,13 @@ hipError_t widen_tiles_launch(const void* src, void* dst, const int64_t* in_stri
 const void* copy_shape_kernel_for(int threads, int unroll, int load_nt, int store_nt);
 hipError_t copy_shape_launch(const void* kernel, const void* src, void* dst, uint64_t bytes, unsigned grid,
                              unsigned threads, hipStream_t stream);
+// Same-walk tiled copy reference (rank 3, packed output); threads 128 or
+// 256 with at most 8 chunks of 16 bytes per lane and group, else
+// hipErrorInvalidValue before any launch.
+hipError_t copy_tiles_launch(const void* src, void* dst, const int64_t* in_stride_b, const int64_t* out_stride_b,
+                             uint32_t rows_total, uint32_t row_bytes_total, uint32_t rows, uint32_t group_bytes,
+                             uint32_t tiles_1, uint32_t groups_2, uint32_t n_groups, unsigned threads, unsigned grid,
+                             hipStream_t stream);
 hipError_t ring_trace_launch(int n_iters, int stages, int loads, int stores, int32_t* out,
                              hipStream_t stream);
 

@@ -31,6 +31,96 @@ __global__ __launch_bounds__(T) void copy_shape_kernel(const char* src, char* ds
   }
 }
 
+// Same-walk reference of a tiled copy: the tiles of a rank-3 tensor (dim 0
+// one slab per tile, `rows` rows along dim 1, the innermost dim contiguous)
+// go to a packed output of the same shape in groups of neighbouring tiles
+// along the innermost dim, with no LDS and no ring.  Group g is tile row
+// g / groups_per_row and group g % groups_per_row of it; workgroup w takes
+// groups w, w+G, ... with the next group's loads issued before the current
+// group's stores, so two groups are in flight as in a 2-slot ring.  Lane
+// chunk c = u * T + lane of a group is row c / chunks_per_row and 16-byte
+// column c % chunks_per_row; chunks past the tensor's edge take the
+// out-of-bounds offset (loads read zeros, stores are dropped).
+struct CopyTilesArgs {
+  const char* src;
+  char* dst;
+  int64_t in_stride[2], out_stride[2];  // bytes per index of dims 0 and 1
+  uint32_t rows_total;                  // extent of dim 1
+  uint32_t row_bytes_total;             // innermost extent in bytes
+  uint32_t rows;                        // tile rows
+  uint32_t group_bytes;                 // bytes of one group row (a multiple of 16)
+  uint32_t tiles_1, groups_2;           // tiles along dim 1, groups along the innermost dim
+  uint32_t n_groups;
+};
+
+template <int T, int R>
+struct TileGroup {
+  __amdgpu_buffer_rsrc_t rin, rout;
+  uint32_t xo[R], oo[R];
+
+  __device__ __forceinline__ void locate(const CopyTilesArgs& A, uint32_t g) {
+    const uint32_t c2 = g % A.groups_2;
+    const uint32_t q = g / A.groups_2;
+    const uint32_t t1 = q % A.tiles_1;
+    const uint32_t t0 = q / A.tiles_1;
+    const uint32_t row0 = t1 * A.rows;
+    const uint32_t nrows = A.rows_total - row0 < A.rows ? A.rows_total - row0 : A.rows;
+    const uint32_t col0 = c2 * A.group_bytes;
+    const uint32_t ncol = A.row_bytes_total - col0 < A.group_bytes ? A.row_bytes_total - col0 : A.group_bytes;
+    const int64_t ib = t0 * A.in_stride[0] + row0 * A.in_stride[1] + col0;
+    const int64_t ob = t0 * A.out_stride[0] + row0 * A.out_stride[1] + col0;
+    const uint32_t cpr = A.group_bytes / 16u;
+    rin = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(A.src) + ib, 0, 0x7FFFFFFF, 0x00020000);
+    rout = __builtin_amdgcn_make_buffer_rsrc(A.dst + ob, 0, 0x7FFFFFFF, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const uint32_t c = u * T + threadIdx.x;
+      const uint32_t r = c / cpr, k = (c % cpr) * 16u;
+      const bool ok = r < nrows && k < ncol;
+      xo[u] = ok ? static_cast<uint32_t>(r * A.in_stride[1]) + k : kOobOffset;
+      oo[u] = ok ? static_cast<uint32_t>(r * A.out_stride[1]) + k : kOobOffset;
+    }
+  }
+  __device__ __forceinline__ void load(u32x4 (&v)[R]) const {
+#pragma unroll
+    for (int u = 0; u < R; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rin, xo[u], 0, 2);
+  }
+  __device__ __forceinline__ void store(const u32x4 (&v)[R]) const {
+#pragma unroll
+    for (int u = 0; u < R; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rout, oo[u], 0, 2);
+  }
+};
+
+template <int T, int R>
+__global__ __launch_bounds__(T) void copy_tiles_kernel(const CopyTilesArgs A) {
+  const uint32_t grid = gridDim.x;
+  uint32_t g = blockIdx.x;
+  if (g >= A.n_groups) return;
+  TileGroup<T, R> a, b;
+  u32x4 va[R], vb[R];
+  a.locate(A, g);
+  a.load(va);
+  for (;;) {
+    const uint32_t g1 = g + grid;
+    const bool more1 = g1 < A.n_groups;
+    if (more1) {
+      b.locate(A, g1);
+      b.load(vb);
+    }
+    a.store(va);
+    if (!more1) break;
+    const uint32_t g2 = g1 + grid;
+    const bool more2 = g2 < A.n_groups;
+    if (more2) {
+      a.locate(A, g2);
+      a.load(va);
+    }
+    b.store(vb);
+    if (!more2) break;
+    g = g2;
+  }
+}
+
 }  // namespace dev
 
 namespace {
@@ -60,6 +150,35 @@ const void* copy_shape_kernel_for(int threads, int unroll, int load_nt, int stor
   for (const CopyShape& c : kCopyShapes)
     if (c.threads == threads && c.unroll == unroll && c.load_nt == load_nt && c.store_nt == store_nt) return c.kernel;
   return nullptr;
+}
+
+hipError_t copy_tiles_launch(const void* src, void* dst, const int64_t* in_stride_b, const int64_t* out_stride_b,
+                             uint32_t rows_total, uint32_t row_bytes_total, uint32_t rows, uint32_t group_bytes,
+                             uint32_t tiles_1, uint32_t groups_2, uint32_t n_groups, unsigned threads, unsigned grid,
+                             hipStream_t stream) {
+  dev::CopyTilesArgs A{};
+  A.src = static_cast<const char*>(src);
+  A.dst = static_cast<char*>(dst);
+  for (int d = 0; d < 2; ++d) {
+    A.in_stride[d] = in_stride_b[d];
+    A.out_stride[d] = out_stride_b[d];
+  }
+  A.rows_total = rows_total;
+  A.row_bytes_total = row_bytes_total;
+  A.rows = rows;
+  A.group_bytes = group_bytes;
+  A.tiles_1 = tiles_1;
+  A.groups_2 = groups_2;
+  A.n_groups = n_groups;
+  const uint32_t chunks = rows * (group_bytes / 16u);
+  const void* k = nullptr;
+  if (threads == 128 && chunks <= 512) k = reinterpret_cast<const void*>(&dev::copy_tiles_kernel<128, 4>);
+  else if (threads == 128 && chunks <= 1024) k = reinterpret_cast<const void*>(&dev::copy_tiles_kernel<128, 8>);
+  else if (threads == 256 && chunks <= 1024) k = reinterpret_cast<const void*>(&dev::copy_tiles_kernel<256, 4>);
+  else if (threads == 256 && chunks <= 2048) k = reinterpret_cast<const void*>(&dev::copy_tiles_kernel<256, 8>);
+  if (!k) return hipErrorInvalidValue;
+  void* params[] = {&A};
+  return hipLaunchKernel(k, dim3(grid), dim3(threads), params, 0, stream);
 }
 
 hipError_t copy_shape_launch(const void* kernel, const void* src, void* dst, uint64_t bytes, unsigned grid,

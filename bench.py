@@ -19,7 +19,7 @@ runs on) and the CPU oracle timed on a bounded sample of the same workload.
 
 Other modes (measurement aids):
   --workload NAME   one workload alone (c1 c2 c3 c5, the references copy_ref /
-                    read_ref / write_ref / widen_ref / widen_tiles_ref, calib,
+                    read_ref / write_ref / widen_ref / widen_tiles_ref / tiles_copy_ref, calib,
                     and pointwise / reduce / rowsum)
   --fixed-cost      the streamed fma and the reference copy over 1..128 slabs of
                     the tensor: per-launch fixed cost and per-byte rate of each
@@ -86,7 +86,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None,
                     choices=["c1", "c2", "c3", "c4", "c5", "calib", "copy_ref", "read_ref", "write_ref", "widen_ref",
-                             "widen_tiles_ref", "pointwise",
+                             "widen_tiles_ref", "tiles_copy_ref", "pointwise",
                              "reduce", "rowsum"],
                     help="measure one workload alone (default: c4 with ring_stages and configs); calib: torch's "
                          "copy of 256 MiB, the known-size kernel that scales HBM counters; copy_ref / read_ref / "
@@ -222,6 +222,19 @@ def build(name, ctx, stages=None):
         out = dict(bytes=x.nbytes * 2, dtype="f16",
                    config={"workload": f"tile copy, [128,500,1024] f16, 128x32 tiles, {threads} threads"},
                    key="tile_copy_f16_128x500x1024")
+    elif name == "tiles_copy_ref":
+        threads = args.threads or 128
+        shape = (128, 500, 1024)
+        x = W.normal_f16(shape, seed=3)
+        for _ in range(sets):
+            xd, yd = ctx.to_dev(x), ctx.empty(x.nbytes)
+            launches.append(lambda xd=xd, yd=yd: acp.acp_debug_copy_tiles(
+                yd, xd, 2, shape, _packed(shape), (1, 128, 32), 2, threads, G, stream))
+        out = dict(bytes=x.nbytes * 2, dtype="f16",
+                   config={"workload": f"reference register-path copy with the tile copy's walk: [128,500,1024] "
+                                       f"f16, 128x32 tiles in pairs along the rows, {threads} threads, {G} "
+                                       f"workgroups, two pairs in flight, no LDS, no ring"},
+                   key="tile_copy_reference_f16_128x500x1024")
     elif name == "c5":
         threads = args.threads or 256
         S = stages or args.stages or 4

@@ -347,6 +347,26 @@ acp_status acp_debug_stream_copy(void* dst, const void* src, int64_t bytes, int 
 acp_status acp_debug_stream_copy_shape(void* dst, const void* src, int64_t bytes, int workgroups, int threads,
                                        int unroll, int load_nt, int store_nt, void* hip_stream);
 
+/* Measurement reference with the walk of a persistent tiled copy (not part
+ * of the pipelined path): dst = src over a rank-3 tensor `src` (element
+ * `src_strides`, innermost 1, 16-byte multiples in bytes) of `esize`-byte
+ * elements into a packed tensor `dst` of the same `shape`, with no LDS and
+ * no ring.  Tiles are `box` = (1, rows, cols); `tiles_per_trip` neighbouring
+ * tiles along the innermost dim form a group, and workgroup w of
+ * `workgroups` (0: one per compute unit, never more than the groups) takes
+ * groups w, w+G, ... in row-major order, issuing the next group's 16-byte
+ * non-temporal loads before the current group's stores (two groups in
+ * flight, as in a 2-slot ring).  Edge tiles are clipped to the tensor.  It
+ * gives the rate a plain register-path copy reaches over the same tiles and
+ * order as acp_tile_copy's persistent grid.  ACP_ERR_INVALID for null
+ * pointers, esize not 1/2/4/8, threads not 128/256, tiles_per_trip not
+ * 1/2/4, box[0] != 1, rows or groups not whole 16-byte chunks, more than 8
+ * chunks per lane and group, misaligned pointers or strides, or
+ * overlapping buffers. */
+acp_status acp_debug_copy_tiles(void* dst, const void* src, int esize, const int64_t* shape,
+                                const int64_t* src_strides, const int32_t* box, int tiles_per_trip, int threads,
+                                int workgroups, void* hip_stream);
+
 /* Measurement references for one direction (not part of the pipelined
  * path), with acp_debug_stream_copy's walk: 256-thread workgroups, 16 KiB
  * blocks w, w+G, ..., four 16-byte non-temporal accesses per lane;

@@ -291,6 +291,28 @@ def test_reference_copy_shape_rejects_unbuilt_shapes():
     assert np.all(host(yd, np.uint8) == 2)
 
 
+@pytest.mark.parametrize("shape,pitch,box,tpt,threads,wgs", [
+    ((3, 300, 320), 336, (1, 128, 32), 2, 128, 0),     # ragged rows; five whole pairs per tile row
+    ((2, 130, 352), 352, (1, 128, 32), 2, 128, 7),     # eleven tiles: the last pair is one tile wide
+    ((2, 77, 96), 104, (1, 64, 32), 1, 128, 5),         # one tile per group, 64-byte rows
+    ((1, 40, 512), 512, (1, 16, 64), 4, 256, 0),        # four tiles per group, 512-byte rows
+])
+def test_reference_tiled_copy_walk(shape, pitch, box, tpt, threads, wgs):
+    # the same-walk copy reference moves every element of a strided f16
+    # source into a packed output (row padding never read) and writes
+    # nothing past it
+    say(f"reference tiled copy {shape} pitch {pitch} box {box} x{tpt}, {threads} threads, wgs {wgs}")
+    rng = np.random.default_rng(36)
+    storage = rng.integers(0, 2**16, size=(shape[0], shape[1], pitch), dtype=np.uint64).astype(np.uint16)
+    xd = dev(storage)
+    n = int(np.prod(shape))
+    yd = empty_bytes(n * 2 + 64, 0x5A)
+    acp.acp_debug_copy_tiles(yd, xd, 2, shape, (shape[1] * pitch, pitch, 1), box, tpt, threads, wgs, stream())
+    y = host(yd, np.uint8)
+    assert np.array_equal(y[:n * 2].view(np.uint16).reshape(shape), storage[:, :, :shape[2]])
+    assert np.all(y[n * 2:] == 0x5A)
+
+
 def _reduce_case(dt, src_shape, dst_shape, box, threads, values, swz=0, seed=51):
     npdt = {"u32": np.uint32, "f32": np.float32, "f16": np.float16}[dt]
     rng = np.random.default_rng(seed)
