@@ -110,7 +110,8 @@ int device_lds_limit() { return device_attr(hipDeviceAttributeMaxSharedMemoryPer
 // Launch knobs read once from the environment (measurement aids; the
 // defaults are the measured best on MI355X):
 //   ACP_XCD_REMAP=0  keep blockIdx order for persistent grids (default: tiles
-//                    of consecutive workgroups stay on one XCD)
+//                    of consecutive workgroups stay on one XCD, except for
+//                    copies of whole 128-byte lines); =2 remap those too
 //   ACP_STORE_NT=0   cached stores (default: non-temporal)
 //   ACP_LOAD_NT=0|1  cached / non-temporal direct-to-LDS loads (default:
 //                    non-temporal for contiguous stages on a linear grid)
@@ -131,9 +132,14 @@ bool env_flag(const char* name, bool dflt) {
   return e[0] != '0';
 }
 
-bool xcd_remap_enabled() {
-  static const bool on = env_flag("ACP_XCD_REMAP", true);
-  return on;
+// 0: never remap, 1: the default rule, 2: remap every eligible grid
+int xcd_remap_mode() {
+  static const int mode = [] {
+    const char* e = std::getenv("ACP_XCD_REMAP");
+    if (!e || !e[0]) return 1;
+    return e[0] == '0' ? 0 : (e[0] == '2' ? 2 : 1);
+  }();
+  return mode;
 }
 
 // Everything one launch of the engine needs.
@@ -539,7 +545,8 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   // their neighbours and measured faster without it (128x32 float16 tiles
   // in pairs over [128,500,1024]: 4.69 TB/s against 4.48).
   const bool whole_lines = q.mode == 0 && (static_cast<int64_t>(q.stage_box[r - 1]) * ei) % 128 == 0;
-  A.xcd_remap = (grid % 8 == 0 && grid >= 16 && xcd_remap_enabled() && !whole_lines) ? 1 : 0;
+  const int remap = xcd_remap_mode();
+  A.xcd_remap = (grid % 8 == 0 && grid >= 16 && remap != 0 && (!whole_lines || remap == 2)) ? 1 : 0;
   L->grid = grid;
   L->block = static_cast<unsigned>(q.threads);
   L->lds = static_cast<unsigned>(lds);
@@ -556,6 +563,7 @@ std::string describe(const Launch& L) {
          " rounds " + std::to_string(L.args.outer) + " srow " + std::to_string(L.key.srow) + " variant " +
          std::to_string(L.key.variant) + " grid " + std::to_string(L.grid) + " threads " +
          std::to_string(L.block) + " slots " + std::to_string(L.args.stages) + " lds " + std::to_string(L.lds) +
+         (L.args.xcd_remap ? " xcd-remap" : "") +
          (m == 8 || m == 10 ? std::string(L.args.red_local ? " wave-local" : " lds partials") : std::string());
 }
 

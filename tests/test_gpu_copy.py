@@ -74,6 +74,9 @@ def test_c3_full_size_copy():
     acp.acp_tile_copy(src, dst, 128, stream())
     torch.cuda.synchronize()
     assert torch.equal(xd, yd)
+    # pairs of tiles per trip (128-byte rows, 8 rounds), whole lines: no XCD remap
+    kernel = acp.acp_last_kernel()
+    assert kernel.startswith("general copy vec 16 rounds 8 ") and "xcd-remap" not in kernel, kernel
 
 
 @pytest.mark.parametrize("mode", [1, 2, 3])

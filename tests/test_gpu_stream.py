@@ -122,6 +122,7 @@ def test_c4_full_size_bench_config(stage_box, stages, threads, workgroups, round
     say(f"C4 full fma [128,500,1024] stage {stage_box} S={stages} {threads} threads, {workgroups} workgroups")
     x, a, b, y = _fma_case(shape, stage_box, stage_box, stages, threads, workgroups)
     assert acp.acp_last_kernel().startswith(f"stream linear grid vec 16 rounds {rounds} srow 1")
+    assert acp.acp_last_kernel().endswith(" xcd-remap")
     assert np.array_equal(y.view(np.uint32), _c4_reference(x, a, b))
 
 
