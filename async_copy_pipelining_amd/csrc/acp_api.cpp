@@ -384,18 +384,21 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   L->key = acp::KernelKey{q.op, q.mode == 0 ? ACP_U32 : static_cast<int>(x.dtype),
                           q.mode == 0 ? ACP_U32 : (q.mode == 4 ? ACP_F32 : static_cast<int>(o.dtype)), p.vec_bytes,
                           q.mode, 0, 0};
-  // streaming on a linear grid with 16-byte rounds: the lean kernel
+  // streaming on a linear grid with 16-byte rounds: the lean kernel; a
+  // tile copy whose tiles form a linear grid (a single tile among them) is
+  // the same stream with the copy op, and its smaller argument block and
+  // set-up shorten a latency-bound launch
   static const bool fast_ok = env_flag("ACP_FAST_PATH", true);
   bool fast = false;
   // (two tensors: with both on the direct-to-LDS ring)
-  if (fast_ok && q.mode == 2 && A.lin && p.vec_bytes == 16 && (q.n_in == 1 || q.binary == 1) &&
+  if (fast_ok && (q.mode == 2 || q.mode == 0) && A.lin && p.vec_bytes == 16 && (q.n_in == 1 || q.binary == 1) &&
       (p.outer == 1 || p.outer == 2 || p.outer == 4 || p.outer == 8)) {
     acp::KernelKey fk = L->key;
     fk.mode = 3;
     fk.outer = p.outer;
     fk.variant = q.binary;
     static const bool srow_ok = env_flag("ACP_SCALAR_ROWS", true);
-    fk.srow = (A.row_uniform && srow_ok) ? 1 : 0;
+    fk.srow = (q.mode == 2 && A.row_uniform && srow_ok) ? 1 : 0;
     if (acp::engine_kernel(fk)) {
       L->key = fk;
       fast = true;
@@ -559,7 +562,9 @@ std::string describe(const Launch& L) {
                                       "general stream",     "general reduce-add", "general row reduction",
                                       "tile linear grid",   "row reduction linear grid"};
   const int m = L.key.mode;
-  return std::string(m >= 0 && m <= 10 ? kinds[m] : "?") + " vec " + std::to_string(L.key.vec_bytes) +
+  const bool lin_copy = m == 3 && L.key.op == ACP_OP_COPY;
+  return std::string(lin_copy ? "copy linear grid" : (m >= 0 && m <= 10 ? kinds[m] : "?")) + " vec " +
+         std::to_string(L.key.vec_bytes) +
          " rounds " + std::to_string(L.args.outer) + " srow " + std::to_string(L.key.srow) + " variant " +
          std::to_string(L.key.variant) + " grid " + std::to_string(L.grid) + " threads " +
          std::to_string(L.block) + " slots " + std::to_string(L.args.stages) + " lds " + std::to_string(L.lds) +
@@ -785,7 +790,7 @@ acp_status build_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, i
     tile_schedule(p2, 1, threads, 0, &unused_w, &q2.stages, &unused_tpt);
     q2.tiles_per_trip = 1;
     Launch L2;
-    if (prepare(q2, &L2) == ACP_OK && L2.key.mode == 4) return keep(res, L2);
+    if (prepare(q2, &L2) == ACP_OK && (L2.key.mode == 4 || L2.key.mode == 3)) return keep(res, L2);
   }
   Launch L;
   const acp_status st = prepare(q, &L);

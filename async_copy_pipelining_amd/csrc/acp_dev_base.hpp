@@ -76,8 +76,21 @@ constexpr uint32_t kLinArgLines = arg_lines(0, offsetof(EngineArgs, xstep)) |
                                   arg_lines(offsetof(EngineArgs, ax_count), sizeof(EngineArgs));
 static_assert(__builtin_popcount(kLinArgLines) <= 15, "one batch of scalar loads");
 
+// More than 15 lines take several batches, each a trip to memory.  Then one
+// vector load, lane k reading a word of line k, goes out first and brings
+// every line into L2 while the first batch is in flight, so the later
+// batches hit L2.  The returned word feeds `karg_warm_done`, which the
+// kernel places before its first ring load: the wait for the vector load
+// falls there, and the ring's vmcnt counts start from zero.
 template <uint32_t LINES = kAllArgLines>
-__device__ __forceinline__ void prefetch_kargs() {
+__device__ __forceinline__ uint32_t prefetch_kargs() {
+  uint32_t warm = 0;
+  if constexpr (__builtin_popcount(LINES) > 15) {
+    typedef const uint32_t __attribute__((address_space(1))) GWord;
+    GWord* g = (GWord*)(__builtin_amdgcn_kernarg_segment_ptr());
+    const uint32_t lane = threadIdx.x & 63u;
+    if (lane < static_cast<uint32_t>(kArgLines) && ((LINES >> lane) & 1u)) warm = g[lane * 16u];
+  }
   typedef const uint32_t __attribute__((address_space(4))) CWord;
   CWord* w = (CWord*)(__builtin_amdgcn_kernarg_segment_ptr());
   uint32_t x = 0;
@@ -85,7 +98,10 @@ __device__ __forceinline__ void prefetch_kargs() {
   for (int k = 0; k < kArgLines; ++k)
     if ((LINES >> k) & 1u) x ^= w[k * 16];
   asm volatile("" ::"s"(x));
+  return warm;
 }
+
+__device__ __forceinline__ void karg_warm_done(uint32_t warm) { asm volatile("" ::"v"(warm) : "memory"); }
 
 // XOR swizzle of a stage-relative LDS byte offset: the 16-byte chunk index
 // within its span takes the 128-byte row index modulo the span's chunk

@@ -444,7 +444,7 @@ struct GenPolicy {
 };
 
 template <class OP, int MODE, int OUTER, bool SROW, int ZSET, bool GROUP, bool NT>
-__device__ __forceinline__ void gen_body(CArgs* A, unsigned char* lds) {
+__device__ __forceinline__ void gen_body(CArgs* A, unsigned char* lds, uint32_t warm) {
   const int lane = threadIdx.x & 63;
   const int wave = uni(static_cast<int>(threadIdx.x >> 6));
   const uint32_t grid = gridDim.x;
@@ -457,7 +457,10 @@ __device__ __forceinline__ void gen_body(CArgs* A, unsigned char* lds) {
   const uint32_t mine = per_wg ? (first < A->n_tiles ? min(per_wg, A->n_tiles - first) : 0u)
                                : (wg < groups ? (groups - wg + grid - 1) / grid : 0);
   const int n = static_cast<int>(mine * A->subs);  // ring trips
-  if (n == 0) return;
+  if (n == 0) {
+    karg_warm_done(warm);
+    return;
+  }
   LaneMap m;
   // the lane map with the axes outside the rounds (store with reduce-add
   // keeps the per-round walk: measured 1.6 % faster there)
@@ -595,6 +598,7 @@ __device__ __forceinline__ void gen_body(CArgs* A, unsigned char* lds) {
   }
   p.tab1 = TripRow{0, 0, 0, 0, 0, 0};
   p.fill(0, 0u);
+  karg_warm_done(warm);
   typedef ChunkShape<OP, 16> CS;
   constexpr int NS = GenPolicy<OP, MODE, OUTER, SROW, ZSET, GROUP, NT>::NS;
   // copies and streams with one tile per trip take the ring whose waits are
@@ -618,15 +622,15 @@ __device__ __forceinline__ void gen_body(CArgs* A, unsigned char* lds) {
 template <class OP, int MODE, int OUTER, bool SROW, int ZSET = 0, bool GROUP = false>
 __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
-  prefetch_kargs();
+  const uint32_t warm = prefetch_kargs();
   CArgs* A = kargs();
   if constexpr (MODE == 0) {
     if (A->load_nt && A->store_nt) {
-      gen_body<OP, MODE, OUTER, SROW, ZSET, GROUP, true>(A, lds);
+      gen_body<OP, MODE, OUTER, SROW, ZSET, GROUP, true>(A, lds, warm);
       return;
     }
   }
-  gen_body<OP, MODE, OUTER, SROW, ZSET, GROUP, false>(A, lds);
+  gen_body<OP, MODE, OUTER, SROW, ZSET, GROUP, false>(A, lds, warm);
 }
 
 }  // namespace dev

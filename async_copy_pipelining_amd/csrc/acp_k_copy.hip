@@ -1,5 +1,5 @@
-// Engine instantiations: tile copy (raw bytes moved as 32-bit words) and the
-// store with reduce-add.
+// Engine instantiations: tile copy (raw bytes moved as 32-bit words; on a
+// linear tile grid through the linear kernel) and the store with reduce-add.
 #include "acp_engine_impl.hpp"
 
 namespace acp {
@@ -7,6 +7,8 @@ using namespace dev;
 namespace {
 const KernelEntry kTable[] = {
     ACP_BOTH(kOpCopy, kU32, kU32, 0, Op<kOpCopy, kU32, kU32>),
+    // linear tile grid (one tile per stage, contiguous row-major grid)
+    ACP_LIN(kOpCopy, kU32, kU32, Op<kOpCopy, kU32, kU32>),
     // general lean kernel
     ACP_GEN(kOpCopy, kU32, kU32, 0, Op<kOpCopy, kU32, kU32>),
     // store with reduce-add

@@ -19,7 +19,8 @@ runs on) and the CPU oracle timed on a bounded sample of the same workload.
 
 Other modes (measurement aids):
   --workload NAME   one workload alone (c1 c2 c3 c5, the references copy_ref /
-                    read_ref / write_ref / widen_ref / widen_tiles_ref / tiles_copy_ref, calib,
+                    read_ref / write_ref / widen_ref / widen_tiles_ref / tiles_copy_ref /
+                    tile_ref, calib,
                     and pointwise / reduce / rowsum)
   --fixed-cost      the streamed fma and the reference copy over 1..128 slabs of
                     the tensor: per-launch fixed cost and per-byte rate of each
@@ -86,7 +87,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None,
                     choices=["c1", "c2", "c3", "c4", "c5", "calib", "copy_ref", "read_ref", "write_ref", "widen_ref",
-                             "widen_tiles_ref", "tiles_copy_ref", "pointwise",
+                             "widen_tiles_ref", "tiles_copy_ref", "tile_ref", "pointwise",
                              "reduce", "rowsum"],
                     help="measure one workload alone (default: c4 with ring_stages and configs); calib: torch's "
                          "copy of 256 MiB, the known-size kernel that scales HBM counters; copy_ref / read_ref / "
@@ -197,6 +198,19 @@ def build(name, ctx, stages=None):
                    config={"workload": f"swizzled tile copy, one 8x256 f16 tile (128-byte swizzle), {threads} "
                                        "threads (latency-bound: microseconds per launch)"},
                    key="tile_copy_swizzled_f16_8x256")
+    elif name == "tile_ref":
+        # the latency floor beside c1: a plain register-path copy of the same
+        # 4 KiB by one 64-thread workgroup (16-byte loads, then stores), no LDS
+        x = W.tile_bits_f16((8, 256), seed=1)
+        for _ in range(sets):
+            xd, yd = ctx.to_dev(x), ctx.empty(x.nbytes)
+            launches.append(lambda xd=xd, yd=yd:
+                            acp.acp_debug_stream_copy_shape(yd, xd, x.nbytes, 1, 64, 16, 1, 1, stream))
+        unit = "us"
+        out = dict(bytes=x.nbytes * 2, dtype="f16",
+                   config={"workload": "reference register-path copy of one 8x256 f16 tile (4 KiB), one workgroup "
+                                       "of 64 threads, no LDS (latency-bound: microseconds per launch)"},
+                   key="tile_copy_reference_4KiB")
     elif name == "c2":
         threads = args.threads or 256
         x = W.sqrt_tiles_f32(65536, seed=2)

@@ -37,9 +37,36 @@ def test_c1_swizzled_copy_is_bit_identical_and_image_matches():
     info = acp.acp_plan_query(src, 64)
     assert (info["rank"], info["vec"], info["outer"]) == (3, 8, 4)
     acp.acp_tile_copy(src, dst, 64, stream())
+    assert acp.acp_last_kernel().startswith("copy linear grid vec 16 rounds 4 "), acp.acp_last_kernel()
     assert np.array_equal(host(yd, np.uint16), x.view(np.uint16).reshape(-1))
     p = P.plan("f16", (8, 256), (256, 1), (8, 256), P.SWIZZLE_128B, threads=64)
     assert _lds_image(src, 0, 64, 4096) == T.lds_image(x.reshape(-1), p, 0)
+
+
+@pytest.mark.parametrize("dt,shape,box,swz,threads,kind", [
+    ("f32", (300, 32, 32), (1, 32, 32), 0, 256, "copy linear grid vec 16 rounds 1 "),      # persistent, 300 tiles
+    ("f32", (513, 32, 32), (1, 32, 32), 0, 128, "copy linear grid vec 16 rounds 2 "),      # persistent, ragged
+    ("f16", (7, 8, 256), (1, 8, 256), 3, 64, "copy linear grid vec 16 rounds 4 "),        # one workgroup per tile
+    ("f16", (3, 16, 256), (1, 16, 256), 3, 128, "copy linear grid vec 16 rounds 4 "),     # two atoms per row
+    ("f32", (2, 64, 32), (1, 64, 32), 1, 64, "copy linear grid vec 16 rounds 8 "),        # 32-byte swizzle
+    ("f16", (3, 300, 96), (1, 128, 32), 0, 128, "general copy"),                          # ragged: general kernel
+])
+def test_linear_grid_tile_copies(dt, shape, box, swz, threads, kind):
+    # tile copies whose tiles form a contiguous row-major grid run on the
+    # linear kernel: bit-identical, one workgroup per tile or persistent
+    say(f"linear-grid copy {dt} {shape} box {box} swizzle {swz} threads {threads}")
+    npdt = {"f16": np.uint16, "f32": np.uint32}[dt]
+    rng = np.random.default_rng(37)
+    x = rng.integers(0, 2 ** (8 * np.dtype(npdt).itemsize), size=shape, dtype=np.uint64).astype(npdt)
+    xd, yd = dev(x), empty_bytes(x.nbytes + 64, 0x5A)
+    st = packed_strides(shape)
+    src = encode(dt, xd, shape, st, box, swz)
+    dst = encode(dt, yd, shape, st, box, swz)
+    acp.acp_tile_copy(src, dst, threads, stream())
+    assert acp.acp_last_kernel().startswith(kind), acp.acp_last_kernel()
+    y = host(yd, np.uint8)
+    assert np.array_equal(y[:x.nbytes].view(npdt).reshape(shape), x)
+    assert np.all(y[x.nbytes:] == 0x5A)
 
 
 @pytest.mark.parametrize("threads", [64, 128, 256])
