@@ -183,6 +183,42 @@ def test_status_codes_and_reasons():
         assert e.value.status == acp.ACP_ERR_INVALID and why in e.value.reason
 
 
+def test_reference_copy_arguments_are_checked_on_the_host():
+    # the copy-shape and tiled-copy references refuse bad requests before
+    # any launch: unbuilt shapes are unsupported, malformed ones invalid
+    for args, status, why in (
+            ((256, 3, 1, 1), acp.ACP_ERR_UNSUPPORTED, "shape"),
+            ((96, 4, 1, 1), acp.ACP_ERR_UNSUPPORTED, "shape"),
+            ((256, 4, 2, 1), acp.ACP_ERR_INVALID, "policies"),
+            ((256, 4, 1, -1), acp.ACP_ERR_INVALID, "policies")):
+        with pytest.raises(acp.AcpError) as e:
+            acp.acp_debug_stream_copy_shape(FAKE_BASE * 8, FAKE_BASE, 4096, 0, *args)
+        assert e.value.status == status and why in e.value.reason, e.value.reason
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_debug_stream_copy_shape(FAKE_BASE, FAKE_BASE + 64, 4096, 0, 256, 4, 1, 1)
+    assert e.value.status == acp.ACP_ERR_INVALID and "overlap" in e.value.reason
+    shape, strides = (2, 300, 352), (300 * 352, 352, 1)
+    out = FAKE_BASE * 64
+    for kw, why in (
+            (dict(esize=3), "element size"),
+            (dict(threads=64), "threads"),
+            (dict(tiles_per_trip=3), "tiles per trip"),
+            (dict(box=(2, 128, 32)), "dim 0"),
+            (dict(box=(1, 128, 3)), "16-byte"),
+            (dict(box=(1, 256, 32)), "8 chunks"),
+            (dict(strides=(300 * 352, 352, 2)), "innermost"),
+            (dict(strides=(300 * 352, 348, 1)), "16-byte multiples"),
+            (dict(src=FAKE_BASE + 2), "aligned"),
+            (dict(dst=FAKE_BASE + 4096), "overlap")):
+        a = dict(dst=out, src=FAKE_BASE, esize=2, shape=shape, strides=strides, box=(1, 128, 32),
+                 tiles_per_trip=2, threads=128)
+        a.update(kw)
+        with pytest.raises(acp.AcpError) as e:
+            acp.acp_debug_copy_tiles(a["dst"], a["src"], a["esize"], a["shape"], a["strides"], a["box"],
+                                     a["tiles_per_trip"], a["threads"])
+        assert e.value.status == acp.ACP_ERR_INVALID and why in e.value.reason, (kw, e.value.reason)
+
+
 def test_memory_shared_between_a_written_tensor_and_another_operand_is_rejected():
     """Workgroups read and write different tensors with no ordering between
     them, so every entry point refuses a written tensor that shares bytes
