@@ -50,6 +50,7 @@ def test_c1_swizzled_copy_is_bit_identical_and_image_matches():
     ("f16", (3, 16, 256), (1, 16, 256), 3, 128, "copy linear grid vec 16 rounds 4 "),     # two atoms per row
     ("f32", (2, 64, 32), (1, 64, 32), 1, 64, "copy linear grid vec 16 rounds 8 "),        # 32-byte swizzle
     ("f16", (3, 300, 96), (1, 128, 32), 0, 128, "general copy"),                          # ragged: general kernel
+    ("f16", (38400, 64), (128, 32), 0, 128, "copy linear grid vec 16 rounds 8 "),         # paired tiles: whole rows
 ])
 def test_linear_grid_tile_copies(dt, shape, box, swz, threads, kind):
     # tile copies whose tiles form a contiguous row-major grid run on the
