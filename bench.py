@@ -453,8 +453,8 @@ def measure_config(name, ctx, steps, warmup):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only: every box has one MI355X; "
-                                   "run with --gpus 1", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the path runs on one GPU only (each GPU would take its own slab; no "
+                                   "collective is part of it): run with --gpus 1", "n_gpus": args.gpus}))
         sys.exit(2)
     ctx = Ctx(args)
     if args.fixed_cost:
