@@ -6,6 +6,8 @@ streamed through a 4-stage LDS ring (stage = two 1024-element rows, 256
 threads, one persistent workgroup per CU), the configuration the HBM-roofline
 target is quoted on.  One step = one launch of acp_stream_ewise over the whole
 tensor.  The same line reports the 2-, 3- and 4-stage rings ("ring_stages"),
+a plain register-path copy of the same bytes on the same device and the
+ring's fraction of it ("copy_reference"),
 the other workloads ("configs": the swizzled 8x256 tile copy, the 32x32 tile
 sqrt, the 128x32 tile copy and the rank-5 exp stream, each with its roofline
 figures and its own CPU-oracle baseline) and the CPU oracle of the streamed
@@ -504,6 +506,13 @@ def main():
     del wl, fns
     ctx.torch.cuda.empty_cache()
     if name == "c4" and args.workload is None and not args.no_configs:
+        # the same box's ceiling beside the headline: a plain register-path
+        # copy (no LDS, no ring) of the same 262 MB read and written, timed
+        # the same way
+        ref = measure_config("copy_ref", ctx, args.steps, args.warmup)
+        result["copy_reference"] = {"value": ref["value"], "unit": "GB/s", "frac": ref["frac"],
+                                    "workload": ref["config"]["workload"],
+                                    "ring_fraction_of_copy": round(value / ref["value"], 4)}
         configs = {}
         for c in ("c1", "c2", "c3", "c5"):
             configs[c] = measure_config(c, ctx, args.steps, args.warmup)
