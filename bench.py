@@ -10,7 +10,8 @@ a plain register-path copy of the same bytes on the same device and the
 ring's fraction of it ("copy_reference"),
 the other workloads ("configs": the swizzled 8x256 tile copy, the 32x32 tile
 sqrt, the 128x32 tile copy and the rank-5 exp stream, each with its roofline
-figures and its own CPU-oracle baseline) and the CPU oracle of the streamed
+figures, a plain copy of its bytes with its own walk ("reference") and its
+own CPU-oracle baseline) and the CPU oracle of the streamed
 fma.  Inputs are seeded synthetic tensors resident in HBM; three buffer sets
 are rotated so that consecutive steps never hit data left in the 256 MB
 last-level cache by the previous one.
@@ -514,8 +515,18 @@ def main():
                                     "workload": ref["config"]["workload"],
                                     "ring_fraction_of_copy": round(value / ref["value"], 4)}
         configs = {}
+        # each config beside a plain register-path copy of its bytes with its
+        # walk (no LDS, no ring): the 4 KiB tile, the contiguous tensor, the
+        # paired 128x32 tiles, the rank-5 tiles and stages
+        walk_ref = {"c1": "tile_ref", "c2": "copy_ref", "c3": "tiles_copy_ref", "c5": "widen_tiles_ref"}
         for c in ("c1", "c2", "c3", "c5"):
             configs[c] = measure_config(c, ctx, args.steps, args.warmup)
+            r = measure_config(walk_ref[c], ctx, args.steps, args.warmup)
+            v, rv = configs[c]["value"], r["value"]
+            configs[c]["reference"] = {"workload": r["config"]["workload"], "value": rv, "unit": r["unit"],
+                                       "fraction": round(rv / v if r["unit"].startswith("us") else v / rv, 4)}
+            if r.get("kernel_us") is not None:
+                configs[c]["reference"]["kernel_us"] = r["kernel_us"]
             if not args.no_cpu_baseline:
                 configs[c]["cpu_baseline"] = cpu_baseline_config(c, args.config_cpu_seconds)
         result["configs"] = configs
