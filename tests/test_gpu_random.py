@@ -4,7 +4,10 @@ every swizzle mode, 64-256 threads, 1-4 ring slots, one workgroup per tile
 or persistent grids.  A configuration the planner declines (or that needs
 more LDS than a workgroup has) is skipped and counted; the rest must match
 the oracle bit for bit (exp: within one ulp; row sums of small integers:
-exactly)."""
+exactly).  ACP_RANDOM_CASES sets the configurations per seed block (40 by
+default; 2000 runs 24 000 configurations over the six entry points)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -19,7 +22,8 @@ from tests.gpu_util import dev, empty_bytes, host, packed_strides, stream, ulp_d
 NP = {"u8": np.uint8, "u16": np.uint16, "u32": np.uint32, "f16": np.float16, "f32": np.float32}
 BITS = {1: np.uint8, 2: np.uint16, 4: np.uint32}
 SKIP = (acp.ACP_ERR_DECLINED, acp.ACP_ERR_UNSUPPORTED, acp.ACP_ERR_LDS)
-CASES = 40
+CASES = int(os.environ.get("ACP_RANDOM_CASES", "40"))
+SEED_BLOCKS = [0, max(1000, CASES)]   # two disjoint blocks of CASES seeds
 
 
 def say(msg):
@@ -136,7 +140,7 @@ def _tally(ran, total, floor):
     assert ran >= floor, f"only {ran} of {total} random configurations ran"
 
 
-@pytest.mark.parametrize("seed0", [0, 1000])
+@pytest.mark.parametrize("seed0", SEED_BLOCKS)
 def test_random_tile_copy(seed0):
     ran = 0
     for seed in range(seed0, seed0 + CASES):
@@ -164,7 +168,7 @@ def test_random_tile_copy(seed0):
     _tally(ran, CASES, CASES // 2)
 
 
-@pytest.mark.parametrize("seed0", [0, 1000])
+@pytest.mark.parametrize("seed0", SEED_BLOCKS)
 def test_random_tile_ewise(seed0):
     ran = 0
     for seed in range(seed0, seed0 + CASES):
@@ -197,7 +201,7 @@ def test_random_tile_ewise(seed0):
     _tally(ran, CASES, CASES // 2)
 
 
-@pytest.mark.parametrize("seed0", [0, 1000])
+@pytest.mark.parametrize("seed0", SEED_BLOCKS)
 def test_random_stream_ewise(seed0):
     ran = 0
     for seed in range(seed0, seed0 + CASES):
@@ -232,7 +236,7 @@ def test_random_stream_ewise(seed0):
     _tally(ran, CASES, CASES // 2)
 
 
-@pytest.mark.parametrize("seed0", [0, 1000])
+@pytest.mark.parametrize("seed0", SEED_BLOCKS)
 def test_random_two_tensor_stream(seed0):
     ran = 0
     for seed in range(seed0, seed0 + CASES):
@@ -261,7 +265,7 @@ def test_random_two_tensor_stream(seed0):
     _tally(ran, CASES, CASES // 2)
 
 
-@pytest.mark.parametrize("seed0", [0, 1000])
+@pytest.mark.parametrize("seed0", SEED_BLOCKS)
 def test_random_tile_reduce(seed0):
     ran = 0
     for seed in range(seed0, seed0 + CASES):
@@ -297,7 +301,7 @@ def test_random_tile_reduce(seed0):
     _tally(ran, CASES, CASES // 2)
 
 
-@pytest.mark.parametrize("seed0", [0, 1000])
+@pytest.mark.parametrize("seed0", SEED_BLOCKS)
 def test_random_row_reduction(seed0):
     ran = 0
     for seed in range(seed0, seed0 + CASES):
