@@ -110,6 +110,8 @@ def parse():
     ap.add_argument("--wg-per-cu", type=int, default=1)
     ap.add_argument("--c5-stage", default="1,1,1,64,64", help="c5: the stage box (outermost first)")
     ap.add_argument("--c5-box", default="1,2,16,64,64", help="c5: the tile box (outermost first)")
+    ap.add_argument("--c5-swizzle", type=int, default=128, choices=[0, 32, 64, 128],
+                    help="c5: the LDS swizzle span in bytes (0: none)")
     ap.add_argument("--sets", type=int, default=3, help="rotated buffer sets")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="budget of the streamed-fma oracle sample")
     ap.add_argument("--config-cpu-seconds", type=float, default=2.0, help="budget of each config's oracle sample")
@@ -259,20 +261,22 @@ def build(name, ctx, stages=None):
         shape, pitch = (4, 8, 64, 128, 256), 264
         c5_stage = tuple(int(v) for v in args.c5_stage.split(","))
         c5_box = tuple(int(v) for v in args.c5_box.split(","))
+        c5_swz = {0: acp.ACP_SWIZZLE_NONE, 32: acp.ACP_SWIZZLE_32B, 64: acp.ACP_SWIZZLE_64B,
+                  128: acp.ACP_SWIZZLE_128B}[args.c5_swizzle]
         c5_wgs = 0 if args.workgroups is None else args.workgroups
         storage, strides = W.padded_uniform_f16(shape, pitch=pitch, seed=5)
         n = int(np.prod(shape))
         for _ in range(sets):
             xd, yd = ctx.to_dev(storage), ctx.empty(n * 4)
-            xdesc = acp.acp_encode_tiled("f16", xd, shape, strides, c5_box, acp.ACP_SWIZZLE_128B)
+            xdesc = acp.acp_encode_tiled("f16", xd, shape, strides, c5_box, c5_swz)
             ydesc = acp.acp_encode_tiled("f32", yd, shape, _packed(shape), c5_box)
             launches.append(lambda xdesc=xdesc, ydesc=ydesc, keep=(xd, yd):
                             acp.acp_stream_ewise("exp", ydesc, xdesc, None, None, c5_stage, S, threads, c5_wgs,
                                                  stream))
         out = dict(bytes=n * 2 + n * 4, dtype="f16->f32",
                    config={"workload": f"rank-5 exp (4,8,64,128,256) f16 pitch 264 -> f32, box {c5_box}, "
-                                       f"{S}-stage swizzled ring, stage {c5_stage}"},
-                   key=f"stream_exp_rank5_s{S}")
+                                       f"{S}-stage ring, {args.c5_swizzle}-byte swizzle, stage {c5_stage}"},
+                   key=f"stream_exp_rank5_s{S}" + ("" if args.c5_swizzle == 128 else f"_swz{args.c5_swizzle}"))
     elif name == "pointwise":
         rows, S, threads = args.rows or 4, args.stages or 2, args.threads or 256
         shape, stage = (128, 500, 1024), (1, rows, 1024)
