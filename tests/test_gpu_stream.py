@@ -195,16 +195,21 @@ def test_exp_exhaustive_f16_inputs_within_one_ulp():
     print(f"exp table: {np.count_nonzero(d == 0)} / {len(d)} bit-exact", flush=True)
 
 
-def test_c5_small_rank5_exp():
+@pytest.mark.parametrize("mode,threads", [(acp.ACP_SWIZZLE_128B, 256), (acp.ACP_SWIZZLE_64B, 256),
+                                          (acp.ACP_SWIZZLE_32B, 256), (acp.ACP_SWIZZLE_32B, 128),
+                                          (acp.ACP_SWIZZLE_32B, 512)])
+def test_c5_small_rank5_exp(mode, threads):
+    # every swizzle mode, at 2, 4 and 1 rounds per wave under the 32-byte one
     shape, pitch = (1, 2, 4, 64, 128), 136
-    say(f"C5 small rank-5 exp {shape} pitch {pitch}")
+    say(f"C5 small rank-5 exp {shape} pitch {pitch} swizzle {mode} threads {threads}")
     storage, strides = W.padded_uniform_f16(shape, pitch=pitch, seed=5)
     xd = dev(storage)
     n = int(np.prod(shape))
     yd = empty_bytes(n * 4)
-    xdesc = encode("f16", xd, shape, strides, (1, 2, 4, 64, 64), acp.ACP_SWIZZLE_128B)
+    xdesc = encode("f16", xd, shape, strides, (1, 2, 4, 64, 64), mode)
     ydesc = encode("f32", yd, shape, packed_strides(shape), (1, 2, 4, 64, 64))
-    acp.acp_stream_ewise("exp", ydesc, xdesc, None, None, (1, 1, 1, 64, 64), 4, 256, 0, stream())
+    acp.acp_stream_ewise("exp", ydesc, xdesc, None, None, (1, 1, 1, 64, 64), 4, threads, 0, stream())
+    assert acp.acp_last_kernel().startswith("general stream"), acp.acp_last_kernel()
     y = host(yd, np.float32, shape)
     x = W.strided_view(storage, shape, strides)
     ref = REF.ewise("exp", [x], np.float32)
@@ -238,7 +243,8 @@ def test_c5_full_size_matches_exp_table():
 
 @pytest.mark.parametrize("threads,stage_box,mode", [(256, (1, 2, 64, 128), 3), (256, (1, 1, 64, 128), 3),
                                                     (64, (1, 1, 8, 128), 3), (256, (1, 1, 64, 128), 1),
-                                                    (64, (1, 1, 8, 128), 2)])
+                                                    (64, (1, 1, 8, 128), 2), (256, (1, 1, 64, 64), 1),
+                                                    (512, (1, 1, 64, 128), 1)])
 def test_widening_stream_pieces_ragged(threads, stage_box, mode):
     # float16 -> float32 sqrt: 8-byte input pieces, 16-byte stores; 70 rows
     # = 64 + 6 cut the last stage; padded input pitch 136
