@@ -27,6 +27,9 @@ Other modes (measurement aids):
                     and pointwise / reduce / rowsum)
   --fixed-cost      the streamed fma and the reference copy over 1..128 slabs of
                     the tensor: per-launch fixed cost and per-byte rate of each
+  --copy-sweep      plain register-path copies of the c4 bytes in 10 workgroup
+                    shapes x 4 grids, and the reference shape under every pair
+                    of load / store cache policies
 """
 from __future__ import annotations
 
@@ -94,7 +97,9 @@ def parse():
                              "reduce", "rowsum"],
                     help="measure one workload alone (default: c4 with ring_stages and configs); calib: torch's "
                          "copy of 256 MiB, the known-size kernel that scales HBM counters; copy_ref / read_ref / "
-                         "write_ref: the library's register-path reference streams over the c4 tensor")
+                         "write_ref: the library's register-path reference streams over the c4 tensor; "
+                         "widen_ref: a contiguous f16 -> f32 widening stream; widen_tiles_ref / tiles_copy_ref / "
+                         "tile_ref: plain copies with the walks of c5, c3 and c1")
     ap.add_argument("--stages", type=int, default=None,
                     help="ring slots (default: the measured best per workload; c4 and c5: 4)")
     ap.add_argument("--z-staging", default="ring", choices=["ring", "set"],
