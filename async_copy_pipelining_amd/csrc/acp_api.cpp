@@ -111,7 +111,8 @@ int device_lds_limit() { return device_attr(hipDeviceAttributeMaxSharedMemoryPer
 // defaults are the measured best on MI355X):
 //   ACP_XCD_REMAP=0  keep blockIdx order for persistent grids (default: tiles
 //                    of consecutive workgroups stay on one XCD, except for
-//                    copies of whole 128-byte lines); =2 remap those too
+//                    copies of whole 128-byte lines on a 2-D tile walk); =2
+//                    remap those too
 //   ACP_STORE_NT=0   cached stores (default: non-temporal)
 //   ACP_LOAD_NT=0|1  cached / non-temporal direct-to-LDS loads (default:
 //                    non-temporal for contiguous stages on a linear grid)
@@ -544,10 +545,13 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   if (q.workgroups > 0) grid = static_cast<unsigned>(q.workgroups);
   // consecutive tiles (which often share cache lines at their edges) run on
   // one XCD and hence one L2: blockIdx b -> (b % 8) * (G / 8) + b / 8.
-  // Copies whose staged rows are whole 128-byte lines share no line with
-  // their neighbours and measured faster without it (128x32 float16 tiles
-  // in pairs over [128,500,1024]: 4.69 TB/s against 4.48).
-  const bool whole_lines = q.mode == 0 && (static_cast<int64_t>(q.stage_box[r - 1]) * ei) % 128 == 0;
+  // Copies walking a 2-D tile grid whose staged rows are whole 128-byte
+  // lines share no line with their neighbours and measured faster without
+  // it (128x32 float16 tiles in pairs over [128,500,1024]: 4.69 TB/s against
+  // 4.48); copies of contiguous tiles on a linear grid keep it (8 KiB tiles:
+  // 6.25-6.27 TB/s against 6.19).
+  const bool whole_lines =
+      q.mode == 0 && !A.lin && (static_cast<int64_t>(q.stage_box[r - 1]) * ei) % 128 == 0;
   const int remap = xcd_remap_mode();
   A.xcd_remap = (grid % 8 == 0 && grid >= 16 && remap != 0 && (!whole_lines || remap == 2)) ? 1 : 0;
   L->grid = grid;

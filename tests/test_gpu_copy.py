@@ -64,7 +64,11 @@ def test_linear_grid_tile_copies(dt, shape, box, swz, threads, kind):
     src = encode(dt, xd, shape, st, box, swz)
     dst = encode(dt, yd, shape, st, box, swz)
     acp.acp_tile_copy(src, dst, threads, stream())
-    assert acp.acp_last_kernel().startswith(kind), acp.acp_last_kernel()
+    kernel = acp.acp_last_kernel()
+    assert kernel.startswith(kind), kernel
+    # persistent grids of contiguous tiles keep the XCD remap; one workgroup
+    # per tile (grid below 16 or not a multiple of 8) has none
+    assert kernel.endswith(" xcd-remap") == (" grid 256 " in kernel), kernel
     y = host(yd, np.uint8)
     assert np.array_equal(y[:x.nbytes].view(npdt).reshape(shape), x)
     assert np.all(y[x.nbytes:] == 0x5A)
