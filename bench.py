@@ -438,6 +438,43 @@ def roofline(wl, avg_ms, median_ms):
             "median_event_bracketed_launch_ms": round(median_ms, 5), "kernel_source_hash": kernel_hash()}
 
 
+def c1_graph_replay_us(ctx, steps):
+    """The swizzled 8x256 tile copy with the host out of the loop: `steps`
+    launches (rotating buffer sets) captured in one HIP graph on a side
+    stream and replayed; microseconds per launch, and whether the replayed
+    copies are bit-identical."""
+    torch, acp, W = ctx.torch, ctx.acp, ctx.W
+    x = W.tile_bits_f16((8, 256), seed=1)
+    shape = x.shape
+    bufs = [(ctx.to_dev(x), ctx.empty(x.nbytes)) for _ in range(ctx.args.sets)]
+    descs = [(acp.acp_encode_tiled("f16", xd, shape, _packed(shape), shape, acp.ACP_SWIZZLE_128B),
+              acp.acp_encode_tiled("f16", yd, shape, _packed(shape), shape, acp.ACP_SWIZZLE_128B)) for xd, yd in bufs]
+    for xdesc, ydesc in descs:          # plan and cache the launches outside the capture
+        acp.acp_tile_copy(xdesc, ydesc, 64, ctx.stream)
+    torch.cuda.synchronize()
+    for _, yd in bufs:
+        yd.zero_()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(steps):
+            xdesc, ydesc = descs[i % len(descs)]
+            acp.acp_tile_copy(xdesc, ydesc, 64, h)
+    g.replay()
+    torch.cuda.synchronize()
+    exact = all(torch.equal(xd, yd) for xd, yd in bufs)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / steps
+    del g
+    return round(us, 2), exact
+
+
 def measure_config(name, ctx, steps, warmup):
     """One of the other workloads: its throughput (microseconds per launch for
     the latency-bound single tile), the launch the library chose, and its
@@ -451,6 +488,8 @@ def measure_config(name, ctx, steps, warmup):
         entry = {"value": round(avg * 1e3, 2), "unit": "us per launch", "back_to_back_us": round(avg * 1e3, 2),
                  "event_bracketed_median_us": round(med * 1e3, 2),
                  "kernel_us": _profile_field(wl["key"], "kernel_average_ns")}
+        if name == "c1":
+            entry["graph_replay_us"], entry["graph_replay_bit_exact"] = c1_graph_replay_us(ctx, steps)
         if entry["kernel_us"] is not None:
             entry["kernel_us"] = round(entry["kernel_us"] / 1e3, 2)
     else:
