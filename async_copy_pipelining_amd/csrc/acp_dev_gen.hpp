@@ -609,6 +609,14 @@ __device__ __forceinline__ void gen_body(CArgs* A, unsigned char* lds, uint32_t 
       return;
     }
   }
+  // grouped reduce-add: atomics only on a group's last trip, counted as none
+  // per trip (the waits are then only stronger), one tile per trip
+  if constexpr (MODE == 3 && GROUP) {
+    if (tpt_log2 == 0) {
+      run_ring_fixed<NS * OUTER, 0>(p, n, uni(A->stages));
+      return;
+    }
+  }
   const int d = (NS * OUTER + ((OP::ROW && !SROW) ? L.ab_instr : 0)) << tpt_log2;
   // grouped reduce-add stores only on a group's last trip: counting none
   // per trip only makes the waits stronger
@@ -616,15 +624,15 @@ __device__ __forceinline__ void gen_body(CArgs* A, unsigned char* lds, uint32_t 
   run_ring(p, n, uni(A->stages), d, st << tpt_log2);
 }
 
-// Copies with non-temporal loads and stores (the default for tile copies)
-// get a body with the cache policy fixed at compile time, so no load or
-// store of a trip branches on it.
+// Copies and grouped reduce-adds with non-temporal loads and stores get a
+// body with the cache policy fixed at compile time, so no load or store of a
+// trip branches on it.
 template <class OP, int MODE, int OUTER, bool SROW, int ZSET = 0, bool GROUP = false>
 __global__ __launch_bounds__(1024) void gen_kernel_t(const EngineArgs) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
   const uint32_t warm = prefetch_kargs();
   CArgs* A = kargs();
-  if constexpr (MODE == 0) {
+  if constexpr (MODE == 0 || (MODE == 3 && GROUP)) {
     if (A->load_nt && A->store_nt) {
       gen_body<OP, MODE, OUTER, SROW, ZSET, GROUP, true>(A, lds, warm);
       return;
