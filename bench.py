@@ -364,6 +364,9 @@ def build(name, ctx, stages=None):
                    key="widen_tiles_reference_rank5")
     elif name in ("copy_ref", "read_ref", "write_ref"):
         nbytes = 128 * 500 * 1024 * 4
+        # Reads alone need more bytes in flight than one 16 KiB batch per CU:
+        # the read-only stream runs two workgroups per CU by default.
+        Gr = 2 * G if args.workgroups is None else G
         for _ in range(sets):
             xd = ctx.torch.ones(nbytes, dtype=ctx.torch.uint8, device=ctx.dev)
             yd = ctx.empty(nbytes)
@@ -371,7 +374,7 @@ def build(name, ctx, stages=None):
             if name == "copy_ref":
                 launches.append(lambda xd=xd, yd=yd: acp.acp_debug_stream_copy(yd, xd, nbytes, G, stream))
             elif name == "read_ref":
-                launches.append(lambda xd=xd, s=sums: acp.acp_debug_stream_read(xd, nbytes, s, G, stream))
+                launches.append(lambda xd=xd, s=sums: acp.acp_debug_stream_read(xd, nbytes, s, Gr, stream))
             else:
                 launches.append(lambda yd=yd: acp.acp_debug_stream_fill(yd, nbytes, 0x3F800000, G, stream))
         what = {"copy_ref": ("copy", 2 * nbytes, "stream_copy_reference_262MB"),
@@ -379,7 +382,7 @@ def build(name, ctx, stages=None):
                 "write_ref": ("write-only stream", nbytes, "stream_write_reference_262MB")}[name]
         out = dict(bytes=what[1], dtype="u8",
                    config={"workload": f"reference register-path {what[0]} of 262144000 B (the c4 tensor), "
-                                       f"{G} workgroups"},
+                                       f"{Gr if name == 'read_ref' else G} workgroups"},
                    key=what[2])
     elif name == "calib":
         nbytes = 256 << 20
