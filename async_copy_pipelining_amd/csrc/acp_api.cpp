@@ -547,8 +547,8 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   // one XCD and hence one L2: blockIdx b -> (b % 8) * (G / 8) + b / 8.
   // Copies walking a 2-D tile grid whose staged rows are whole 128-byte
   // lines share no line with their neighbours and measured faster without
-  // it (128x32 float16 tiles in pairs over [128,500,1024]: 4.69 TB/s against
-  // 4.48); copies of contiguous tiles on a linear grid keep it (8 KiB tiles:
+  // it (128x32 float16 tiles in pairs over [128,500,1024]: 4.79 TB/s against
+  // 4.60); copies of contiguous tiles on a linear grid keep it (8 KiB tiles:
   // 6.25-6.27 TB/s against 6.19).
   const bool whole_lines =
       q.mode == 0 && !A.lin && (static_cast<int64_t>(q.stage_box[r - 1]) * ei) % 128 == 0;
@@ -681,12 +681,12 @@ int device_cu_count() { return device_attr(hipDeviceAttributeMultiprocessorCount
 // (default 2); a group (one ring trip) is 1, 2 or 4 consecutive tiles.
 // Defaults, the best measured on MI355X (the environment overrides them):
 // * copy: one tile per trip and one workgroup per CU (fewer concurrent
-//   streams keep DRAM pages open; 128x32 float16 tiles ran 4.1 TB/s at one
-//   workgroup per CU against 3.2-3.3 TB/s at 2-4);
+//   streams keep DRAM pages open; 128x32 float16 tiles, one per trip, ran
+//   3.9 TB/s at one workgroup per CU against 3.4 TB/s at 2 or 4);
 // * elementwise: trips of about 16 KiB (ACP_TILES_PER_TRIP: 1, 2, 4) and
 //   about 32 KiB of loads in flight per CU (ACP_TILE_WG_PER_CU), within 32
-//   waves per CU and the LDS (32x32 float32 sqrt: 5.0-5.4 TB/s with 4 tiles
-//   per trip against 4.5-4.9 with one).
+//   waves per CU and the LDS (32x32 float32 sqrt: 6.1 TB/s with 4 tiles per
+//   trip against 5.7 with two and 4.2 with one).
 int tile_wg_per_cu_env() {
   static const int v = [] {
     const char* e = std::getenv("ACP_TILE_WG_PER_CU");
@@ -771,7 +771,7 @@ acp_status build_tile_copy(const acp_tile_desc* src, const acp_tile_desc* dst, i
   // instruction reads and writes whole lines instead of line pieces; each
   // tile still moves in its own rounds of the partition.  A copy's result
   // does not depend on how tiles are grouped into trips.  128x32 float16
-  // tiles over [128,500,1024]: 4.6 TB/s paired against 4.1-4.3 alone.
+  // tiles over [128,500,1024]: 4.6-4.8 TB/s paired against 3.9 alone.
   // ACP_TILE_MERGE=0 keeps one tile per trip.
   static const bool merge_ok = env_flag("ACP_TILE_MERGE", true);
   const int r = s.rank;
@@ -852,7 +852,7 @@ acp_status build_tile_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_
   acp_status st = prepare(q, &L);
   if (st != ACP_OK) return st;
   // The linear tile kernel streams best with one workgroup per CU (32x32
-  // float32 sqrt: 6.00-6.03 against 5.87-5.88 TB/s with two); the general
+  // float32 sqrt: 6.13 against 5.98 TB/s with two); the general
   // kernel keeps the schedule's count, whose extra waves cover the LDS round
   // trip of its output image.
   const int cus = device_cu_count();

@@ -24,11 +24,15 @@ def test_profile_summaries_name_their_commands_and_kernel_sources():
     for name in names:
         text = open(os.path.join(PROFILES, name), encoding="utf-8").read()
         assert re.search(r"^kernel_source_hash: [0-9a-f]{16}$", text, re.M), name
-        cmds = re.findall(r"^\s+rocprofv3 .* -- python3 \$R/bench\.py .*$", text, re.M)
-        assert cmds, name
-        for c in cmds:
+        # a profiled run (optionally with the row's environment exported
+        # first), or the plain default bench run whose line a summary records
+        cmds = re.findall(r"^\s+(?:<env> )?rocprofv3 .* -- python3 \$R/bench\.py .*$", text, re.M)
+        plain = re.findall(r"^\s+python3 \$R/bench\.py.*$", text, re.M)
+        assert cmds or plain, name
+        for c in cmds + plain:
             # only committed files run: the bench itself, no helper scripts
             assert "_work" not in c, c
+        for c in cmds:
             assert re.search(r" -d \$R/\S+ ", c), c       # output under the repository root
 
 
