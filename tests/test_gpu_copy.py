@@ -398,12 +398,12 @@ def test_reference_read_and_fill_streams():
     # the one-direction measurement references: the read stream's per-
     # workgroup XORs fold to the XOR of every 16-byte word of the source;
     # the fill writes its pattern over exactly the requested bytes
-    n = (3 << 20) + 4096 + 48                     # a short last block
+    n = (9 << 20) + 4096 + 48                     # a short last block; 577 blocks of 16 KiB
     say(f"reference read / fill streams over {n} bytes")
     rng = np.random.default_rng(31)
     x = rng.integers(0, 2**32, size=n // 4, dtype=np.uint64).astype(np.uint32)
     xd = dev(x)
-    for wgs in (0, 7, 300):
+    for wgs in (0, 7, 300, 512):                  # 512: two per CU, as the bench's read reference
         sums = empty_bytes(16 * 512, 0x00)
         acp.acp_debug_stream_read(xd, n, sums, wgs, stream())
         g = wgs or 256
