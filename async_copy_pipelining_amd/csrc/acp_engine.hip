@@ -1,5 +1,6 @@
 // Kernel registry, launch helpers, the two debug kernels of the engine and the
 // register-path reference copy.
+#include <mutex>
 #include <unordered_map>
 
 #include "acp_engine_impl.hpp"
@@ -299,20 +300,31 @@ const void* engine_kernel(const KernelKey& k) {
   return lookup_stream_f16(k);
 }
 
-// Raise a kernel's dynamic-LDS limit only when a launch needs more than any
-// earlier one on this device (per thread: the attribute is process state, so
-// a second thread setting it again is harmless).
+// Raise a kernel's dynamic-LDS limit when a launch needs more than any
+// earlier one on this device.  The attribute is process state shared by
+// every calling thread, so it only ever grows: one process-wide record,
+// changed under a lock, holds the limit set per (kernel, device), and a
+// thread-local copy answers repeat launches without the lock (a limit once
+// set is never lowered, so the copy stays valid).
 hipError_t ensure_lds_limit(const void* kernel, unsigned lds_bytes) {
-  thread_local std::unordered_map<uint64_t, unsigned> done;  // (kernel, device) -> limit set
+  thread_local std::unordered_map<uint64_t, unsigned> seen;  // (kernel, device) -> limit known to be set
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   const uint64_t key = (static_cast<uint64_t>(reinterpret_cast<uintptr_t>(kernel)) << 8) ^ static_cast<uint64_t>(dev);
-  const auto it = done.find(key);
-  if (it != done.end() && it->second >= lds_bytes) return hipSuccess;
-  const hipError_t err =
-      hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_bytes));
-  if (err == hipSuccess) done[key] = lds_bytes;
-  return err;
+  const auto it = seen.find(key);
+  if (it != seen.end() && it->second >= lds_bytes) return hipSuccess;
+  static std::mutex lock;
+  static std::unordered_map<uint64_t, unsigned> set;  // (kernel, device) -> limit set in this process
+  std::lock_guard<std::mutex> guard(lock);
+  unsigned& limit = set[key];
+  if (limit < lds_bytes) {
+    const hipError_t err =
+        hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_bytes));
+    if (err != hipSuccess) return err;
+    limit = lds_bytes;
+  }
+  seen[key] = limit;
+  return hipSuccess;
 }
 
 hipError_t engine_launch(const void* kernel, const EngineArgs& args, unsigned grid, unsigned block,

@@ -252,3 +252,47 @@ def test_memory_shared_between_a_written_tensor_and_another_operand_is_rejected(
     with pytest.raises(acp.AcpError) as e:
         acp.acp_tile_ewise("sqrt", h, [x], 256)
     assert e.value.status == acp.ACP_ERR_INVALID
+
+
+def test_host_calls_from_many_threads():
+    # encode and plan from eight threads at once: every answer, and every
+    # rejection reason (kept per thread), equals the single-threaded one
+    import threading
+    cases = [c[:7] for c in WORKED] + [
+        ("f16", (8, 256), (256, 1), (8, 300), 0, 64, True),           # declined: no vector width fits
+        ("f32", (64, 30), (30, 1), (4, 30), 3, 64, False),            # declined: row not in 16-byte chunks
+        ("f16", (8, 256), (256, 2), (8, 256), 0, 64, True),           # declined: innermost stride not 1
+        ("f32", (600, 64), (64, 1), (600, 64), 0, 96, False),         # invalid: threads not a multiple of 64
+    ]
+
+    def run(case):
+        dt, shape, strides, box, swz, threads, copy_only = case
+        try:
+            d = acp.acp_encode_tiled(dt, FAKE_BASE, shape, strides, box, swz)
+            q = acp.acp_plan_query(d, threads, copy_only)
+            return ("ok", tuple(sorted((k, str(v)) for k, v in q.items())))
+        except acp.AcpError as e:
+            return ("err", e.status, str(e))
+
+    want = [run(c) for c in cases]
+    assert any(w[0] == "err" for w in want) and any(w[0] == "ok" for w in want)
+    errors = []
+    start = threading.Barrier(8)
+
+    def worker(k):
+        order = list(range(len(cases)))
+        random.Random(k).shuffle(order)
+        start.wait()
+        for _ in range(200):
+            for i in order:
+                got = run(cases[i])
+                if got != want[i]:
+                    errors.append((k, i, got, want[i]))
+                    return
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors[:3]
