@@ -1007,7 +1007,7 @@ acp_status build_tile_reduce(acp_op op, const acp_tile_desc* dst, const acp_tile
         // slots (ACP_REDUCE_WG_PER_CU, ACP_REDUCE_STAGES): the best of 2-8
         // workgroups per CU x 2-4 slots x 4 or 8 KiB tiles measured on 128
         // float32 contributions per element of [500,1024] (8 KiB tiles, two
-        // per CU: 4.8 TB/s).  Few destination tiles: split each one's
+        // per CU: 5.1 TB/s).  Few destination tiles: split each one's
         // contributions over k workgroups (k atomic adds per element instead
         // of one).
         int64_t k = 1;
