@@ -107,6 +107,15 @@ std::atomic<int> g_cu_count[kMaxDevices];
 
 int device_lds_limit() { return device_attr(hipDeviceAttributeMaxSharedMemoryPerBlock, g_lds_limit, 65536); }
 
+// ACP_TILE_STAGES (1..4): ring slots of persistent tile grids; 0 when unset.
+int tile_stages_env() {
+  static const int v = [] {
+    const char* e = std::getenv("ACP_TILE_STAGES");
+    return (e && std::atoi(e) > 0 && std::atoi(e) <= 4) ? std::atoi(e) : 0;
+  }();
+  return v;
+}
+
 // Launch knobs read once from the environment (measurement aids; the
 // defaults are the measured best on MI355X):
 //   ACP_XCD_REMAP=0  keep blockIdx order for persistent grids (default: tiles
@@ -127,6 +136,8 @@ int device_lds_limit() { return device_attr(hipDeviceAttributeMaxSharedMemoryPer
 //   ACP_SCALAR_ROWS=0  stage per-row scalars in LDS even when rows are uniform per wave block
 //   ACP_REDUCE_LOCAL=0, ACP_REDUCE_GROUPED=0  row sums through LDS partials only; reduce-add over
 //                    batch dims with one atomic per staged element
+//   ACP_BLOCKED_COPY=0  whole-line tile copies on persistent grids walk every
+//                    G-th tile instead of a blocked run of consecutive tiles
 bool env_flag(const char* name, bool dflt) {
   const char* e = std::getenv(name);
   if (!e || !e[0]) return dflt;
@@ -492,7 +503,22 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   const int64_t groups = (n_tiles + (int64_t(1) << tpt_log2) - 1) >> tpt_log2;
   const int64_t trips_max = subs * ((q.workgroups > 0 && q.workgroups < groups)
                                         ? (groups + q.workgroups - 1) / q.workgroups : 1);
-  const int slots = static_cast<int>(q.stages < trips_max ? q.stages : trips_max);
+  // Copies whose staged rows are whole 128-byte lines, on a persistent grid
+  // of the general kernel, walk blocked runs of consecutive tiles (workgroup
+  // w: tiles w * per, ..., (w + 1) * per - 1) instead of every G-th tile, so
+  // the trips a workgroup has in flight cover neighbouring pieces of the
+  // same rows, through a ring of 3 slots (128x32 float16 tiles in pairs over
+  // [128,500,1024]: 4.88-4.90 TB/s against 4.70-4.80 on the cyclic walk,
+  // and 0-1.4 % more with 3 slots than with 2 on three boxes).  Tiles of half lines keep the
+  // cyclic walk with the XCD remap (3.83 against 3.77 TB/s).
+  // ACP_BLOCKED_COPY=0 keeps the cyclic walk everywhere.
+  static const bool blocked_ok = env_flag("ACP_BLOCKED_COPY", true);
+  const bool whole_lines =
+      q.mode == 0 && !A.lin && (static_cast<int64_t>(q.stage_box[r - 1]) * ei) % 128 == 0;
+  const bool blocked = blocked_ok && whole_lines && L->key.mode == 4 && q.workgroups > 0 && tpt_log2 == 0 &&
+                       n_tiles > q.workgroups;
+  const int want_slots = (blocked && tile_stages_env() == 0) ? 3 : q.stages;
+  const int slots = static_cast<int>(want_slots < trips_max ? want_slots : trips_max);
   A.stages = slots < 1 ? 1 : slots;
   // The staged output image lies after the ring, one per workgroup: each
   // lane writes its chunks there and reads the same bytes back before its
@@ -543,15 +569,14 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   }
   unsigned grid = static_cast<unsigned>(n_tiles);
   if (q.workgroups > 0) grid = static_cast<unsigned>(q.workgroups);
+  if (blocked) A.per_wg = static_cast<uint32_t>((n_tiles + grid - 1) / grid);
   // consecutive tiles (which often share cache lines at their edges) run on
   // one XCD and hence one L2: blockIdx b -> (b % 8) * (G / 8) + b / 8.
   // Copies walking a 2-D tile grid whose staged rows are whole 128-byte
-  // lines share no line with their neighbours and measured faster without
-  // it (128x32 float16 tiles in pairs over [128,500,1024]: 4.79 TB/s against
-  // 4.60); copies of contiguous tiles on a linear grid keep it (8 KiB tiles:
-  // 6.25-6.27 TB/s against 6.19).
-  const bool whole_lines =
-      q.mode == 0 && !A.lin && (static_cast<int64_t>(q.stage_box[r - 1]) * ei) % 128 == 0;
+  // lines share no line with their neighbours and go without it (128x32
+  // float16 tiles in pairs over [128,500,1024]: 4.79 TB/s against 4.60 on
+  // the cyclic walk, equal on the blocked one); copies of contiguous tiles
+  // on a linear grid keep it (8 KiB tiles: 6.25-6.27 TB/s against 6.19).
   const int remap = xcd_remap_mode();
   A.xcd_remap = (grid % 8 == 0 && grid >= 16 && remap != 0 && (!whole_lines || remap == 2)) ? 1 : 0;
   L->grid = grid;
@@ -572,7 +597,7 @@ std::string describe(const Launch& L) {
          " rounds " + std::to_string(L.args.outer) + " srow " + std::to_string(L.key.srow) + " variant " +
          std::to_string(L.key.variant) + " grid " + std::to_string(L.grid) + " threads " +
          std::to_string(L.block) + " slots " + std::to_string(L.args.stages) + " lds " + std::to_string(L.lds) +
-         (L.args.xcd_remap ? " xcd-remap" : "") +
+         (L.key.mode == 4 && L.args.per_wg ? " blocked-walk" : "") + (L.args.xcd_remap ? " xcd-remap" : "") +
          (m == 8 || m == 10 ? std::string(L.args.red_local ? " wave-local" : " lds partials") : std::string());
 }
 
@@ -698,10 +723,7 @@ int tile_wg_per_cu_env() {
 void tile_schedule(const acp::Plan& p, int n_in, int threads, int64_t out_image, int* workgroups, int* stages,
                    int* tiles_per_trip) {
   const int env_per_cu = tile_wg_per_cu_env();
-  static const int slots = [] {
-    const char* e = std::getenv("ACP_TILE_STAGES");
-    return (e && std::atoi(e) > 0 && std::atoi(e) <= 4) ? std::atoi(e) : 2;
-  }();
+  const int slots = tile_stages_env() ? tile_stages_env() : 2;
   static const int env_tpt = [] {
     const char* e = std::getenv("ACP_TILES_PER_TRIP");
     const int v = e ? std::atoi(e) : 0;

@@ -51,6 +51,7 @@ struct CopyTilesArgs {
   uint32_t group_bytes;                 // bytes of one group row (a multiple of 16)
   uint32_t tiles_1, groups_2;           // tiles along dim 1, groups along the innermost dim
   uint32_t n_groups;
+  uint32_t per;                         // groups per workgroup of a blocked walk (0: cyclic walk)
 };
 
 template <int T, int R>
@@ -91,26 +92,30 @@ struct TileGroup {
   }
 };
 
+// Workgroup w takes groups w, w+G, ... (cyclic walk) or the run w * per,
+// ..., (w + 1) * per - 1 (blocked walk).
 template <int T, int R>
 __global__ __launch_bounds__(T) void copy_tiles_kernel(const CopyTilesArgs A) {
   const uint32_t grid = gridDim.x;
-  uint32_t g = blockIdx.x;
-  if (g >= A.n_groups) return;
+  const uint32_t step = A.per ? 1u : grid;
+  uint32_t g = A.per ? blockIdx.x * A.per : blockIdx.x;
+  const uint32_t end = A.per ? min(A.n_groups, g + A.per) : A.n_groups;
+  if (g >= end) return;
   TileGroup<T, R> a, b;
   u32x4 va[R], vb[R];
   a.locate(A, g);
   a.load(va);
   for (;;) {
-    const uint32_t g1 = g + grid;
-    const bool more1 = g1 < A.n_groups;
+    const uint32_t g1 = g + step;
+    const bool more1 = g1 < end;
     if (more1) {
       b.locate(A, g1);
       b.load(vb);
     }
     a.store(va);
     if (!more1) break;
-    const uint32_t g2 = g1 + grid;
-    const bool more2 = g2 < A.n_groups;
+    const uint32_t g2 = g1 + step;
+    const bool more2 = g2 < end;
     if (more2) {
       a.locate(A, g2);
       a.load(va);
@@ -170,6 +175,9 @@ hipError_t copy_tiles_launch(const void* src, void* dst, const int64_t* in_strid
   A.tiles_1 = tiles_1;
   A.groups_2 = groups_2;
   A.n_groups = n_groups;
+  // the library's walk for persistent tile copies: blocked runs when a
+  // group row is whole 128-byte lines, else every G-th group
+  A.per = (group_bytes % 128u == 0 && n_groups > grid) ? (n_groups + grid - 1) / grid : 0u;
   const uint32_t chunks = rows * (group_bytes / 16u);
   const void* k = nullptr;
   if (threads == 128 && chunks <= 512) k = reinterpret_cast<const void*>(&dev::copy_tiles_kernel<128, 4>);

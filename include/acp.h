@@ -353,12 +353,14 @@ acp_status acp_debug_stream_copy_shape(void* dst, const void* src, int64_t bytes
  * elements into a packed tensor `dst` of the same `shape`, with no LDS and
  * no ring.  Tiles are `box` = (1, rows, cols); `tiles_per_trip` neighbouring
  * tiles along the innermost dim form a group, and workgroup w of
- * `workgroups` (0: one per compute unit, never more than the groups) takes
- * groups w, w+G, ... in row-major order, issuing the next group's 16-byte
- * non-temporal loads before the current group's stores (two groups in
- * flight, as in a 2-slot ring).  Edge tiles are clipped to the tensor.  It
- * gives the rate a plain register-path copy reaches over the same tiles and
- * order as acp_tile_copy's persistent grid.  ACP_ERR_INVALID for null
+ * `workgroups` (0: one per compute unit, never more than the groups) walks
+ * the groups in row-major order as acp_tile_copy's persistent grid does: a
+ * run of ceil(groups / G) consecutive groups from w * ceil(groups / G) when
+ * a group row is whole 128-byte lines, else groups w, w+G, ...  It issues
+ * the next group's 16-byte non-temporal loads before the current group's
+ * stores (two groups in flight, as in a 2-slot ring).  Edge tiles are
+ * clipped to the tensor.  It gives the rate a plain register-path copy
+ * reaches over the same tiles and order as acp_tile_copy's persistent grid.  ACP_ERR_INVALID for null
  * pointers, esize not 1/2/4/8, threads not 128/256, tiles_per_trip not
  * 1/2/4, box[0] != 1, rows or groups not whole 16-byte chunks, more than 8
  * chunks per lane and group, misaligned pointers or strides, or

@@ -106,9 +106,10 @@ def test_c3_full_size_copy():
     acp.acp_tile_copy(src, dst, 128, stream())
     torch.cuda.synchronize()
     assert torch.equal(xd, yd)
-    # pairs of tiles per trip (128-byte rows, 8 rounds), whole lines: no XCD remap
+    # pairs of tiles per trip (128-byte rows, 8 rounds), whole lines: blocked
+    # runs of consecutive pairs per workgroup, no XCD remap
     kernel = acp.acp_last_kernel()
-    assert kernel.startswith("general copy vec 16 rounds 8 ") and "xcd-remap" not in kernel, kernel
+    assert kernel.startswith("general copy vec 16 rounds 8 ") and kernel.endswith(" blocked-walk"), kernel
 
 
 @pytest.mark.parametrize("mode", [1, 2, 3])
@@ -188,6 +189,7 @@ def test_swizzle_shrunk_inner_box(mode, dt, shape, box, threads):
     ((40, 130, 96), (1, 64, 32), 128),       # three tiles per row: the second pair holds one tile
     ((6, 300, 1000), (1, 128, 32), 128),     # 1000 = 31 * 32 + 8: the last tile of a row is cut
     ((8, 64, 256), (1, 16, 16), 64),         # 32-byte rows: four tiles per trip
+    ((19, 300, 320), (1, 128, 32), 128),     # 285 pairs over 256 workgroups: runs of two, the last one short
 ])
 def test_paired_tiles_per_trip(shape, box, threads):
     # a persistent copy of tiles narrower than a cache line stages
@@ -202,6 +204,9 @@ def test_paired_tiles_per_trip(shape, box, threads):
     src = encode("f16", xd, shape, packed_strides(shape), box)
     dst = encode("f16", yd, shape, ost, box)
     acp.acp_tile_copy(src, dst, threads, stream())
+    kernel = acp.acp_last_kernel()
+    if shape == (19, 300, 320):
+        assert kernel.endswith(" blocked-walk"), kernel
     y = host(yd, np.uint16).reshape(shape[0], shape[1], pitch)
     assert np.array_equal(y[:, :, :shape[-1]], x.view(np.uint16))
     assert not np.any(y[:, :, shape[-1]:])
@@ -329,6 +334,7 @@ def test_reference_copy_shape_rejects_unbuilt_shapes():
 @pytest.mark.parametrize("shape,pitch,box,tpt,threads,wgs", [
     ((3, 300, 320), 336, (1, 128, 32), 2, 128, 0),     # ragged rows; five whole pairs per tile row
     ((2, 130, 352), 352, (1, 128, 32), 2, 128, 7),     # eleven tiles: the last pair is one tile wide
+    ((5, 130, 352), 352, (1, 128, 32), 2, 128, 9),     # 60 pairs in runs of 7 over 9 workgroups, the last short
     ((2, 77, 96), 104, (1, 64, 32), 1, 128, 5),         # one tile per group, 64-byte rows
     ((1, 40, 512), 512, (1, 16, 64), 4, 256, 0),        # four tiles per group, 512-byte rows
 ])
