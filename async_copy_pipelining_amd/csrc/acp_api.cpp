@@ -702,8 +702,10 @@ int device_cu_count() { return device_attr(hipDeviceAttributeMultiprocessorCount
 
 // Tile copy and tile elementwise: the result of a tile does not depend on
 // which workgroup moves it, so large tile counts run on a persistent grid
-// that walks tile groups w, w+G, ... through a ring of ACP_TILE_STAGES slots
-// (default 2); a group (one ring trip) is 1, 2 or 4 consecutive tiles.
+// that walks tile groups w, w+G, ... (whole-line copies: a blocked run of
+// consecutive groups, see prepare) through a ring of ACP_TILE_STAGES slots
+// (default 2; 3 for those blocked copies); a group (one ring trip) is 1, 2
+// or 4 consecutive tiles.
 // Defaults, the best measured on MI355X (the environment overrides them):
 // * copy: one tile per trip and one workgroup per CU (fewer concurrent
 //   streams keep DRAM pages open; 128x32 float16 tiles, one per trip, ran

@@ -257,8 +257,9 @@ def build(name, ctx, stages=None):
                 yd, xd, 2, shape, _packed(shape), (1, 128, 32), 2, threads, G, stream))
         out = dict(bytes=x.nbytes * 2, dtype="f16",
                    config={"workload": f"reference register-path copy with the tile copy's walk: [128,500,1024] "
-                                       f"f16, 128x32 tiles in pairs along the rows, {threads} threads, {G} "
-                                       f"workgroups, two pairs in flight, no LDS, no ring"},
+                                       f"f16, 128x32 tiles in pairs along the rows, blocked runs of consecutive "
+                                       f"pairs per workgroup, {threads} threads, {G} workgroups, two pairs in "
+                                       f"flight, no LDS, no ring"},
                    key="tile_copy_reference_f16_128x500x1024")
     elif name == "c5":
         threads = args.threads or 256
