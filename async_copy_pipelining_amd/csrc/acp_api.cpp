@@ -124,7 +124,8 @@ int tile_stages_env() {
 //                    remap those too
 //   ACP_STORE_NT=0   cached stores (default: non-temporal)
 //   ACP_LOAD_NT=0|1  cached / non-temporal direct-to-LDS loads (default:
-//                    non-temporal for contiguous stages on a linear grid)
+//                    non-temporal for contiguous stages on a linear grid and
+//                    for copies of whole line-aligned 128-byte rows)
 // Non-temporal on both sides measured 6.2 TB/s against 5.8 TB/s cached for
 // the 262 MB fp32 stream (the staged data is touched once); cached loads
 // measured 3.6 against 3.1 TB/s for 128x32 float16 tiles, whose 64-byte rows
@@ -319,17 +320,21 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
     A.lin_r = lin ? lr : 0;
   }
   // Loads go out non-temporal only where no two stages share a cache line:
-  // a linear grid of contiguous stages (each input byte is read once).
-  // Elsewhere (2-D tiles whose rows are shorter than a line, padded rows)
-  // the neighbouring stage reads the rest of the line from L2.
+  // a linear grid of contiguous stages (each input byte is read once), and
+  // copies whose staged rows are whole 128-byte lines at line-aligned
+  // addresses (paired 128x32 float16 tiles over [128,500,1024]: 1.5 % faster
+  // than cached).  Elsewhere (2-D tiles whose rows are shorter than a line,
+  // padded rows) the neighbouring stage reads the rest of the line from L2.
   static const bool store_nt = env_flag("ACP_STORE_NT", true);
   static const int load_nt_env = [] {
     const char* e = std::getenv("ACP_LOAD_NT");
     return (!e || !e[0]) ? -1 : (e[0] != '0' ? 1 : 0);
   }();
   const bool contiguous_stages = A.lin && A.lin_x == p.tile_bytes() && A.lin_x % 128 == 0;
+  bool line_rows = q.mode == 0 && (static_cast<int64_t>(q.stage_box[r - 1]) * ei) % 128 == 0 && x.gbase % 128 == 0;
+  for (int d = 0; d + 1 < r; ++d) line_rows = line_rows && (x.strides[d] * ei) % 128 == 0;
   A.store_nt = store_nt ? 1 : 0;
-  A.load_nt = load_nt_env >= 0 ? load_nt_env : (contiguous_stages ? 1 : 0);
+  A.load_nt = load_nt_env >= 0 ? load_nt_env : ((contiguous_stages || line_rows) ? 1 : 0);
   if (n_tiles * subs >= (int64_t(1) << 31)) return ret(ACP_ERR_UNSUPPORTED, "more than 2^31 stages");
   A.n_tiles = static_cast<uint32_t>(n_tiles);
   A.subs = static_cast<uint32_t>(subs);
