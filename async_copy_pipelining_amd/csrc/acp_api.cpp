@@ -512,18 +512,16 @@ acp_status prepare(const EngineRequest& q, Launch* L) {
   // of the general kernel, walk blocked runs of consecutive tiles (workgroup
   // w: tiles w * per, ..., (w + 1) * per - 1) instead of every G-th tile, so
   // the trips a workgroup has in flight cover neighbouring pieces of the
-  // same rows, through a ring of 3 slots (128x32 float16 tiles in pairs over
-  // [128,500,1024]: 4.88-4.90 TB/s against 4.70-4.80 on the cyclic walk,
-  // and 0-1.4 % more with 3 slots than with 2 on three boxes).  Tiles of half lines keep the
-  // cyclic walk with the XCD remap (3.83 against 3.77 TB/s).
-  // ACP_BLOCKED_COPY=0 keeps the cyclic walk everywhere.
+  // same rows (128x32 float16 tiles in pairs over [128,500,1024]: 4.88-4.90
+  // TB/s against 4.70-4.80 on the cyclic walk, with cached loads).  Tiles of
+  // half lines keep the cyclic walk with the XCD remap (3.83 against 3.77
+  // TB/s).  ACP_BLOCKED_COPY=0 keeps the cyclic walk everywhere.
   static const bool blocked_ok = env_flag("ACP_BLOCKED_COPY", true);
   const bool whole_lines =
       q.mode == 0 && !A.lin && (static_cast<int64_t>(q.stage_box[r - 1]) * ei) % 128 == 0;
   const bool blocked = blocked_ok && whole_lines && L->key.mode == 4 && q.workgroups > 0 && tpt_log2 == 0 &&
                        n_tiles > q.workgroups;
-  const int want_slots = (blocked && tile_stages_env() == 0) ? 3 : q.stages;
-  const int slots = static_cast<int>(want_slots < trips_max ? want_slots : trips_max);
+  const int slots = static_cast<int>(q.stages < trips_max ? q.stages : trips_max);
   A.stages = slots < 1 ? 1 : slots;
   // The staged output image lies after the ring, one per workgroup: each
   // lane writes its chunks there and reads the same bytes back before its
@@ -709,8 +707,7 @@ int device_cu_count() { return device_attr(hipDeviceAttributeMultiprocessorCount
 // which workgroup moves it, so large tile counts run on a persistent grid
 // that walks tile groups w, w+G, ... (whole-line copies: a blocked run of
 // consecutive groups, see prepare) through a ring of ACP_TILE_STAGES slots
-// (default 2; 3 for those blocked copies); a group (one ring trip) is 1, 2
-// or 4 consecutive tiles.
+// (default 2); a group (one ring trip) is 1, 2 or 4 consecutive tiles.
 // Defaults, the best measured on MI355X (the environment overrides them):
 // * copy: one tile per trip and one workgroup per CU (fewer concurrent
 //   streams keep DRAM pages open; 128x32 float16 tiles, one per trip, ran
