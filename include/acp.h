@@ -186,7 +186,11 @@ acp_status acp_plan_query(const acp_tile_desc* desc, int threads, int copy_only,
  * ([tma] and [ldgsts] "Demonstration program").  One workgroup per tile
  * while the tiles fit one grid of one workgroup per CU; beyond that a
  * persistent grid (one workgroup per CU, environment ACP_TILE_WG_PER_CU)
- * walks tiles w, w+G, ... through a 2-slot ring (ACP_TILE_STAGES).
+ * walks tiles w, w+G, ... through a 2-slot ring (ACP_TILE_STAGES); tiles
+ * narrower than a 128-byte line are staged side by side in pairs (or
+ * fours), and a workgroup whose staged rows are whole lines takes a run of
+ * consecutive tiles instead (ACP_BLOCKED_COPY=0: the cyclic walk).  The
+ * result does not depend on the walk.
  * `src` and `dst` must have equal dtype, shape and box ([tma]
  * validate_copy_op); `dst` may have other strides.  ACP_ERR_INVALID when
  * the byte ranges of src and dst (base to last element) intersect. */
