@@ -250,7 +250,9 @@ acp_status acp_stream_ewise(acp_op op, const acp_tile_desc* out, const acp_tile_
  * 2^32.  Floating-point additions land in no fixed order: the result is
  * the exactly rounded sum whenever every partial sum is representable (in
  * particular with one contribution per element).  Tile counts above the
- * persistent grid walk tiles w, w+G, ... as acp_tile_copy does.  When dst
+ * grid run on a persistent grid: workgroup w walks tiles w, w+G, ..., or,
+ * when contributions are summed over a dim, a run of whole groups of the
+ * tiles that add into one destination tile.  When dst
  * has src's shape and strides (one contribution per element) and the dtype
  * is a float, no atomics are needed: both tensors ride the LDS ring and the
  * sum is stored into dst in place.
