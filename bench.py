@@ -505,6 +505,12 @@ def measure_config(name, ctx, steps, warmup):
     return entry
 
 
+def progress(msg: str) -> None:
+    """One line per measurement phase on stderr (stdout carries only the
+    JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -519,10 +525,12 @@ def main():
         copy_sweep(ctx)
         return
     name = args.workload or "c4"
+    progress(f"workload {name}: building inputs")
     wl = build(name, ctx)
     fns = wl["launches"]
     ring = None
     if name == "c4" and not args.no_ring_sweep:
+        progress("ring sweep: 2, 3 and 4 slots")
         # the 2-, 3- and 4-stage rings, back to back like `value` (measured
         # before the headline's own warm-up and timed region)
         ring = {}
@@ -536,6 +544,7 @@ def main():
     # launch of the kernel, so the event pair's time over K is the kernel's
     # average launch duration (the figure rocprofv3's kernel trace reports per
     # dispatch, plus the dispatch gap).
+    progress(f"timed region: {args.warmup} warm-up, {args.steps} steps")
     ms_per_step = time_launches(ctx, fns, args.steps, args.warmup)
     kernel = ctx.acp.acp_last_kernel()
     median = bracketed_median(ctx, fns, args.steps)
@@ -562,6 +571,7 @@ def main():
         # the same box's ceiling beside the headline: a plain register-path
         # copy (no LDS, no ring) of the same 262 MB read and written, timed
         # the same way
+        progress("copy reference")
         ref = measure_config("copy_ref", ctx, args.steps, args.warmup)
         result["copy_reference"] = {"value": ref["value"], "unit": "GB/s", "frac": ref["frac"],
                                     "workload": ref["config"]["workload"],
@@ -572,6 +582,7 @@ def main():
         # paired 128x32 tiles, the rank-5 tiles and stages
         walk_ref = {"c1": "tile_ref", "c2": "copy_ref", "c3": "tiles_copy_ref", "c5": "widen_tiles_ref"}
         for c in ("c1", "c2", "c3", "c5"):
+            progress(f"config {c} and its reference")
             configs[c] = measure_config(c, ctx, args.steps, args.warmup)
             r = measure_config(walk_ref[c], ctx, args.steps, args.warmup)
             v, rv = configs[c]["value"], r["value"]
@@ -580,9 +591,11 @@ def main():
             if r.get("kernel_us") is not None:
                 configs[c]["reference"]["kernel_us"] = r["kernel_us"]
             if not args.no_cpu_baseline:
+                progress(f"config {c}: CPU oracle sample")
                 configs[c]["cpu_baseline"] = cpu_baseline_config(c, args.config_cpu_seconds)
         result["configs"] = configs
     if not args.no_cpu_baseline:
+        progress("CPU oracle samples")
         if name == "c4":
             result["cpu_baseline"] = cpu_baseline_c4(args.cpu_seconds)
             result["cpu_baseline_all_cores"] = cpu_baseline_c4_parallel(args.cpu_seconds)
