@@ -452,3 +452,28 @@ def test_repeated_calls_reuse_or_rebuild_their_launch():
             kern = acp.acp_last_kernel()
             assert f" grid {wgs} threads {threads} slots {stages} " in kern, kern
             assert np.array_equal(host(outs[k], np.uint32, shape), ref), (rep, stages, threads, wgs, k)
+
+
+def test_ring_at_the_lds_limit_and_one_row_past_it():
+    # four 40 KiB slots take the whole 160 KiB of LDS a workgroup may hold on
+    # the MI355X: the ring runs and equals the oracle; 44 KiB slots need
+    # 176 KiB and are refused on the host (ACP_ERR_LDS) before any launch.
+    # 16 stages over 4 workgroups: 4 trips each, so the ring keeps 4 slots
+    shape = (4, 40, 1024)
+    say(f"sqrt stream {shape}, stage (1,10,1024) x 4 slots (160 KiB), 640 threads")
+    x = np.abs(W.sqrt_tiles_f32(160, seed=71)).reshape(shape)
+    xd, yd = dev(x), empty_bytes(x.nbytes)
+    st = packed_strides(shape)
+    xdesc, ydesc = encode("f32", xd, shape, st, (1, 10, 1024)), encode("f32", yd, shape, st, (1, 10, 1024))
+    acp.acp_stream_ewise("sqrt", ydesc, xdesc, None, None, (1, 10, 1024), 4, 640, 4, stream())
+    kernel = acp.acp_last_kernel()
+    assert " threads 640 slots 4 lds 163840" in kernel, kernel
+    want = REF.ewise("sqrt", [x], np.float32).view(np.uint32)
+    assert np.array_equal(host(yd, np.float32, shape).view(np.uint32), want)
+    shape2 = (4, 44, 1024)
+    x2d, y2d = empty_bytes(int(np.prod(shape2)) * 4), empty_bytes(int(np.prod(shape2)) * 4)
+    st2 = packed_strides(shape2)
+    x2, y2 = encode("f32", x2d, shape2, st2, (1, 11, 1024)), encode("f32", y2d, shape2, st2, (1, 11, 1024))
+    with pytest.raises(acp.AcpError) as e:
+        acp.acp_stream_ewise("sqrt", y2, x2, None, None, (1, 11, 1024), 4, 704, 4, stream())
+    assert e.value.status == acp.ACP_ERR_LDS and "180224" in str(e.value), str(e.value)
