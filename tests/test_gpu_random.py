@@ -5,7 +5,8 @@ or persistent grids.  A configuration the planner declines (or that needs
 more LDS than a workgroup has) is skipped and counted; the rest must match
 the oracle bit for bit (exp: within one ulp; row sums of small integers:
 exactly).  ACP_RANDOM_CASES sets the configurations per seed block (40 by
-default; 2000 runs 24 000 configurations over the six entry points)."""
+default; 2000 runs 24 000 configurations over the six entry points, and a
+quarter as many persistent whole-line copies aimed at the blocked walk)."""
 import os
 
 import numpy as np
@@ -166,6 +167,46 @@ def test_random_tile_copy(seed0):
             ran += 1
             _check("copy", host(yd, NP[dt], shape), x)
     _tally(ran, CASES, CASES // 2)
+
+
+@pytest.mark.parametrize("seed0", SEED_BLOCKS)
+def test_random_blocked_walk_copies(seed0):
+    # persistent copies whose staged rows are whole 128-byte lines walk
+    # blocked runs of consecutive tiles: ragged tile counts, narrow tiles
+    # staged in pairs, swizzles, line-aligned sources (non-temporal loads)
+    # and padded ones (cached loads); most configurations must take that walk
+    n_cases = max(8, CASES // 4)
+    ran = blocked = 0
+    for seed in range(seed0 + 50000, seed0 + 50000 + n_cases):
+        rng = np.random.default_rng(seed)
+        dt = str(rng.choice(["u8", "f16", "f32"]))
+        es = np.dtype(NP[dt]).itemsize
+        row_b = int(rng.choice([64, 128, 256]))          # tile row bytes (64: staged in pairs)
+        cols = row_b // es
+        inner = cols * int(rng.integers(2, 9))
+        rows_box = int(rng.choice([8, 16, 32, 64]))
+        n_rows = int(rng.integers(rows_box, 4 * rows_box + 1))
+        per_slab = -(-n_rows // rows_box) * (inner // cols)
+        shape = (-(-300 // per_slab) * 2 + int(rng.integers(0, 5)), n_rows, inner)
+        box = (1, rows_box, cols)
+        swz = int(rng.choice([0, 3])) if row_b <= 128 else 0
+        threads = _threads(rng, rows_box * row_b)
+        say(f"seed {seed}: blocked-walk copy {dt} {shape} box {box} swizzle {swz} threads {threads}")
+        x = _values(rng, dt, shape)
+        xd, xs = _padded(rng, x)
+        yd = empty_bytes(x.nbytes)
+        try:
+            src = acp.acp_encode_tiled(dt, xd, shape, xs, box, swz)
+            dst = acp.acp_encode_tiled(dt, yd, shape, packed_strides(shape), box, swz)
+        except acp.AcpError as e:
+            assert e.status in SKIP
+            continue
+        if _run(lambda: acp.acp_tile_copy(src, dst, threads, stream())):
+            ran += 1
+            blocked += acp.acp_last_kernel().endswith(" blocked-walk")
+            _check("copy", host(yd, NP[dt], shape), x)
+    _tally(ran, n_cases, n_cases // 2)
+    assert blocked >= ran // 2, f"{blocked} of {ran} copies took the blocked walk"
 
 
 @pytest.mark.parametrize("seed0", SEED_BLOCKS)
